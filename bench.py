@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Throughput of the TurboQuant KV-cache quantizer hot path on one MI355X.
+
+Workload (one step): encode then decode the whole Qwen3-8B-shaped KV cache,
+36 layers x 8 KV heads x 16384 tokens x head_dim 128, K and V fp16
+(synthetic: N(0,1) entries times per-channel log-normal scales, 2 outlier
+channels per head at 10x), in the block-32 layout (one fp16 norm per 32
+values) at 3 bits (3.5 bits per value).  Inputs are resident in HBM before
+the timed region; each step runs tq_quantize(K), tq_quantize(V),
+tq_dequantize(K), tq_dequantize(V) through the C ABI.
+
+Prints one JSON line.  `value` is fp16 KV GB/s encoded+decoded: fp16 bytes
+read by the encodes plus fp16 bytes written by the decodes, per second.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+LAYERS, KV_HEADS, TOKENS, HEAD_DIM, DT = 36, 8, 16384, 128, 32
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(units: int, bits: int) -> dict:
+    fp16 = units * DT * 2
+    codes = units * DT * bits // 8
+    norms = units * 2
+    return {"fp16": fp16, "compressed": codes + norms, "per_launch": fp16 + codes + norms}
+
+
+def make_cache(tq, torch, dev):
+    import synth
+    from synth import workloads
+
+    rows = LAYERS * KV_HEADS * TOKENS
+    t0 = time.time()
+    w = workloads.qwen3_8b_kv()
+    log(f"generated K/V ({2 * rows * HEAD_DIM * 2 / 2**30:.2f} GiB fp16) in {time.time() - t0:.1f}s")
+    k = torch.from_numpy(w["k"].reshape(rows, HEAD_DIM)).to(dev)
+    v = torch.from_numpy(w["v"].reshape(rows, HEAD_DIM)).to(dev)
+    del w["k"], w["v"]
+    return k, v, w["signs_k"], w["signs_v"], rows
+
+
+class Codec:
+    def __init__(self, tq, torch, dev, rows, bits, signs_k, signs_v):
+        self.tq, self.rows, self.bits = tq, rows, bits
+        self.qk = tq.Quantizer(HEAD_DIM, DT, bits, signs_k)
+        self.qv = tq.Quantizer(HEAD_DIM, DT, bits, signs_v)
+        units = rows * HEAD_DIM // DT
+        self.units = units
+        cb = units * DT * bits // 8
+        self.ck = torch.empty(cb, dtype=torch.uint8, device=dev)
+        self.cv = torch.empty(cb, dtype=torch.uint8, device=dev)
+        self.nk = torch.empty(units, dtype=torch.float16, device=dev)
+        self.nv = torch.empty(units, dtype=torch.float16, device=dev)
+
+    def encode(self, k, v):
+        self.tq.tq_quantize(self.qk, k, self.rows, HEAD_DIM, self.ck, self.nk)
+        self.tq.tq_quantize(self.qv, v, self.rows, HEAD_DIM, self.cv, self.nv)
+
+    def decode(self, ok, ov):
+        self.tq.tq_dequantize(self.qk, self.ck, self.nk, None, None, self.rows, ok, self.tq.TQ_F16, HEAD_DIM)
+        self.tq.tq_dequantize(self.qv, self.cv, self.nv, None, None, self.rows, ov, self.tq.TQ_F16, HEAD_DIM)
+
+
+def time_steps(torch, fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def per_kernel_ms(torch, codec, k, v, ok, ov, reps):
+    """Average duration (ms) of one encode launch and one decode launch, from HIP events
+    recorded on the stream the kernels run on (torch's current stream)."""
+    tq = codec.tq
+    enc, dec = [], []
+    for _ in range(reps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        tq.tq_quantize(codec.qk, k, codec.rows, HEAD_DIM, codec.ck, codec.nk)
+        e[1].record()
+        tq.tq_dequantize(codec.qk, codec.ck, codec.nk, None, None, codec.rows, ok, tq.TQ_F16, HEAD_DIM)
+        e[2].record()
+        torch.cuda.synchronize()
+        enc.append(e[0].elapsed_time(e[1]))
+        dec.append(e[1].elapsed_time(e[2]))
+    enc.sort()
+    dec.sort()
+    return enc[len(enc) // 2], dec[len(dec) // 2], min(enc), min(dec)
+
+
+def cpu_baseline(rows_total: int, bits: int, target_s: float = 15.0) -> dict:
+    """The fp64 oracle (as it stands) on a bounded sample of the same cache: encode + decode of
+    a slice of whole head vectors, timed on the host; reported in the same unit (fp16 GB/s)."""
+    import numpy as np
+
+    import synth
+    from oracle import Codebook, dequantize, quantize
+
+    cb = Codebook.build(bits, DT)
+    signs = synth.signs(0, synth.STREAM_SIGNS_K, DT)
+    rows = 4096
+    x = synth.kv_tensor(0, 1, 1, 0, rows, HEAD_DIM).reshape(rows, HEAD_DIM).astype(np.float64)
+    done_rows, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < target_s:
+        q = quantize(x, signs, cb)
+        dequantize(q["codes"], q["norms"], signs, cb)
+        done_rows += rows
+    dt_s = time.perf_counter() - t0
+    fp16_bytes = done_rows * HEAD_DIM * 2 * 2  # encoded in + decoded out
+    return {"value": fp16_bytes / dt_s / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done_rows} head vectors ({done_rows * HEAD_DIM // DT} blocks) of layer 0 / head 0 K, "
+                      f"encode+decode at {bits} bits, {dt_s:.1f} s single-threaded numpy float64"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this quantizer's hot path has no cross-GPU step, and runs on more "
+              "than one GPU are not part of this build (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import kv_cache_vector_amd as tq
+
+    tq.lib()
+    dev = torch.device("cuda:0")
+    k, v, signs_k, signs_v, rows = make_cache(tq, torch, dev)
+    ok, ov = torch.empty_like(k), torch.empty_like(v)
+
+    results = {}
+    for bits in (3, 4):
+        codec = Codec(tq, torch, dev, rows, bits, signs_k, signs_v)
+
+        def step():
+            codec.encode(k, v)
+            codec.decode(ok, ov)
+
+        ms = time_steps(torch, step, args.steps, args.warmup)
+        enc_ms, dec_ms, enc_min, dec_min = per_kernel_ms(torch, codec, k, v, ok, ov, max(5, args.steps // 2))
+        ab = algorithmic_bytes(codec.units, bits)
+        results[bits] = {"ms": ms, "enc_ms": enc_ms, "dec_ms": dec_ms, "enc_min": enc_min, "dec_min": dec_min,
+                         "bytes": ab, "units": codec.units}
+        log(f"{bits}-bit: step {ms:.3f} ms, encode {enc_ms:.3f} ms ({ab['per_launch'] / enc_ms / 1e6:.0f} GB/s), "
+            f"decode {dec_ms:.3f} ms ({ab['per_launch'] / dec_ms / 1e6:.0f} GB/s)")
+        del codec
+        torch.cuda.empty_cache()
+
+    r = results[3]
+    fp16_bytes_step = 2 * 2 * r["bytes"]["fp16"]  # K and V, encoded and decoded
+    value = fp16_bytes_step / (r["ms"] * 1e-3) / 1e9
+    dom = "decode" if r["dec_ms"] >= r["enc_ms"] else "encode"
+    dom_ms = max(r["dec_ms"], r["enc_ms"])
+    achieved = r["bytes"]["per_launch"] / (dom_ms * 1e-3) / 1e9
+    r4 = results[4]
+    out = {
+        "metric": "fp16 KV GB/s encoded+decoded (fraction of HBM peak); QJL scores/sec",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "qwen3_8b_kv_block32_turbo3", "layers": LAYERS, "kv_heads": KV_HEADS,
+                   "tokens": TOKENS, "head_dim": HEAD_DIM, "block": DT, "bits": 3, "kv_dtype": "f16",
+                   "step": "quantize K, quantize V, dequantize K, dequantize V"},
+        "roofline": {"bound": "hbm", "kernel": f"{dom} (turbo3, one K half-cache per launch)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "fraction_of_hbm_peak": round((2 * 2 * r["bytes"]["per_launch"]) / (r["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "encode": {"turbo3_GBs": round(r["bytes"]["per_launch"] / r["enc_ms"] / 1e6, 1),
+                   "turbo4_GBs": round(r4["bytes"]["per_launch"] / r4["enc_ms"] / 1e6, 1),
+                   "turbo3_blocks_per_s": round(r["units"] / (r["enc_ms"] * 1e-3)),
+                   "turbo3_ms": round(r["enc_ms"], 4), "turbo4_ms": round(r4["enc_ms"], 4)},
+        "decode": {"turbo3_GBs": round(r["bytes"]["per_launch"] / r["dec_ms"] / 1e6, 1),
+                   "turbo4_GBs": round(r4["bytes"]["per_launch"] / r4["dec_ms"] / 1e6, 1),
+                   "turbo3_blocks_per_s": round(r["units"] / (r["dec_ms"] * 1e-3)),
+                   "turbo3_ms": round(r["dec_ms"], 4), "turbo4_ms": round(r4["dec_ms"], 4)},
+        "turbo4_value": round(2 * 2 * r4["bytes"]["fp16"] / (r4["ms"] * 1e-3) / 1e9, 1),
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        out["cpu_baseline"] = cpu_baseline(rows, 3)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,207 @@
+/*
+ * tq.h -- C ABI of libtq, the MI355X (gfx950) TurboQuant KV-cache quantizer.
+ *
+ * Sources (cited by short tag below):
+ *   [Scratch] "TurboQuant From Scratch on Real KV Tensors -- What 3 Bits
+ *             Actually Cost, and Why the Forks Beat the Paper's Layout"
+ *             (www.sotaaz.com/post/turboquant-scratch-en)
+ *   [README]  "turboquant-pytorch" README (github, ringlorn/turboquant-pytorch)
+ *   [Fork]    "TurboQuant KV Cache Quantization (Experimental)",
+ *             llama.cpp-turboquant docs/turboquant.md
+ *   [Blog]    "TurboQuant: 3-Bit Compression with Zero Overhead"
+ *             (cneuralnets.xyz/blog/turboquant)
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are plain HIP device addresses allocated by the caller
+ *     (e.g. torch tensors' data_ptr()).  The library never allocates, frees or
+ *     synchronises on the compute calls; scratch space comes from a caller
+ *     workspace sized with tq_workspace_size().
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Kernels are
+ *     enqueued on it and the call returns without waiting; faults inside a
+ *     kernel surface at the caller's next synchronisation.
+ *   - Arguments are validated on the host before anything is launched.  A
+ *     call that returns anything but TQ_OK has launched nothing, except
+ *     TQ_ERR_HIP, which reports a launch failure.  tq_last_error() gives a
+ *     human-readable reason (per thread).
+ *   - n = 0 rows/keys/tokens is a valid no-op that returns TQ_OK.
+ *   - Non-finite inputs give unspecified (but memory-safe) outputs.
+ *   - Calls are stateless and thread-safe; calls on different streams may
+ *     overlap if their output buffers do not.
+ *
+ * Data layout (all little-endian, row-major):
+ *   A "unit" is a dt-long slice of a head vector: the whole vector
+ *   (dt = head_dim) or one block of the block-32 layout (dt = 32, [Scratch]
+ *   §7, [Fork] "GGML Types").  A row of head_dim elements holds
+ *   head_dim / dt units.
+ *   codes   : [units][dt * bits / 8] bytes.  Each unit is a run of 32-
+ *             coordinate groups; a group is a little-endian bit stream with
+ *             coordinate j at bits [bits*j, bits*j + bits).  The stored
+ *             b-bit code of coordinate i is the sign-magnitude form of its
+ *             bucket index idx (0..2^b-1, ascending centroids): with
+ *             h = 2^(b-1), code = idx - h if idx >= h, else
+ *             2^(b-1) | (h - 1 - idx).
+ *   norms   : [units] of norm_dtype (the unit's L2 norm, [Scratch] §2 step 1).
+ *   qjl_bits: [units][m / 8] bytes, projection i at bit i%8 of byte i/8,
+ *             1 meaning sign(+), i.e. (S r)_i >= 0.
+ *   qjl_rnorm: [units] binary16, the residual norm ||r||.
+ */
+#ifndef TQ_H_
+#define TQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_ERR_INVALID_ARG = 1, /* a pointer, size, stride, alignment or flag is wrong */
+  TQ_ERR_UNSUPPORTED = 2, /* a valid but unimplemented combination */
+  TQ_ERR_WORKSPACE = 3,   /* workspace missing or smaller than tq_workspace_size() */
+  TQ_ERR_HIP = 4          /* the HIP runtime reported an error */
+} tq_status;
+
+typedef enum { TQ_F16 = 0, TQ_F32 = 1 } tq_dtype;
+
+enum {
+  TQ_NORM_CORRECT = 1u, /* rescale the reconstructed direction to unit length ([Scratch] §6) */
+  TQ_QJL = 2u           /* add the 1-bit QJL residual stage ([Scratch] §2, [README]) */
+};
+
+enum { TQ_OP_QJL_SCORES = 1, TQ_OP_DECODE_ATTN = 2 };
+
+/*
+ * Lloyd-Max codebook for a coordinate distributed N(0, 1/dim) ([Scratch] §2
+ * step 3: computed once per bit width, no calibration).  Plain host data.
+ * unit_* are the N(0,1) values; the N(0,1/dim) values are unit_* / sqrt(dim).
+ * Only the first 2^bits centroids and 2^bits - 1 bounds are meaningful.
+ */
+typedef struct {
+  int bits;                     /* 1..4 */
+  int dim;                      /* transform length the codebook is scaled for */
+  double unit_centroids[16];    /* ascending, symmetric about 0 */
+  double unit_bounds[15];       /* midpoints of neighbouring centroids */
+  float centroids[16];          /* fp32(unit_centroids / sqrt(dim)) */
+  float bounds[15];             /* fp32(unit_bounds / sqrt(dim)) */
+  double distortion;            /* E[(X - Q(X))^2] for X ~ N(0,1) */
+} tq_codebook;
+
+/*
+ * Fill *out with the Lloyd-Max quantizer of N(0,1/dim) at `bits` bits.
+ * Host only, float64 fixed-point iteration.  bits in 1..4, dim a power of two
+ * in 2..4096.  Errors: TQ_ERR_INVALID_ARG.
+ */
+tq_status tq_codebook_init(tq_codebook* out, int bits, int dim);
+
+/*
+ * One quantizer (e.g. the key quantizer or the value quantizer of a cache).
+ *   head_dim   elements per input row, a multiple of dt
+ *   dt         transform / normalisation length: 32, 64, 128 or 256
+ *   bits       1..4, must equal cb->bits; cb->dim must equal dt
+ *   flags      TQ_NORM_CORRECT and/or TQ_QJL
+ *   qjl_m      number of QJL projections (TQ_QJL only): 32..256, multiple of 32
+ *   x_dtype    element type of the input rows (TQ_F16 or TQ_F32)
+ *   norm_dtype type of the stored norms (TQ_F16 or TQ_F32)
+ *   cb         host pointer to the codebook
+ *   signs      host pointer, dt values each exactly +1 or -1: the random
+ *              diagonal D of the rotation y = H D u ([Scratch] §2 step 2)
+ *   qjl_params device pointer written by tq_qjl_prepare (TQ_QJL only)
+ */
+typedef struct {
+  int head_dim;
+  int dt;
+  int bits;
+  unsigned flags;
+  int qjl_m;
+  tq_dtype x_dtype;
+  tq_dtype norm_dtype;
+  const tq_codebook* cb;
+  const float* signs;
+  const void* qjl_params;
+} tq_config;
+
+/* Bytes of device memory tq_qjl_prepare writes for (m, dt). */
+size_t tq_qjl_params_size(int m, int dt);
+
+/*
+ * Prepare the QJL projection for cfg: from the host matrix S ([m][dt] fp32,
+ * i.i.d. N(0,1) entries, [README] estimator) compute S~ = S D H in float64 on
+ * the host and copy S~ (float64 and float32 copies) to params_dev
+ * (>= tq_qjl_params_size(m, dt) bytes, 16-byte aligned).  Because H and D
+ * are symmetric involutions, the residual of the unrotated unit vector
+ * projects as S (u - D H c) = S~ (y - c), so the device works in the rotated
+ * domain.  Set-up only: this call synchronises `stream`.
+ */
+tq_status tq_qjl_prepare(const tq_config* cfg, const float* S_host, void* params_dev, size_t params_bytes,
+                         void* stream);
+
+/*
+ * Encode n_rows rows ([Scratch] §2 steps 1-3, [Fork] "How it works"):
+ * per unit n = ||x||, u = x / n, y = H D u, idx_i = #{bounds < y_i} (a value
+ * on an edge goes to the lower cell), codes packed as described above, n
+ * stored as norm_dtype.  With TQ_QJL (dt == head_dim required) also
+ * r = u - D H c[idx], qjl_rnorm = ||r|| and qjl_bits = [S r >= 0].
+ *   x        device, rows of ld_x elements (ld_x >= head_dim); 16-byte
+ *            aligned, ld_x * element size a multiple of 16 bytes
+ *   codes    device, 4-byte aligned, n_rows * head_dim/dt units
+ *   norms    device, aligned to norm_dtype
+ *   qjl_bits, qjl_rnorm  device (TQ_QJL), otherwise ignored
+ * A zero unit stores norm 0 and the codes of idx = 2^(b-1) - 1.
+ */
+tq_status tq_quantize(const tq_config* cfg, const void* x, int64_t n_rows, int64_t ld_x, uint8_t* codes,
+                      void* norms, uint8_t* qjl_bits, void* qjl_rnorm, void* stream);
+
+/*
+ * Decode n_rows rows ([Scratch] §2 "un-rotate", §6 norm correction,
+ * [Fork] "How it works"): c = centroid(code), optional QJL correction
+ * c += sqrt(pi/2) * rnorm / m * S~^T sign (in the rotated domain), optional
+ * norm correction c /= ||c||, then x~ = n * D H c written as y_dtype rows of
+ * stride ld_y (16-byte aligned like x).
+ */
+tq_status tq_dequantize(const tq_config* cfg, const uint8_t* codes, const void* norms, const uint8_t* qjl_bits,
+                        const void* qjl_rnorm, int64_t n_rows, void* y, tq_dtype y_dtype, int64_t ld_y,
+                        void* stream);
+
+/*
+ * QJL inner-product scores ([README] combined estimator):
+ *   scores[i][j] = n_j * ( <q_i, D H c_j> + rnorm_j * sqrt(pi/2)/m * <S q_i, sign_j> )
+ * for n_q query rows (q_dtype, row stride ld_q >= head_dim, head_dim == dt)
+ * against n_k keys encoded with TQ_QJL.  scores: device fp32 [n_q][ld_s],
+ * ld_s >= n_k.  Norm correction is not applied to scores (TQ_NORM_CORRECT
+ * is rejected).  ws: device workspace of tq_workspace_size(TQ_OP_QJL_SCORES,
+ * cfg, n_q, 0, 0) bytes.
+ */
+tq_status tq_qjl_scores(const tq_config* cfg, const void* q, tq_dtype q_dtype, int64_t n_q, int64_t ld_q,
+                        const uint8_t* codes, const void* norms, const uint8_t* qjl_bits, const void* qjl_rnorm,
+                        int64_t n_k, float* scores, int64_t ld_s, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Single-token decode attention over a quantized cache ([Fork] "Fused tile
+ * path": q is rotated once, scores and the value sum are formed in the
+ * rotated domain, one inverse transform per output block):
+ *   out[h] = sum_j softmax_j(scale * <q_h, k~_j>) v~_j
+ * with query head h reading KV head h / (n_q_heads / n_kv_heads).
+ * K and V units are (kv head, token, block) ordered: kcfg/vcfg give their
+ * formats (same head_dim, no QJL, no norm correction).  q: [n_q_heads][head_dim]
+ * of q_dtype; out: device fp32 [n_q_heads][head_dim].  ws: device workspace of
+ * tq_workspace_size(TQ_OP_DECODE_ATTN, kcfg, n_q_heads, n_kv_heads, n_tokens)
+ * bytes.  scale <= 0 selects 1/sqrt(head_dim).
+ */
+tq_status tq_decode_attn(const tq_config* kcfg, const tq_config* vcfg, const void* q, tq_dtype q_dtype,
+                         int n_q_heads, int n_kv_heads, int64_t n_tokens, const uint8_t* k_codes, const void* k_norms,
+                         const uint8_t* v_codes, const void* v_norms, float scale, float* out, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* Workspace bytes for op (TQ_OP_*) with sizes (a, b, c) as described per op; 0 if none. */
+size_t tq_workspace_size(int op, const tq_config* cfg, int64_t a, int64_t b, int64_t c);
+
+const char* tq_status_str(tq_status s);
+const char* tq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H_ */

@@ -1,0 +1,97 @@
+// Device helpers shared by the HIP kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tq {
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Value of v held by lane (lane ^ mask), mask in {1, 2, 4}.  The partner
+// lanes always belong to the same unit, so they are active together.
+__device__ __forceinline__ float lane_xor(float v, int mask) {
+  int iv = __builtin_bit_cast(int, v);
+  int r;
+  if (mask == 1)
+    r = __builtin_amdgcn_mov_dpp(iv, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
+  else if (mask == 2)
+    r = __builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
+  else
+    r = __builtin_amdgcn_ds_swizzle(iv, 0x1F | (4 << 10));   // bitmask swizzle: xor 4 within 32 lanes
+  return __builtin_bit_cast(float, r);
+}
+
+__device__ __forceinline__ double lane_xor(double v, int mask) {
+  uint64_t u = __builtin_bit_cast(uint64_t, v);
+  float lo = __builtin_bit_cast(float, (uint32_t)u), hi = __builtin_bit_cast(float, (uint32_t)(u >> 32));
+  lo = lane_xor(lo, mask);
+  hi = lane_xor(hi, mask);
+  return __builtin_bit_cast(double, (uint64_t)__builtin_bit_cast(uint32_t, lo) |
+                                        ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32));
+}
+
+// Sum of v over the LPU consecutive lanes of a unit (LPU in {1,2,4,8}).
+template <int LPU, typename T>
+__device__ __forceinline__ T unit_sum(T v) {
+#pragma unroll
+  for (int m = 1; m < LPU; m <<= 1) v += lane_xor(v, m);
+  return v;
+}
+
+// In-register Walsh-Hadamard butterflies over the 32 values of one lane
+// (coordinate bits 0..4), unnormalised: (a, b) -> (a + b, a - b).
+template <typename T>
+__device__ __forceinline__ void fwht32_inlane(T* v) {
+#pragma unroll
+  for (int bit = 1; bit < 32; bit <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (!(i & bit)) {
+        T a = v[i], b = v[i | bit];
+        v[i] = a + b;
+        v[i | bit] = a - b;
+      }
+    }
+  }
+}
+
+// Butterflies over coordinate bits 5.. held in lane bits 0.. (LPU lanes per
+// unit): the lane whose bit is clear keeps a + b, its partner keeps a - b.
+template <int LPU, typename T>
+__device__ __forceinline__ void fwht_crosslane(T* v, int q) {
+#pragma unroll
+  for (int m = 1; m < LPU; m <<= 1) {
+    const bool upper = (q & m) != 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      T p = lane_xor(v[i], m);
+      v[i] = upper ? p - v[i] : v[i] + p;
+    }
+  }
+}
+
+// Sign mask of D for the coordinate pair (2i, 2i+1) of a lane's 32-group,
+// placed on the two binary16 sign bits of a packed pair.
+__device__ __forceinline__ uint32_t pair_sign_mask(uint32_t dword, int i) {
+  return (((dword >> (2 * i)) & 1u) << 15) | (((dword >> (2 * i + 1)) & 1u) << 31);
+}
+
+// Place code (BITS wide) of coordinate j into a little-endian group stream.
+template <int BITS>
+__device__ __forceinline__ void put_code(uint32_t* w, int j, uint32_t code) {
+  const int pos = BITS * j;
+  w[pos >> 5] |= code << (pos & 31);
+  if ((pos & 31) + BITS > 32) w[(pos >> 5) + 1] |= code >> (32 - (pos & 31));
+}
+
+template <int BITS>
+__device__ __forceinline__ uint32_t get_code(const uint32_t* w, int j) {
+  const int pos = BITS * j;
+  uint32_t c = w[pos >> 5] >> (pos & 31);
+  if ((pos & 31) + BITS > 32) c |= w[(pos >> 5) + 1] << (32 - (pos & 31));
+  return c & ((1u << BITS) - 1);
+}
+
+}  // namespace tq

@@ -1,0 +1,374 @@
+// Host side of libtq: codebook solver, QJL parameter preparation, argument
+// validation and kernel dispatch for the C ABI declared in include/tq.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "tq_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+tq_status fail(tq_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+tq_status fail(tq_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+tq_status ok() {
+  g_last_error.clear();
+  return TQ_OK;
+}
+
+tq_status hip_fail(hipError_t e, const char* where) {
+  return fail(TQ_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------------------
+// Lloyd-Max for N(0,1) ([Scratch] §2 step 3; [README]: solved once per bit
+// width by numerical integration).  Jacobi iteration of the two optimality
+// conditions (edges at midpoints, levels at conditional means) from a uniform
+// grid on [-3, 3]; the Gaussian is log-concave so the fixed point is unique.
+// ---------------------------------------------------------------------------
+double std_pdf(double x) { return std::isinf(x) ? 0.0 : std::exp(-0.5 * x * x) * 0.39894228040143267794; }
+
+// P(a < X < b) computed from the tail on the far side of zero to avoid cancellation
+double std_mass(double a, double b) {
+  if (a >= 0.0) return 0.5 * (std::erfc(a * M_SQRT1_2) - std::erfc(b * M_SQRT1_2));
+  if (b <= 0.0) return 0.5 * (std::erfc(-b * M_SQRT1_2) - std::erfc(-a * M_SQRT1_2));
+  return 1.0 - 0.5 * std::erfc(-a * M_SQRT1_2) - 0.5 * std::erfc(b * M_SQRT1_2);
+}
+
+void solve_lloyd_max(int bits, double* levels, double* edges, double* distortion) {
+  const int L = 1 << bits;
+  std::vector<double> c(L), t(L - 1), nc(L);
+  for (int i = 0; i < L; ++i) c[i] = -3.0 + 6.0 * (i + 0.5) / L;
+  for (int it = 0; it < 1000000; ++it) {
+    for (int k = 0; k + 1 < L; ++k) t[k] = 0.5 * (c[k] + c[k + 1]);
+    double moved = 0.0;
+    for (int i = 0; i < L; ++i) {
+      double a = i == 0 ? -INFINITY : t[i - 1];
+      double b = i == L - 1 ? INFINITY : t[i];
+      nc[i] = (std_pdf(a) - std_pdf(b)) / std_mass(a, b);
+      moved = std::max(moved, std::fabs(nc[i] - c[i]));
+    }
+    c = nc;
+    if (moved <= 1e-15) break;
+  }
+  for (int i = 0; i < L / 2; ++i) {  // exact symmetry
+    double m = 0.5 * (c[L - 1 - i] - c[i]);
+    c[i] = -m;
+    c[L - 1 - i] = m;
+  }
+  double sum = 0.0;
+  for (int k = 0; k + 1 < L; ++k) t[k] = 0.5 * (c[k] + c[k + 1]);
+  t[L / 2 - 1] = 0.0;
+  for (int i = 0; i < L; ++i) {
+    double a = i == 0 ? -INFINITY : t[i - 1];
+    double b = i == L - 1 ? INFINITY : t[i];
+    sum += std_mass(a, b) * c[i] * c[i];
+  }
+  for (int i = 0; i < L; ++i) levels[i] = c[i];
+  for (int k = 0; k + 1 < L; ++k) edges[k] = t[k];
+  *distortion = 1.0 - sum;
+}
+
+bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+size_t esize(tq_dtype t) { return t == TQ_F32 ? 4 : 2; }
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+tq_status check_config(const tq_config* cfg, const char* who) {
+  if (!cfg) return fail(TQ_ERR_INVALID_ARG, "%s: cfg is NULL", who);
+  if (cfg->dt != 32 && cfg->dt != 64 && cfg->dt != 128 && cfg->dt != 256)
+    return fail(TQ_ERR_INVALID_ARG, "%s: dt must be 32, 64, 128 or 256 (got %d)", who, cfg->dt);
+  if (cfg->head_dim <= 0 || cfg->head_dim % cfg->dt || cfg->head_dim > 65536)
+    return fail(TQ_ERR_INVALID_ARG, "%s: head_dim (%d) must be a positive multiple of dt (%d), <= 65536", who,
+                cfg->head_dim, cfg->dt);
+  if (cfg->bits < 1 || cfg->bits > 4)
+    return fail(TQ_ERR_UNSUPPORTED, "%s: bits must be 1..4 (got %d)", who, cfg->bits);
+  if (!cfg->cb) return fail(TQ_ERR_INVALID_ARG, "%s: codebook is NULL", who);
+  if (cfg->cb->bits != cfg->bits || cfg->cb->dim != cfg->dt)
+    return fail(TQ_ERR_INVALID_ARG, "%s: codebook (bits %d, dim %d) does not match config (bits %d, dt %d)", who,
+                cfg->cb->bits, cfg->cb->dim, cfg->bits, cfg->dt);
+  if (!cfg->signs) return fail(TQ_ERR_INVALID_ARG, "%s: signs is NULL", who);
+  for (int i = 0; i < cfg->dt; ++i)
+    if (cfg->signs[i] != 1.0f && cfg->signs[i] != -1.0f)
+      return fail(TQ_ERR_INVALID_ARG, "%s: signs[%d] = %g is not +1 or -1", who, i, (double)cfg->signs[i]);
+  if (cfg->flags & ~(unsigned)(TQ_NORM_CORRECT | TQ_QJL))
+    return fail(TQ_ERR_INVALID_ARG, "%s: unknown flag bits 0x%x", who, cfg->flags);
+  if ((cfg->x_dtype != TQ_F16 && cfg->x_dtype != TQ_F32) || (cfg->norm_dtype != TQ_F16 && cfg->norm_dtype != TQ_F32))
+    return fail(TQ_ERR_INVALID_ARG, "%s: dtype must be TQ_F16 or TQ_F32", who);
+  if (cfg->flags & TQ_QJL) {
+    if (cfg->head_dim != cfg->dt)
+      return fail(TQ_ERR_UNSUPPORTED, "%s: QJL needs one unit per row (dt == head_dim)", who);
+    if (cfg->qjl_m < 32 || cfg->qjl_m > 256 || cfg->qjl_m % 32)
+      return fail(TQ_ERR_INVALID_ARG, "%s: qjl_m must be a multiple of 32 in 32..256 (got %d)", who, cfg->qjl_m);
+    if (cfg->qjl_m * cfg->dt > 16384)
+      return fail(TQ_ERR_UNSUPPORTED, "%s: QJL needs qjl_m * dt <= 16384 (the projection is staged in 64 KiB of LDS)",
+                  who);
+  }
+  return TQ_OK;
+}
+
+tq_status check_params(const tq_config* cfg, const char* who) {
+  if (!cfg->qjl_params) return fail(TQ_ERR_INVALID_ARG, "%s: qjl_params is NULL (call tq_qjl_prepare)", who);
+  if (!aligned(cfg->qjl_params, 16)) return fail(TQ_ERR_INVALID_ARG, "%s: qjl_params must be 16-byte aligned", who);
+  return TQ_OK;
+}
+
+tq_status check_rows(const char* who, const char* name, const void* p, int64_t n_rows, int64_t ld, int head_dim,
+                     size_t es) {
+  if (!p) return fail(TQ_ERR_INVALID_ARG, "%s: %s is NULL", who, name);
+  if (ld < head_dim) return fail(TQ_ERR_INVALID_ARG, "%s: ld of %s (%lld) < head_dim (%d)", who, name, (long long)ld,
+                                 head_dim);
+  if (!aligned(p, 16) || (ld * (int64_t)es) % 16)
+    return fail(TQ_ERR_INVALID_ARG, "%s: %s must be 16-byte aligned with a row stride that is a multiple of 16 bytes",
+                who, name);
+  if (n_rows > (int64_t)(INT64_MAX / 4) / (ld * (int64_t)es))
+    return fail(TQ_ERR_INVALID_ARG, "%s: %s size overflows", who, name);
+  return TQ_OK;
+}
+
+void fill_dbits(const tq_config& cfg, uint32_t* dbits) {
+  for (int w = 0; w < 8; ++w) dbits[w] = 0;
+  for (int c = 0; c < cfg.dt; ++c)
+    if (cfg.signs[c] < 0.0f) dbits[c / 32] |= 1u << (c % 32);
+}
+
+// N(0,1) centroid of each stored code: code = s << (b-1) | m, with the
+// positive half's m-th level for s = 0 and its negative for s = 1.
+template <typename T>
+void fill_levels(const tq_codebook& cb, T* level) {
+  const int L = 1 << cb.bits, h = L / 2;
+  for (int code = 0; code < 16; ++code) level[code] = 0;
+  for (int code = 0; code < L; ++code) {
+    int s = code >> (cb.bits - 1), m = code & (h - 1);
+    int idx = s ? h - 1 - m : h + m;
+    level[code] = (T)cb.unit_centroids[idx];
+  }
+}
+
+template <typename T>
+void fill_thr(const tq_codebook& cb, T* thr) {
+  const int L = 1 << cb.bits, h = L / 2;
+  for (int k = 0; k < 8; ++k) thr[k] = (T)INFINITY;
+  for (int k = 0; k + 1 < h; ++k) thr[k] = (T)cb.unit_bounds[h + k];  // edges above 0, ascending
+}
+
+void fwht_inplace(double* v, int d) {
+  for (int bit = 1; bit < d; bit <<= 1)
+    for (int i = 0; i < d; ++i)
+      if (!(i & bit)) {
+        double a = v[i], b = v[i | bit];
+        v[i] = a + b;
+        v[i | bit] = a - b;
+      }
+  double s = 1.0 / std::sqrt((double)d);
+  for (int i = 0; i < d; ++i) v[i] *= s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tq_status_str(tq_status s) {
+  switch (s) {
+    case TQ_OK: return "ok";
+    case TQ_ERR_INVALID_ARG: return "invalid argument";
+    case TQ_ERR_UNSUPPORTED: return "unsupported combination";
+    case TQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case TQ_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* tq_last_error(void) { return g_last_error.c_str(); }
+
+tq_status tq_codebook_init(tq_codebook* out, int bits, int dim) {
+  if (!out) return fail(TQ_ERR_INVALID_ARG, "tq_codebook_init: out is NULL");
+  if (bits < 1 || bits > 4) return fail(TQ_ERR_INVALID_ARG, "tq_codebook_init: bits must be 1..4 (got %d)", bits);
+  if (!is_pow2(dim) || dim < 2 || dim > 4096)
+    return fail(TQ_ERR_INVALID_ARG, "tq_codebook_init: dim must be a power of two in 2..4096 (got %d)", dim);
+  std::memset(out, 0, sizeof(*out));
+  out->bits = bits;
+  out->dim = dim;
+  solve_lloyd_max(bits, out->unit_centroids, out->unit_bounds, &out->distortion);
+  const double s = 1.0 / std::sqrt((double)dim);
+  for (int i = 0; i < (1 << bits); ++i) out->centroids[i] = (float)(out->unit_centroids[i] * s);
+  for (int i = 0; i + 1 < (1 << bits); ++i) out->bounds[i] = (float)(out->unit_bounds[i] * s);
+  return ok();
+}
+
+size_t tq_qjl_params_size(int m, int dt) {
+  if (m <= 0 || dt <= 0) return 0;
+  size_t b = (size_t)m * dt * (sizeof(double) + sizeof(float));
+  return (b + 255) & ~(size_t)255;
+}
+
+tq_status tq_qjl_prepare(const tq_config* cfg, const float* S_host, void* params_dev, size_t params_bytes,
+                         void* stream) {
+  tq_status st = check_config(cfg, "tq_qjl_prepare");
+  if (st) return st;
+  if (!(cfg->flags & TQ_QJL)) return fail(TQ_ERR_INVALID_ARG, "tq_qjl_prepare: cfg has no TQ_QJL flag");
+  if (!S_host || !params_dev) return fail(TQ_ERR_INVALID_ARG, "tq_qjl_prepare: NULL pointer");
+  if (!aligned(params_dev, 16)) return fail(TQ_ERR_INVALID_ARG, "tq_qjl_prepare: params_dev must be 16-byte aligned");
+  const int m = cfg->qjl_m, dt = cfg->dt;
+  if (params_bytes < tq_qjl_params_size(m, dt))
+    return fail(TQ_ERR_WORKSPACE, "tq_qjl_prepare: params buffer has %zu bytes, needs %zu", params_bytes,
+                tq_qjl_params_size(m, dt));
+  std::vector<double> s64((size_t)m * dt);
+  std::vector<float> s32((size_t)m * dt);
+  for (int p = 0; p < m; ++p) {
+    double* row = &s64[(size_t)p * dt];
+    for (int j = 0; j < dt; ++j) row[j] = (double)S_host[(size_t)p * dt + j] * (double)cfg->signs[j];
+    fwht_inplace(row, dt);  // (S D H)[p] = H (S D)[p]^T, H symmetric
+    for (int j = 0; j < dt; ++j) s32[(size_t)p * dt + j] = (float)row[j];
+  }
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(params_dev, s64.data(), s64.size() * sizeof(double), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync((char*)params_dev + s64.size() * sizeof(double), s32.data(), s32.size() * sizeof(float),
+                       hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "tq_qjl_prepare");
+  return ok();
+}
+
+tq_status tq_quantize(const tq_config* cfg, const void* x, int64_t n_rows, int64_t ld_x, uint8_t* codes, void* norms,
+                      uint8_t* qjl_bits, void* qjl_rnorm, void* stream) {
+  const char* who = "tq_quantize";
+  tq_status st = check_config(cfg, who);
+  if (st) return st;
+  if (n_rows < 0) return fail(TQ_ERR_INVALID_ARG, "%s: n_rows < 0", who);
+  if (n_rows == 0) return ok();
+  if ((st = check_rows(who, "x", x, n_rows, ld_x, cfg->head_dim, esize(cfg->x_dtype)))) return st;
+  if (!codes || !aligned(codes, 4)) return fail(TQ_ERR_INVALID_ARG, "%s: codes must be non-NULL, 4-byte aligned", who);
+  if (!norms || !aligned(norms, esize(cfg->norm_dtype)))
+    return fail(TQ_ERR_INVALID_ARG, "%s: norms must be non-NULL and aligned to its element size", who);
+  hipStream_t s = (hipStream_t)stream;
+  if (cfg->flags & TQ_QJL) {
+    if ((st = check_params(cfg, who))) return st;
+    if (!qjl_bits || !aligned(qjl_bits, 4) || !qjl_rnorm || !aligned(qjl_rnorm, 2))
+      return fail(TQ_ERR_INVALID_ARG, "%s: QJL needs qjl_bits (4-byte aligned) and qjl_rnorm (2-byte aligned)", who);
+    tq::QjlEncodeArgs a{};
+    a.x = x;
+    a.ld_x = ld_x;
+    a.codes = codes;
+    a.norms = norms;
+    a.qjl_bits = qjl_bits;
+    a.rnorm = (uint16_t*)qjl_rnorm;
+    a.n_units = n_rows;
+    a.s_rot = (const double*)cfg->qjl_params;
+    a.m = cfg->qjl_m;
+    fill_dbits(*cfg, a.dbits);
+    fill_thr(*cfg->cb, a.thr);
+    fill_levels(*cfg->cb, a.level);
+    hipError_t e = tq::launch_qjl_encode(*cfg, a, s);
+    if (e != hipSuccess) return hip_fail(e, who);
+    return ok();
+  }
+  tq::EncodeArgs a{};
+  a.x = x;
+  a.ld_x = ld_x;
+  a.codes = codes;
+  a.norms = norms;
+  a.groups_per_row = cfg->head_dim / 32;
+  a.n_groups = n_rows * a.groups_per_row;
+  a.contiguous = ld_x == cfg->head_dim;
+  fill_dbits(*cfg, a.dbits);
+  fill_thr(*cfg->cb, a.thr);
+  hipError_t e = tq::launch_encode(*cfg, a, s);
+  if (e != hipSuccess) return hip_fail(e, who);
+  return ok();
+}
+
+tq_status tq_dequantize(const tq_config* cfg, const uint8_t* codes, const void* norms, const uint8_t* qjl_bits,
+                        const void* qjl_rnorm, int64_t n_rows, void* y, tq_dtype y_dtype, int64_t ld_y,
+                        void* stream) {
+  const char* who = "tq_dequantize";
+  tq_status st = check_config(cfg, who);
+  if (st) return st;
+  if (y_dtype != TQ_F16 && y_dtype != TQ_F32) return fail(TQ_ERR_INVALID_ARG, "%s: bad y_dtype", who);
+  if (n_rows < 0) return fail(TQ_ERR_INVALID_ARG, "%s: n_rows < 0", who);
+  if (n_rows == 0) return ok();
+  if ((st = check_rows(who, "y", y, n_rows, ld_y, cfg->head_dim, esize(y_dtype)))) return st;
+  if (!codes || !aligned(codes, 4)) return fail(TQ_ERR_INVALID_ARG, "%s: codes must be non-NULL, 4-byte aligned", who);
+  if (!norms || !aligned(norms, esize(cfg->norm_dtype)))
+    return fail(TQ_ERR_INVALID_ARG, "%s: norms must be non-NULL and aligned to its element size", who);
+  hipStream_t s = (hipStream_t)stream;
+  const bool nc = (cfg->flags & TQ_NORM_CORRECT) != 0;
+  if (cfg->flags & TQ_QJL) {
+    if ((st = check_params(cfg, who))) return st;
+    if (!qjl_bits || !aligned(qjl_bits, 4) || !qjl_rnorm || !aligned(qjl_rnorm, 2))
+      return fail(TQ_ERR_INVALID_ARG, "%s: QJL needs qjl_bits (4-byte aligned) and qjl_rnorm (2-byte aligned)", who);
+    tq::QjlDecodeArgs a{};
+    a.codes = codes;
+    a.norms = norms;
+    a.qjl_bits = qjl_bits;
+    a.rnorm = (const uint16_t*)qjl_rnorm;
+    a.m = cfg->qjl_m;
+    a.s_rot = (const float*)((const char*)cfg->qjl_params + (size_t)cfg->qjl_m * cfg->dt * sizeof(double));
+    a.y = y;
+    a.ld_y = ld_y;
+    a.n_units = n_rows;
+    fill_dbits(*cfg, a.dbits);
+    fill_levels(*cfg->cb, a.level);
+    a.qjl_scale = (float)(std::sqrt((double)cfg->dt) * std::sqrt(M_PI / 2.0) / cfg->qjl_m);
+    a.inv_dt = 1.0f / cfg->dt;
+    a.inv_sqrt_dt = (float)(1.0 / std::sqrt((double)cfg->dt));
+    hipError_t e = tq::launch_qjl_decode(*cfg, a, nc, y_dtype, s);
+    if (e != hipSuccess) return hip_fail(e, who);
+    return ok();
+  }
+  tq::DecodeArgs a{};
+  a.codes = codes;
+  a.norms = norms;
+  a.y = y;
+  a.ld_y = ld_y;
+  a.groups_per_row = cfg->head_dim / 32;
+  a.n_groups = n_rows * a.groups_per_row;
+  a.contiguous = ld_y == cfg->head_dim;
+  fill_dbits(*cfg, a.dbits);
+  fill_levels(*cfg->cb, a.level);
+  a.inv_dt = 1.0f / cfg->dt;
+  a.inv_sqrt_dt = (float)(1.0 / std::sqrt((double)cfg->dt));
+  hipError_t e = tq::launch_decode(*cfg, a, nc, y_dtype, s);
+  if (e != hipSuccess) return hip_fail(e, who);
+  return ok();
+}
+
+tq_status tq_qjl_scores(const tq_config* cfg, const void* q, tq_dtype q_dtype, int64_t n_q, int64_t ld_q,
+                        const uint8_t* codes, const void* norms, const uint8_t* qjl_bits, const void* qjl_rnorm,
+                        int64_t n_k, float* scores, int64_t ld_s, void* ws, size_t ws_bytes, void* stream) {
+  (void)cfg; (void)q; (void)q_dtype; (void)n_q; (void)ld_q; (void)codes; (void)norms; (void)qjl_bits;
+  (void)qjl_rnorm; (void)n_k; (void)scores; (void)ld_s; (void)ws; (void)ws_bytes; (void)stream;
+  return fail(TQ_ERR_UNSUPPORTED, "tq_qjl_scores: not available in this build");
+}
+
+tq_status tq_decode_attn(const tq_config* kcfg, const tq_config* vcfg, const void* q, tq_dtype q_dtype,
+                         int n_q_heads, int n_kv_heads, int64_t n_tokens, const uint8_t* k_codes, const void* k_norms,
+                         const uint8_t* v_codes, const void* v_norms, float scale, float* out, void* ws,
+                         size_t ws_bytes, void* stream) {
+  (void)kcfg; (void)vcfg; (void)q; (void)q_dtype; (void)n_q_heads; (void)n_kv_heads; (void)n_tokens; (void)k_codes;
+  (void)k_norms; (void)v_codes; (void)v_norms; (void)scale; (void)out; (void)ws; (void)ws_bytes; (void)stream;
+  return fail(TQ_ERR_UNSUPPORTED, "tq_decode_attn: not available in this build");
+}
+
+size_t tq_workspace_size(int op, const tq_config* cfg, int64_t a, int64_t b, int64_t c) {
+  (void)op; (void)cfg; (void)a; (void)b; (void)c;
+  return 0;
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// Internal declarations shared by the host dispatcher and the HIP kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq.h"
+
+namespace tq {
+
+constexpr int kMaxDt = 256;
+constexpr int kBlock = 256;  // threads per workgroup for the streaming kernels
+
+// Arguments of the encode kernel (one 32-coordinate group per lane).
+struct EncodeArgs {
+  const void* x;
+  int64_t ld_x;            // row stride in elements
+  uint8_t* codes;
+  void* norms;
+  int64_t n_groups;        // rows * head_dim / 32
+  int32_t groups_per_row;  // head_dim / 32
+  int32_t contiguous;      // ld_x == head_dim
+  uint32_t dbits[8];       // D: bit c%32 of word c/32 set when D_c = -1
+  float thr[8];            // positive N(0,1) cell edges t_1 < t_2 < ... (the edge at 0 is implicit)
+};
+
+// Arguments of the decode kernel.
+struct DecodeArgs {
+  const uint8_t* codes;
+  const void* norms;
+  void* y;
+  int64_t ld_y;
+  int64_t n_groups;
+  int32_t groups_per_row;
+  int32_t contiguous;
+  uint32_t dbits[8];
+  float level[16];   // N(0,1) centroid of each stored code (sign-magnitude order)
+  float inv_dt;      // 1 / dt
+  float inv_sqrt_dt; // 1 / sqrt(dt)
+};
+
+// QJL arguments (dt == head_dim, one unit per row).
+struct QjlEncodeArgs {
+  const void* x;
+  int64_t ld_x;
+  uint8_t* codes;
+  void* norms;
+  uint8_t* qjl_bits;
+  uint16_t* rnorm;
+  int64_t n_units;
+  const double* s_rot;  // S~ = S D H, [m][dt] float64
+  uint32_t dbits[8];
+  double thr[8];        // positive N(0,1) cell edges
+  double level[16];     // N(0,1) centroid by stored code
+  int32_t m;
+};
+
+struct QjlDecodeArgs {
+  const uint8_t* codes;
+  const void* norms;
+  const uint8_t* qjl_bits;
+  const uint16_t* rnorm;
+  const float* s_rot;   // S~ [m][dt] float32
+  void* y;
+  int64_t ld_y;
+  int64_t n_units;
+  uint32_t dbits[8];
+  float level[16];
+  int32_t m;
+  float qjl_scale;      // sqrt(dt) * sqrt(pi/2) / m
+  float inv_dt;
+  float inv_sqrt_dt;
+};
+
+// launchers (return hipGetLastError() of the launch)
+hipError_t launch_encode(const tq_config& cfg, const EncodeArgs& a, hipStream_t s);
+hipError_t launch_decode(const tq_config& cfg, const DecodeArgs& a, bool nc, tq_dtype y_dtype, hipStream_t s);
+hipError_t launch_qjl_encode(const tq_config& cfg, const QjlEncodeArgs& a, hipStream_t s);
+hipError_t launch_qjl_decode(const tq_config& cfg, const QjlDecodeArgs& a, bool nc, tq_dtype y_dtype, hipStream_t s);
+
+}  // namespace tq

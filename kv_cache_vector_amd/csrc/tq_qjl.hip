@@ -1,0 +1,296 @@
+// QJL stage kernels for gfx950: encode with the 1-bit residual sketch, and
+// dequantize with the QJL correction ([Scratch] §2 "QJL residual";
+// [README] two-stage description and combined estimator).
+//
+// Encode works in float64 so that the bucket indices and sign bits it
+// decides are exact except within ~1e-15 of an edge: the residual's sign
+// bits sign((S r)_p) are only meaningful to the estimator if they agree
+// with the exact projection.  S~ = S D H (host-prepared) is staged in LDS;
+// because H and D are symmetric involutions, S (u - D H c) = S~ (y - c),
+// so the residual never leaves the rotated domain.
+#include <hip/hip_fp16.h>
+
+#include "tq_device.h"
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+template <int BITS>
+__device__ __forceinline__ uint32_t magnitude_index64(double a, const double* T) {
+  if constexpr (BITS == 1) {
+    return 0u;
+  } else if constexpr (BITS == 2) {
+    return a > T[0] ? 1u : 0u;
+  } else if constexpr (BITS == 3) {
+    const bool c1 = a > T[1];
+    const double t = c1 ? T[2] : T[0];
+    return (c1 ? 2u : 0u) + (a > t ? 1u : 0u);
+  } else {
+    const bool c1 = a > T[3];
+    const double t2 = c1 ? T[5] : T[1];
+    const bool c2 = a > t2;
+    const double lo = c1 ? T[4] : T[0];
+    const double hi = c1 ? T[6] : T[2];
+    const double t3 = c2 ? hi : lo;
+    return (c1 ? 4u : 0u) + (c2 ? 2u : 0u) + (a > t3 ? 1u : 0u);
+  }
+}
+
+template <int BITS, int LPU, bool IN_F32, bool NORM_F32>
+__global__ __launch_bounds__(kBlock) void qjl_encode_kernel(QjlEncodeArgs a, const float* __restrict__ s_rot32) {
+  constexpr int DT = 32 * LPU;
+  extern __shared__ float s_lds[];  // S~ [m][DT] float32
+  const int m = a.m;
+  for (int i = threadIdx.x; i < m * DT; i += kBlock) s_lds[i] = s_rot32[i];
+  __shared__ double lvl[16];
+  if (threadIdx.x < 16) lvl[threadIdx.x] = a.level[threadIdx.x];
+  __syncthreads();
+
+  const int q = (int)(threadIdx.x % LPU);
+  const uint32_t dword = a.dbits[q];
+  const double inv_sqrt_dt = 1.0 / __builtin_sqrt((double)DT);
+  const int64_t n_groups = a.n_units * LPU;
+  const int64_t stride = (int64_t)gridDim.x * kBlock;
+  for (int64_t g0 = (int64_t)blockIdx.x * kBlock; g0 < n_groups; g0 += stride) {
+    const int64_t g = g0 + threadIdx.x;
+    const bool valid = g < n_groups;
+    const int64_t u = g / LPU;
+    double v[32];
+    if (valid) {
+      if constexpr (IN_F32) {
+        const float* p = static_cast<const float*>(a.x) + u * a.ld_x + 32 * q;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) v[j] = (double)p[j];
+      } else {
+        const __half* p = static_cast<const __half*>(a.x) + u * a.ld_x + 32 * q;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) v[j] = (double)__half2float(p[j]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) v[j] = 0.0;
+    }
+    double ss = 0.0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      ss = __builtin_fma(v[j], v[j], ss);
+      if ((dword >> j) & 1u) v[j] = -v[j];
+    }
+    ss = unit_sum<LPU>(ss);
+    const double n = __builtin_sqrt(ss);
+    double T[7];
+#pragma unroll
+    for (int k = 0; k < 7; ++k) T[k] = a.thr[k] * n;
+    fwht32_inlane(v);
+    fwht_crosslane<LPU>(v, q);
+
+    // codes, and the rotated-domain residual e = y - c (unit-vector scale)
+    uint32_t word[BITS];
+#pragma unroll
+    for (int k = 0; k < BITS; ++k) word[k] = 0u;
+    const double yscale = n > 0.0 ? inv_sqrt_dt / n : 0.0;
+    double e[32];
+    double rr = 0.0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const double y = v[j];
+      const uint32_t neg = (y > 0.0) ? 0u : 1u;
+      const uint32_t code = (neg << (BITS - 1)) | magnitude_index64<BITS>(__builtin_fabs(y), T);
+      put_code<BITS>(word, j, code);
+      e[j] = y * yscale - lvl[code] * inv_sqrt_dt;
+      rr = __builtin_fma(e[j], e[j], rr);
+    }
+    rr = unit_sum<LPU>(rr);
+
+    // z_p = sum_i S~[p][i] e_i; bit p = [z_p >= 0]
+    uint32_t sbits[8];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) sbits[w] = 0u;
+    for (int p = 0; p < m; ++p) {
+      const float* row = s_lds + p * DT + 32 * q;
+      double part = 0.0;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) part = __builtin_fma((double)row[j], e[j], part);
+      part = unit_sum<LPU>(part);
+      if (part >= 0.0) sbits[p >> 5] |= 1u << (p & 31);
+    }
+    if (valid) {
+      uint32_t* cp = reinterpret_cast<uint32_t*>(a.codes + g * (4 * BITS));
+#pragma unroll
+      for (int k = 0; k < BITS; ++k) cp[k] = word[k];
+      uint32_t* bp = reinterpret_cast<uint32_t*>(a.qjl_bits) + u * (m / 32);
+      for (int w = q; w < m / 32; w += LPU) bp[w] = sbits[w];
+      if (q == 0) {
+        if constexpr (NORM_F32)
+          static_cast<float*>(a.norms)[u] = (float)n;
+        else
+          static_cast<__half*>(a.norms)[u] = __float2half_rn((float)n);
+        a.rnorm[u] = __half_as_ushort(__float2half_rn((float)__builtin_sqrt(rr)));
+      }
+    }
+  }
+}
+
+template <int BITS, int LPU, bool OUT_F32, bool NORM_F32, bool NC>
+__global__ __launch_bounds__(kBlock) void qjl_decode_kernel(QjlDecodeArgs a) {
+  constexpr int DT = 32 * LPU;
+  extern __shared__ float s_lds[];  // S~ [m][DT] float32
+  const int m = a.m;
+  for (int i = threadIdx.x; i < m * DT; i += kBlock) s_lds[i] = a.s_rot[i];
+  __shared__ float lut[16];
+  if (threadIdx.x < 16) lut[threadIdx.x] = a.level[threadIdx.x];
+  __syncthreads();
+  const int q = (int)(threadIdx.x % LPU);
+  const uint32_t dword = a.dbits[q];
+  const int64_t n_groups = a.n_units * LPU;
+  const int64_t stride = (int64_t)gridDim.x * kBlock;
+  for (int64_t g0 = (int64_t)blockIdx.x * kBlock; g0 < n_groups; g0 += stride) {
+    const int64_t g = g0 + threadIdx.x;
+    const bool valid = g < n_groups;
+    const int64_t u = g / LPU;
+    uint32_t word[BITS];
+    uint32_t sb[8];
+    float n = 0.0f, rho = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) sb[w] = 0u;
+    if (valid) {
+      const uint32_t* cp = reinterpret_cast<const uint32_t*>(a.codes + g * (4 * BITS));
+#pragma unroll
+      for (int k = 0; k < BITS; ++k) word[k] = cp[k];
+      const uint32_t* bp = reinterpret_cast<const uint32_t*>(a.qjl_bits) + u * (m / 32);
+      for (int w = 0; w < m / 32; ++w) sb[w] = bp[w];
+      if constexpr (NORM_F32)
+        n = static_cast<const float*>(a.norms)[u];
+      else
+        n = __half2float(static_cast<const __half*>(a.norms)[u]);
+      rho = __half2float(__ushort_as_half(a.rnorm[u]));
+    } else {
+#pragma unroll
+      for (int k = 0; k < BITS; ++k) word[k] = 0u;
+    }
+    float v[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) v[j] = lut[get_code<BITS>(word, j)];
+    // QJL correction in the rotated domain, in the N(0,1)-per-coordinate scale:
+    // c += sqrt(dt) * sqrt(pi/2) * rho / m * (S~^T sigma)
+    const float cs = a.qjl_scale * rho;
+    float corr[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) corr[j] = 0.0f;
+    for (int p = 0; p < m; ++p) {
+      const float sg = ((sb[p >> 5] >> (p & 31)) & 1u) ? 1.0f : -1.0f;
+      const float* row = s_lds + p * DT + 32 * q;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) corr[j] = __builtin_fmaf(row[j], sg, corr[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 32; ++j) v[j] = __builtin_fmaf(cs, corr[j], v[j]);
+    float scale;
+    if constexpr (NC) {
+      float ss = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) ss = __builtin_fmaf(v[j], v[j], ss);
+      ss = unit_sum<LPU>(ss);
+      scale = n * a.inv_sqrt_dt / __builtin_sqrtf(ss);
+    } else {
+      scale = n * a.inv_dt;
+    }
+    fwht32_inlane(v);
+    fwht_crosslane<LPU>(v, q);
+    if (!valid) continue;
+    if constexpr (OUT_F32) {
+      float* p = static_cast<float*>(a.y) + u * a.ld_y + 32 * q;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) p[j] = ((dword >> j) & 1u) ? -(v[j] * scale) : v[j] * scale;
+    } else {
+      __half* p = static_cast<__half*>(a.y) + u * a.ld_y + 32 * q;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const float o = v[j] * scale;
+        p[j] = __float2half_rn(((dword >> j) & 1u) ? -o : o);
+      }
+    }
+  }
+}
+
+int64_t qjl_grid(int64_t n_groups) {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
+      cus = prop.multiProcessorCount;
+    if (cus <= 0) cus = 256;
+  }
+  int64_t need = (n_groups + kBlock - 1) / kBlock;
+  int64_t cap = (int64_t)cus * 4;
+  return need < cap ? need : cap;
+}
+
+template <int BITS, int LPU>
+hipError_t qjl_encode_dispatch(const tq_config& cfg, const QjlEncodeArgs& a, hipStream_t s) {
+  const float* s32 = reinterpret_cast<const float*>(a.s_rot + (size_t)a.m * 32 * LPU);
+  const size_t lds = (size_t)a.m * 32 * LPU * sizeof(float);
+  dim3 grid((unsigned)qjl_grid(a.n_units * LPU)), block(kBlock);
+  const bool in32 = cfg.x_dtype == TQ_F32, n32 = cfg.norm_dtype == TQ_F32;
+  if (!in32 && !n32) hipLaunchKernelGGL((qjl_encode_kernel<BITS, LPU, false, false>), grid, block, lds, s, a, s32);
+  if (!in32 && n32) hipLaunchKernelGGL((qjl_encode_kernel<BITS, LPU, false, true>), grid, block, lds, s, a, s32);
+  if (in32 && !n32) hipLaunchKernelGGL((qjl_encode_kernel<BITS, LPU, true, false>), grid, block, lds, s, a, s32);
+  if (in32 && n32) hipLaunchKernelGGL((qjl_encode_kernel<BITS, LPU, true, true>), grid, block, lds, s, a, s32);
+  return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t qjl_encode_lpu(const tq_config& cfg, const QjlEncodeArgs& a, hipStream_t s) {
+  switch (cfg.dt) {
+    case 32: return qjl_encode_dispatch<BITS, 1>(cfg, a, s);
+    case 64: return qjl_encode_dispatch<BITS, 2>(cfg, a, s);
+    case 128: return qjl_encode_dispatch<BITS, 4>(cfg, a, s);
+    default: return qjl_encode_dispatch<BITS, 8>(cfg, a, s);
+  }
+}
+
+template <int BITS, int LPU, bool NC>
+hipError_t qjl_decode_dispatch(const tq_config& cfg, const QjlDecodeArgs& a, tq_dtype yt, hipStream_t s) {
+  const size_t lds = (size_t)a.m * 32 * LPU * sizeof(float);
+  dim3 grid((unsigned)qjl_grid(a.n_units * LPU)), block(kBlock);
+  const bool o32 = yt == TQ_F32, n32 = cfg.norm_dtype == TQ_F32;
+  if (!o32 && !n32) hipLaunchKernelGGL((qjl_decode_kernel<BITS, LPU, false, false, NC>), grid, block, lds, s, a);
+  if (!o32 && n32) hipLaunchKernelGGL((qjl_decode_kernel<BITS, LPU, false, true, NC>), grid, block, lds, s, a);
+  if (o32 && !n32) hipLaunchKernelGGL((qjl_decode_kernel<BITS, LPU, true, false, NC>), grid, block, lds, s, a);
+  if (o32 && n32) hipLaunchKernelGGL((qjl_decode_kernel<BITS, LPU, true, true, NC>), grid, block, lds, s, a);
+  return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t qjl_decode_lpu(const tq_config& cfg, const QjlDecodeArgs& a, bool nc, tq_dtype yt, hipStream_t s) {
+  switch (cfg.dt) {
+    case 32: return nc ? qjl_decode_dispatch<BITS, 1, true>(cfg, a, yt, s) : qjl_decode_dispatch<BITS, 1, false>(cfg, a, yt, s);
+    case 64: return nc ? qjl_decode_dispatch<BITS, 2, true>(cfg, a, yt, s) : qjl_decode_dispatch<BITS, 2, false>(cfg, a, yt, s);
+    case 128: return nc ? qjl_decode_dispatch<BITS, 4, true>(cfg, a, yt, s) : qjl_decode_dispatch<BITS, 4, false>(cfg, a, yt, s);
+    default: return nc ? qjl_decode_dispatch<BITS, 8, true>(cfg, a, yt, s) : qjl_decode_dispatch<BITS, 8, false>(cfg, a, yt, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_qjl_encode(const tq_config& cfg, const QjlEncodeArgs& a, hipStream_t s) {
+  switch (cfg.bits) {
+    case 1: return qjl_encode_lpu<1>(cfg, a, s);
+    case 2: return qjl_encode_lpu<2>(cfg, a, s);
+    case 3: return qjl_encode_lpu<3>(cfg, a, s);
+    default: return qjl_encode_lpu<4>(cfg, a, s);
+  }
+}
+
+hipError_t launch_qjl_decode(const tq_config& cfg, const QjlDecodeArgs& a, bool nc, tq_dtype y_dtype, hipStream_t s) {
+  switch (cfg.bits) {
+    case 1: return qjl_decode_lpu<1>(cfg, a, nc, y_dtype, s);
+    case 2: return qjl_decode_lpu<2>(cfg, a, nc, y_dtype, s);
+    case 3: return qjl_decode_lpu<3>(cfg, a, nc, y_dtype, s);
+    default: return qjl_decode_lpu<4>(cfg, a, nc, y_dtype, s);
+  }
+}
+
+}  // namespace tq

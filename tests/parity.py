@@ -1,0 +1,97 @@
+"""Comparison helpers for GPU-vs-oracle parity (test infrastructure).
+
+Tolerances (the spec criteria for this quantizer, read as follows):
+  * codes: bit-exact except coordinates whose oracle value sqrt(dt)*y lies
+    within BAND = 1e-6 of a cell edge (0 included); there the GPU code must be
+    one of the two cells next to that edge.  The in-band fraction is reported.
+  * QJL sign bits: bit-exact except projections with |z| < 1e-6 * rho (z is
+    N(0, rho^2) for S with N(0,1) entries, so this is the same 1e-6-of-sigma
+    band as for the codes).
+  * norms: fp16 within 1 ulp of the oracle's fp16(n); fp32 within 2 ulp.
+  * dequantized values: |x~_gpu - x~_orc| / n <= 1e-5 on fp32 output (n the
+    stored norm both sides use); fp16 output within 1 fp16 ulp of the oracle's
+    value rounded to fp16.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import code_to_index, unpack_codes, unpack_sign_bits
+
+BAND = 1e-6
+
+
+def edge_distance(y_unit: np.ndarray, cb) -> np.ndarray:
+    edges = np.asarray(cb.unit_bounds, dtype=np.float64)
+    return np.min(np.abs(y_unit[..., None] - edges), axis=-1)
+
+
+def check_codes(gpu_codes: np.ndarray, orc: dict, cb, bits: int, dt: int) -> dict:
+    g = unpack_codes(gpu_codes.reshape(-1, dt * bits // 8), bits, dt)
+    o = unpack_codes(orc["codes"], bits, dt)
+    dist = edge_distance(orc["y_unit"], cb)
+    in_band = dist < BAND
+    mism = g != o
+    out_of_band = mism & ~in_band
+    gi, oi = code_to_index(g, bits), code_to_index(o, bits)
+    assert not out_of_band.any(), (
+        f"{int(out_of_band.sum())} code mismatches outside the band; first at {np.argwhere(out_of_band)[:5].tolist()}, "
+        f"gpu idx {gi[out_of_band][:5].tolist()} oracle idx {oi[out_of_band][:5].tolist()} "
+        f"dist {dist[out_of_band][:5].tolist()}")
+    assert np.all(np.abs(gi[mism] - oi[mism]) <= 1), "in-band mismatch is not a neighbouring cell"
+    return {"coords": int(g.size), "in_band": int(in_band.sum()), "in_band_mismatch": int(mism.sum())}
+
+
+def f16_ulp_diff(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """|a - b| in units of binary16 ulps (monotone integer mapping of the bit patterns)."""
+    def key(x):
+        u = np.asarray(x, dtype=np.float16).view(np.uint16).astype(np.int32)
+        return np.where(u & 0x8000, -(u & 0x7FFF), u)
+    return np.abs(key(a) - key(b))
+
+
+def f32_ulp_diff(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    def key(x):
+        u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.int64)
+        return np.where(u & 0x80000000, -(u & 0x7FFFFFFF), u)
+    return np.abs(key(a) - key(b))
+
+
+def check_norms(gpu_norms: np.ndarray, orc_norms: np.ndarray) -> dict:
+    if orc_norms.dtype == np.float16:
+        d = f16_ulp_diff(gpu_norms, orc_norms)
+        assert d.max(initial=0) <= 1, f"fp16 norms differ by {d.max()} ulp"
+    else:
+        d = f32_ulp_diff(gpu_norms, orc_norms)
+        assert d.max(initial=0) <= 2, f"fp32 norms differ by {d.max()} ulp"
+    return {"norms": int(d.size), "norm_ulp_mismatch": int((d > 0).sum())}
+
+
+def check_decoded_f32(gpu: np.ndarray, orc: np.ndarray, norms: np.ndarray, dt: int, tol: float = 1e-5) -> float:
+    g = gpu.reshape(-1, dt).astype(np.float64)
+    o = orc.reshape(-1, dt)
+    n = np.asarray(norms, dtype=np.float64).reshape(-1)
+    safe = np.where(n > 0, n, 1.0)
+    err = np.abs(g - o) / safe[:, None]
+    err[n == 0] = np.abs(g[n == 0] - o[n == 0])
+    worst = float(err.max(initial=0.0))
+    assert worst <= tol, f"decoded values differ by {worst:.3g} (relative to the unit norm)"
+    return worst
+
+
+def check_decoded_f16(gpu: np.ndarray, orc: np.ndarray) -> int:
+    d = f16_ulp_diff(gpu.reshape(-1), orc.reshape(-1).astype(np.float16))
+    assert d.max(initial=0) <= 1, f"fp16 outputs differ by {d.max()} ulp"
+    return int((d > 0).sum())
+
+
+def check_sign_bits(gpu_bits: np.ndarray, orc: dict, m: int) -> dict:
+    g = unpack_sign_bits(gpu_bits.reshape(-1, m // 8), m)
+    o = unpack_sign_bits(orc["qjl_bits"], m)
+    z = orc["z"]
+    rho = orc["rho_exact"][:, None]
+    in_band = np.abs(z) < BAND * rho
+    mism = g != o
+    bad = mism & ~in_band
+    assert not bad.any(), f"{int(bad.sum())} sign-bit mismatches outside the band; |z|/rho = {(np.abs(z)/rho)[bad][:5]}"
+    return {"bits": int(g.size), "in_band": int(in_band.sum()), "in_band_mismatch": int(mism.sum())}

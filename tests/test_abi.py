@@ -1,0 +1,126 @@
+"""C ABI checks that need no GPU: the library loads and exports every symbol
+include/tq.h declares, the host codebook solver agrees with the oracle, and
+argument validation rejects bad calls before anything is launched."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import kv_cache_vector_amd as tq
+from oracle import Codebook
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+FAKE = 0x100000  # an aligned, never-dereferenced address: every call below fails validation first
+
+
+def _declared():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            names |= set(re.findall(r"^\s*(?:tq_status|size_t|const char\*)\s+(tq_\w+)\s*\(", text, re.M))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert {"tq_codebook_init", "tq_quantize", "tq_dequantize", "tq_qjl_scores", "tq_decode_attn"} <= names
+    lib = ctypes.CDLL(tq.LIB_PATH)
+    for n in sorted(names):
+        assert hasattr(lib, n), n
+    assert names == set(tq.EXPORTED)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("dim", [32, 64, 128, 256])
+def test_host_codebook_matches_oracle(bits, dim):
+    cb = tq.tq_codebook_init(bits, dim)
+    orc = Codebook.build(bits, dim)
+    L = 1 << bits
+    np.testing.assert_allclose(np.array(cb.unit_centroids[:L]), orc.unit_levels, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(np.array(cb.unit_bounds[:L - 1]), orc.unit_bounds, atol=1e-12, rtol=0)
+    np.testing.assert_array_equal(np.array(cb.centroids[:L], dtype=np.float32), orc.levels.astype(np.float32))
+    np.testing.assert_array_equal(np.array(cb.bounds[:L - 1], dtype=np.float32), orc.bounds.astype(np.float32))
+    assert cb.distortion == pytest.approx(orc.distortion, abs=1e-12)
+
+
+def test_codebook_init_rejects_bad_arguments():
+    cb = tq.tq_codebook()
+    L = tq.lib()
+    assert L.tq_codebook_init(ctypes.byref(cb), 0, 32) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_codebook_init(ctypes.byref(cb), 5, 32) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_codebook_init(ctypes.byref(cb), 3, 48) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_codebook_init(None, 3, 32) == tq.TQ_ERR_INVALID_ARG
+
+
+def _q(**kw):
+    args = dict(head_dim=128, dt=32, bits=3, signs=np.ones(kw.get("dt", 32)))
+    args.update(kw)
+    return tq.Quantizer(**args)
+
+
+def _quantize(qz, x=FAKE, n_rows=4, ld=None, codes=FAKE, norms=FAKE, bits=None, rnorm=None):
+    ld = qz.cfg.head_dim if ld is None else ld
+    return tq.lib().tq_quantize(ctypes.byref(qz.cfg), x, n_rows, ld, codes, norms, bits, rnorm, None)
+
+
+def test_quantize_validation():
+    E, U, OK = tq.TQ_ERR_INVALID_ARG, tq.TQ_ERR_UNSUPPORTED, tq.TQ_OK
+    qz = _q()
+    assert _quantize(qz, n_rows=0) == OK  # empty input is a no-op
+    assert _quantize(qz, n_rows=-1) == E
+    assert _quantize(qz, x=None) == E
+    assert _quantize(qz, x=FAKE + 2) == E  # misaligned rows
+    assert _quantize(qz, ld=100) == E  # stride below head_dim
+    assert _quantize(qz, ld=132) == E  # stride not a multiple of 16 bytes
+    assert _quantize(qz, codes=FAKE + 2) == E
+    assert _quantize(qz, norms=None) == E
+    assert _quantize(qz, n_rows=1 << 60) == E  # size overflow
+    bad = _q()
+    bad.cfg.bits = 5
+    assert _quantize(bad) == U
+    bad = _q()
+    bad.cfg.dt = 48
+    assert _quantize(bad) == E
+    assert _quantize(_q(head_dim=96, dt=64, signs=np.ones(64))) == E
+    s = np.ones(32)
+    s[3] = 0.5
+    assert _quantize(_q(signs=s)) == E
+    bad = _q()
+    bad.cfg.flags = 8
+    assert _quantize(bad) == E
+    bad = _q()
+    bad.cfg.bits = 4  # codebook built for 3 bits
+    assert _quantize(bad) == E
+    assert _quantize(_q(flags=tq.TQ_QJL, qjl_m=128)) == U  # QJL needs dt == head_dim
+    qj = _q(head_dim=128, dt=128, bits=2, signs=np.ones(128), flags=tq.TQ_QJL, qjl_m=128)
+    assert _quantize(qj, bits=FAKE, rnorm=FAKE) == E  # no prepared parameters
+    qj.cfg.qjl_params = FAKE
+    assert _quantize(qj) == E  # no sign-bit / residual-norm outputs
+    qj.cfg.qjl_m = 100
+    assert _quantize(qj, bits=FAKE, rnorm=FAKE) == E
+    assert "qjl_m" in tq.lib().tq_last_error().decode()
+
+
+def test_dequantize_validation():
+    E, OK = tq.TQ_ERR_INVALID_ARG, tq.TQ_OK
+    qz = _q()
+    L = tq.lib()
+    call = lambda **k: L.tq_dequantize(ctypes.byref(qz.cfg), k.get("codes", FAKE), k.get("norms", FAKE), None, None,
+                                       k.get("n", 4), k.get("y", FAKE), k.get("yt", tq.TQ_F16), k.get("ld", 128), None)
+    assert call(n=0) == OK
+    assert call(yt=7) == E
+    assert call(y=None) == E
+    assert call(y=FAKE + 8) == E
+    assert call(ld=64) == E
+    assert call(codes=None) == E
+
+
+def test_status_strings():
+    L = tq.lib()
+    assert L.tq_status_str(tq.TQ_OK) == b"ok"
+    assert L.tq_status_str(tq.TQ_ERR_WORKSPACE).startswith(b"workspace")
+    assert L.tq_status_str(99) == b"unknown status"

@@ -1,0 +1,192 @@
+"""GPU parity of tq_quantize / tq_dequantize (no QJL) against the oracle.
+
+Every case runs the HIP path through the C ABI and the oracle on the same
+seeded inputs; decode parity runs the oracle on the GPU's own codes and norms.
+Sizes span several workgroups plus a ragged tail; the matrix covers every
+transform length, bit width, input/norm dtype and output dtype.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import Codebook, dequantize, quantize
+from tests.parity import check_codes, check_decoded_f16, check_decoded_f32, check_norms
+
+torch = pytest.importorskip("torch")
+import kv_cache_vector_amd as tq  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _run_encode(qz, x_np, ld=None):
+    """Encode rows x_np [n_rows, head_dim] (float16/float32) on the GPU; returns (codes, norms) as numpy."""
+    cfg = qz.cfg
+    n_rows, hd = x_np.shape
+    ld = hd if ld is None else ld
+    host = np.zeros((n_rows, ld), dtype=x_np.dtype)
+    host[:, :hd] = x_np
+    x = torch.from_numpy(host).to(DEV)
+    units = n_rows * qz.units_per_row
+    codes = torch.full((units * qz.code_bytes(),), 0xA5, dtype=torch.uint8, device=DEV)
+    norms = torch.full((units,), -7.0, dtype=torch.float32 if cfg.norm_dtype == tq.TQ_F32 else torch.float16,
+                       device=DEV)
+    tq.tq_quantize(qz, x, n_rows, ld, codes, norms)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), norms.cpu().numpy()
+
+
+def _run_decode(qz, codes_np, norms_np, n_rows, y_dtype, ld=None):
+    hd = qz.cfg.head_dim
+    ld = hd if ld is None else ld
+    codes = torch.from_numpy(codes_np).to(DEV)
+    norms = torch.from_numpy(norms_np).to(DEV)
+    y = torch.full((n_rows, ld), 1234.0, dtype=torch.float32 if y_dtype == tq.TQ_F32 else torch.float16, device=DEV)
+    tq.tq_dequantize(qz, codes, norms, None, None, n_rows, y, y_dtype, ld)
+    torch.cuda.synchronize()
+    out = y.cpu().numpy()
+    if ld > hd:
+        assert np.all(out[:, hd:] == 1234.0), "decode wrote outside the rows"
+    return out[:, :hd]
+
+
+def _roundtrip(x_np, dt, bits, seed, x_dtype, norm_dtype, nc=False, ld=None, y_dtypes=(tq.TQ_F32, tq.TQ_F16)):
+    n_rows, hd = x_np.shape
+    signs = synth.signs(seed, 2, dt)
+    qz = tq.Quantizer(hd, dt, bits, signs, flags=tq.TQ_NORM_CORRECT if nc else 0, x_dtype=x_dtype,
+                      norm_dtype=norm_dtype)
+    cb = Codebook.build(bits, dt)
+    codes, norms = _run_encode(qz, x_np, ld)
+    orc = quantize(x_np.astype(np.float64), signs, cb, norm_dtype=np.float32 if norm_dtype == tq.TQ_F32 else np.float16)
+    stats = check_codes(codes, orc, cb, bits, dt)
+    stats.update(check_norms(norms, orc["norms"]))
+    ref = dequantize(codes.reshape(-1, dt * bits // 8), norms, signs, cb, nc=nc)
+    for yt in y_dtypes:
+        y = _run_decode(qz, codes, norms, n_rows, yt, ld)
+        if yt == tq.TQ_F32:
+            stats["decode_err"] = check_decoded_f32(y, ref, norms, dt)
+        else:
+            stats["f16_ulp_off"] = check_decoded_f16(y, ref)
+    return stats, codes, norms, orc
+
+
+@pytest.mark.parametrize("dt", [32, 64, 128, 256])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_matrix_f16(dt, bits):
+    hd = max(dt, 128)
+    n_rows = 333  # several workgroups of groups plus a ragged tail
+    x = synth.kv_tensor(dt + bits, 1, 1, 0, n_rows, hd).reshape(n_rows, hd)
+    stats, *_ = _roundtrip(x, dt, bits, seed=dt * 10 + bits, x_dtype=tq.TQ_F16, norm_dtype=tq.TQ_F16)
+    print(stats)
+
+
+@pytest.mark.parametrize("dt", [32, 128])
+@pytest.mark.parametrize("bits", [2, 3])
+def test_matrix_f32_strided(dt, bits):
+    hd, n_rows = 256, 129
+    x = synth.normal_f32(7, 0, n_rows * hd).reshape(n_rows, hd) * 3.0
+    stats, *_ = _roundtrip(x, dt, bits, seed=5, x_dtype=tq.TQ_F32, norm_dtype=tq.TQ_F32, ld=hd + 4)
+    print(stats)
+
+
+def test_vectors_fp32_config_and_mse():
+    """4096 x 128 fp32 N(0,1), 3 bits, one fp32 norm per vector; MSE of the unit vectors ~ 0.034."""
+    from synth.workloads import vectors_fp32
+
+    w = vectors_fp32()
+    x = w["x"]
+    qz = tq.Quantizer(128, 128, 3, w["signs"], x_dtype=tq.TQ_F32, norm_dtype=tq.TQ_F32)
+    cb = Codebook.build(3, 128)
+    codes, norms = _run_encode(qz, x)
+    orc = quantize(x.astype(np.float64), w["signs"], cb, norm_dtype=np.float32)
+    check_codes(codes, orc, cb, 3, 128)
+    check_norms(norms, orc["norms"])
+    y = _run_decode(qz, codes, norms, len(x), tq.TQ_F32)
+    ref = dequantize(codes.reshape(-1, 48), norms, w["signs"], cb)
+    check_decoded_f32(y, ref, norms, 128)
+    u = x.astype(np.float64) / np.linalg.norm(x.astype(np.float64), axis=1, keepdims=True)
+    mse = np.mean(np.sum((u - y.astype(np.float64) / norms[:, None]) ** 2, axis=1))
+    assert mse == pytest.approx(0.034, abs=0.001)
+
+
+def test_norm_correction_llama_shape():
+    """head_dim 64, 4 bits, per-vector norm + norm correction (small slice of the Llama-3.2-1B-shaped cache)."""
+    from synth.workloads import llama_1b_kv
+
+    w = llama_1b_kv(layers=2, heads=8, tokens=300)
+    for half, s in (("k", "signs_k"), ("v", "signs_v")):
+        x = w[half].reshape(-1, 64)
+        stats, codes, norms, _ = _roundtrip(x, 64, 4, seed=0, x_dtype=tq.TQ_F16, norm_dtype=tq.TQ_F16, nc=True)
+        qz = tq.Quantizer(64, 64, 4, w[s], flags=tq.TQ_NORM_CORRECT)
+        y = _run_decode(qz, codes, norms, len(x), tq.TQ_F32)
+        lengths = np.linalg.norm(y.astype(np.float64), axis=1)
+        np.testing.assert_allclose(lengths, norms.astype(np.float64), rtol=2e-6)
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_block32_qwen_shape(bits):
+    """Block-32 layout on a slice of the Qwen3-8B-shaped cache (outlier channels)."""
+    from synth.workloads import qwen3_8b_kv
+
+    w = qwen3_8b_kv(layers=2, heads=2, tokens=1000)
+    for half, s in (("k", "signs_k"), ("v", "signs_v")):
+        x = w[half].reshape(-1, 128)
+        stats, *_ = _roundtrip(x, 32, bits, seed=0, x_dtype=tq.TQ_F16, norm_dtype=tq.TQ_F16)
+        print(half, stats)
+
+
+def test_edge_cases():
+    hd, dt = 128, 32
+    x = np.zeros((70, hd), dtype=np.float16)
+    x[1] = 1.0  # all-equal
+    x[2, 0] = 1.0  # one-hot
+    x[3] = np.float16(6.0e-8)  # subnormal magnitude
+    x[4] = np.float16(2000.0)  # large entries (norm 2.3e4, still a finite fp16)
+    x[5, ::2] = -2.5
+    x[6] = synth.normal_f16(1, 0, hd)
+    x[7:] = synth.normal_f16(2, 0, 63 * hd).reshape(63, hd)
+    for bits in (1, 2, 3, 4):
+        signs = synth.signs(9, 2, dt)
+        qz = tq.Quantizer(hd, dt, bits, signs)
+        cb = Codebook.build(bits, dt)
+        codes, norms = _run_encode(qz, x)
+        orc = quantize(x.astype(np.float64), signs, cb)
+        # structured rows hit cell edges exactly: only neighbouring cells are accepted there
+        check_codes(codes, orc, cb, bits, dt)
+        check_norms(norms, orc["norms"])
+        # a zero row stores norm 0 and decodes to zeros
+        assert np.all(norms[:4] == 0)
+        y = _run_decode(qz, codes, norms, len(x), tq.TQ_F32)
+        assert np.all(y[0] == 0)
+        ref = dequantize(codes.reshape(-1, dt * bits // 8), norms, signs, cb)
+        check_decoded_f32(y, ref, norms, dt)
+
+
+def test_empty_input_is_noop():
+    qz = tq.Quantizer(128, 32, 3, np.ones(32))
+    codes = torch.full((16,), 7, dtype=torch.uint8, device=DEV)
+    norms = torch.zeros(4, dtype=torch.float16, device=DEV)
+    x = torch.zeros((1, 128), dtype=torch.float16, device=DEV)
+    tq.tq_quantize(qz, x, 0, 128, codes, norms)
+    torch.cuda.synchronize()
+    assert torch.all(codes == 7)
+
+
+def test_deterministic_repeat():
+    from synth.workloads import qwen3_8b_kv
+
+    w = qwen3_8b_kv(layers=1, heads=2, tokens=2048)
+    x = torch.from_numpy(w["k"].reshape(-1, 128)).to(DEV)
+    qz = tq.Quantizer(128, 32, 3, w["signs_k"])
+    n = x.shape[0]
+    outs = []
+    for _ in range(2):
+        codes = torch.empty(n * 4 * 12, dtype=torch.uint8, device=DEV)
+        norms = torch.empty(n * 4, dtype=torch.float16, device=DEV)
+        tq.tq_quantize(qz, x, n, 128, codes, norms)
+        outs.append((codes.clone(), norms.clone()))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
