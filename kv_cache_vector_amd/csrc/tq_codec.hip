@@ -95,11 +95,14 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
                                                         group_offset(g, a.groups_per_row, a.ld_x, a.contiguous));
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          u32x4 t = __builtin_nontemporal_load(p + k);
-          v[4 * k] = __builtin_bit_cast(float, t.x);
-          v[4 * k + 1] = __builtin_bit_cast(float, t.y);
-          v[4 * k + 2] = __builtin_bit_cast(float, t.z);
-          v[4 * k + 3] = __builtin_bit_cast(float, t.w);
+          // copy the elements out as integers first: bit-casting an ext-vector
+          // element expression directly reads element 0 with this compiler
+          const u32x4 t = __builtin_nontemporal_load(p + k);
+          const uint32_t e0 = t.x, e1 = t.y, e2 = t.z, e3 = t.w;
+          v[4 * k] = __builtin_bit_cast(float, e0);
+          v[4 * k + 1] = __builtin_bit_cast(float, e1);
+          v[4 * k + 2] = __builtin_bit_cast(float, e2);
+          v[4 * k + 3] = __builtin_bit_cast(float, e3);
         }
       } else {
 #pragma unroll

@@ -69,7 +69,7 @@ def _roundtrip(x_np, dt, bits, seed, x_dtype, norm_dtype, nc=False, ld=None, y_d
         if yt == tq.TQ_F32:
             stats["decode_err"] = check_decoded_f32(y, ref, norms, dt)
         else:
-            stats["f16_ulp_off"] = check_decoded_f16(y, ref)
+            stats["f16_ulp_off"] = check_decoded_f16(y, ref, norms, dt)
     return stats, codes, norms, orc
 
 
@@ -88,7 +88,7 @@ def test_matrix_f16(dt, bits):
 def test_matrix_f32_strided(dt, bits):
     hd, n_rows = 256, 129
     x = synth.normal_f32(7, 0, n_rows * hd).reshape(n_rows, hd) * 3.0
-    stats, *_ = _roundtrip(x, dt, bits, seed=5, x_dtype=tq.TQ_F32, norm_dtype=tq.TQ_F32, ld=hd + 4)
+    stats, *_ = _roundtrip(x, dt, bits, seed=5, x_dtype=tq.TQ_F32, norm_dtype=tq.TQ_F32, ld=hd + 8)
     print(stats)
 
 
