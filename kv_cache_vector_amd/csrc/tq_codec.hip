@@ -1,20 +1,30 @@
 // Encode and decode kernels (no QJL stage) for gfx950.
 //
 // Work split: one lane owns one 32-coordinate group (64 contiguous bytes of
-// fp16 input, or 128 of fp32).  A unit of dt coordinates spans LPU = dt/32
+// fp16, or 128 of fp32).  A unit of dt coordinates spans LPU = dt/32
 // consecutive lanes, so coordinate c of a unit lives in lane c/32, register
 // c%32.  The Walsh-Hadamard butterflies of coordinate bits 0..4 run inside a
 // lane's registers; bits 5.. (dt >= 64) pair lanes of the same quad with DPP
-// (or a swizzle for the third lane bit).  Norms are lane reductions.  The
-// packed code word of a group is built in registers and written with one
-// vector store, so loads and stores are contiguous across the wavefront.
+// (or a swizzle for the third lane bit).  Norms are lane reductions.
+//
+// Memory: each wave moves its 64 groups through a private LDS tile, so every
+// global load and store instruction covers one contiguous 1 KiB span across
+// the wavefront (lane l <-> bytes [16 l, 16 l + 16)); the tile re-deals the
+// 16-byte chunks so that each lane ends up with its own group.  Codes and
+// norms are already contiguous per lane and go straight to memory.
 //
 // Encode ([Scratch] §2 steps 1-3; [Fork] "How it works"):
-//   n = ||x||, yhat = H_unnorm (D x), code from comparing |yhat| with t_k * n
-//   (t_k the N(0,1) cell edges; sqrt(dt) * y = yhat / n so no per-element
-//   division is needed).
-// Decode: c = level(code), optional norm correction, x~ = n * D H_unnorm c / dt
-//   (or n * D H_unnorm c / (sqrt(dt) ||c||) with norm correction).
+//   n = ||x||, yhat = H_unnorm (D x); since sqrt(dt) * y = yhat / n the cell
+//   of a coordinate is found by comparing |yhat| with t_k * n (t_k the N(0,1)
+//   cell edges), with no per-element division.  The code bits are produced
+//   most-significant first and shifted straight into the packed word, so
+//   bucketize and bit-pack are one chain: per bit one compare and one
+//   add-with-carry (w = 2 w + [|yhat| > t]); the sign bit is shifted in from
+//   the float's sign.
+// Decode: c = level(code) looked up two coordinates at a time in an LDS
+//   table that already holds the first butterfly (c_a + c_b, c_a - c_b),
+//   optional norm correction, x~ = n * D H_unnorm c / dt (or with norm
+//   correction n * D H_unnorm c / (sqrt(dt) ||c||)).
 #include <hip/hip_fp16.h>
 
 #include "tq_device.h"
@@ -23,115 +33,170 @@
 namespace tq {
 namespace {
 
+constexpr int kWaves = kBlock / 64;
+
 __device__ __forceinline__ int64_t group_offset(int64_t g, int32_t gpr, int64_t ld, int32_t contiguous) {
   if (contiguous) return g * 32;
   const int64_t row = g / gpr;
   return row * ld + (g - row * gpr) * 32;
 }
 
-// Magnitude index m = #{k : t_k < a} over the 2^(BITS-1) - 1 positive edges T (binary search).
+// w = 2 w + [|y| > t]; returns the lane mask of the comparison.
+__device__ __forceinline__ uint64_t shift_in_gt(uint32_t& w, float y, float t) {
+  uint64_t m, carry;
+  asm("v_cmp_gt_f32_e64 %1, |%3|, %4\n\t"
+      "v_addc_co_u32_e64 %0, %2, %0, %0, %1"
+      : "+v"(w), "=&s"(m), "=&s"(carry)
+      : "v"(y), "v"(t));
+  return m;
+}
+
+__device__ __forceinline__ float select_mask(uint64_t m, float if_false, float if_true) {
+  float r;
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(if_false), "v"(if_true), "s"(m));
+  return r;
+}
+
+// w = (w << 1) | signbit(y)
+__device__ __forceinline__ void shift_in_sign(uint32_t& w, float y) {
+  w = __builtin_amdgcn_alignbit(w, __builtin_bit_cast(uint32_t, y), 31);
+}
+
+// Shift the code of one coordinate, most significant bit first, into the
+// packed words.  Bit p of the 32-coordinate group (p = BITS*j + k) lives in
+// word p/32; since the caller walks j downwards and the bits of one code
+// from the top, every word receives its bits from bit 31 down to bit 0.
 template <int BITS>
-__device__ __forceinline__ uint32_t magnitude_index(float a, const float* T) {
-  if constexpr (BITS == 1) {
-    return 0u;
-  } else if constexpr (BITS == 2) {
-    return a > T[0] ? 1u : 0u;
+__device__ __forceinline__ void code_chain(uint32_t* word, int j, float y, const float* T) {
+  const int p_top = BITS * j + BITS - 1;
+  shift_in_sign(word[p_top >> 5], y);
+  if constexpr (BITS == 2) {
+    shift_in_gt(word[(p_top - 1) >> 5], y, T[0]);
   } else if constexpr (BITS == 3) {
-    const bool c1 = a > T[1];
-    const float t = c1 ? T[2] : T[0];
-    return (c1 ? 2u : 0u) + (a > t ? 1u : 0u);
-  } else {
-    const bool c1 = a > T[3];
-    const float t2 = c1 ? T[5] : T[1];
-    const bool c2 = a > t2;
-    const float lo = c1 ? T[4] : T[0];
-    const float hi = c1 ? T[6] : T[2];
-    const float t3 = c2 ? hi : lo;
-    return (c1 ? 4u : 0u) + (c2 ? 2u : 0u) + (a > t3 ? 1u : 0u);
+    const uint64_t c1 = shift_in_gt(word[(p_top - 1) >> 5], y, T[1]);
+    shift_in_gt(word[(p_top - 2) >> 5], y, select_mask(c1, T[0], T[2]));
+  } else if constexpr (BITS == 4) {
+    const uint64_t c1 = shift_in_gt(word[(p_top - 1) >> 5], y, T[3]);
+    const float lo = select_mask(c1, T[0], T[4]);
+    const float hi = select_mask(c1, T[2], T[6]);
+    const uint64_t c2 = shift_in_gt(word[(p_top - 2) >> 5], y, select_mask(c1, T[1], T[5]));
+    shift_in_gt(word[(p_top - 3) >> 5], y, select_mask(c2, lo, hi));
+  }
+}
+
+// Stored words of a zero unit: every coordinate takes the cell just below 0,
+// i.e. code (sign 1, magnitude 0).
+template <int BITS>
+__device__ __forceinline__ uint32_t zero_unit_word(int k) {
+  uint32_t w = 0;
+  for (int j = 0; j < 32; ++j) {
+    const int p = BITS * j + BITS - 1;
+    if ((p >> 5) == k) w |= 1u << (p & 31);
+  }
+  return w;
+}
+
+// fp16 pair -> (lo + hi, lo - hi) in fp32 with one rounding each (fma_mix reads the halves directly).
+__device__ __forceinline__ void butterfly_f16_pair(uint32_t w, float& s, float& d) {
+  asm("v_fma_mix_f32 %0, %1, 1.0, %1 op_sel:[1,0,0] op_sel_hi:[1,0,1]" : "=v"(s) : "v"(w));
+  asm("v_fma_mix_f32 %0, -%1, 1.0, %1 op_sel:[1,0,0] op_sel_hi:[1,0,1]" : "=v"(d) : "v"(w));
+}
+
+// In-register butterflies over coordinate bits FIRST..4 (bits below FIRST already done).
+template <int FIRST>
+__device__ __forceinline__ void fwht32_from(float* v) {
+#pragma unroll
+  for (int bit = 1 << FIRST; bit < 32; bit <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (!(i & bit)) {
+        const float a = v[i], b = v[i | bit];
+        v[i] = a + b;
+        v[i | bit] = a - b;
+      }
+    }
   }
 }
 
 template <int BITS, int LPU, bool IN_F32, bool NORM_F32>
 __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
-  const int q = (int)(threadIdx.x % LPU);
+  constexpr int CH = IN_F32 ? 8 : 4;  // 16-byte chunks per group
+  constexpr int PITCH = 16 * CH + 16;  // LDS bytes per staged group (padded against bank conflicts)
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kWaves][64 * PITCH];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint8_t* tile = stage[wave];
+  const int q = lane % LPU;
   const uint32_t dword = a.dbits[q];
-  uint32_t dmask[16];
+  float thr[7];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) dmask[i] = pair_sign_mask(dword, i);
+  for (int k = 0; k < 7; ++k) thr[k] = a.thr[k];
+  const char* xbase = static_cast<const char*>(a.x);
+  constexpr int ES = IN_F32 ? 4 : 2;
+
   const int64_t stride = (int64_t)gridDim.x * kBlock;
-  for (int64_t g0 = (int64_t)blockIdx.x * kBlock; g0 < a.n_groups; g0 += stride) {
-    const int64_t g = g0 + threadIdx.x;
+  for (int64_t w0 = (int64_t)blockIdx.x * kBlock + wave * 64; w0 < a.n_groups; w0 += stride) {
+    // ---- coalesced load of the wave's 64 groups, re-dealt through LDS ----
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int ci = 64 * k + lane;
+      const int grp = ci / CH, c = ci % CH;
+      const int64_t g = w0 + grp;
+      u32x4 t = {0u, 0u, 0u, 0u};
+      if (g < a.n_groups) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(
+            xbase + ES * group_offset(g, a.groups_per_row, a.ld_x, a.contiguous) + 16 * c);
+        t = __builtin_nontemporal_load(p);
+      }
+      *reinterpret_cast<u32x4*>(tile + grp * PITCH + 16 * c) = t;
+    }
+    __builtin_amdgcn_wave_barrier();
+    uint32_t w[4 * CH];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const u32x4 t = *reinterpret_cast<const u32x4*>(tile + lane * PITCH + 16 * c);
+      w[4 * c] = t.x;
+      w[4 * c + 1] = t.y;
+      w[4 * c + 2] = t.z;
+      w[4 * c + 3] = t.w;
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    const int64_t g = w0 + lane;
     const bool valid = g < a.n_groups;
     float v[32];
     float ss = 0.0f;
     if constexpr (!IN_F32) {
-      uint32_t w[16];
-      if (valid) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.x) +
-                                                        group_offset(g, a.groups_per_row, a.ld_x, a.contiguous));
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          u32x4 t = __builtin_nontemporal_load(p + k);
-          w[4 * k] = t.x;
-          w[4 * k + 1] = t.y;
-          w[4 * k + 2] = t.z;
-          w[4 * k + 3] = t.w;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) w[i] = 0u;
-      }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        half2v h = __builtin_bit_cast(half2v, w[i]);
+        const half2v h = __builtin_bit_cast(half2v, w[i]);
         ss = __builtin_amdgcn_fdot2(h, h, ss, false);
-        h = __builtin_bit_cast(half2v, w[i] ^ dmask[i]);
-        v[2 * i] = (float)h.x;
-        v[2 * i + 1] = (float)h.y;
+        butterfly_f16_pair(w[i] ^ pair_sign_mask(dword, i), v[2 * i], v[2 * i + 1]);
       }
+      fwht32_from<1>(v);
     } else {
-      if (valid) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(a.x) +
-                                                        group_offset(g, a.groups_per_row, a.ld_x, a.contiguous));
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          // copy the elements out as integers first: bit-casting an ext-vector
-          // element expression directly reads element 0 with this compiler
-          const u32x4 t = __builtin_nontemporal_load(p + k);
-          const uint32_t e0 = t.x, e1 = t.y, e2 = t.z, e3 = t.w;
-          v[4 * k] = __builtin_bit_cast(float, e0);
-          v[4 * k + 1] = __builtin_bit_cast(float, e1);
-          v[4 * k + 2] = __builtin_bit_cast(float, e2);
-          v[4 * k + 3] = __builtin_bit_cast(float, e3);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) v[i] = 0.0f;
-      }
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
-        ss = __builtin_fmaf(v[i], v[i], ss);
-        v[i] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v[i]) ^ (((dword >> i) & 1u) << 31));
+        const float x = __builtin_bit_cast(float, w[i]);
+        ss = __builtin_fmaf(x, x, ss);
+        v[i] = __builtin_bit_cast(float, w[i] ^ (((dword >> i) & 1u) << 31));
       }
+      fwht32_from<0>(v);
     }
     ss = unit_sum<LPU>(ss);
     const float n = __builtin_sqrtf(ss);
+    fwht_crosslane<LPU>(v, q);
     float T[7];
 #pragma unroll
-    for (int k = 0; k < 7; ++k) T[k] = a.thr[k] * n;
-
-    fwht32_inlane(v);
-    fwht_crosslane<LPU>(v, q);
+    for (int k = 0; k < 7; ++k) T[k] = thr[k] * n;
 
     uint32_t word[BITS];
 #pragma unroll
     for (int k = 0; k < BITS; ++k) word[k] = 0u;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const float y = v[j];
-      const uint32_t neg = (y > 0.0f) ? 0u : 1u;  // a zero coordinate belongs to the lower cell
-      const uint32_t code = (neg << (BITS - 1)) | magnitude_index<BITS>(__builtin_fabsf(y), T);
-      put_code<BITS>(word, j, code);
+    for (int j = 31; j >= 0; --j) code_chain<BITS>(word, j, v[j], T);
+    if (n == 0.0f) {
+#pragma unroll
+      for (int k = 0; k < BITS; ++k) word[k] = zero_unit_word<BITS>(k);
     }
     if (valid) {
       uint32_t* cp = reinterpret_cast<uint32_t*>(a.codes + g * (4 * BITS));
@@ -148,19 +213,50 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
   }
 }
 
+// Pair table: entry (code_a | code_b << BITS) = (c_a + c_b, c_a - c_b), N(0,1) scale.
+template <int BITS>
+__device__ __forceinline__ void fill_pair_table(float2* tab, const float* level) {
+  constexpr int L = 1 << BITS;
+  for (int e = threadIdx.x; e < L * L; e += kBlock) {
+    const float ca = level[e & (L - 1)], cb = level[e >> BITS];
+    tab[e] = make_float2(ca + cb, ca - cb);
+  }
+}
+
+// Byte offset (8 * key) of the pair (2i, 2i+1) in the pair table.
+template <int BITS>
+__device__ __forceinline__ uint32_t pair_key8(const uint32_t* word, int i) {
+  constexpr int PB = 2 * BITS;
+  const int pos = PB * i;
+  const int wi = pos >> 5, sh = pos & 31;
+  uint32_t key;
+  if (sh + PB <= 32)
+    key = __builtin_amdgcn_ubfe(word[wi], sh, PB);
+  else
+    key = __builtin_amdgcn_ubfe(__builtin_amdgcn_alignbit(word[wi + 1], word[wi], sh), 0, PB);
+  return key << 3;
+}
+
 template <int BITS, int LPU, bool OUT_F32, bool NORM_F32, bool NC>
 __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs a) {
-  __shared__ float lut[16];
-  if (threadIdx.x < 16) lut[threadIdx.x] = a.level[threadIdx.x];
+  constexpr int L = 1 << BITS;
+  constexpr int CH = OUT_F32 ? 8 : 4;
+  constexpr int PITCH = 16 * CH + 16;
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kWaves][64 * PITCH];
+  __shared__ float2 ptab[L * L];
+  fill_pair_table<BITS>(ptab, a.level);
   __syncthreads();
-  const int q = (int)(threadIdx.x % LPU);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint8_t* tile = stage[wave];
+  const char* tabp = reinterpret_cast<const char*>(ptab);
+  const int q = lane % LPU;
   const uint32_t dword = a.dbits[q];
-  uint32_t dmask[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) dmask[i] = pair_sign_mask(dword, i);
+  char* ybase = static_cast<char*>(a.y);
+  constexpr int ES = OUT_F32 ? 4 : 2;
+
   const int64_t stride = (int64_t)gridDim.x * kBlock;
-  for (int64_t g0 = (int64_t)blockIdx.x * kBlock; g0 < a.n_groups; g0 += stride) {
-    const int64_t g = g0 + threadIdx.x;
+  for (int64_t w0 = (int64_t)blockIdx.x * kBlock + wave * 64; w0 < a.n_groups; w0 += stride) {
+    const int64_t g = w0 + lane;
     const bool valid = g < a.n_groups;
     uint32_t word[BITS];
     float n = 0.0f;
@@ -179,44 +275,54 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs a) {
     }
     float v[32];
 #pragma unroll
-    for (int j = 0; j < 32; ++j) v[j] = lut[get_code<BITS>(word, j)];
+    for (int i = 0; i < 16; ++i) {
+      const float2 e = *reinterpret_cast<const float2*>(tabp + pair_key8<BITS>(word, i));
+      v[2 * i] = e.x;
+      v[2 * i + 1] = e.y;
+    }
     float scale;
     if constexpr (NC) {
       float ss = 0.0f;
 #pragma unroll
       for (int j = 0; j < 32; ++j) ss = __builtin_fmaf(v[j], v[j], ss);
-      ss = unit_sum<LPU>(ss);
-      scale = n * a.inv_sqrt_dt / __builtin_sqrtf(ss);
+      ss = unit_sum<LPU>(ss);  // = 2 * ||c||^2: each pair contributes (a+b)^2 + (a-b)^2
+      scale = n * a.inv_sqrt_dt * __builtin_sqrtf(2.0f / ss);
     } else {
       scale = n * a.inv_dt;
     }
-    fwht32_inlane(v);
+    fwht32_from<1>(v);
     fwht_crosslane<LPU>(v, q);
-    if (!valid) continue;
+
+    // ---- stage the group's output in LDS, then store it coalesced ----
+    uint32_t o[4 * CH];
     if constexpr (!OUT_F32) {
-      uint32_t o[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const __half lo = __float2half_rn(v[2 * i] * scale);
         const __half hi = __float2half_rn(v[2 * i + 1] * scale);
-        o[i] = ((uint32_t)__half_as_ushort(lo) | ((uint32_t)__half_as_ushort(hi) << 16)) ^ dmask[i];
+        o[i] = ((uint32_t)__half_as_ushort(lo) | ((uint32_t)__half_as_ushort(hi) << 16)) ^ pair_sign_mask(dword, i);
       }
-      u32x4* p = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.y) +
-                                          group_offset(g, a.groups_per_row, a.ld_y, a.contiguous));
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        __builtin_nontemporal_store(u32x4{o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]}, p + k);
     } else {
-      uint32_t o[32];
 #pragma unroll
-      for (int i = 0; i < 32; ++i)
-        o[i] = __builtin_bit_cast(uint32_t, v[i] * scale) ^ (((dword >> i) & 1u) << 31);
-      u32x4* p = reinterpret_cast<u32x4*>(static_cast<float*>(a.y) +
-                                          group_offset(g, a.groups_per_row, a.ld_y, a.contiguous));
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-        __builtin_nontemporal_store(u32x4{o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]}, p + k);
+      for (int i = 0; i < 32; ++i) o[i] = __builtin_bit_cast(uint32_t, v[i] * scale) ^ (((dword >> i) & 1u) << 31);
     }
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+      *reinterpret_cast<u32x4*>(tile + lane * PITCH + 16 * c) = u32x4{o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]};
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int ci = 64 * k + lane;
+      const int grp = ci / CH, c = ci % CH;
+      const int64_t gg = w0 + grp;
+      const u32x4 t = *reinterpret_cast<const u32x4*>(tile + grp * PITCH + 16 * c);
+      if (gg < a.n_groups) {
+        u32x4* p = reinterpret_cast<u32x4*>(ybase + ES * group_offset(gg, a.groups_per_row, a.ld_y, a.contiguous) +
+                                            16 * c);
+        __builtin_nontemporal_store(t, p);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -270,7 +376,8 @@ hipError_t decode_dispatch_dtype(const tq_config& cfg, const DecodeArgs& a, tq_d
 
 template <int BITS, int LPU>
 hipError_t decode_dispatch_nc(const tq_config& cfg, const DecodeArgs& a, bool nc, tq_dtype yt, hipStream_t s) {
-  return nc ? decode_dispatch_dtype<BITS, LPU, true>(cfg, a, yt, s) : decode_dispatch_dtype<BITS, LPU, false>(cfg, a, yt, s);
+  return nc ? decode_dispatch_dtype<BITS, LPU, true>(cfg, a, yt, s)
+            : decode_dispatch_dtype<BITS, LPU, false>(cfg, a, yt, s);
 }
 
 template <int BITS>
