@@ -152,6 +152,11 @@ def main():
     k, v, signs_k, signs_v, rows = make_cache(tq, torch, dev)
     ok, ov = torch.empty_like(k), torch.empty_like(v)
 
+    # streaming-copy reference on the same buffers (read 1.125 GiB + write 1.125 GiB)
+    copy_ms = time_steps(torch, lambda: ok.copy_(k), 10, 2)
+    copy_gbs = 2 * k.numel() * 2 / (copy_ms * 1e-3) / 1e9
+    log(f"device copy of one half-cache: {copy_ms:.3f} ms ({copy_gbs:.0f} GB/s read+write)")
+
     results = {}
     for bits in (3, 4):
         codec = Codec(tq, torch, dev, rows, bits, signs_k, signs_v)
@@ -206,6 +211,7 @@ def main():
                    "turbo3_blocks_per_s": round(r["units"] / (r["dec_ms"] * 1e-3)),
                    "turbo3_ms": round(r["dec_ms"], 4), "turbo4_ms": round(r4["dec_ms"], 4)},
         "turbo4_value": round(2 * 2 * r4["bytes"]["fp16"] / (r4["ms"] * 1e-3) / 1e9, 1),
+        "copy_reference_GBs": round(copy_gbs, 1),
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")

@@ -35,10 +35,96 @@ namespace {
 
 constexpr int kWaves = kBlock / 64;
 
-__device__ __forceinline__ int64_t group_offset(int64_t g, int32_t gpr, int64_t ld, int32_t contiguous) {
-  if (contiguous) return g * 32;
-  const int64_t row = g / gpr;
-  return row * ld + (g - row * gpr) * 32;
+// Streaming hints and launch width (measured on MI355X; see the tuning notes in the design doc).
+#ifndef TQ_LOAD_NT
+#define TQ_LOAD_NT 1
+#endif
+#ifndef TQ_STORE_NT
+#define TQ_STORE_NT 1
+#endif
+#ifndef TQ_GRID_PER_CU
+#define TQ_GRID_PER_CU 16
+#endif
+
+__device__ __forceinline__ u32x4 load_stream(const u32x4* p) {
+#if TQ_LOAD_NT
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+
+__device__ __forceinline__ void store_stream(u32x4 v, u32x4* p) {
+#if TQ_STORE_NT
+  __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
+}
+
+// Element offset of group g: rows of ld elements, gpr groups per row.
+template <bool CONTIG>
+__device__ __forceinline__ int64_t group_offset(int64_t g, int32_t gpr, int64_t ld) {
+  if constexpr (CONTIG) {
+    return g * 32;
+  } else {
+    const int64_t row = g / gpr;
+    return row * ld + (g - row * gpr) * 32;
+  }
+}
+
+// Copy the wave's 64 groups (CH 16-byte chunks each) from global memory into
+// the wave's LDS tile, group grp at tile + grp * PITCH.  Instruction k moves
+// chunks 64k .. 64k+63 of the wave's span, so each instruction covers one
+// contiguous 1 KiB when rows are contiguous.  Full waves issue every load
+// before the first LDS write; the last, partial wave checks each chunk.
+template <int CH, int PITCH, int ES, bool CONTIG>
+__device__ __forceinline__ void stage_in(uint8_t* tile, const char* base, int64_t w0, int64_t n_groups, int32_t gpr,
+                                         int64_t ld, int lane) {
+  u32x4 t[CH];
+  if (w0 + 64 <= n_groups) {
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int ci = 64 * k + lane;
+      const int grp = ci / CH, c = ci % CH;
+      t[k] = load_stream(reinterpret_cast<const u32x4*>(base + ES * group_offset<CONTIG>(w0 + grp, gpr, ld) + 16 * c));
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int ci = 64 * k + lane;
+      const int grp = ci / CH, c = ci % CH;
+      t[k] = u32x4{0u, 0u, 0u, 0u};
+      if (w0 + grp < n_groups)
+        t[k] = load_stream(reinterpret_cast<const u32x4*>(base + ES * group_offset<CONTIG>(w0 + grp, gpr, ld) + 16 * c));
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < CH; ++k) {
+    const int ci = 64 * k + lane;
+    *reinterpret_cast<u32x4*>(tile + (ci / CH) * PITCH + 16 * (ci % CH)) = t[k];
+  }
+}
+
+// Write the wave's 64 staged groups from the LDS tile to global memory, one
+// contiguous 1 KiB span per store instruction (the mirror of stage_in).
+template <int CH, int PITCH, int ES, bool CONTIG>
+__device__ __forceinline__ void stage_out(const uint8_t* tile, char* base, int64_t w0, int64_t n_groups, int32_t gpr,
+                                          int64_t ld, int lane) {
+  u32x4 t[CH];
+#pragma unroll
+  for (int k = 0; k < CH; ++k) {
+    const int ci = 64 * k + lane;
+    t[k] = *reinterpret_cast<const u32x4*>(tile + (ci / CH) * PITCH + 16 * (ci % CH));
+  }
+  const bool full = w0 + 64 <= n_groups;
+#pragma unroll
+  for (int k = 0; k < CH; ++k) {
+    const int ci = 64 * k + lane;
+    const int grp = ci / CH, c = ci % CH;
+    if (full || w0 + grp < n_groups)
+      store_stream(t[k], reinterpret_cast<u32x4*>(base + ES * group_offset<CONTIG>(w0 + grp, gpr, ld) + 16 * c));
+  }
 }
 
 // w = 2 w + [|y| > t]; returns the lane mask of the comparison.
@@ -118,7 +204,7 @@ __device__ __forceinline__ void fwht32_from(float* v) {
   }
 }
 
-template <int BITS, int LPU, bool IN_F32, bool NORM_F32>
+template <int BITS, int LPU, bool IN_F32, bool NORM_F32, bool CONTIG>
 __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
   constexpr int CH = IN_F32 ? 8 : 4;  // 16-byte chunks per group
   constexpr int PITCH = 16 * CH + 16;  // LDS bytes per staged group (padded against bank conflicts)
@@ -136,19 +222,7 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
   const int64_t stride = (int64_t)gridDim.x * kBlock;
   for (int64_t w0 = (int64_t)blockIdx.x * kBlock + wave * 64; w0 < a.n_groups; w0 += stride) {
     // ---- coalesced load of the wave's 64 groups, re-dealt through LDS ----
-#pragma unroll
-    for (int k = 0; k < CH; ++k) {
-      const int ci = 64 * k + lane;
-      const int grp = ci / CH, c = ci % CH;
-      const int64_t g = w0 + grp;
-      u32x4 t = {0u, 0u, 0u, 0u};
-      if (g < a.n_groups) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(
-            xbase + ES * group_offset(g, a.groups_per_row, a.ld_x, a.contiguous) + 16 * c);
-        t = __builtin_nontemporal_load(p);
-      }
-      *reinterpret_cast<u32x4*>(tile + grp * PITCH + 16 * c) = t;
-    }
+    stage_in<CH, PITCH, ES, CONTIG>(tile, xbase, w0, a.n_groups, a.groups_per_row, a.ld_x, lane);
     __builtin_amdgcn_wave_barrier();
     uint32_t w[4 * CH];
 #pragma unroll
@@ -237,7 +311,7 @@ __device__ __forceinline__ uint32_t pair_key8(const uint32_t* word, int i) {
   return key << 3;
 }
 
-template <int BITS, int LPU, bool OUT_F32, bool NORM_F32, bool NC>
+template <int BITS, int LPU, bool OUT_F32, bool NORM_F32, bool NC, bool CONTIG>
 __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs a) {
   constexpr int L = 1 << BITS;
   constexpr int CH = OUT_F32 ? 8 : 4;
@@ -310,18 +384,7 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs a) {
     for (int c = 0; c < CH; ++c)
       *reinterpret_cast<u32x4*>(tile + lane * PITCH + 16 * c) = u32x4{o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]};
     __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int k = 0; k < CH; ++k) {
-      const int ci = 64 * k + lane;
-      const int grp = ci / CH, c = ci % CH;
-      const int64_t gg = w0 + grp;
-      const u32x4 t = *reinterpret_cast<const u32x4*>(tile + grp * PITCH + 16 * c);
-      if (gg < a.n_groups) {
-        u32x4* p = reinterpret_cast<u32x4*>(ybase + ES * group_offset(gg, a.groups_per_row, a.ld_y, a.contiguous) +
-                                            16 * c);
-        __builtin_nontemporal_store(t, p);
-      }
-    }
+    stage_out<CH, PITCH, ES, CONTIG>(tile, ybase, w0, a.n_groups, a.groups_per_row, a.ld_y, lane);
     __builtin_amdgcn_wave_barrier();
   }
 }
@@ -338,46 +401,54 @@ int64_t grid_for(int64_t n_groups) {
     if (cus <= 0) cus = 256;
   }
   int64_t need = (n_groups + kBlock - 1) / kBlock;
-  int64_t cap = (int64_t)cus * 16;
+  int64_t cap = (int64_t)cus * TQ_GRID_PER_CU;
   return need < cap ? need : cap;
 }
 
-template <int BITS, int LPU>
+template <int BITS, int LPU, bool CONTIG>
 hipError_t encode_dispatch_dtype(const tq_config& cfg, const EncodeArgs& a, hipStream_t s) {
   dim3 grid((unsigned)grid_for(a.n_groups)), block(kBlock);
   const bool in32 = cfg.x_dtype == TQ_F32, n32 = cfg.norm_dtype == TQ_F32;
-  if (!in32 && !n32) hipLaunchKernelGGL((encode_kernel<BITS, LPU, false, false>), grid, block, 0, s, a);
-  if (!in32 && n32) hipLaunchKernelGGL((encode_kernel<BITS, LPU, false, true>), grid, block, 0, s, a);
-  if (in32 && !n32) hipLaunchKernelGGL((encode_kernel<BITS, LPU, true, false>), grid, block, 0, s, a);
-  if (in32 && n32) hipLaunchKernelGGL((encode_kernel<BITS, LPU, true, true>), grid, block, 0, s, a);
+  if (!in32 && !n32) hipLaunchKernelGGL((encode_kernel<BITS, LPU, false, false, CONTIG>), grid, block, 0, s, a);
+  if (!in32 && n32) hipLaunchKernelGGL((encode_kernel<BITS, LPU, false, true, CONTIG>), grid, block, 0, s, a);
+  if (in32 && !n32) hipLaunchKernelGGL((encode_kernel<BITS, LPU, true, false, CONTIG>), grid, block, 0, s, a);
+  if (in32 && n32) hipLaunchKernelGGL((encode_kernel<BITS, LPU, true, true, CONTIG>), grid, block, 0, s, a);
   return hipGetLastError();
+}
+
+template <int BITS, int LPU>
+hipError_t encode_dispatch_contig(const tq_config& cfg, const EncodeArgs& a, hipStream_t s) {
+  return a.contiguous ? encode_dispatch_dtype<BITS, LPU, true>(cfg, a, s) : encode_dispatch_dtype<BITS, LPU, false>(cfg, a, s);
 }
 
 template <int BITS>
 hipError_t encode_dispatch_lpu(const tq_config& cfg, const EncodeArgs& a, hipStream_t s) {
   switch (cfg.dt) {
-    case 32: return encode_dispatch_dtype<BITS, 1>(cfg, a, s);
-    case 64: return encode_dispatch_dtype<BITS, 2>(cfg, a, s);
-    case 128: return encode_dispatch_dtype<BITS, 4>(cfg, a, s);
-    default: return encode_dispatch_dtype<BITS, 8>(cfg, a, s);
+    case 32: return encode_dispatch_contig<BITS, 1>(cfg, a, s);
+    case 64: return encode_dispatch_contig<BITS, 2>(cfg, a, s);
+    case 128: return encode_dispatch_contig<BITS, 4>(cfg, a, s);
+    default: return encode_dispatch_contig<BITS, 8>(cfg, a, s);
   }
 }
 
-template <int BITS, int LPU, bool NC>
+template <int BITS, int LPU, bool NC, bool CONTIG>
 hipError_t decode_dispatch_dtype(const tq_config& cfg, const DecodeArgs& a, tq_dtype yt, hipStream_t s) {
   dim3 grid((unsigned)grid_for(a.n_groups)), block(kBlock);
   const bool o32 = yt == TQ_F32, n32 = cfg.norm_dtype == TQ_F32;
-  if (!o32 && !n32) hipLaunchKernelGGL((decode_kernel<BITS, LPU, false, false, NC>), grid, block, 0, s, a);
-  if (!o32 && n32) hipLaunchKernelGGL((decode_kernel<BITS, LPU, false, true, NC>), grid, block, 0, s, a);
-  if (o32 && !n32) hipLaunchKernelGGL((decode_kernel<BITS, LPU, true, false, NC>), grid, block, 0, s, a);
-  if (o32 && n32) hipLaunchKernelGGL((decode_kernel<BITS, LPU, true, true, NC>), grid, block, 0, s, a);
+  if (!o32 && !n32) hipLaunchKernelGGL((decode_kernel<BITS, LPU, false, false, NC, CONTIG>), grid, block, 0, s, a);
+  if (!o32 && n32) hipLaunchKernelGGL((decode_kernel<BITS, LPU, false, true, NC, CONTIG>), grid, block, 0, s, a);
+  if (o32 && !n32) hipLaunchKernelGGL((decode_kernel<BITS, LPU, true, false, NC, CONTIG>), grid, block, 0, s, a);
+  if (o32 && n32) hipLaunchKernelGGL((decode_kernel<BITS, LPU, true, true, NC, CONTIG>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
 template <int BITS, int LPU>
 hipError_t decode_dispatch_nc(const tq_config& cfg, const DecodeArgs& a, bool nc, tq_dtype yt, hipStream_t s) {
-  return nc ? decode_dispatch_dtype<BITS, LPU, true>(cfg, a, yt, s)
-            : decode_dispatch_dtype<BITS, LPU, false>(cfg, a, yt, s);
+  if (a.contiguous)
+    return nc ? decode_dispatch_dtype<BITS, LPU, true, true>(cfg, a, yt, s)
+              : decode_dispatch_dtype<BITS, LPU, false, true>(cfg, a, yt, s);
+  return nc ? decode_dispatch_dtype<BITS, LPU, true, false>(cfg, a, yt, s)
+            : decode_dispatch_dtype<BITS, LPU, false, false>(cfg, a, yt, s);
 }
 
 template <int BITS>

@@ -43,9 +43,8 @@ __global__ __launch_bounds__(kBlock) void qjl_encode_kernel(QjlEncodeArgs a, con
   extern __shared__ float s_lds[];  // S~ [m][DT] float32
   const int m = a.m;
   for (int i = threadIdx.x; i < m * DT; i += kBlock) s_lds[i] = s_rot32[i];
-  __shared__ double lvl[16];
-  if (threadIdx.x < 16) lvl[threadIdx.x] = a.level[threadIdx.x];
   __syncthreads();
+  const double* lvl = a.level;  // read from the kernel-argument segment (the LDS budget goes to S~)
 
   const int q = (int)(threadIdx.x % LPU);
   const uint32_t dword = a.dbits[q];
@@ -138,9 +137,8 @@ __global__ __launch_bounds__(kBlock) void qjl_decode_kernel(QjlDecodeArgs a) {
   extern __shared__ float s_lds[];  // S~ [m][DT] float32
   const int m = a.m;
   for (int i = threadIdx.x; i < m * DT; i += kBlock) s_lds[i] = a.s_rot[i];
-  __shared__ float lut[16];
-  if (threadIdx.x < 16) lut[threadIdx.x] = a.level[threadIdx.x];
   __syncthreads();
+  const float* lut = a.level;  // read from the kernel-argument segment (the LDS budget goes to S~)
   const int q = (int)(threadIdx.x % LPU);
   const uint32_t dword = a.dbits[q];
   const int64_t n_groups = a.n_units * LPU;

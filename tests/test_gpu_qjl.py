@@ -1,0 +1,88 @@
+"""GPU parity of the QJL stage (encode with the residual sketch, dequantize with
+the QJL correction) against the oracle, through the C ABI."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import Codebook, code_to_index, dequantize, quantize, unpack_codes
+from tests.parity import BAND, check_codes, check_decoded_f32, check_norms, check_sign_bits, edge_distance
+
+torch = pytest.importorskip("torch")
+import kv_cache_vector_amd as tq  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _encode(keys, dt, bits, m, seed, nc=False):
+    n = keys.shape[0]
+    signs = synth.signs(seed, 2, dt)
+    S = synth.gaussian_matrix(seed + 1, 0, m, dt)
+    qz = tq.Quantizer(dt, dt, bits, signs, flags=tq.TQ_QJL | (tq.TQ_NORM_CORRECT if nc else 0), qjl_m=m)
+    params = torch.empty(tq.tq_qjl_params_size(m, dt), dtype=torch.uint8, device=DEV)
+    tq.tq_qjl_prepare(qz, S, params)
+    x = torch.from_numpy(keys).to(DEV)
+    codes = torch.full((n * dt * bits // 8,), 0x5A, dtype=torch.uint8, device=DEV)
+    norms = torch.empty(n, dtype=torch.float16, device=DEV)
+    sbits = torch.full((n * m // 8,), 0x33, dtype=torch.uint8, device=DEV)
+    rnorm = torch.empty(n, dtype=torch.float16, device=DEV)
+    tq.tq_quantize(qz, x, n, dt, codes, norms, sbits, rnorm)
+    torch.cuda.synchronize()
+    return qz, signs, S, codes, norms, sbits, rnorm
+
+
+@pytest.mark.parametrize("dt,m,bits", [(128, 128, 2), (128, 64, 1), (64, 128, 3), (64, 64, 2), (128, 96, 2)])
+def test_qjl_encode_decode(dt, m, bits):
+    n = 1000  # several workgroups plus a ragged tail
+    keys = synth.kv_tensor(dt + m + bits, 1, 1, 0, n, dt, n_outliers=0).reshape(n, dt)
+    qz, signs, S, codes, norms, sbits, rnorm = _encode(keys, dt, bits, m, seed=dt + bits)
+    cb = Codebook.build(bits, dt)
+    orc = quantize(keys.astype(np.float64), signs, cb, S=S)
+    codes_np, norms_np = codes.cpu().numpy(), norms.cpu().numpy()
+    stats = check_codes(codes_np, orc, cb, bits, dt)
+    check_norms(norms_np, orc["norms"])
+    # sign bits and residual norms: compare units whose indices matched exactly
+    same = np.all(unpack_codes(codes_np.reshape(n, -1), bits, dt) == unpack_codes(orc["codes"], bits, dt), axis=1)
+    sb = sbits.cpu().numpy().reshape(n, m // 8)
+    sub = {k: v[same] for k, v in orc.items()}
+    st = check_sign_bits(sb[same], sub, m)
+    check_norms(rnorm.cpu().numpy()[same], orc["rho"][same])
+    print(stats, st)
+    # dequantize with the QJL correction (fp32 output), oracle on the GPU's own codes
+    for nc in (False, True):
+        qz.cfg.flags = tq.TQ_QJL | (tq.TQ_NORM_CORRECT if nc else 0)
+        y = torch.empty((n, dt), dtype=torch.float32, device=DEV)
+        tq.tq_dequantize(qz, codes, norms, sbits, rnorm, n, y, tq.TQ_F32, dt)
+        torch.cuda.synchronize()
+        ref = dequantize(codes_np.reshape(n, -1), norms_np, signs, cb, nc=nc, qjl_bits=sb, rho=rnorm.cpu().numpy(),
+                         S=S)
+        check_decoded_f32(y.cpu().numpy(), ref, norms_np, dt)
+
+
+def test_qjl_keys_full_size_sampled():
+    """65536 keys x 128 fp16, 2-bit MSE + 1-bit QJL, m = 128, S from seed 1: the whole set on the GPU,
+    the oracle on a strided sample of 2048 keys."""
+    from synth.workloads import qjl_keys
+
+    w = qjl_keys()
+    keys = w["keys"]
+    n, dt, bits, m = keys.shape[0], 128, 2, 128
+    qz = tq.Quantizer(dt, dt, bits, w["signs"], flags=tq.TQ_QJL, qjl_m=m)
+    params = torch.empty(tq.tq_qjl_params_size(m, dt), dtype=torch.uint8, device=DEV)
+    tq.tq_qjl_prepare(qz, w["S"], params)
+    x = torch.from_numpy(keys).to(DEV)
+    codes = torch.empty(n * 32, dtype=torch.uint8, device=DEV)
+    norms = torch.empty(n, dtype=torch.float16, device=DEV)
+    sbits = torch.empty(n * 16, dtype=torch.uint8, device=DEV)
+    rnorm = torch.empty(n, dtype=torch.float16, device=DEV)
+    tq.tq_quantize(qz, x, n, dt, codes, norms, sbits, rnorm)
+    torch.cuda.synchronize()
+    idx = np.arange(0, n, 32)
+    cb = Codebook.build(bits, dt)
+    orc = quantize(keys[idx].astype(np.float64), w["signs"], cb, S=w["S"])
+    c = codes.cpu().numpy().reshape(n, 32)[idx]
+    st = check_codes(c, orc, cb, bits, dt)
+    check_norms(norms.cpu().numpy()[idx], orc["norms"])
+    sb = check_sign_bits(sbits.cpu().numpy().reshape(n, 16)[idx], orc, m)
+    assert st["in_band"] <= 1e-5 * st["coords"] + 1
+    print(st, sb)
