@@ -349,12 +349,114 @@ tq_status tq_dequantize(const tq_config* cfg, const uint8_t* codes, const void* 
   return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+struct ScoreLayout {
+  int64_t n_q_pad, n_k_pad, rq, rk, planes;
+  size_t off_qrec, off_qscale, off_krec, off_kscale, total;
+};
+
+size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+ScoreLayout score_layout(const tq_config& cfg, int64_t n_q, int64_t n_k) {
+  ScoreLayout L{};
+  const int64_t kd = (cfg.dt + 63) / 64 * 64, km = (cfg.qjl_m + 63) / 64 * 64;
+  const int64_t tile = tq::scores_key_tile(cfg.bits);
+  L.planes = (int64_t)1 << (cfg.bits - 1);
+  L.n_q_pad = (n_q + 15) / 16 * 16;
+  L.n_k_pad = (n_k + tile - 1) / tile * tile;
+  L.rq = 2 * (kd + km);
+  L.rk = L.planes * kd + km;
+  L.off_qrec = 0;
+  L.off_qscale = round256(L.off_qrec + (size_t)(L.n_q_pad * L.rq));
+  L.off_krec = round256(L.off_qscale + (size_t)L.n_q_pad * 2 * sizeof(float));
+  L.off_kscale = round256(L.off_krec + (size_t)(L.n_k_pad * L.rk));
+  L.total = round256(L.off_kscale + (size_t)L.n_k_pad * 2 * sizeof(float));
+  return L;
+}
+
+tq_status check_scores_config(const tq_config* cfg, const char* who) {
+  tq_status st = check_config(cfg, who);
+  if (st) return st;
+  if (!(cfg->flags & TQ_QJL)) return fail(TQ_ERR_INVALID_ARG, "%s: cfg has no TQ_QJL flag", who);
+  if (cfg->flags & TQ_NORM_CORRECT)
+    return fail(TQ_ERR_UNSUPPORTED, "%s: norm correction does not apply to inner-product scores", who);
+  if (cfg->bits > 3) return fail(TQ_ERR_UNSUPPORTED, "%s: QJL scores support 1..3-bit MSE stages", who);
+  if (cfg->dt > 128 || cfg->qjl_m > 128)
+    return fail(TQ_ERR_UNSUPPORTED, "%s: QJL scores support head_dim <= 128 and qjl_m <= 128", who);
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 tq_status tq_qjl_scores(const tq_config* cfg, const void* q, tq_dtype q_dtype, int64_t n_q, int64_t ld_q,
                         const uint8_t* codes, const void* norms, const uint8_t* qjl_bits, const void* qjl_rnorm,
                         int64_t n_k, float* scores, int64_t ld_s, void* ws, size_t ws_bytes, void* stream) {
-  (void)cfg; (void)q; (void)q_dtype; (void)n_q; (void)ld_q; (void)codes; (void)norms; (void)qjl_bits;
-  (void)qjl_rnorm; (void)n_k; (void)scores; (void)ld_s; (void)ws; (void)ws_bytes; (void)stream;
-  return fail(TQ_ERR_UNSUPPORTED, "tq_qjl_scores: not available in this build");
+  const char* who = "tq_qjl_scores";
+  tq_status st = check_scores_config(cfg, who);
+  if (st) return st;
+  if (q_dtype != TQ_F16 && q_dtype != TQ_F32) return fail(TQ_ERR_INVALID_ARG, "%s: bad q_dtype", who);
+  if (n_q < 0 || n_k < 0) return fail(TQ_ERR_INVALID_ARG, "%s: negative sizes", who);
+  if (n_q == 0 || n_k == 0) return ok();
+  if (n_q > ((int64_t)1 << 31) || n_k > ((int64_t)1 << 31))
+    return fail(TQ_ERR_UNSUPPORTED, "%s: at most 2^31 queries and keys per call", who);
+  if (!q || !aligned(q, esize(q_dtype)) || ld_q < cfg->head_dim)
+    return fail(TQ_ERR_INVALID_ARG, "%s: q must be non-NULL, element-aligned, ld_q >= head_dim", who);
+  if (!codes || !aligned(codes, 4) || !norms || !aligned(norms, esize(cfg->norm_dtype)) || !qjl_bits ||
+      !aligned(qjl_bits, 4) || !qjl_rnorm || !aligned(qjl_rnorm, 2))
+    return fail(TQ_ERR_INVALID_ARG, "%s: codes, norms, qjl_bits and qjl_rnorm must be non-NULL and aligned", who);
+  if (!scores || !aligned(scores, 4) || ld_s < n_k)
+    return fail(TQ_ERR_INVALID_ARG, "%s: scores must be non-NULL, 4-byte aligned, ld_s >= n_k", who);
+  if (n_q > INT64_MAX / 8 / ld_s) return fail(TQ_ERR_INVALID_ARG, "%s: scores size overflows", who);
+  if ((st = check_params(cfg, who))) return st;
+  const ScoreLayout L = score_layout(*cfg, n_q, n_k);
+  if (!ws || !aligned(ws, 256) || ws_bytes < L.total)
+    return fail(TQ_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned with %zu bytes (got %zu)", who, L.total,
+                ws_bytes);
+  tq::ScoreArgs a{};
+  a.q = q;
+  a.ld_q = ld_q;
+  a.n_q = n_q;
+  a.n_q_pad = L.n_q_pad;
+  a.codes = codes;
+  a.norms = norms;
+  a.qjl_bits = qjl_bits;
+  a.rnorm = (const uint16_t*)qjl_rnorm;
+  a.n_k = n_k;
+  a.n_k_pad = L.n_k_pad;
+  a.scores = scores;
+  a.ld_s = ld_s;
+  char* w = (char*)ws;
+  a.qrec = (int8_t*)(w + L.off_qrec);
+  a.qscale = (float*)(w + L.off_qscale);
+  a.krec = (int8_t*)(w + L.off_krec);
+  a.kscale = (float*)(w + L.off_kscale);
+  a.s_rot32 = (const float*)((const char*)cfg->qjl_params + (size_t)cfg->qjl_m * cfg->dt * sizeof(double));
+  fill_dbits(*cfg, a.dbits);
+  // ternary plane weights: level(mag) = sum over the bit subsets t of mag of w_t (Moebius inversion)
+  const int h = 1 << (cfg->bits - 1);
+  for (int t = 0; t < 8; ++t) a.plane_w[t] = 0.0f;
+  for (int t = 0; t < h; ++t) {
+    double wt = 0.0;
+    for (int s = 0; s < h; ++s)
+      if ((s & t) == s)
+        wt += (((__builtin_popcount(t) - __builtin_popcount(s)) & 1) ? -1.0 : 1.0) * cfg->cb->unit_centroids[h + s];
+    a.plane_w[t] = (float)wt;
+  }
+  a.dt = cfg->dt;
+  a.m = cfg->qjl_m;
+  a.kd = (cfg->dt + 63) / 64 * 64;
+  a.km = (cfg->qjl_m + 63) / 64 * 64;
+  a.q_f32 = q_dtype == TQ_F32;
+  a.inv_sqrt_dt = (float)(1.0 / std::sqrt((double)cfg->dt));
+  a.qjl_const = (float)(std::sqrt(M_PI / 2.0) / cfg->qjl_m);
+  hipError_t e = tq::launch_qjl_scores(*cfg, a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, who);
+  return ok();
 }
 
 tq_status tq_decode_attn(const tq_config* kcfg, const tq_config* vcfg, const void* q, tq_dtype q_dtype,
@@ -367,7 +469,11 @@ tq_status tq_decode_attn(const tq_config* kcfg, const tq_config* vcfg, const voi
 }
 
 size_t tq_workspace_size(int op, const tq_config* cfg, int64_t a, int64_t b, int64_t c) {
-  (void)op; (void)cfg; (void)a; (void)b; (void)c;
+  (void)c;
+  if (op == TQ_OP_QJL_SCORES) {
+    if (check_scores_config(cfg, "tq_workspace_size") || a < 0 || b < 0) return 0;
+    return score_layout(*cfg, a, b).total;
+  }
   return 0;
 }
 

@@ -72,10 +72,36 @@ struct QjlDecodeArgs {
   float inv_sqrt_dt;
 };
 
+// QJL scores (tq_qjl_scores): workspace-resident operands for the int8 MFMA kernel.
+struct ScoreArgs {
+  const void* q;
+  int64_t ld_q;
+  int64_t n_q, n_q_pad;      // queries, padded to a multiple of 16
+  const uint8_t* codes;
+  const void* norms;
+  const uint8_t* qjl_bits;
+  const uint16_t* rnorm;
+  int64_t n_k, n_k_pad;      // keys, padded to the scores key tile
+  float* scores;
+  int64_t ld_s;
+  int8_t* qrec;              // [n_q_pad][2*(kd+km)]: qhat hi, qhat lo, p hi, p lo (int8 limbs)
+  float* qscale;             // [n_q_pad][2]: fixed-point scale of qhat / sqrt(dt), of p * sqrt(pi/2)/m
+  int8_t* krec;              // [n_k_pad][planes*kd + km]: ternary planes, then the +-1 sign plane
+  float* kscale;             // [n_k_pad][2]: n_j, n_j * rho_j
+  const float* s_rot32;      // S~ [m][dt] float32
+  uint32_t dbits[8];
+  float plane_w[8];          // weight of each ternary plane (N(0,1) scale)
+  int32_t dt, m, kd, km;     // kd, km: dt and m rounded up to 64
+  int32_t q_f32;
+  float inv_sqrt_dt, qjl_const;
+};
+
 // launchers (return hipGetLastError() of the launch)
 hipError_t launch_encode(const tq_config& cfg, const EncodeArgs& a, hipStream_t s);
 hipError_t launch_decode(const tq_config& cfg, const DecodeArgs& a, bool nc, tq_dtype y_dtype, hipStream_t s);
 hipError_t launch_qjl_encode(const tq_config& cfg, const QjlEncodeArgs& a, hipStream_t s);
 hipError_t launch_qjl_decode(const tq_config& cfg, const QjlDecodeArgs& a, bool nc, tq_dtype y_dtype, hipStream_t s);
+hipError_t launch_qjl_scores(const tq_config& cfg, const ScoreArgs& a, hipStream_t s);
+int64_t scores_key_tile(int bits);
 
 }  // namespace tq

@@ -1,0 +1,121 @@
+"""GPU parity of tq_qjl_scores against the oracle's QJL estimator.
+
+Keys are encoded on the GPU (tq_quantize with TQ_QJL); the oracle then scores
+the GPU's own codes, norms, sign bits and residual norms, so the comparison
+isolates the scoring kernels.  Tolerance: |score_gpu - score_orc| <= 1e-4 *
+n_j * ||q_i|| (the Cauchy-Schwarz scale of the score; a pointwise relative
+error is undefined for scores near zero).
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import Codebook, qjl_scores
+
+torch = pytest.importorskip("torch")
+import kv_cache_vector_amd as tq  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL = 1e-4
+
+
+class Keys:
+    def __init__(self, keys, dt, bits, m, signs, S):
+        n = keys.shape[0]
+        self.n, self.dt, self.bits, self.m = n, dt, bits, m
+        self.signs, self.S = signs, S
+        self.qz = tq.Quantizer(dt, dt, bits, signs, flags=tq.TQ_QJL, qjl_m=m)
+        self.params = torch.empty(tq.tq_qjl_params_size(m, dt), dtype=torch.uint8, device=DEV)
+        tq.tq_qjl_prepare(self.qz, S, self.params)
+        x = torch.from_numpy(keys).to(DEV)
+        self.codes = torch.empty(n * dt * bits // 8, dtype=torch.uint8, device=DEV)
+        self.norms = torch.empty(n, dtype=torch.float16, device=DEV)
+        self.sbits = torch.empty(n * m // 8, dtype=torch.uint8, device=DEV)
+        self.rnorm = torch.empty(n, dtype=torch.float16, device=DEV)
+        tq.tq_quantize(self.qz, x, n, dt, self.codes, self.norms, self.sbits, self.rnorm)
+
+    def scores(self, q_np, ld_s=None):
+        nq = q_np.shape[0]
+        qt = torch.from_numpy(q_np).to(DEV)
+        qtype = tq.TQ_F32 if q_np.dtype == np.float32 else tq.TQ_F16
+        ld_s = self.n if ld_s is None else ld_s
+        out = torch.full((nq, ld_s), -99.0, dtype=torch.float32, device=DEV)
+        wsb = tq.tq_workspace_size(tq.TQ_OP_QJL_SCORES, self.qz, nq, self.n)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+        tq.tq_qjl_scores(self.qz, qt, qtype, nq, self.dt, self.codes, self.norms, self.sbits, self.rnorm, self.n, out,
+                         ld_s, ws, wsb)
+        torch.cuda.synchronize()
+        o = out.cpu().numpy()
+        if ld_s > self.n:
+            assert np.all(o[:, self.n:] == -99.0), "scores written outside the rows"
+        return o[:, :self.n]
+
+    def host(self):
+        n = self.n
+        return (self.codes.cpu().numpy().reshape(n, -1), self.norms.cpu().numpy(),
+                self.sbits.cpu().numpy().reshape(n, -1), self.rnorm.cpu().numpy())
+
+    def oracle(self, q_np, rows=None, cols=None):
+        codes, norms, sb, rn = self.host()
+        cols = np.arange(self.n) if cols is None else cols
+        q = q_np if rows is None else q_np[rows]
+        cb = Codebook.build(self.bits, self.dt)
+        return qjl_scores(q.astype(np.float64), codes[cols], norms[cols], sb[cols], rn[cols], self.signs, cb, self.S)
+
+
+def _check(gpu, orc, q, norms):
+    scale = np.linalg.norm(q.astype(np.float64), axis=1)[:, None] * norms.astype(np.float64)[None, :]
+    err = np.abs(gpu.astype(np.float64) - orc)
+    bound = TOL * scale + 1e-30
+    worst = float(np.max(err / np.maximum(scale, 1e-30)))
+    assert np.all(err <= bound), f"score error {worst:.3g} of n*||q|| exceeds {TOL}"
+    return worst
+
+
+@pytest.mark.parametrize("bits,dt,m,qdt", [(2, 128, 128, np.float16), (1, 128, 128, np.float32),
+                                           (3, 128, 64, np.float16), (2, 64, 128, np.float32),
+                                           (3, 64, 64, np.float16)])
+def test_scores_matrix(bits, dt, m, qdt):
+    n_k, n_q = 1000, 70  # ragged against the 16-query blocks and the 128/256-key tiles
+    keys = synth.kv_tensor(bits + dt, 1, 1, 0, n_k, dt, n_outliers=0).reshape(n_k, dt)
+    signs = synth.signs(bits, 2, dt)
+    S = synth.gaussian_matrix(bits + 1, 0, m, dt)
+    K = Keys(keys, dt, bits, m, signs, S)
+    q = synth.normal_f16(bits, 6, n_q * dt).reshape(n_q, dt).astype(qdt)
+    gpu = K.scores(q, ld_s=n_k + 7)
+    orc = K.oracle(q)
+    worst = _check(gpu, orc, q, K.host()[1][None, :][0])
+    print(f"bits={bits} dt={dt} m={m}: worst error {worst:.2e} of n*||q||")
+
+
+def test_scores_full_size_sampled():
+    """4096 queries x 65536 keys x 128, 2-bit + QJL (m = 128): the full score matrix on the GPU,
+    the oracle on 48 sampled queries x 4096 sampled keys."""
+    from synth.workloads import qjl_keys
+
+    w = qjl_keys()
+    K = Keys(w["keys"], 128, 2, 128, w["signs"], w["S"])
+    gpu = K.scores(w["q"])
+    rng = np.random.default_rng(0)
+    rows = np.sort(rng.choice(w["q"].shape[0], 48, replace=False))
+    cols = np.sort(rng.choice(K.n, 4096, replace=False))
+    orc = K.oracle(w["q"], rows, cols)
+    worst = _check(gpu[np.ix_(rows, cols)], orc, w["q"][rows], K.host()[1][cols])
+    print(f"full-size sample worst error {worst:.2e} of n*||q||")
+
+
+@pytest.mark.parametrize("total_bits", [2, 3, 4])
+@pytest.mark.parametrize("n_k", [512, 2048, 8192])
+def test_needle_retrieval(total_bits, n_k):
+    """A key planted near the query among random keys is the top-1 score (total_bits = MSE bits + 1 QJL bit)."""
+    dt = m = 128
+    rng = np.random.default_rng(total_bits * 100000 + n_k)
+    keys = synth.normal_f16(total_bits, 0, n_k * dt).reshape(n_k, dt).astype(np.float32)
+    q = synth.normal_f16(total_bits, 6, dt).reshape(1, dt).astype(np.float32)
+    needle = int(rng.integers(n_k))
+    keys[needle] = q[0] + 0.3 * rng.standard_normal(dt)
+    keys = keys.astype(np.float16)
+    K = Keys(keys, dt, total_bits - 1, m, synth.signs(total_bits, 2, dt), synth.gaussian_matrix(1, 0, m, dt))
+    gpu = K.scores(q.astype(np.float16))
+    assert int(np.argmax(gpu[0])) == needle
