@@ -389,6 +389,38 @@ tq_status check_scores_config(const tq_config* cfg, const char* who) {
   return TQ_OK;
 }
 
+// Decode attention: block-32 K and V (fp16 norms, 3 or 4 bits, no QJL or norm
+// correction), head_dim 128 or 256, up to 16 query heads per KV head.
+tq_status check_attn_config(const tq_config* kcfg, const tq_config* vcfg, int n_q_heads, int n_kv_heads,
+                            int64_t n_tokens, const char* who) {
+  tq_status st = check_config(kcfg, who);
+  if (st) return st;
+  if ((st = check_config(vcfg, who))) return st;
+  if (n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads || n_tokens < 0)
+    return fail(TQ_ERR_INVALID_ARG, "%s: need n_q_heads a positive multiple of n_kv_heads and n_tokens >= 0", who);
+  if (kcfg->head_dim != vcfg->head_dim) return fail(TQ_ERR_INVALID_ARG, "%s: K and V head_dim differ", who);
+  if (kcfg->dt != 32 || vcfg->dt != 32 || (kcfg->head_dim != 128 && kcfg->head_dim != 256))
+    return fail(TQ_ERR_UNSUPPORTED, "%s: needs the block-32 layout (dt = 32) with head_dim 128 or 256", who);
+  if ((kcfg->bits != 3 && kcfg->bits != 4) || (vcfg->bits != 3 && vcfg->bits != 4))
+    return fail(TQ_ERR_UNSUPPORTED, "%s: K and V must be 3- or 4-bit", who);
+  if (kcfg->flags || vcfg->flags)
+    return fail(TQ_ERR_UNSUPPORTED, "%s: QJL and norm correction are not supported in attention", who);
+  if (kcfg->norm_dtype != TQ_F16 || vcfg->norm_dtype != TQ_F16)
+    return fail(TQ_ERR_UNSUPPORTED, "%s: K and V norms must be fp16", who);
+  if (n_q_heads / n_kv_heads > 16) return fail(TQ_ERR_UNSUPPORTED, "%s: at most 16 query heads per KV head", who);
+  if (n_kv_heads > 65535 || n_tokens > ((int64_t)1 << 40))
+    return fail(TQ_ERR_UNSUPPORTED, "%s: at most 65535 KV heads and 2^40 tokens", who);
+  return TQ_OK;
+}
+
+// one fp32 partial (head_dim sums, running max, running sum) per wave, query head and token range
+size_t attn_workspace(const tq_config& kcfg, int n_q_heads, int n_kv_heads, int64_t n_tokens) {
+  const int64_t per_wg = tq::attn_tokens_per_wg();
+  const int64_t wgs = (n_tokens + per_wg - 1) / per_wg;
+  const int64_t parts = (int64_t)n_kv_heads * wgs * 4 * (n_q_heads / n_kv_heads);
+  return round256((size_t)parts * (size_t)(kcfg.head_dim + 2) * sizeof(float));
+}
+
 }  // namespace
 
 extern "C" {
@@ -463,9 +495,49 @@ tq_status tq_decode_attn(const tq_config* kcfg, const tq_config* vcfg, const voi
                          int n_q_heads, int n_kv_heads, int64_t n_tokens, const uint8_t* k_codes, const void* k_norms,
                          const uint8_t* v_codes, const void* v_norms, float scale, float* out, void* ws,
                          size_t ws_bytes, void* stream) {
-  (void)kcfg; (void)vcfg; (void)q; (void)q_dtype; (void)n_q_heads; (void)n_kv_heads; (void)n_tokens; (void)k_codes;
-  (void)k_norms; (void)v_codes; (void)v_norms; (void)scale; (void)out; (void)ws; (void)ws_bytes; (void)stream;
-  return fail(TQ_ERR_UNSUPPORTED, "tq_decode_attn: not available in this build");
+  const char* who = "tq_decode_attn";
+  tq_status st = check_attn_config(kcfg, vcfg, n_q_heads, n_kv_heads, n_tokens, who);
+  if (st) return st;
+  if (q_dtype != TQ_F16 && q_dtype != TQ_F32) return fail(TQ_ERR_INVALID_ARG, "%s: bad q_dtype", who);
+  if (!(scale <= 0.0f || std::isfinite(scale))) return fail(TQ_ERR_INVALID_ARG, "%s: scale is not finite", who);
+  if (n_tokens == 0) return ok();
+  if (!q || !aligned(q, esize(q_dtype)) || !out || !aligned(out, 4))
+    return fail(TQ_ERR_INVALID_ARG, "%s: q and out must be non-NULL and element-aligned", who);
+  if (!k_codes || !aligned(k_codes, 4) || !v_codes || !aligned(v_codes, 4) || !k_norms || !aligned(k_norms, 2) ||
+      !v_norms || !aligned(v_norms, 2))
+    return fail(TQ_ERR_INVALID_ARG, "%s: codes must be 4-byte and norms 2-byte aligned, non-NULL", who);
+  const size_t need = attn_workspace(*kcfg, n_q_heads, n_kv_heads, n_tokens);
+  if (!ws || !aligned(ws, 256) || ws_bytes < need)
+    return fail(TQ_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned with %zu bytes (got %zu)", who, need,
+                ws_bytes);
+  tq::AttnArgs a{};
+  a.q = q;
+  a.q_f32 = q_dtype == TQ_F32;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.group = n_q_heads / n_kv_heads;
+  a.head_dim = kcfg->head_dim;
+  a.n_tokens = n_tokens;
+  a.k_codes = k_codes;
+  a.k_norms = (const uint16_t*)k_norms;
+  a.v_codes = v_codes;
+  a.v_norms = (const uint16_t*)v_norms;
+  a.out = out;
+  a.part = (float*)ws;
+  a.tokens_per_wg = tq::attn_tokens_per_wg();
+  a.wg_per_head = (int32_t)((n_tokens + a.tokens_per_wg - 1) / a.tokens_per_wg);
+  uint32_t db[8];
+  fill_dbits(*kcfg, db);
+  a.kdbits = db[0];
+  fill_dbits(*vcfg, db);
+  a.vdbits = db[0];
+  fill_levels(*kcfg->cb, a.klevel);
+  fill_levels(*vcfg->cb, a.vlevel);
+  const double sc = scale > 0.0f ? (double)scale : 1.0 / std::sqrt((double)kcfg->head_dim);
+  a.kscale = (float)(sc / std::sqrt(32.0));
+  hipError_t e = tq::launch_decode_attn(kcfg->bits, vcfg->bits, a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, who);
+  return ok();
 }
 
 size_t tq_workspace_size(int op, const tq_config* cfg, int64_t a, int64_t b, int64_t c) {
@@ -473,6 +545,10 @@ size_t tq_workspace_size(int op, const tq_config* cfg, int64_t a, int64_t b, int
   if (op == TQ_OP_QJL_SCORES) {
     if (check_scores_config(cfg, "tq_workspace_size") || a < 0 || b < 0) return 0;
     return score_layout(*cfg, a, b).total;
+  }
+  if (op == TQ_OP_DECODE_ATTN) {
+    if (a <= 0 || b <= 0 || a > 65536 || a % b || c < 0 || check_config(cfg, "tq_workspace_size")) return 0;
+    return attn_workspace(*cfg, (int)a, (int)b, c);
   }
   return 0;
 }

@@ -96,6 +96,26 @@ struct ScoreArgs {
   float inv_sqrt_dt, qjl_const;
 };
 
+// Decode attention (tq_decode_attn), block-32 K and V with fp16 norms.
+struct AttnArgs {
+  const void* q;
+  int32_t q_f32;
+  int32_t n_q_heads, n_kv_heads, group;  // group = n_q_heads / n_kv_heads, <= 16
+  int32_t head_dim;
+  int64_t n_tokens;
+  const uint8_t* k_codes;
+  const uint16_t* k_norms;
+  const uint8_t* v_codes;
+  const uint16_t* v_norms;
+  float* out;
+  float* part;               // [n_kv_heads][wg_per_head][group][head_dim + 2] partial (acc, max, sum)
+  int32_t wg_per_head;
+  int32_t tokens_per_wg;
+  uint32_t kdbits, vdbits;   // D_K, D_V of the 32-long blocks
+  float klevel[16], vlevel[16];
+  float kscale;              // softmax scale / sqrt(32): score = kscale * sum_b n_b <H D q_b, c_b>
+};
+
 // launchers (return hipGetLastError() of the launch)
 hipError_t launch_encode(const tq_config& cfg, const EncodeArgs& a, hipStream_t s);
 hipError_t launch_decode(const tq_config& cfg, const DecodeArgs& a, bool nc, tq_dtype y_dtype, hipStream_t s);
@@ -103,5 +123,7 @@ hipError_t launch_qjl_encode(const tq_config& cfg, const QjlEncodeArgs& a, hipSt
 hipError_t launch_qjl_decode(const tq_config& cfg, const QjlDecodeArgs& a, bool nc, tq_dtype y_dtype, hipStream_t s);
 hipError_t launch_qjl_scores(const tq_config& cfg, const ScoreArgs& a, hipStream_t s);
 int64_t scores_key_tile(int bits);
+hipError_t launch_decode_attn(int kbits, int vbits, const AttnArgs& a, hipStream_t s);
+int attn_tokens_per_wg();
 
 }  // namespace tq
