@@ -11,6 +11,15 @@ tq_dequantize(K), tq_dequantize(V) through the C ABI.
 
 Prints one JSON line.  `value` is fp16 KV GB/s encoded+decoded: fp16 bytes
 read by the encodes plus fp16 bytes written by the decodes, per second.
+
+Two more workloads are timed and reported beside it (not part of `value`):
+  qjl   65536 keys x 128 fp16 encoded at 2 bits + the 1-bit QJL residual
+        (dense Gaussian S, m = 128), then scored against 4096 queries
+        (32 heads x 128 tokens): keys/s and scores/s;
+  attn  single-token decode attention over a 131072-token cache, head_dim
+        256, 4 KV heads, 16 query heads, 3-bit block-32 K and V: time per
+        call and compressed bytes read per second, with the cache warm in the
+        last-level cache and with it flushed before each call.
 """
 from __future__ import annotations
 
@@ -24,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+INT8_PEAK_TOPS = 5000.0
 LAYERS, KV_HEADS, TOKENS, HEAD_DIM, DT = 36, 8, 16384, 128, 32
 
 
@@ -131,12 +141,124 @@ def cpu_baseline(rows_total: int, bits: int, target_s: float = 15.0) -> dict:
                       f"encode+decode at {bits} bits, {dt_s:.1f} s single-threaded numpy float64"}
 
 
+def event_ms(torch, fn, reps, before=None):
+    """Median and minimum duration (ms) of fn() from HIP events on the current stream;
+    before() runs untimed ahead of each repetition."""
+    ts = []
+    for _ in range(reps):
+        if before is not None:
+            before()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ts.sort()
+    return ts[len(ts) // 2], ts[0]
+
+
+def bench_qjl(tq, torch, dev, reps):
+    """QJL workload: encode 65536 keys (2-bit MSE + QJL, m = 128), score 4096 queries against them."""
+    from synth import workloads
+
+    w = workloads.qjl_keys()
+    n, d, m, bits = w["keys"].shape[0], 128, 128, 2
+    nq = w["q"].shape[0]
+    qz = tq.Quantizer(d, d, bits, w["signs"], flags=tq.TQ_QJL, qjl_m=m)
+    params = torch.empty(tq.tq_qjl_params_size(m, d), dtype=torch.uint8, device=dev)
+    tq.tq_qjl_prepare(qz, w["S"], params)
+    x = torch.from_numpy(w["keys"]).to(dev)
+    q = torch.from_numpy(w["q"]).to(dev)
+    codes = torch.empty(n * d * bits // 8, dtype=torch.uint8, device=dev)
+    norms = torch.empty(n, dtype=torch.float16, device=dev)
+    sbits = torch.empty(n * m // 8, dtype=torch.uint8, device=dev)
+    rnorm = torch.empty(n, dtype=torch.float16, device=dev)
+    scores = torch.empty((nq, n), dtype=torch.float32, device=dev)
+    wsb = tq.tq_workspace_size(tq.TQ_OP_QJL_SCORES, qz, nq, n)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+    def enc():
+        tq.tq_quantize(qz, x, n, d, codes, norms, sbits, rnorm)
+
+    def score():
+        tq.tq_qjl_scores(qz, q, tq.TQ_F16, nq, d, codes, norms, sbits, rnorm, n, scores, n, ws, wsb)
+
+    for _ in range(2):
+        enc()
+        score()
+    enc_ms, enc_min = event_ms(torch, enc, reps)
+    sc_ms, sc_min = event_ms(torch, score, reps)
+    key_bytes = n * (d * 2 + d * bits // 8 + 2 + m // 8 + 2)  # fp16 key in; codes, norm, signs, rho out
+    n_scores = nq * n
+    # int8 MFMA work of the scoring kernel: per score, hi and lo limbs of the rotated query against
+    # 2^(b-1) ternary centroid planes, and of the projected query against the sign plane
+    macs = n_scores * 2 * ((1 << (bits - 1)) * d + m)
+    out = {"workload": "65536 keys x 128 fp16, 2-bit + QJL m=128; 4096 queries",
+           "encode_ms": round(enc_ms, 4), "keys_per_s": round(n / (enc_ms * 1e-3)),
+           "encode_GBs": round(key_bytes / (enc_ms * 1e-3) / 1e9, 1),
+           "scores_ms": round(sc_ms, 4), "scores_ms_min": round(sc_min, 4),
+           "scores_per_s": round(n_scores / (sc_ms * 1e-3)),
+           "scores_write_GBs": round(4 * n_scores / (sc_ms * 1e-3) / 1e9, 1),
+           "scores_int8_mfma_TOPS": round(2 * macs / (sc_ms * 1e-3) / 1e12, 1),
+           "scores_int8_mfma_frac": round(2 * macs / (sc_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)}
+    log(f"qjl: encode {enc_ms:.4f} ms ({out['keys_per_s']:.3g} keys/s), scores {sc_ms:.4f} ms "
+        f"({out['scores_per_s']:.3g} scores/s, {out['scores_write_GBs']} GB/s written)")
+    return out
+
+
+def bench_attn(tq, torch, dev, reps):
+    """Decode attention: 16 query heads over a 131072-token, 4-KV-head, head_dim-256 turbo3 cache."""
+    from synth import workloads
+
+    w = workloads.decode_cache()
+    H, T, hd = w["k"].shape[1], w["k"].shape[2], w["k"].shape[3]
+    hq = w["q"].shape[0]
+    rows = H * T
+    kq = tq.Quantizer(hd, 32, 3, w["signs_k"])
+    vq = tq.Quantizer(hd, 32, 3, w["signs_v"])
+    units = rows * hd // 32
+    plane = {}
+    for name, qz in (("k", kq), ("v", vq)):
+        x = torch.from_numpy(w[name].reshape(rows, hd)).to(dev)
+        plane[name] = (torch.empty(units * 12, dtype=torch.uint8, device=dev),
+                       torch.empty(units, dtype=torch.float16, device=dev))
+        tq.tq_quantize(qz, x, rows, hd, plane[name][0], plane[name][1])
+        del x
+    q = torch.from_numpy(w["q"]).to(dev)
+    out = torch.empty((hq, hd), dtype=torch.float32, device=dev)
+    wsb = tq.tq_workspace_size(tq.TQ_OP_DECODE_ATTN, kq, hq, H, T)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def attn():
+        tq.tq_decode_attn(kq, vq, q, tq.TQ_F16, hq, H, T, plane["k"][0], plane["k"][1], plane["v"][0],
+                          plane["v"][1], 0.0, out, ws, wsb)
+
+    for _ in range(3):
+        attn()
+    warm_ms, warm_min = event_ms(torch, attn, reps)
+    cold_ms, cold_min = event_ms(torch, attn, reps, before=lambda: flush.zero_())
+    nbytes = 2 * units * (12 + 2)  # K and V codes and norms
+    res = {"workload": "decode attention, head_dim 256, 4 KV heads, 16 query heads, 131072 tokens, turbo3 K/V",
+           "us_flushed": round(cold_ms * 1e3, 2), "us_warm": round(warm_ms * 1e3, 2),
+           "us_min_flushed": round(cold_min * 1e3, 2), "compressed_bytes": nbytes,
+           "GBs_flushed": round(nbytes / (cold_ms * 1e-3) / 1e9, 1),
+           "GBs_warm": round(nbytes / (warm_ms * 1e-3) / 1e9, 1),
+           "frac_hbm_flushed": round(nbytes / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "tokens_per_s_flushed": round(H * T / (cold_ms * 1e-3))}
+    log(f"attn: {cold_ms * 1e3:.1f} us flushed ({res['GBs_flushed']} GB/s), {warm_ms * 1e3:.1f} us warm")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=("all", "codec", "qjl", "attn"), default="all",
+                    help="run one workload (for profiling runs); the JSON line needs 'all'")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this quantizer's hot path has no cross-GPU step, and runs on more "
@@ -149,6 +271,10 @@ def main():
 
     tq.lib()
     dev = torch.device("cuda:0")
+    reps = max(5, args.steps)
+    if args.only in ("qjl", "attn"):
+        (bench_qjl if args.only == "qjl" else bench_attn)(tq, torch, dev, reps)
+        return
     k, v, signs_k, signs_v, rows = make_cache(tq, torch, dev)
     ok, ov = torch.empty_like(k), torch.empty_like(v)
 
@@ -174,6 +300,15 @@ def main():
             f"decode {dec_ms:.3f} ms ({ab['per_launch'] / dec_ms / 1e6:.0f} GB/s)")
         del codec
         torch.cuda.empty_cache()
+
+    if args.only == "codec":
+        return
+    del k, v, ok, ov
+    torch.cuda.empty_cache()
+    qjl = bench_qjl(tq, torch, dev, reps)
+    torch.cuda.empty_cache()
+    attn = bench_attn(tq, torch, dev, reps)
+    torch.cuda.empty_cache()
 
     r = results[3]
     fp16_bytes_step = 2 * 2 * r["bytes"]["fp16"]  # K and V, encoded and decoded
@@ -212,6 +347,8 @@ def main():
                    "turbo3_ms": round(r["dec_ms"], 4), "turbo4_ms": round(r4["dec_ms"], 4)},
         "turbo4_value": round(2 * 2 * r4["bytes"]["fp16"] / (r4["ms"] * 1e-3) / 1e9, 1),
         "copy_reference_GBs": round(copy_gbs, 1),
+        "qjl": qjl,
+        "attn": attn,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")

@@ -183,14 +183,29 @@ tq_status tq_qjl_scores(const tq_config* cfg, const void* q, tq_dtype q_dtype, i
 /*
  * Single-token decode attention over a quantized cache ([Fork] "Fused tile
  * path": q is rotated once, scores and the value sum are formed in the
- * rotated domain, one inverse transform per output block):
+ * rotated domain, one inverse transform per output block at the end):
  *   out[h] = sum_j softmax_j(scale * <q_h, k~_j>) v~_j
- * with query head h reading KV head h / (n_q_heads / n_kv_heads).
- * K and V units are (kv head, token, block) ordered: kcfg/vcfg give their
- * formats (same head_dim, no QJL, no norm correction).  q: [n_q_heads][head_dim]
- * of q_dtype; out: device fp32 [n_q_heads][head_dim].  ws: device workspace of
- * tq_workspace_size(TQ_OP_DECODE_ATTN, kcfg, n_q_heads, n_kv_heads, n_tokens)
- * bytes.  scale <= 0 selects 1/sqrt(head_dim).
+ * with query head h reading KV head h / (n_q_heads / n_kv_heads) and k~, v~
+ * the tq_dequantize reconstructions of the cached units.
+ *   kcfg, vcfg  formats of K and V: block-32 layout (dt = 32), fp16 norms,
+ *               3 or 4 bits each (K and V may differ), equal head_dim of 128
+ *               or 256, no flags (TQ_ERR_UNSUPPORTED otherwise)
+ *   q           device, [n_q_heads][head_dim] of q_dtype, contiguous
+ *   n_q_heads   a multiple of n_kv_heads, at most 16 query heads per KV head
+ *   k_codes, v_codes  device, 4-byte aligned, units in (kv head, token,
+ *               block) order, i.e. rows of tq_quantize over
+ *               [n_kv_heads][n_tokens][head_dim]
+ *   k_norms, v_norms  device fp16, same unit order
+ *   scale       softmax scale; <= 0 selects 1/sqrt(head_dim)
+ *   out         device fp32 [n_q_heads][head_dim]
+ *   ws          256-byte aligned device workspace of
+ *               tq_workspace_size(TQ_OP_DECODE_ATTN, kcfg, n_q_heads,
+ *               n_kv_heads, n_tokens) bytes (per-wave partial maxima, sums
+ *               and value accumulators; contents are scratch)
+ * Precision: scores use a two-term fp16 split of the rotated query and of the
+ * K centroids (about 2^-22 relative); the value sum takes the softmax weight
+ * times the V norm and the V centroids as fp16 operands (unit roundoff 2^-11)
+ * with fp32 accumulation.  n_tokens = 0 leaves out untouched.
  */
 tq_status tq_decode_attn(const tq_config* kcfg, const tq_config* vcfg, const void* q, tq_dtype q_dtype,
                          int n_q_heads, int n_kv_heads, int64_t n_tokens, const uint8_t* k_codes, const void* k_norms,

@@ -7,24 +7,33 @@
 //   values: sum_j p_j D H c_j = D H sum_j p_j c_j, so the weighted sum stays
 //           in the rotated domain and one inverse transform per output block
 //           runs at the very end.
-// All query heads of one KV head share every K and V read ([Fork] GQA note:
-// the decode kernel must serve the whole query group per KV read).
+// All query heads of one KV head share every K and V read (same page, "Fused
+// kernel": without that GQA amortization a fused kernel loses to f16).
 //
-// Per workgroup: one KV head, a range of tokens, 4 waves of 256 tokens each,
-// 32-token tiles:
-//   K side   each lane expands the 3/4-bit codes of 8 coordinates of one token
-//            through an LDS pair table into fp16 hi/lo operands; three
-//            v_mfma_f32_16x16x32_f16 per 32-block (q_hi c_hi + q_lo c_hi +
-//            q_hi c_lo) give the block dot products to ~2^-22, each scaled by
-//            the block norm in fp32 and summed over blocks.
-//   softmax  online (running max and sum) per query head over 16-lane rows.
-//   V side   codes expanded token-major into a wave-private LDS tile (16-dim
-//            chunks XOR-swizzled by token); ds_read_b64_tr_b16 returns four
-//            tokens of one coordinate per lane, the operand layout of the
-//            value MFMA (K = 32 tokens); the block norms of V are folded into
-//            the softmax weights (A operand, fp16).
-// Each wave writes its partial (acc, max, sum); a merge kernel rescales and
-// adds the partials, then applies D_V H once per 32-block.
+// Work split.  A workgroup owns one KV head and a token range and walks it in
+// 64-token tiles; its 4 waves split the head's 32-blocks (wave w owns blocks
+// w*NB/4 ..), so each wave reads only its blocks' codes and keeps only their
+// accumulators.  Per tile:
+//   loads    next tile's K windows, K/V norms and V records go straight to
+//            registers one tile ahead (no staging buffer);
+//   K side   per owned block, the 64 tokens form 4 subtiles of 16; each lane
+//            expands 8 coordinates of one token through an LDS pair table
+//            into fp16 hi/lo operands, and three v_mfma_f32_16x16x32_f16
+//            (q_hi c_hi + q_lo c_hi + q_hi c_lo) give the block dot products
+//            to ~2^-22.  The query operand of subtile st is non-zero only in
+//            rows st*GP .. st*GP+GP-1 (GP = query heads padded to 4, 8 or 16),
+//            so 16/GP subtiles accumulate into one 16x16 result with every
+//            lane holding live scores; block norms scale it in fp32;
+//   exchange the waves' partial scores (over their own blocks) are summed
+//            through LDS, after which every wave holds the full scores;
+//   softmax  online (running max and sum) per query head;
+//   V side   each lane expands one token's records (pair table, scaled by
+//            the block norm with one packed fp16 multiply per pair) into a
+//            wave-private LDS tile; ds_read_b64_tr_b16 returns four tokens of
+//            one coordinate per lane, the B layout of the value MFMA (K = 32
+//            tokens); the softmax weights are the fp16 A operand.
+// Each workgroup writes one partial (acc, max, sum) per query head; a merge
+// kernel rescales and adds the partials, then applies D_V H once per block.
 #include <hip/hip_fp16.h>
 
 #include "tq_device.h"
@@ -36,49 +45,70 @@ namespace {
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 typedef __attribute__((address_space(3))) short lds_short;
 
-constexpr int kAttnWaves = 4;
-constexpr int kTile = 32;                       // tokens per tile (K of the value MFMA)
-constexpr int kTokPerWave = 256;
-constexpr int kTokPerWG = kAttnWaves * kTokPerWave;
+constexpr int kWaves = 4;
+constexpr int kTile = 64;     // tokens per tile
+constexpr int kMergeLanes = 8;
 
 __device__ __forceinline__ uint32_t pack_h2(_Float16 lo, _Float16 hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
 }
 
-__device__ __forceinline__ float row16_max(float v) {
+// max / sum of v over the lanes that hold the same query head: the 16 lanes of
+// a row group, and the S row groups whose stacked subtiles share the head
+template <int S>
+__device__ __forceinline__ float head_max(float v) {
 #pragma unroll
   for (int m = 1; m < 16; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
+  if (S >= 2) v = fmaxf(v, __shfl_xor(v, 32));
+  if (S >= 4) v = fmaxf(v, __shfl_xor(v, 16));
   return v;
 }
 
-__device__ __forceinline__ float row16_sum(float v) {
+template <int S>
+__device__ __forceinline__ float head_sum(float v) {
 #pragma unroll
   for (int m = 1; m < 16; m <<= 1) v += __shfl_xor(v, m);
+  if (S >= 2) v += __shfl_xor(v, 32);
+  if (S >= 4) v += __shfl_xor(v, 16);
   return v;
 }
 
-// bits [pos, pos + width) of a little-endian multi-word code record
-__device__ __forceinline__ uint32_t bits_at(const uint32_t* w, int pos, int width) {
-  const int wi = pos >> 5, sh = pos & 31;
-  if (sh + width <= 32) return __builtin_amdgcn_ubfe(w[wi], sh, width);
-  return __builtin_amdgcn_ubfe(__builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh), 0, width);
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int NB, int KB, int VB, int GM>
+// One tile's worth of this lane's global data, loaded a tile ahead.
+template <int NBW, int KB, int VB, int NC>
+struct TileRegs {
+  uint32_t kw[NBW][4][2];  // K: 2 words covering this lane's 8 coordinates, per owned block and subtile
+  uint32_t kn[NC];         // K norms (fp16) of the token this lane scales, per accumulator; NBW halves
+  uint32_t vw[NBW][VB];    // V: whole record of token `lane`, per owned block
+  uint32_t vn;             // V norms (fp16) of token `lane`, NBW halves
+};
+
+template <int NB, int KB, int VB, int GP>
 __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   constexpr int HD = NB * 32;
+  constexpr int NBW = NB / kWaves;  // blocks per wave
+  constexpr int S = 16 / GP;        // subtiles stacked per 16x16 accumulator
+  constexpr int NC = 4 / S;         // accumulators per block for the 4 subtiles
   constexpr int KL = 1 << KB, VL = 1 << VB;
-  __shared__ uint2 ktab[KL * KL];      // pair of K codes -> (fp16 hi pair, fp16 lo pair)
-  __shared__ uint32_t vtab[VL * VL];   // pair of V codes -> fp16 pair
-  __shared__ __attribute__((aligned(16))) _Float16 qh[GM * HD];
-  __shared__ __attribute__((aligned(16))) _Float16 ql[GM * HD];
-  __shared__ __attribute__((aligned(16))) _Float16 vt[kAttnWaves][kTile * HD];
-  __shared__ _Float16 vn[kAttnWaves][kTile * NB];
-  __shared__ float pt[kAttnWaves][GM * kTile];
+  constexpr int VROW = NBW * 32;    // fp16 per V tile row (one token, the wave's blocks)
+  constexpr int NCH = 2 * NBW;      // 16-coordinate chunks per V tile row
+  static_assert(NBW == 1 || NBW == 2, "head_dim 128 or 256");
+
+  __shared__ uint2 ktab[KL * KL];     // pair of K codes -> (fp16 hi pair, fp16 lo pair), N(0,1) scale
+  __shared__ uint32_t vtab[VL * VL];  // pair of V codes -> fp16 pair
+  __shared__ __attribute__((aligned(16))) _Float16 vt[kWaves][kTile * VROW];
+  __shared__ __attribute__((aligned(16))) _Float16 pt[kWaves][GP * kTile];
+  __shared__ float xs[2][kWaves][NC * 4][64];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = lane & 15, g = lane >> 4;
@@ -94,9 +124,11 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   for (int e = tid; e < VL * VL; e += 256)
     vtab[e] = pack_h2((_Float16)a.vlevel[e & (VL - 1)], (_Float16)a.vlevel[e >> VB]);
 
-  // rotated query blocks of this KV head's group: qhat_b = H D_K q_b / sqrt(32), split fp16 hi + lo
-  float* qf = reinterpret_cast<float*>(&vt[0][0]);  // GM * HD floats, staging only
-  for (int e = tid; e < GM * HD; e += 256) {
+  // rotated query blocks qhat_b = H D_K q_b / sqrt(32) of the group's heads (rows >= G zero),
+  // FWHT staged in fp32 over the V tile area
+  float* qf = reinterpret_cast<float*>(&vt[0][0]);
+  static_assert(sizeof(vt) >= sizeof(float) * GP * HD, "query staging fits the V tiles");
+  for (int e = tid; e < GP * HD; e += 256) {
     const int r = e / HD, d = e % HD;
     float v = 0.0f;
     if (r < G) {
@@ -107,7 +139,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   }
   __syncthreads();
   for (int hb = 1; hb < 32; hb <<= 1) {
-    for (int e = tid; e < GM * HD / 2; e += 256) {
+    for (int e = tid; e < GP * HD / 2; e += 256) {
       const int r = e / (HD / 2), rem = e % (HD / 2), b = rem / 16, p = rem % 16;
       const int i = (p / hb) * 2 * hb + (p % hb);
       float* blk = qf + r * HD + 32 * b;
@@ -117,223 +149,292 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
     }
     __syncthreads();
   }
-  for (int e = tid; e < GM * HD; e += 256) {
-    const float v = qf[e] * 0.17677669529663688f;  // 1/sqrt(32)
-    const _Float16 h = (_Float16)v;
-    qh[e] = h;
-    ql[e] = (_Float16)(v - (float)h);
-  }
-  __syncthreads();
 
-  // this lane's query operands (read per block from LDS): row = query head of the group,
-  // coordinates 8g..8g+7 of the block; rows >= GM multiply zeros
-  const int qrow = row < GM ? row : 0;
-  const bool qlive = row < GM;
+  // query operands of this lane: row `row` of subtile slot sv is head row % GP when row / GP == sv
+  v8h aqh[NBW][S], aql[NBW][S];
+#pragma unroll
+  for (int bl = 0; bl < NBW; ++bl) {
+    const int b = NBW * wave + bl;
+    v8h h8, l8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float v = qf[(row % GP) * HD + 32 * b + 8 * g + j] * 0.17677669529663688f;  // 1/sqrt(32)
+      h8[j] = (_Float16)v;
+      l8[j] = (_Float16)(v - (float)h8[j]);
+    }
+#pragma unroll
+    for (int sv = 0; sv < S; ++sv) {
+      const bool on = row / GP == sv;
+      const v8h z = {0, 0, 0, 0, 0, 0, 0, 0};
+      aqh[bl][sv] = on ? h8 : z;
+      aql[bl][sv] = on ? l8 : z;
+    }
+  }
+  __syncthreads();  // query staging is overwritten by the V tiles below
 
   const int64_t T = a.n_tokens;
   const uint8_t* kbase = a.k_codes + (int64_t)kvh * T * NB * (4 * KB);
   const uint8_t* vbase = a.v_codes + (int64_t)kvh * T * NB * (4 * VB);
   const uint16_t* knb = a.k_norms + (int64_t)kvh * T * NB;
   const uint16_t* vnb = a.v_norms + (int64_t)kvh * T * NB;
-  _Float16* vtile = vt[wave];
+  const int b0 = NBW * wave;  // first owned block
+
+  // this lane's K window: bits [24g, 24g + 24) of a 3-bit record (funnel shift of the two words
+  // holding them, the second clamped to the record) or word g of a 4-bit one
+  const int kword = KB == 4 ? g : (24 * g) >> 5;
+  const int kword2 = KB == 4 ? g : (kword + 1 < KB ? kword + 1 : KB - 1);
+  const int kshift = KB == 4 ? 0 : (24 * g) & 31;
+  // token (within the tile) whose K norm scales accumulator cc in this lane
+  auto ktok = [&](int cc) { return 16 * (cc * S + (4 * g) / GP) + row; };
+
+  const int64_t t_begin = (int64_t)blockIdx.x * a.tokens_per_wg;
+  const int64_t t_end = t_begin + a.tokens_per_wg < T ? t_begin + a.tokens_per_wg : T;
+
+  using Regs = TileRegs<NBW, KB, VB, NC>;
+  auto load = [&](Regs& r, int64_t tb) {
+#pragma unroll
+    for (int bl = 0; bl < NBW; ++bl) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        int64_t t = tb + 16 * st + row;
+        t = t < T ? t : T - 1;
+        const uint32_t* rp = reinterpret_cast<const uint32_t*>(kbase + (t * NB + b0 + bl) * (4 * KB));
+        r.kw[bl][st][0] = rp[kword];
+        r.kw[bl][st][1] = KB == 4 ? 0u : rp[kword2];
+      }
+    }
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      int64_t t = tb + ktok(cc);
+      t = t < T ? t : T - 1;
+      r.kn[cc] = NBW == 2 ? *reinterpret_cast<const uint32_t*>(knb + t * NB + b0) : (uint32_t)knb[t * NB + b0];
+    }
+    int64_t t = tb + lane;
+    t = t < T ? t : T - 1;
+#pragma unroll
+    for (int bl = 0; bl < NBW; ++bl) {
+      const uint32_t* rp = reinterpret_cast<const uint32_t*>(vbase + (t * NB + b0 + bl) * (4 * VB));
+#pragma unroll
+      for (int q = 0; q < VB; ++q) r.vw[bl][q] = rp[q];
+    }
+    r.vn = NBW == 2 ? *reinterpret_cast<const uint32_t*>(vnb + t * NB + b0) : (uint32_t)vnb[t * NB + b0];
+  };
+
   float m_run[4], lsum[4];
-  v4f acc[NB][2];
+  v4f acc[NBW][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     m_run[i] = -INFINITY;
     lsum[i] = 0.0f;
   }
 #pragma unroll
-  for (int b = 0; b < NB; ++b) acc[b][0] = acc[b][1] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int bl = 0; bl < NBW; ++bl) acc[bl][0] = acc[bl][1] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int64_t t_begin = (int64_t)blockIdx.x * a.tokens_per_wg + (int64_t)wave * kTokPerWave;
-  const int64_t t_end = t_begin + kTokPerWave < T ? t_begin + kTokPerWave : T;
-  for (int64_t tb = t_begin; tb < t_end; tb += kTile) {
-    // ---- value tile: decode token-major into LDS (chunk c of token t at chunk c ^ (t & 7))
+  _Float16* vtile = vt[wave];
+  _Float16* ptile = pt[wave];
+  Regs nxt;
+  if (t_begin < t_end) load(nxt, t_begin);
+  int parity = 0;
+  for (int64_t tb = t_begin; tb < t_end; tb += kTile, parity ^= 1) {
+    const Regs cur = nxt;
+    if (tb + kTile < t_end) load(nxt, tb + kTile);
+
+    // ---- value records of token `lane` -> V tile row `lane` (norm folded in, chunks swizzled)
 #pragma unroll
-    for (int k = 0; k < NB / 2; ++k) {
-      const int u = lane + 64 * k, t = u / NB, b = u % NB;
-      const int64_t tok = tb + t;
-      uint32_t w[VB] = {};
-      _Float16 nv = (_Float16)0.0f;
-      const bool live = tok < T;
-      if (live) {
-        const uint32_t* rp = reinterpret_cast<const uint32_t*>(vbase + (tok * NB + b) * (4 * VB));
-#pragma unroll
-        for (int q = 0; q < VB; ++q) w[q] = rp[q];
-        nv = __builtin_bit_cast(_Float16, vnb[tok * NB + b]);
-      }
-      vn[wave][t * NB + b] = nv;
+    for (int bl = 0; bl < NBW; ++bl) {
+      const _Float16 nv = __builtin_bit_cast(_Float16, (uint16_t)(cur.vn >> (16 * bl)));
+      const v2h nv2 = {nv, nv};
       uint32_t o[16];
 #pragma unroll
-      for (int pp = 0; pp < 16; ++pp) o[pp] = live ? vtab[bits_at(w, 2 * VB * pp, 2 * VB)] : 0u;
+      for (int pp = 0; pp < 16; ++pp) {
+        const int pos = 2 * VB * pp, wi = pos >> 5, sh = pos & 31;
+        const uint32_t bits = sh + 2 * VB <= 32 ? __builtin_amdgcn_ubfe(cur.vw[bl][wi], sh, 2 * VB)
+                                                : __builtin_amdgcn_ubfe(
+                                                      __builtin_amdgcn_alignbit(cur.vw[bl][wi + 1], cur.vw[bl][wi], sh),
+                                                      0, 2 * VB);
+        const v2h c = __builtin_bit_cast(v2h, vtab[bits]);
+        o[pp] = __builtin_bit_cast(uint32_t, c * nv2);
+      }
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const int c = 2 * b + half;
-        _Float16* dst = vtile + t * HD + 16 * (c ^ (t & 7));
+        const int c = 2 * bl + half;
+        _Float16* dst = vtile + lane * VROW + 16 * (c ^ ((lane >> 1) & (NCH - 1)));
         reinterpret_cast<uint4*>(dst)[0] = make_uint4(o[8 * half], o[8 * half + 1], o[8 * half + 2], o[8 * half + 3]);
         reinterpret_cast<uint4*>(dst)[1] = make_uint4(o[8 * half + 4], o[8 * half + 5], o[8 * half + 6], o[8 * half + 7]);
       }
     }
 
-    // ---- key side: scores of 2 x 16 tokens for the group's query heads
-    float s[2][4];
+    // ---- key side: partial scores over the owned blocks
+    float s[NC][4];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int64_t tok = tb + 16 * st + row;
-      const bool live = tok < T;
+    for (int cc = 0; cc < NC; ++cc) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[st][i] = 0.0f;
+      for (int i = 0; i < 4; ++i) s[cc][i] = 0.0f;
+    }
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        // this lane's 8 coordinates 8g..8g+7 of block b: 8*KB bits from bit 8*g*KB of the record
-        uint32_t win = 0u;
-        float nk = 0.0f;
-        if (live) {
-          const uint32_t* rp = reinterpret_cast<const uint32_t*>(kbase + (tok * NB + b) * (4 * KB));
-          const int pos = 8 * KB * g, i0 = pos >> 5, i1 = i0 + 1 < KB ? i0 + 1 : KB - 1;
-          win = __builtin_amdgcn_alignbit(rp[i1], rp[i0], pos & 31);
-          nk = __half2float(__ushort_as_half(knb[tok * NB + b]));
-        }
-        uint32_t bh[4], bl[4];
+    for (int bl = 0; bl < NBW; ++bl) {
 #pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
-          const uint2 e = ktab[__builtin_amdgcn_ubfe(win, 2 * KB * pp, 2 * KB)];
-          bh[pp] = e.x;
-          bl[pp] = e.y;
-        }
-        const v8h bhi = __builtin_bit_cast(v8h, make_uint4(bh[0], bh[1], bh[2], bh[3]));
-        const v8h blo = __builtin_bit_cast(v8h, make_uint4(bl[0], bl[1], bl[2], bl[3]));
+      for (int cc = 0; cc < NC; ++cc) {
         v4f c = {0.0f, 0.0f, 0.0f, 0.0f};
-        const v8h zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
-        const v8h aqh = qlive ? *reinterpret_cast<const v8h*>(&qh[qrow * HD + 32 * b + 8 * g]) : zero8;
-        const v8h aql = qlive ? *reinterpret_cast<const v8h*>(&ql[qrow * HD + 32 * b + 8 * g]) : zero8;
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(aqh, bhi, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(aql, bhi, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(aqh, blo, c, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[st][i] = __builtin_fmaf(nk, c[i], s[st][i]);
+        for (int sv = 0; sv < S; ++sv) {
+          const int st = cc * S + sv;
+          const uint32_t win = KB == 4 ? cur.kw[bl][st][0]
+                                       : __builtin_amdgcn_alignbit(cur.kw[bl][st][1], cur.kw[bl][st][0], kshift);
+          uint32_t bh[4], bo[4];
+#pragma unroll
+          for (int pp = 0; pp < 4; ++pp) {
+            const uint2 e = ktab[__builtin_amdgcn_ubfe(win, 2 * KB * pp, 2 * KB)];
+            bh[pp] = e.x;
+            bo[pp] = e.y;
+          }
+          const v8h bhi = __builtin_bit_cast(v8h, make_uint4(bh[0], bh[1], bh[2], bh[3]));
+          const v8h blo = __builtin_bit_cast(v8h, make_uint4(bo[0], bo[1], bo[2], bo[3]));
+          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(aqh[bl][sv], bhi, c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(aql[bl][sv], bhi, c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(aqh[bl][sv], blo, c, 0, 0, 0);
+        }
+        const float nk = __half2float(__ushort_as_half((uint16_t)(cur.kn[cc] >> (16 * bl))));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[cc][i] = __builtin_fmaf(nk, c[i], s[cc][i]);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s[st][i] = live ? s[st][i] * a.kscale : -INFINITY;
     }
 
-    // ---- online softmax: row 4g + i of the tile, reduced over the 16 token lanes
+    // ---- sum the waves' partial scores
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xs[parity][wave][cc * 4 + i][lane] = s[cc][i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      const bool live = tb + ktok(cc) < T;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) v += xs[parity][w][cc * 4 + i][lane];
+        s[cc][i] = live ? v * a.kscale : -INFINITY;
+      }
+    }
+
+    // ---- online softmax; register i of this lane belongs to head (4g + i) % GP
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float mt = row16_max(fmaxf(s[0][i], s[1][i]));
-      const float m_new = fmaxf(m_run[i], mt);
-      const bool none = m_new == -INFINITY;
-      const float alpha = (none || m_run[i] == -INFINITY) ? 0.0f : __expf(m_run[i] - m_new);
-      const float p0 = none ? 0.0f : __expf(s[0][i] - m_new);
-      const float p1 = none ? 0.0f : __expf(s[1][i] - m_new);
-      lsum[i] = lsum[i] * alpha + row16_sum(p0 + p1);
+      float mt = s[0][i];
+#pragma unroll
+      for (int cc = 1; cc < NC; ++cc) mt = fmaxf(mt, s[cc][i]);
+      mt = head_max<S>(mt);
+      const float m_new = fmaxf(m_run[i], mt);  // finite: every tile holds a live token
+      const float alpha = m_run[i] == -INFINITY ? 0.0f : __expf(m_run[i] - m_new);
+      float ps = 0.0f;
+      const int r = 4 * g + i, h = r % GP, sub = r / GP;
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        const float p = __expf(s[cc][i] - m_new);
+        ps += p;
+        ptile[h * kTile + 16 * (cc * S + sub) + row] = (_Float16)p;
+      }
+      lsum[i] = lsum[i] * alpha + head_sum<S>(ps);
       m_run[i] = m_new;
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        acc[b][0][i] *= alpha;
-        acc[b][1][i] *= alpha;
-      }
-      const int r = 4 * g + i;
-      if (r < GM) {
-        pt[wave][r * kTile + row] = p0;
-        pt[wave][r * kTile + 16 + row] = p1;
+      for (int bl = 0; bl < NBW; ++bl) {
+        acc[bl][0][i] *= alpha;
+        acc[bl][1][i] *= alpha;
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wave_sync();
 
-    // ---- value side: A = softmax weight * value norm (fp16), B = 4 tokens x 1 coordinate per tr read
-    float pa[8];
+    // ---- value side: acc[head][coordinate] += p[head][token] * (nV c)[token][coordinate]
 #pragma unroll
-    for (int j = 0; j < 8; ++j) pa[j] = (row < G && row < GM) ? pt[wave][row * kTile + 8 * g + j] : 0.0f;
+    for (int half = 0; half < kTile / 32; ++half) {
+      const v8h z = {0, 0, 0, 0, 0, 0, 0, 0};
+      const v8h av = row < G ? *reinterpret_cast<const v8h*>(ptile + (row % GP) * kTile + 32 * half + 8 * g) : z;
+      const int t1 = 32 * half + 8 * g + (row >> 2), t2 = t1 + 4;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      v8h av;
+      for (int bl = 0; bl < NBW; ++bl) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) av[j] = (_Float16)(pa[j] * (float)vn[wave][(8 * g + j) * NB + b]);
-#pragma unroll
-      for (int nh = 0; nh < 2; ++nh) {
-        const int c = 2 * b + nh;
-        const int t1 = 8 * g + (row >> 2), t2 = t1 + 4;
-        lds_short* base = (lds_short*)vtile;
-        const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4s*)(base + t1 * HD + 16 * (c ^ (t1 & 7)) + 4 * (row & 3)));
-        const v4s r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4s*)(base + t2 * HD + 16 * (c ^ (t2 & 7)) + 4 * (row & 3)));
-        const v4h h1 = __builtin_bit_cast(v4h, r1), h2 = __builtin_bit_cast(v4h, r2);
-        const v8h bv = {h1[0], h1[1], h1[2], h1[3], h2[0], h2[1], h2[2], h2[3]};
-        acc[b][nh] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc[b][nh], 0, 0, 0);
+        for (int nh = 0; nh < 2; ++nh) {
+          const int c = 2 * bl + nh;
+          lds_short* base = (lds_short*)vtile;
+          const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4s*)(base + t1 * VROW + 16 * (c ^ ((t1 >> 1) & (NCH - 1))) + 4 * (row & 3)));
+          const v4s r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4s*)(base + t2 * VROW + 16 * (c ^ ((t2 >> 1) & (NCH - 1))) + 4 * (row & 3)));
+          const v4h h1 = __builtin_bit_cast(v4h, r1), h2 = __builtin_bit_cast(v4h, r2);
+          const v8h bv = {h1[0], h1[1], h1[2], h1[3], h2[0], h2[1], h2[2], h2[3]};
+          acc[bl][nh] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc[bl][nh], 0, 0, 0);
+        }
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wave_sync();
   }
 
-  // ---- this wave's partial: acc rows = query heads 4g + i, columns = coordinates
-  const int64_t pw = ((int64_t)kvh * a.wg_per_head + blockIdx.x) * kAttnWaves + wave;
-  float* pbase = a.part + pw * G * (HD + 2);
+  // ---- partial of this workgroup: part[kvh][wg][head][HD coordinates, max, sum]
+  float* pbase = a.part + ((int64_t)kvh * a.wg_per_head + blockIdx.x) * G * (HD + 2);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = 4 * g + i;
-    if (r >= G) continue;
+    const int h = 4 * g + i;  // accumulator row = query head
+    if (h >= G) continue;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      pbase[r * (HD + 2) + 32 * b + row] = acc[b][0][i];
-      pbase[r * (HD + 2) + 32 * b + 16 + row] = acc[b][1][i];
+    for (int bl = 0; bl < NBW; ++bl) {
+      pbase[h * (HD + 2) + 32 * (b0 + bl) + row] = acc[bl][0][i];
+      pbase[h * (HD + 2) + 32 * (b0 + bl) + 16 + row] = acc[bl][1][i];
     }
-    if (row == 0) {
-      pbase[r * (HD + 2) + HD] = m_run[i];
-      pbase[r * (HD + 2) + HD + 1] = lsum[i];
+  }
+  // running max / sum of head h are held in register h % 4 of the lanes whose row group maps to h
+  if (wave == 0 && row == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * g + i, h = r % GP;
+      if (r < GP && h < G) {
+        pbase[h * (HD + 2) + HD] = m_run[i];
+        pbase[h * (HD + 2) + HD + 1] = lsum[i];
+      }
     }
   }
 }
 
-// Merge: one workgroup per (query head, 32-block); threads (part lane pl, coordinate dl).
+// Merge: one workgroup per (query head, 32-block); kMergeLanes x 32 threads (partial lane, coordinate).
 __global__ __launch_bounds__(256) void attn_merge(AttnArgs a) {
   const int h = blockIdx.x, b = blockIdx.y, HD = a.head_dim, G = a.group;
   const int kvh = h / G, r = h % G;
   const int tid = threadIdx.x, pl = tid >> 5, dl = tid & 31;
-  const int n_part = a.wg_per_head * kAttnWaves;
-  const float* base = a.part + (int64_t)kvh * n_part * G * (HD + 2);
-  __shared__ float red[8][33];
-  __shared__ float mx;
-  // global max over the partials' running maxima
+  const int n_part = a.wg_per_head;
+  const int64_t stride = (int64_t)G * (HD + 2);
+  const float* base = a.part + (int64_t)kvh * n_part * stride + (int64_t)r * (HD + 2);
+  __shared__ float red[kMergeLanes][33];
+  __shared__ float wmax[4];
   float m = -INFINITY;
-  for (int p = tid; p < n_part; p += 256) m = fmaxf(m, base[((int64_t)p * G + r) * (HD + 2) + HD]);
+  for (int p = tid; p < n_part; p += 256) m = fmaxf(m, base[p * stride + HD]);
+#pragma unroll
   for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  if ((tid & 63) == 0) red[tid >> 6][32] = m;
+  if ((tid & 63) == 0) wmax[tid >> 6] = m;
   __syncthreads();
-  if (tid == 0) {
-    float mm = -INFINITY;
-    for (int w = 0; w < 4; ++w) mm = fmaxf(mm, red[w][32]);
-    mx = mm;
-  }
-  __syncthreads();
-  const float M = mx;
+  const float M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
   float acc = 0.0f, l = 0.0f;
-  for (int p = pl; p < n_part; p += 8) {
-    const float* pb = base + ((int64_t)p * G + r) * (HD + 2);
+#pragma unroll 4
+  for (int p = pl; p < n_part; p += kMergeLanes) {
+    const float* pb = base + p * stride;
     const float mp = pb[HD];
-    if (mp == -INFINITY) continue;
-    const float f = __expf(mp - M);
+    const float f = mp == -INFINITY ? 0.0f : __expf(mp - M);
     acc = __builtin_fmaf(pb[32 * b + dl], f, acc);
     l = __builtin_fmaf(pb[HD + 1], f, l);
   }
-  __syncthreads();
   red[pl][dl] = acc;
   if (dl == 0) red[pl][32] = l;
   __syncthreads();
   if (pl == 0) {
     float s = 0.0f, ls = 0.0f;
-    for (int q = 0; q < 8; ++q) {
+#pragma unroll
+    for (int q = 0; q < kMergeLanes; ++q) {
       s += red[q][dl];
       ls += red[q][32];
     }
     // out = D_V * H_unnorm(acc) / (32 * l): butterflies across the 32 lanes of the first wave
     float v = s;
+#pragma unroll
     for (int hb = 1; hb < 32; hb <<= 1) {
       const float o = __shfl_xor(v, hb);
       v = (dl & hb) ? o - v : v + o;
@@ -349,6 +450,8 @@ hipError_t launch_nb(const AttnArgs& a, hipStream_t s) {
   dim3 grid((unsigned)a.wg_per_head, (unsigned)a.n_kv_heads);
   if (a.group <= 4)
     hipLaunchKernelGGL((attn_kernel<NB, KB, VB, 4>), grid, dim3(256), 0, s, a);
+  else if (a.group <= 8)
+    hipLaunchKernelGGL((attn_kernel<NB, KB, VB, 8>), grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((attn_kernel<NB, KB, VB, 16>), grid, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
@@ -364,7 +467,16 @@ hipError_t launch_bits(const AttnArgs& a, hipStream_t s) {
 
 }  // namespace
 
-int attn_tokens_per_wg() { return kTokPerWG; }
+// Token range per workgroup: a multiple of the 64-token tile that spreads the
+// cache over about 512 workgroups (two per compute unit), 64 .. 8192 tokens.
+int64_t attn_tokens_per_wg(int n_kv_heads, int64_t n_tokens) {
+  const int64_t target = 512;
+  int64_t per = (n_tokens * n_kv_heads + target - 1) / target;
+  per = (per + kTile - 1) / kTile * kTile;
+  if (per < kTile) per = kTile;
+  if (per > 8192) per = 8192;
+  return per;
+}
 
 hipError_t launch_decode_attn(int kbits, int vbits, const AttnArgs& a, hipStream_t s) {
   if (kbits == 3 && vbits == 3) return launch_bits<3, 3>(a, s);

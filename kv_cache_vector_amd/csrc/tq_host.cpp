@@ -413,11 +413,11 @@ tq_status check_attn_config(const tq_config* kcfg, const tq_config* vcfg, int n_
   return TQ_OK;
 }
 
-// one fp32 partial (head_dim sums, running max, running sum) per wave, query head and token range
+// one fp32 partial (head_dim sums, running max, running sum) per query head and token range
 size_t attn_workspace(const tq_config& kcfg, int n_q_heads, int n_kv_heads, int64_t n_tokens) {
-  const int64_t per_wg = tq::attn_tokens_per_wg();
+  const int64_t per_wg = tq::attn_tokens_per_wg(n_kv_heads, n_tokens);
   const int64_t wgs = (n_tokens + per_wg - 1) / per_wg;
-  const int64_t parts = (int64_t)n_kv_heads * wgs * 4 * (n_q_heads / n_kv_heads);
+  const int64_t parts = (int64_t)n_kv_heads * wgs * (n_q_heads / n_kv_heads);
   return round256((size_t)parts * (size_t)(kcfg.head_dim + 2) * sizeof(float));
 }
 
@@ -524,7 +524,7 @@ tq_status tq_decode_attn(const tq_config* kcfg, const tq_config* vcfg, const voi
   a.v_norms = (const uint16_t*)v_norms;
   a.out = out;
   a.part = (float*)ws;
-  a.tokens_per_wg = tq::attn_tokens_per_wg();
+  a.tokens_per_wg = tq::attn_tokens_per_wg(n_kv_heads, n_tokens);
   a.wg_per_head = (int32_t)((n_tokens + a.tokens_per_wg - 1) / a.tokens_per_wg);
   uint32_t db[8];
   fill_dbits(*kcfg, db);

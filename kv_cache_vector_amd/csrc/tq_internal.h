@@ -110,7 +110,7 @@ struct AttnArgs {
   float* out;
   float* part;               // [n_kv_heads][wg_per_head][group][head_dim + 2] partial (acc, max, sum)
   int32_t wg_per_head;
-  int32_t tokens_per_wg;
+  int64_t tokens_per_wg;
   uint32_t kdbits, vdbits;   // D_K, D_V of the 32-long blocks
   float klevel[16], vlevel[16];
   float kscale;              // softmax scale / sqrt(32): score = kscale * sum_b n_b <H D q_b, c_b>
@@ -124,6 +124,6 @@ hipError_t launch_qjl_decode(const tq_config& cfg, const QjlDecodeArgs& a, bool 
 hipError_t launch_qjl_scores(const tq_config& cfg, const ScoreArgs& a, hipStream_t s);
 int64_t scores_key_tile(int bits);
 hipError_t launch_decode_attn(int kbits, int vbits, const AttnArgs& a, hipStream_t s);
-int attn_tokens_per_wg();
+int64_t attn_tokens_per_wg(int n_kv_heads, int64_t n_tokens);
 
 }  // namespace tq
