@@ -58,24 +58,44 @@ __device__ __forceinline__ uint32_t pack_h2(_Float16 lo, _Float16 hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
 }
 
-// max / sum of v over the lanes that hold the same query head: the 16 lanes of
-// a row group, and the S row groups whose stacked subtiles share the head
-template <int S>
-__device__ __forceinline__ float head_max(float v) {
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
-  if (S >= 2) v = fmaxf(v, __shfl_xor(v, 32));
-  if (S >= 4) v = fmaxf(v, __shfl_xor(v, 16));
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Reduction over the lanes that hold the same query head: the 16 lanes of a row
+// (DPP: quad swaps, then rotations by 4 and 8 within the row) and, when S
+// subtiles are stacked, the S rows that share the head (lanes l ^ 32 and
+// l ^ 16, exchanged with the gfx950 permlane swaps).
+template <int S, bool MAX>
+__device__ __forceinline__ float head_reduce(float v) {
+  auto op = [](float x, float y) { return MAX ? fmaxf(x, y) : x + y; };
+  v = op(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = op(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = op(v, dpp<0x124>(v));  // row_ror:4
+  v = op(v, dpp<0x128>(v));  // row_ror:8
+  if (S >= 2) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, v),
+                                                    false, false);
+    v = op(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+  }
+  if (S >= 4) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, v), __builtin_bit_cast(uint32_t, v),
+                                                    false, false);
+    v = op(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+  }
   return v;
 }
 
-template <int S>
-__device__ __forceinline__ float head_sum(float v) {
-#pragma unroll
-  for (int m = 1; m < 16; m <<= 1) v += __shfl_xor(v, m);
-  if (S >= 2) v += __shfl_xor(v, 32);
-  if (S >= 4) v += __shfl_xor(v, 16);
-  return v;
+// Word of a replicated pair table: entry ((w >> sh) & (2^width - 1)), copy selected by the
+// lane's byte offset off (< 4 << lgc), i.e. byte address (entry << (lgc + 2)) | off.
+__device__ __forceinline__ uint32_t lut_word(const uint32_t* table, uint32_t w, int sh, int width, int lgc,
+                                             uint32_t off) {
+  const int up = lgc + 2 - sh;
+  const uint32_t mask = ((1u << width) - 1u) << (lgc + 2);
+  const uint32_t shifted = up >= 0 ? (w << up) : (w >> -up);
+  const uint32_t byte = (shifted & mask) | off;
+  return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(table) + byte);
 }
 
 __device__ __forceinline__ void wave_sync() {
@@ -104,25 +124,35 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   constexpr int NCH = 2 * NBW;      // 16-coordinate chunks per V tile row
   static_assert(NBW == 1 || NBW == 2, "head_dim 128 or 256");
 
-  __shared__ uint2 ktab[KL * KL];     // pair of K codes -> (fp16 hi pair, fp16 lo pair), N(0,1) scale
-  __shared__ uint32_t vtab[VL * VL];  // pair of V codes -> fp16 pair
+  // Pair tables (two codes -> two fp16 levels, N(0,1) scale): K hi part, K lo part, V.  Each
+  // entry is replicated in CK / CV copies interleaved at word granularity; lane l reads copy
+  // l % C, so the random lookups of one instruction fall in distinct LDS banks.
+  constexpr int LGCK = KB == 3 ? 5 : 3, LGCV = VB == 3 ? 5 : 3;
+  constexpr int CK = 1 << LGCK, CV = 1 << LGCV;
+  __shared__ uint32_t kth[KL * KL * CK], ktl[KL * KL * CK];
+  __shared__ uint32_t vtab[VL * VL * CV];
   __shared__ __attribute__((aligned(16))) _Float16 vt[kWaves][kTile * VROW];
   __shared__ __attribute__((aligned(16))) _Float16 pt[kWaves][GP * kTile];
-  __shared__ float xs[2][kWaves][NC * 4][64];
+  constexpr int XSTR = kWaves * NC * 4 + 4;  // per-lane row of the score exchange (+4 breaks bank aliasing)
+  __shared__ __attribute__((aligned(16))) float xs[2][64][XSTR];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = lane & 15, g = lane >> 4;
   const int kvh = blockIdx.y;
   const int G = a.group;
+  const uint32_t koff = (uint32_t)(lane & (CK - 1)) * 4u, voff = (uint32_t)(lane & (CV - 1)) * 4u;
 
-  for (int e = tid; e < KL * KL; e += 256) {
+  for (int x = tid; x < KL * KL * CK; x += 256) {
+    const int e = x / CK;
     const float ca = a.klevel[e & (KL - 1)], cb = a.klevel[e >> KB];
     const _Float16 ha = (_Float16)ca, hb = (_Float16)cb;
-    const _Float16 la = (_Float16)(ca - (float)ha), lb = (_Float16)(cb - (float)hb);
-    ktab[e] = make_uint2(pack_h2(ha, hb), pack_h2(la, lb));
+    kth[x] = pack_h2(ha, hb);
+    ktl[x] = pack_h2((_Float16)(ca - (float)ha), (_Float16)(cb - (float)hb));
   }
-  for (int e = tid; e < VL * VL; e += 256)
-    vtab[e] = pack_h2((_Float16)a.vlevel[e & (VL - 1)], (_Float16)a.vlevel[e >> VB]);
+  for (int x = tid; x < VL * VL * CV; x += 256) {
+    const int e = x / CV;
+    vtab[x] = pack_h2((_Float16)a.vlevel[e & (VL - 1)], (_Float16)a.vlevel[e >> VB]);
+  }
 
   // rotated query blocks qhat_b = H D_K q_b / sqrt(32) of the group's heads (rows >= G zero),
   // FWHT staged in fp32 over the V tile area
@@ -187,8 +217,10 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   // token (within the tile) whose K norm scales accumulator cc in this lane
   auto ktok = [&](int cc) { return 16 * (cc * S + (4 * g) / GP) + row; };
 
-  const int64_t t_begin = (int64_t)blockIdx.x * a.tokens_per_wg;
-  const int64_t t_end = t_begin + a.tokens_per_wg < T ? t_begin + a.tokens_per_wg : T;
+  // tiles are dealt round-robin: workgroup x takes tiles x, x + W, x + 2W, ... (W workgroups per
+  // KV head), so the workgroups in flight stream one contiguous stretch of the cache together
+  const int64_t t_begin = (int64_t)blockIdx.x * kTile;
+  const int64_t t_step = (int64_t)a.wg_per_head * kTile;
 
   using Regs = TileRegs<NBW, KB, VB, NC>;
   auto load = [&](Regs& r, int64_t tb) {
@@ -233,11 +265,11 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   _Float16* vtile = vt[wave];
   _Float16* ptile = pt[wave];
   Regs nxt;
-  if (t_begin < t_end) load(nxt, t_begin);
+  if (t_begin < T) load(nxt, t_begin);
   int parity = 0;
-  for (int64_t tb = t_begin; tb < t_end; tb += kTile, parity ^= 1) {
+  for (int64_t tb = t_begin; tb < T; tb += t_step, parity ^= 1) {
     const Regs cur = nxt;
-    if (tb + kTile < t_end) load(nxt, tb + kTile);
+    if (tb + t_step < T) load(nxt, tb + t_step);
 
     // ---- value records of token `lane` -> V tile row `lane` (norm folded in, chunks swizzled)
 #pragma unroll
@@ -248,11 +280,9 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int pp = 0; pp < 16; ++pp) {
         const int pos = 2 * VB * pp, wi = pos >> 5, sh = pos & 31;
-        const uint32_t bits = sh + 2 * VB <= 32 ? __builtin_amdgcn_ubfe(cur.vw[bl][wi], sh, 2 * VB)
-                                                : __builtin_amdgcn_ubfe(
-                                                      __builtin_amdgcn_alignbit(cur.vw[bl][wi + 1], cur.vw[bl][wi], sh),
-                                                      0, 2 * VB);
-        const v2h c = __builtin_bit_cast(v2h, vtab[bits]);
+        const uint32_t w = sh + 2 * VB <= 32 ? cur.vw[bl][wi] : __builtin_amdgcn_alignbit(cur.vw[bl][wi + 1], cur.vw[bl][wi], sh);
+        const int s2 = sh + 2 * VB <= 32 ? sh : 0;
+        const v2h c = __builtin_bit_cast(v2h, lut_word(vtab, w, s2, 2 * VB, LGCV, voff));
         o[pp] = __builtin_bit_cast(uint32_t, c * nv2);
       }
 #pragma unroll
@@ -284,9 +314,8 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
           uint32_t bh[4], bo[4];
 #pragma unroll
           for (int pp = 0; pp < 4; ++pp) {
-            const uint2 e = ktab[__builtin_amdgcn_ubfe(win, 2 * KB * pp, 2 * KB)];
-            bh[pp] = e.x;
-            bo[pp] = e.y;
+            bh[pp] = lut_word(kth, win, 2 * KB * pp, 2 * KB, LGCK, koff);
+            bo[pp] = lut_word(ktl, win, 2 * KB * pp, 2 * KB, LGCK, koff);
           }
           const v8h bhi = __builtin_bit_cast(v8h, make_uint4(bh[0], bh[1], bh[2], bh[3]));
           const v8h blo = __builtin_bit_cast(v8h, make_uint4(bo[0], bo[1], bo[2], bo[3]));
@@ -302,21 +331,25 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
 
     // ---- sum the waves' partial scores
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xs[parity][wave][cc * 4 + i][lane] = s[cc][i];
-    }
+    for (int cc = 0; cc < NC; ++cc)
+      *reinterpret_cast<float4*>(&xs[parity][lane][(wave * NC + cc) * 4]) = make_float4(s[cc][0], s[cc][1], s[cc][2], s[cc][3]);
     __syncthreads();
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
       const bool live = tb + ktok(cc) < T;
+      float4 v = *reinterpret_cast<const float4*>(&xs[parity][lane][cc * 4]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) v += xs[parity][w][cc * 4 + i][lane];
-        s[cc][i] = live ? v * a.kscale : -INFINITY;
+      for (int w = 1; w < kWaves; ++w) {
+        const float4 u = *reinterpret_cast<const float4*>(&xs[parity][lane][(w * NC + cc) * 4]);
+        v.x += u.x;
+        v.y += u.y;
+        v.z += u.z;
+        v.w += u.w;
       }
+      s[cc][0] = live ? v.x * a.kscale : -INFINITY;
+      s[cc][1] = live ? v.y * a.kscale : -INFINITY;
+      s[cc][2] = live ? v.z * a.kscale : -INFINITY;
+      s[cc][3] = live ? v.w * a.kscale : -INFINITY;
     }
 
     // ---- online softmax; register i of this lane belongs to head (4g + i) % GP
@@ -325,7 +358,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
       float mt = s[0][i];
 #pragma unroll
       for (int cc = 1; cc < NC; ++cc) mt = fmaxf(mt, s[cc][i]);
-      mt = head_max<S>(mt);
+      mt = head_reduce<S, true>(mt);
       const float m_new = fmaxf(m_run[i], mt);  // finite: every tile holds a live token
       const float alpha = m_run[i] == -INFINITY ? 0.0f : __expf(m_run[i] - m_new);
       float ps = 0.0f;
@@ -336,7 +369,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
         ps += p;
         ptile[h * kTile + 16 * (cc * S + sub) + row] = (_Float16)p;
       }
-      lsum[i] = lsum[i] * alpha + head_sum<S>(ps);
+      lsum[i] = lsum[i] * alpha + head_reduce<S, false>(ps);
       m_run[i] = m_new;
 #pragma unroll
       for (int bl = 0; bl < NBW; ++bl) {
