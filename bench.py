@@ -98,23 +98,45 @@ def time_steps(torch, fn, steps, warmup):
 
 
 def per_kernel_ms(torch, codec, k, v, ok, ov, reps):
-    """Average duration (ms) of one encode launch and one decode launch, from HIP events
-    recorded on the stream the kernels run on (torch's current stream)."""
+    """Average duration (ms) of one encode launch and one decode launch, from HIP events recorded on
+    the stream the kernels run on (torch's current stream).  One untimed launch keeps the GPU busy
+    before the first event, so the host's launch latency is not timed; then `reps` encodes and `reps`
+    decodes run back to back between three events."""
     tq = codec.tq
-    enc, dec = [], []
+    enc = lambda: tq.tq_quantize(codec.qk, k, codec.rows, HEAD_DIM, codec.ck, codec.nk)
+    dec = lambda: tq.tq_dequantize(codec.qk, codec.ck, codec.nk, None, None, codec.rows, ok, tq.TQ_F16, HEAD_DIM)
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    enc()
+    e[0].record()
     for _ in range(reps):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        e[0].record()
-        tq.tq_quantize(codec.qk, k, codec.rows, HEAD_DIM, codec.ck, codec.nk)
-        e[1].record()
-        tq.tq_dequantize(codec.qk, codec.ck, codec.nk, None, None, codec.rows, ok, tq.TQ_F16, HEAD_DIM)
-        e[2].record()
-        torch.cuda.synchronize()
-        enc.append(e[0].elapsed_time(e[1]))
-        dec.append(e[1].elapsed_time(e[2]))
-    enc.sort()
-    dec.sort()
-    return enc[len(enc) // 2], dec[len(dec) // 2], min(enc), min(dec)
+        enc()
+    e[1].record()
+    for _ in range(reps):
+        dec()
+    e[2].record()
+    torch.cuda.synchronize()
+    return e[0].elapsed_time(e[1]) / reps, e[1].elapsed_time(e[2]) / reps
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "codec_qwen3_8b_hbm_traffic.txt")
+
+
+def measured_traffic(tag: str):
+    """HBM bytes per launch of the encode/decode kernel `tag` (e.g. 'decode_turbo3') from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None if the kernel source changed since it was taken."""
+    import hashlib
+
+    try:
+        fields = dict(line.split(": ", 1) for line in open(TRAFFIC_PROFILE).read().splitlines()
+                      if ": " in line and not line.startswith("#"))
+    except OSError:
+        return None
+    src = os.path.join(ROOT, "kv_cache_vector_amd", "csrc", "tq_codec.hip")
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != fields.get("codec_source_sha256"):
+        return None
+    v = fields.get(f"{tag}_traffic_bytes")
+    return int(v) if v else None
 
 
 def cpu_baseline(rows_total: int, bits: int, target_s: float = 15.0) -> dict:
@@ -143,7 +165,8 @@ def cpu_baseline(rows_total: int, bits: int, target_s: float = 15.0) -> dict:
 
 def event_ms(torch, fn, reps, before=None):
     """Median and minimum duration (ms) of fn() from HIP events on the current stream;
-    before() runs untimed ahead of each repetition."""
+    before() runs untimed ahead of each repetition (it must keep the GPU busy, e.g. a cache
+    flush, so that the host's launch latency is not timed)."""
     ts = []
     for _ in range(reps):
         if before is not None:
@@ -156,6 +179,20 @@ def event_ms(torch, fn, reps, before=None):
         ts.append(e0.elapsed_time(e1))
     ts.sort()
     return ts[len(ts) // 2], ts[0]
+
+
+def batch_ms(torch, fn, reps):
+    """Average duration (ms) of fn() over `reps` back-to-back calls between two HIP events on the
+    current stream; one untimed call first keeps the GPU busy while the timed calls are queued."""
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
 
 
 def bench_qjl(tq, torch, dev, reps):
@@ -187,8 +224,8 @@ def bench_qjl(tq, torch, dev, reps):
     for _ in range(2):
         enc()
         score()
-    enc_ms, enc_min = event_ms(torch, enc, reps)
-    sc_ms, sc_min = event_ms(torch, score, reps)
+    enc_ms = batch_ms(torch, enc, reps)
+    sc_ms = batch_ms(torch, score, reps)
     key_bytes = n * (d * 2 + d * bits // 8 + 2 + m // 8 + 2)  # fp16 key in; codes, norm, signs, rho out
     n_scores = nq * n
     # int8 MFMA work of the scoring kernel: per score, hi and lo limbs of the rotated query against
@@ -197,7 +234,7 @@ def bench_qjl(tq, torch, dev, reps):
     out = {"workload": "65536 keys x 128 fp16, 2-bit + QJL m=128; 4096 queries",
            "encode_ms": round(enc_ms, 4), "keys_per_s": round(n / (enc_ms * 1e-3)),
            "encode_GBs": round(key_bytes / (enc_ms * 1e-3) / 1e9, 1),
-           "scores_ms": round(sc_ms, 4), "scores_ms_min": round(sc_min, 4),
+           "scores_ms": round(sc_ms, 4),
            "scores_per_s": round(n_scores / (sc_ms * 1e-3)),
            "scores_write_GBs": round(4 * n_scores / (sc_ms * 1e-3) / 1e9, 1),
            "scores_int8_mfma_TOPS": round(2 * macs / (sc_ms * 1e-3) / 1e12, 1),
@@ -237,7 +274,7 @@ def bench_attn(tq, torch, dev, reps):
 
     for _ in range(3):
         attn()
-    warm_ms, warm_min = event_ms(torch, attn, reps)
+    warm_ms = batch_ms(torch, attn, reps)
     cold_ms, cold_min = event_ms(torch, attn, reps, before=lambda: flush.zero_())
     nbytes = 2 * units * (12 + 2)  # K and V codes and norms
     res = {"workload": "decode attention, head_dim 256, 4 KV heads, 16 query heads, 131072 tokens, turbo3 K/V",
@@ -292,10 +329,9 @@ def main():
             codec.decode(ok, ov)
 
         ms = time_steps(torch, step, args.steps, args.warmup)
-        enc_ms, dec_ms, enc_min, dec_min = per_kernel_ms(torch, codec, k, v, ok, ov, max(5, args.steps // 2))
+        enc_ms, dec_ms = per_kernel_ms(torch, codec, k, v, ok, ov, max(5, args.steps // 2))
         ab = algorithmic_bytes(codec.units, bits)
-        results[bits] = {"ms": ms, "enc_ms": enc_ms, "dec_ms": dec_ms, "enc_min": enc_min, "dec_min": dec_min,
-                         "bytes": ab, "units": codec.units}
+        results[bits] = {"ms": ms, "enc_ms": enc_ms, "dec_ms": dec_ms, "bytes": ab, "units": codec.units}
         log(f"{bits}-bit: step {ms:.3f} ms, encode {enc_ms:.3f} ms ({ab['per_launch'] / enc_ms / 1e6:.0f} GB/s), "
             f"decode {dec_ms:.3f} ms ({ab['per_launch'] / dec_ms / 1e6:.0f} GB/s)")
         del codec
@@ -316,6 +352,7 @@ def main():
     dom = "decode" if r["dec_ms"] >= r["enc_ms"] else "encode"
     dom_ms = max(r["dec_ms"], r["enc_ms"])
     achieved = r["bytes"]["per_launch"] / (dom_ms * 1e-3) / 1e9
+    traffic = measured_traffic(f"{dom}_turbo3")
     r4 = results[4]
     out = {
         "metric": "fp16 KV GB/s encoded+decoded (fraction of HBM peak); QJL scores/sec",
@@ -335,7 +372,8 @@ def main():
                    "step": "quantize K, quantize V, dequantize K, dequantize V"},
         "roofline": {"bound": "hbm", "kernel": f"{dom} (turbo3, one K half-cache per launch)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": r["bytes"]["per_launch"], "avg_launch_ms": round(dom_ms, 4)},
         "fraction_of_hbm_peak": round((2 * 2 * r["bytes"]["per_launch"]) / (r["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "encode": {"turbo3_GBs": round(r["bytes"]["per_launch"] / r["enc_ms"] / 1e6, 1),
                    "turbo4_GBs": round(r4["bytes"]["per_launch"] / r4["enc_ms"] / 1e6, 1),
