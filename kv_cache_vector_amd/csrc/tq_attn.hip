@@ -98,6 +98,10 @@ __device__ __forceinline__ uint32_t lut_word(const uint32_t* table, uint32_t w, 
   return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(table) + byte);
 }
 
+// Workgroup barrier for LDS traffic only: this wave's LDS operations have completed, nothing is
+// waited for on the global-memory side, so prefetched tiles stay in flight across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -181,23 +185,16 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   }
 
   // query operands of this lane: row `row` of subtile slot sv is head row % GP when row / GP == sv
-  v8h aqh[NBW][S], aql[NBW][S];
+  // (the masked copies are formed at each use, which keeps 16/GP - 1 copies out of the registers)
+  v8h qh8[NBW], ql8[NBW];
 #pragma unroll
   for (int bl = 0; bl < NBW; ++bl) {
     const int b = NBW * wave + bl;
-    v8h h8, l8;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float v = qf[(row % GP) * HD + 32 * b + 8 * g + j] * 0.17677669529663688f;  // 1/sqrt(32)
-      h8[j] = (_Float16)v;
-      l8[j] = (_Float16)(v - (float)h8[j]);
-    }
-#pragma unroll
-    for (int sv = 0; sv < S; ++sv) {
-      const bool on = row / GP == sv;
-      const v8h z = {0, 0, 0, 0, 0, 0, 0, 0};
-      aqh[bl][sv] = on ? h8 : z;
-      aql[bl][sv] = on ? l8 : z;
+      qh8[bl][j] = (_Float16)v;
+      ql8[bl][j] = (_Float16)(v - (float)qh8[bl][j]);
     }
   }
   __syncthreads();  // query staging is overwritten by the V tiles below
@@ -209,10 +206,10 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   const uint16_t* vnb = a.v_norms + (int64_t)kvh * T * NB;
   const int b0 = NBW * wave;  // first owned block
 
-  // this lane's K window: bits [24g, 24g + 24) of a 3-bit record (funnel shift of the two words
-  // holding them, the second clamped to the record) or word g of a 4-bit one
-  const int kword = KB == 4 ? g : (24 * g) >> 5;
-  const int kword2 = KB == 4 ? g : (kword + 1 < KB ? kword + 1 : KB - 1);
+  // this lane's K window: bits [24g, 24g + 24) of a 3-bit record, from the 8 bytes at word
+  // kword (0, 0, 1, 1 for g = 0..3) by a funnel shift of 0, 24, 16 or 40 bits (the last one
+  // takes the high word alone), or word g of a 4-bit record
+  const int kword = KB == 4 ? g : (g >= 2 ? 1 : 0);
   const int kshift = KB == 4 ? 0 : (24 * g) & 31;
   // token (within the tile) whose K norm scales accumulator cc in this lane
   auto ktok = [&](int cc) { return 16 * (cc * S + (4 * g) / GP) + row; };
@@ -230,9 +227,15 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
       for (int st = 0; st < 4; ++st) {
         int64_t t = tb + 16 * st + row;
         t = t < T ? t : T - 1;
-        const uint32_t* rp = reinterpret_cast<const uint32_t*>(kbase + (t * NB + b0 + bl) * (4 * KB));
-        r.kw[bl][st][0] = rp[kword];
-        r.kw[bl][st][1] = KB == 4 ? 0u : rp[kword2];
+        const uint32_t* rp = reinterpret_cast<const uint32_t*>(kbase + (t * NB + b0 + bl) * (4 * KB)) + kword;
+        if (KB == 4) {
+          r.kw[bl][st][0] = rp[0];
+          r.kw[bl][st][1] = 0u;
+        } else {
+          const uint2 w = *reinterpret_cast<const uint2*>(rp);
+          r.kw[bl][st][0] = g == 3 ? w.y : w.x;
+          r.kw[bl][st][1] = w.y;
+        }
       }
     }
 #pragma unroll
@@ -264,12 +267,13 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
 
   _Float16* vtile = vt[wave];
   _Float16* ptile = pt[wave];
-  Regs nxt;
-  if (t_begin < T) load(nxt, t_begin);
+  // three register sets in rotation keep two tiles of loads in flight behind the one in use
+  Regs ra, rb, rc;
+  if (t_begin < T) load(ra, t_begin);
+  if (t_begin + t_step < T) load(rb, t_begin + t_step);
   int parity = 0;
-  for (int64_t tb = t_begin; tb < T; tb += t_step, parity ^= 1) {
-    const Regs cur = nxt;
-    if (tb + t_step < T) load(nxt, tb + t_step);
+  auto tile = [&](const Regs& cur, Regs& fill, int64_t tb) {
+    if (tb + 2 * t_step < T) load(fill, tb + 2 * t_step);
 
     // ---- value records of token `lane` -> V tile row `lane` (norm folded in, chunks swizzled)
 #pragma unroll
@@ -319,9 +323,13 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
           }
           const v8h bhi = __builtin_bit_cast(v8h, make_uint4(bh[0], bh[1], bh[2], bh[3]));
           const v8h blo = __builtin_bit_cast(v8h, make_uint4(bo[0], bo[1], bo[2], bo[3]));
-          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(aqh[bl][sv], bhi, c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(aql[bl][sv], bhi, c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(aqh[bl][sv], blo, c, 0, 0, 0);
+          uint32_t on = row / GP == sv ? 0xFFFFFFFFu : 0u;
+          asm volatile("" : "+v"(on));  // opaque: the masked operands are not hoisted out of the loop
+          const v8h ah = __builtin_bit_cast(v8h, __builtin_bit_cast(u32x4, qh8[bl]) & on);
+          const v8h al = __builtin_bit_cast(v8h, __builtin_bit_cast(u32x4, ql8[bl]) & on);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bhi, c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bhi, c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, blo, c, 0, 0, 0);
         }
         const float nk = __half2float(__ushort_as_half((uint16_t)(cur.kn[cc] >> (16 * bl))));
 #pragma unroll
@@ -333,7 +341,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc)
       *reinterpret_cast<float4*>(&xs[parity][lane][(wave * NC + cc) * 4]) = make_float4(s[cc][0], s[cc][1], s[cc][2], s[cc][3]);
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
       const bool live = tb + ktok(cc) < T;
@@ -402,6 +410,14 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
       }
     }
     wave_sync();
+    parity ^= 1;
+  };
+  for (int64_t tb = t_begin; tb < T; tb += 3 * t_step) {
+    tile(ra, rc, tb);
+    if (tb + t_step >= T) break;
+    tile(rb, ra, tb + t_step);
+    if (tb + 2 * t_step >= T) break;
+    tile(rc, rb, tb + 2 * t_step);
   }
 
   // ---- partial of this workgroup: part[kvh][wg][head][HD coordinates, max, sum]
