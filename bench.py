@@ -97,26 +97,65 @@ def time_steps(torch, fn, steps, warmup):
     return start.elapsed_time(stop) / steps
 
 
+def capture_step(torch, step, outputs):
+    """Capture one step (its four launches) in a HIP graph.  The graph runs the same kernels on the
+    same buffers; its replays are checked against an eager step, with eager work in between, before
+    they are timed.  Returns None (eager timing) if a replay differs."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outputs]
+    for _ in range(3):
+        for t in outputs:
+            t.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        if not all(torch.equal(a, b) for a, b in zip(ref, outputs)):
+            log("graph replay differs from the eager step; timing eager launches")
+            return None
+        step()
+        torch.cuda.synchronize()
+    return graph
+
+
 def per_kernel_ms(torch, codec, k, v, ok, ov, reps):
-    """Average duration (ms) of one encode launch and one decode launch, from HIP events recorded on
-    the stream the kernels run on (torch's current stream).  One untimed launch keeps the GPU busy
-    before the first event, so the host's launch latency is not timed; then `reps` encodes and `reps`
-    decodes run back to back between three events."""
+    """Average duration (ms) of one encode launch and one decode launch inside the step sequence
+    (quantize K, quantize V, dequantize K, dequantize V, so every launch streams from HBM as in the
+    step), from HIP events recorded between the launches on the stream they run on (torch's
+    current stream).  One untimed step first keeps the GPU busy, so host launch latency is not
+    timed; each interval also holds the launch gap before its kernel."""
     tq = codec.tq
-    enc = lambda: tq.tq_quantize(codec.qk, k, codec.rows, HEAD_DIM, codec.ck, codec.nk)
-    dec = lambda: tq.tq_dequantize(codec.qk, codec.ck, codec.nk, None, None, codec.rows, ok, tq.TQ_F16, HEAD_DIM)
+    launches = [lambda: tq.tq_quantize(codec.qk, k, codec.rows, HEAD_DIM, codec.ck, codec.nk),
+                lambda: tq.tq_quantize(codec.qv, v, codec.rows, HEAD_DIM, codec.cv, codec.nv),
+                lambda: tq.tq_dequantize(codec.qk, codec.ck, codec.nk, None, None, codec.rows, ok, tq.TQ_F16, HEAD_DIM),
+                lambda: tq.tq_dequantize(codec.qv, codec.cv, codec.nv, None, None, codec.rows, ov, tq.TQ_F16, HEAD_DIM)]
     torch.cuda.synchronize()
-    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    enc()
-    e[0].record()
+    for f in launches:
+        f()
+    ev = []
     for _ in range(reps):
-        enc()
-    e[1].record()
-    for _ in range(reps):
-        dec()
-    e[2].record()
+        for f in launches:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            ev.append(e)
+            f()
+    end = torch.cuda.Event(enable_timing=True)
+    end.record()
+    ev.append(end)
     torch.cuda.synchronize()
-    return e[0].elapsed_time(e[1]) / reps, e[1].elapsed_time(e[2]) / reps
+    d = [ev[i].elapsed_time(ev[i + 1]) for i in range(len(ev) - 1)]
+    enc = [d[i] for i in range(len(d)) if i % 4 in (0, 1)]
+    dec = [d[i] for i in range(len(d)) if i % 4 in (2, 3)]
+    return sum(enc) / len(enc), sum(dec) / len(dec)
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "codec_qwen3_8b_hbm_traffic.txt")
@@ -292,8 +331,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a captured step")
     ap.add_argument("--only", choices=("all", "codec", "qjl", "attn"), default="all",
                     help="run one workload (for profiling runs); the JSON line needs 'all'")
     args = ap.parse_args()
@@ -328,10 +368,14 @@ def main():
             codec.encode(k, v)
             codec.decode(ok, ov)
 
-        ms = time_steps(torch, step, args.steps, args.warmup)
+        graph = None if args.no_graph else capture_step(torch, step, [codec.ck, codec.cv, codec.nk, codec.nv, ok, ov])
+        ms = time_steps(torch, graph.replay if graph is not None else step, args.steps, args.warmup)
+        graphed = graph is not None
+        del graph
         enc_ms, dec_ms = per_kernel_ms(torch, codec, k, v, ok, ov, max(5, args.steps // 2))
         ab = algorithmic_bytes(codec.units, bits)
-        results[bits] = {"ms": ms, "enc_ms": enc_ms, "dec_ms": dec_ms, "bytes": ab, "units": codec.units}
+        results[bits] = {"ms": ms, "enc_ms": enc_ms, "dec_ms": dec_ms, "bytes": ab, "units": codec.units,
+                         "graphed": graphed}
         log(f"{bits}-bit: step {ms:.3f} ms, encode {enc_ms:.3f} ms ({ab['per_launch'] / enc_ms / 1e6:.0f} GB/s), "
             f"decode {dec_ms:.3f} ms ({ab['per_launch'] / dec_ms / 1e6:.0f} GB/s)")
         del codec
@@ -369,7 +413,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "qwen3_8b_kv_block32_turbo3", "layers": LAYERS, "kv_heads": KV_HEADS,
                    "tokens": TOKENS, "head_dim": HEAD_DIM, "block": DT, "bits": 3, "kv_dtype": "f16",
-                   "step": "quantize K, quantize V, dequantize K, dequantize V"},
+                   "step": "quantize K, quantize V, dequantize K, dequantize V",
+                   "launch": "hip graph of the step's four launches" if results[3]["graphed"] else "eager launches"},
         "roofline": {"bound": "hbm", "kernel": f"{dom} (turbo3, one K half-cache per launch)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,

@@ -30,12 +30,16 @@
 #include "tq_device.h"
 #include "tq_internal.h"
 
+// the LDS copy statements set M0 themselves; nothing else in these kernels uses it
+#pragma clang diagnostic ignored "-Winline-asm"
+
 namespace tq {
 namespace {
 
 constexpr int kWaves = kBlock / 64;
 
-// Streaming hints and launch width (measured on MI355X; see the tuning notes in the design doc).
+// Streaming hints and launch width (nontemporal loads and stores and 32 workgroups per compute unit
+// measured fastest on MI355X for these streaming kernels).
 #ifndef TQ_LOAD_NT
 #define TQ_LOAD_NT 1
 #endif
@@ -43,7 +47,10 @@ constexpr int kWaves = kBlock / 64;
 #define TQ_STORE_NT 1
 #endif
 #ifndef TQ_GRID_PER_CU
-#define TQ_GRID_PER_CU 16
+#define TQ_GRID_PER_CU 32
+#endif
+#ifndef TQ_DEC_LGC
+#define TQ_DEC_LGC 1
 #endif
 
 __device__ __forceinline__ u32x4 load_stream(const u32x4* p) {
@@ -287,6 +294,163 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
   }
 }
 
+// Asynchronous copies global -> LDS (global_load_lds): lane l's data lands at m0 + 16 l (12- and
+// 16-byte copies) or m0 + 4 l (4- and 2-byte copies); m0 must be wave-uniform.  Written as inline
+// assembly: the compiler neither waits for them nor orders later LDS reads behind them, so a copy
+// for the next iteration can stay in flight across this iteration's stores; the caller waits by
+// hand (vmcnt counts these copies, loads and stores together, in issue order).
+template <int BYTES>
+__device__ __forceinline__ void lds_copy(const void* g, const void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  if constexpr (BYTES == 16)
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory");
+  else if constexpr (BYTES == 12)
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx3 %0, off" ::"v"(g), "s"(m0) : "memory");
+  else if constexpr (BYTES == 4)
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0) : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_ushort %0, off" ::"v"(g), "s"(m0) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Copy the code record and norm of group g (lane's own) into the wave's LDS slots: records at
+// rec_lds + 16 l (BITS = 3, 4) or word planes rec_lds + 256 k + 4 l (BITS = 1, 2), norms at
+// n_lds + 4 l.  Returns the number of copy instructions.
+template <int BITS, bool NORM_F32>
+__device__ __forceinline__ void copy_rec(const uint8_t* codes, const void* norms, int64_t g, uint8_t* rec_lds,
+                                         uint8_t* n_lds) {
+  const uint8_t* cp = codes + g * (4 * BITS);
+  if constexpr (BITS == 3 || BITS == 4) {
+    lds_copy<4 * BITS>(cp, rec_lds);
+  } else {
+#pragma unroll
+    for (int k = 0; k < BITS; ++k) lds_copy<4>(cp + 4 * k, rec_lds + 256 * k);
+  }
+  if constexpr (NORM_F32)
+    lds_copy<4>(static_cast<const float*>(norms) + g, n_lds);
+  else
+    lds_copy<2>(static_cast<const uint16_t*>(norms) + g, n_lds);
+}
+
+typedef _Float16 v8h_t __attribute__((ext_vector_type(8)));
+typedef float v16f_t __attribute__((ext_vector_type(16)));
+
+// Record word k of a 32-coordinate group whose coordinates 0..15 were packed into lo[] and
+// 16..31 into hi[] (16 BITS-bit codes each, little-endian bit streams).
+template <int BITS>
+__device__ __forceinline__ uint32_t join_halves(const uint32_t* lo, const uint32_t* hi, int k) {
+  if constexpr (BITS == 1) {
+    return (lo[0] & 0xFFFFu) | (hi[0] << 16);
+  } else if constexpr (BITS == 2) {
+    return k == 0 ? lo[0] : hi[0];
+  } else if constexpr (BITS == 3) {
+    return k == 0 ? lo[0] : k == 1 ? (lo[1] & 0xFFFFu) | (hi[0] << 16) : (hi[0] >> 16) | (hi[1] << 16);
+  } else {
+    return k < 2 ? lo[k] : hi[k - 2];
+  }
+}
+
+// Block-32 encode of fp16 rows with the Walsh-Hadamard transform on MFMA.
+// For a set of 32 groups, Yhat^T = M X^T with M = H_unnorm diag(D) (entries
+// +-1, exact in fp16) and X the fp16 inputs: products are exact and the sums
+// are accumulated in fp32, two v_mfma_f32_32x32x16_f16 per set and two sets
+// per wave (the wave's 64 groups, staged through LDS as in encode_kernel).
+// The rows of M are permuted so that output lane half h holds coordinates
+// 16h .. 16h+15 of its group in accumulator registers 0..15; each lane
+// bucketizes and packs those 16 with the same most-significant-first chain
+// as encode_kernel, and one permlane32 swap per segment word hands every lane
+// both halves of the record it stores.  The norm comes from the fp16 inputs
+// (dot2 of the lane's 16 values plus the partner lane's).
+template <int BITS, bool NORM_F32, bool CONTIG>
+__global__ __launch_bounds__(kBlock) void encode32_mfma_kernel(EncodeArgs a) {
+  constexpr int CH = 4, PITCH = 16 * CH + 16;
+  constexpr int SEGW = (16 * BITS + 31) / 32;  // words of one lane's 16-code segment
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kWaves][64 * PITCH];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n32 = lane & 31, h = lane >> 5;
+  uint8_t* tile = stage[wave];
+  const uint32_t dword = a.dbits[0];
+  // A operand of K chunk kc: lane holds A[m][k] for row m = n32, k = 16 kc + 8 h + j, with
+  // A[m][k] = H[pi(m)][k] D[k] and pi(m) the coordinate that accumulator row m should carry
+  const int pm = 16 * ((n32 >> 2) & 1) + 4 * (n32 >> 3) + (n32 & 3);
+  v8h_t am[2];
+#pragma unroll
+  for (int kc = 0; kc < 2; ++kc) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int k = 16 * kc + 8 * h + j;
+      const uint32_t neg = ((uint32_t)__builtin_popcount(pm & k) ^ (dword >> k)) & 1u;
+      am[kc][j] = neg ? (_Float16)-1.0f : (_Float16)1.0f;
+    }
+  }
+  float thr[7];
+#pragma unroll
+  for (int k = 0; k < 7; ++k) thr[k] = a.thr[k];
+  const char* xbase = static_cast<const char*>(a.x);
+
+  const int64_t stride = (int64_t)gridDim.x * kBlock;
+  for (int64_t w0 = (int64_t)blockIdx.x * kBlock + wave * 64; w0 < a.n_groups; w0 += stride) {
+    stage_in<CH, PITCH, 2, CONTIG>(tile, xbase, w0, a.n_groups, a.groups_per_row, a.ld_x, lane);
+    __builtin_amdgcn_wave_barrier();
+    uint32_t seg[2][SEGW];
+    float nrm[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      // B operand: coordinates 8h .. 8h+7 (chunk 0) and 16+8h .. 16+8h+7 (chunk 1) of group 32s + n32
+      const uint8_t* gp = tile + (32 * s + n32) * PITCH + 16 * h;
+      const v8h_t b0 = *reinterpret_cast<const v8h_t*>(gp);
+      const v8h_t b1 = *reinterpret_cast<const v8h_t*>(gp + 32);
+      float ss = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const half2v p0 = {b0[2 * i], b0[2 * i + 1]}, p1 = {b1[2 * i], b1[2 * i + 1]};
+        ss = __builtin_amdgcn_fdot2(p0, p0, ss, false);
+        ss = __builtin_amdgcn_fdot2(p1, p1, ss, false);
+      }
+      const v16f_t z = {};
+      v16f_t y = __builtin_amdgcn_mfma_f32_32x32x16_f16(am[0], b0, z, 0, 0, 0);
+      y = __builtin_amdgcn_mfma_f32_32x32x16_f16(am[1], b1, y, 0, 0, 0);
+      const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, ss), __builtin_bit_cast(uint32_t, ss),
+                                                      false, false);
+      const float n = __builtin_sqrtf(__builtin_bit_cast(float, (uint32_t)r[0]) +
+                                      __builtin_bit_cast(float, (uint32_t)r[1]));
+      nrm[s] = n;
+      float T[7];
+#pragma unroll
+      for (int k = 0; k < 7; ++k) T[k] = thr[k] * n;
+#pragma unroll
+      for (int k = 0; k < SEGW; ++k) seg[s][k] = 0u;
+#pragma unroll
+      for (int j = 15; j >= 0; --j) code_chain<BITS>(seg[s], j, y[j], T);
+    }
+    __builtin_amdgcn_wave_barrier();
+    // lanes < 32 store group n32 (set 0), lanes >= 32 group 32 + n32 (set 1): the swap leaves the
+    // half with coordinates 0..15 of the stored group in r[0] and the half with 16..31 in r[1]
+    uint32_t lo[SEGW], hi[SEGW];
+#pragma unroll
+    for (int k = 0; k < SEGW; ++k) {
+      const auto r = __builtin_amdgcn_permlane32_swap(seg[0][k], seg[1][k], false, false);
+      lo[k] = r[0];
+      hi[k] = r[1];
+    }
+    const float n = h ? nrm[1] : nrm[0];
+    const int64_t g = w0 + lane;
+    if (g < a.n_groups) {
+      uint32_t* cp = reinterpret_cast<uint32_t*>(a.codes + g * (4 * BITS));
+#pragma unroll
+      for (int k = 0; k < BITS; ++k)
+        __builtin_nontemporal_store(n == 0.0f ? zero_unit_word<BITS>(k) : join_halves<BITS>(lo, hi, k), cp + k);
+      if constexpr (NORM_F32)
+        static_cast<float*>(a.norms)[g] = n;
+      else
+        static_cast<__half*>(a.norms)[g] = __float2half_rn(n);
+    }
+  }
+}
+
 // Pair table: entry (code_a | code_b << BITS) = (c_a + c_b, c_a - c_b), N(0,1) scale.
 template <int BITS>
 __device__ __forceinline__ void fill_pair_table(float2* tab, const float* level) {
@@ -389,6 +553,163 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs a) {
   }
 }
 
+// Block-32 decode with the inverse transform on MFMA: for a set of 32 groups,
+// Xhat^T = Minv C^T with Minv = diag(D) H_unnorm (entries +-1) and C the
+// centroids in the N(0,1) scale, each split into fp16 hi + lo parts.  The pair
+// table yields, per lookup of two codes, (hi pair, lo pair); two lookups form
+// one B operand [hi hi lo lo hi hi lo lo] of four coordinates, and the A
+// operand repeats each Minv entry on the hi and lo slot, so Minv (c_hi + c_lo)
+// is summed in fp32 by four v_mfma_f32_32x32x16_f16 per set.  Output rows are
+// permuted as in encode32_mfma_kernel (lane half h: coordinates 16h..16h+15),
+// scaled by n / 32 (or n / ||Xhat|| with norm correction, ||Xhat||^2 =
+// 32 ||c||^2), staged in LDS and stored coalesced.
+template <int BITS, bool OUT_F32, bool NORM_F32, bool NC, bool CONTIG>
+__global__ __launch_bounds__(kBlock) void decode32_mfma_kernel(DecodeArgs a) {
+  constexpr int L = 1 << BITS;
+  constexpr int CH = OUT_F32 ? 8 : 4, PITCH = 16 * CH + 16, ES = OUT_F32 ? 4 : 2;
+  constexpr int LGC = TQ_DEC_LGC, NCOPY = 1 << LGC;  // pair-table copies (lane l reads copy l % NCOPY)
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kWaves][64 * PITCH];
+  __shared__ __attribute__((aligned(16))) uint2 ptab[L * L * NCOPY];
+  __shared__ __attribute__((aligned(16))) uint8_t pre_rec[kWaves][1024];
+  __shared__ __attribute__((aligned(16))) uint8_t pre_norm[kWaves][256];
+  for (int x = threadIdx.x; x < L * L * NCOPY; x += kBlock) {
+    const int e = x >> LGC;
+    const float ca = a.level[e & (L - 1)], cb = a.level[e >> BITS];
+    const _Float16 ha = (_Float16)ca, hb = (_Float16)cb;
+    const _Float16 la = (_Float16)(ca - (float)ha), lb = (_Float16)(cb - (float)hb);
+    ptab[x] = make_uint2((uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16),
+                         (uint32_t)__builtin_bit_cast(uint16_t, la) | ((uint32_t)__builtin_bit_cast(uint16_t, lb) << 16));
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n32 = lane & 31, h = lane >> 5;
+  uint8_t* tile = stage[wave];
+  const char* tabp = reinterpret_cast<const char*>(ptab);
+  const uint32_t toff = (uint32_t)(lane & (NCOPY - 1)) * 8u;
+  const uint32_t dword = a.dbits[0];
+  // A operand of MFMA f: row m = n32 carries output coordinate pm; slot 8h + j is code
+  // coordinate 8f + 4h + {0,1,0,1,2,3,2,3}[j] (hi parts on slots 0,1,4,5, lo parts on 2,3,6,7)
+  const int pm = 16 * ((n32 >> 2) & 1) + 4 * (n32 >> 3) + (n32 & 3);
+  v8h_t am[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = 8 * f + 4 * h + ((j >> 2) << 1) + (j & 1);
+      const uint32_t neg = ((uint32_t)__builtin_popcount(pm & c) ^ (dword >> pm)) & 1u;
+      am[f][j] = neg ? (_Float16)-1.0f : (_Float16)1.0f;
+    }
+  }
+  char* ybase = static_cast<char*>(a.y);
+
+  // The record and norm of the next iteration are copied into LDS before this iteration's stores
+  // are issued, so the wait for them at the top of an iteration leaves the previous iteration's
+  // stores (4 for a full wave) in flight.
+  const int64_t stride = (int64_t)gridDim.x * kBlock;
+  uint8_t* rec_lds = pre_rec[wave];
+  uint8_t* n_lds = pre_norm[wave];
+  const int64_t first = (int64_t)blockIdx.x * kBlock + wave * 64;
+  copy_rec<BITS, NORM_F32>(a.codes, a.norms, first + lane < a.n_groups ? first + lane : a.n_groups - 1, rec_lds, n_lds);
+  bool prev_full = false;
+  for (int64_t w0 = first; w0 < a.n_groups; w0 += stride) {
+    if (prev_full)
+      wait_vm<4>();
+    else
+      wait_vm<0>();
+    const int64_t g = w0 + lane;
+    uint32_t rec[BITS];
+    float n = 0.0f;
+    {
+      uint32_t pr[BITS], pn;
+      if constexpr (BITS == 3 || BITS == 4) {
+#pragma unroll
+        for (int k = 0; k < BITS; ++k) pr[k] = reinterpret_cast<const uint32_t*>(rec_lds)[4 * lane + k];
+      } else {
+#pragma unroll
+        for (int k = 0; k < BITS; ++k) pr[k] = reinterpret_cast<const uint32_t*>(rec_lds + 256 * k)[lane];
+      }
+      pn = reinterpret_cast<const uint32_t*>(n_lds)[lane];
+      const bool live = g < a.n_groups;
+#pragma unroll
+      for (int k = 0; k < BITS; ++k) rec[k] = live ? pr[k] : 0u;
+      const float nf = NORM_F32 ? __builtin_bit_cast(float, pn) : __half2float(__ushort_as_half((uint16_t)pn));
+      n = live ? nf : 0.0f;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slots read before the next copy lands
+    {
+      const int64_t gn = w0 + stride + lane;
+      copy_rec<BITS, NORM_F32>(a.codes, a.norms, gn < a.n_groups ? gn : a.n_groups - 1, rec_lds, n_lds);
+    }
+    prev_full = w0 + 64 <= a.n_groups;
+    // every lane gets the records and norms of both sets (lanes 0..31: set 0, 32..63: set 1)
+    uint32_t rs[2][BITS];
+#pragma unroll
+    for (int k = 0; k < BITS; ++k) {
+      const auto r = __builtin_amdgcn_permlane32_swap(rec[k], rec[k], false, false);
+      rs[0][k] = r[0];
+      rs[1][k] = r[1];
+    }
+    const auto rn = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, n), __builtin_bit_cast(uint32_t, n),
+                                                     false, false);
+    const float ns[2] = {__builtin_bit_cast(float, (uint32_t)rn[0]), __builtin_bit_cast(float, (uint32_t)rn[1])};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      // this lane's codes start at coordinate 4h of each 8-coordinate chunk: shift the record by 4h codes
+      uint32_t w[BITS];
+#pragma unroll
+      for (int k = 0; k < BITS; ++k)
+        w[k] = __builtin_amdgcn_alignbit(k + 1 < BITS ? rs[s][k + 1] : 0u, rs[s][k], 4 * BITS * h);
+      v16f_t y = {};
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        uint2 e[2];
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          const int pos = 8 * BITS * f + 2 * BITS * pp, wi = pos >> 5, sh = pos & 31;
+          const uint32_t key = sh + 2 * BITS <= 32
+                                   ? __builtin_amdgcn_ubfe(w[wi], sh, 2 * BITS)
+                                   : __builtin_amdgcn_ubfe(__builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh), 0, 2 * BITS);
+          e[pp] = *reinterpret_cast<const uint2*>(tabp + ((key << (LGC + 3)) | toff));
+        }
+        const v8h_t b = __builtin_bit_cast(v8h_t, u32x4{e[0].x, e[0].y, e[1].x, e[1].y});
+        y = __builtin_amdgcn_mfma_f32_32x32x16_f16(am[f], b, y, 0, 0, 0);
+      }
+      float scale;
+      if constexpr (NC) {
+        float ss = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ss = __builtin_fmaf(y[i], y[i], ss);
+        const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, ss), __builtin_bit_cast(uint32_t, ss),
+                                                        false, false);
+        scale = ns[s] / __builtin_sqrtf(__builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]));
+      } else {
+        scale = ns[s] * a.inv_dt;
+      }
+      uint8_t* dst = tile + (32 * s + n32) * PITCH + ES * 16 * h;
+      if constexpr (!OUT_F32) {
+        uint32_t o[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const __half lo = __float2half_rn(y[2 * i] * scale), hi = __float2half_rn(y[2 * i + 1] * scale);
+          o[i] = (uint32_t)__half_as_ushort(lo) | ((uint32_t)__half_as_ushort(hi) << 16);
+        }
+        reinterpret_cast<u32x4*>(dst)[0] = u32x4{o[0], o[1], o[2], o[3]};
+        reinterpret_cast<u32x4*>(dst)[1] = u32x4{o[4], o[5], o[6], o[7]};
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          reinterpret_cast<u32x4*>(dst)[c] =
+              u32x4{__builtin_bit_cast(uint32_t, y[4 * c] * scale), __builtin_bit_cast(uint32_t, y[4 * c + 1] * scale),
+                    __builtin_bit_cast(uint32_t, y[4 * c + 2] * scale), __builtin_bit_cast(uint32_t, y[4 * c + 3] * scale)};
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    stage_out<CH, PITCH, ES, CONTIG>(tile, ybase, w0, a.n_groups, a.groups_per_row, a.ld_y, lane);
+    __builtin_amdgcn_wave_barrier();
+  }
+  wait_vm<0>();  // the last (unused) copy must land before the workgroup's LDS is released
+}
+
 // Workgroups per launch: enough resident waves to cover HBM latency, with a
 // grid-stride loop over the rest (amortises the per-lane set-up).
 int64_t grid_for(int64_t n_groups) {
@@ -409,6 +730,15 @@ template <int BITS, int LPU, bool CONTIG>
 hipError_t encode_dispatch_dtype(const tq_config& cfg, const EncodeArgs& a, hipStream_t s) {
   dim3 grid((unsigned)grid_for(a.n_groups)), block(kBlock);
   const bool in32 = cfg.x_dtype == TQ_F32, n32 = cfg.norm_dtype == TQ_F32;
+  if constexpr (LPU == 1) {
+    if (!in32) {
+      if (n32)
+        hipLaunchKernelGGL((encode32_mfma_kernel<BITS, true, CONTIG>), grid, block, 0, s, a);
+      else
+        hipLaunchKernelGGL((encode32_mfma_kernel<BITS, false, CONTIG>), grid, block, 0, s, a);
+      return hipGetLastError();
+    }
+  }
   if (!in32 && !n32) hipLaunchKernelGGL((encode_kernel<BITS, LPU, false, false, CONTIG>), grid, block, 0, s, a);
   if (!in32 && n32) hipLaunchKernelGGL((encode_kernel<BITS, LPU, false, true, CONTIG>), grid, block, 0, s, a);
   if (in32 && !n32) hipLaunchKernelGGL((encode_kernel<BITS, LPU, true, false, CONTIG>), grid, block, 0, s, a);
@@ -435,6 +765,13 @@ template <int BITS, int LPU, bool NC, bool CONTIG>
 hipError_t decode_dispatch_dtype(const tq_config& cfg, const DecodeArgs& a, tq_dtype yt, hipStream_t s) {
   dim3 grid((unsigned)grid_for(a.n_groups)), block(kBlock);
   const bool o32 = yt == TQ_F32, n32 = cfg.norm_dtype == TQ_F32;
+  if constexpr (LPU == 1) {
+    if (!o32 && !n32) hipLaunchKernelGGL((decode32_mfma_kernel<BITS, false, false, NC, CONTIG>), grid, block, 0, s, a);
+    if (!o32 && n32) hipLaunchKernelGGL((decode32_mfma_kernel<BITS, false, true, NC, CONTIG>), grid, block, 0, s, a);
+    if (o32 && !n32) hipLaunchKernelGGL((decode32_mfma_kernel<BITS, true, false, NC, CONTIG>), grid, block, 0, s, a);
+    if (o32 && n32) hipLaunchKernelGGL((decode32_mfma_kernel<BITS, true, true, NC, CONTIG>), grid, block, 0, s, a);
+    return hipGetLastError();
+  }
   if (!o32 && !n32) hipLaunchKernelGGL((decode_kernel<BITS, LPU, false, false, NC, CONTIG>), grid, block, 0, s, a);
   if (!o32 && n32) hipLaunchKernelGGL((decode_kernel<BITS, LPU, false, true, NC, CONTIG>), grid, block, 0, s, a);
   if (o32 && !n32) hipLaunchKernelGGL((decode_kernel<BITS, LPU, true, false, NC, CONTIG>), grid, block, 0, s, a);
