@@ -26,13 +26,17 @@ ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-function"]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-munsafe-fp-atomics", "-ffp-contract=fast"]
+# Per-file code generation options.  The codec kernels read every MFMA result
+# straight into VALU work; keeping MFMA results in arch VGPRs instead of AGPRs
+# saves one v_accvgpr_read per result there.
+PER_FILE = {"tq_codec.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     cmd = [HIPCC] + COMMON
     if src.endswith(".hip"):
-        cmd += DEVICE + ["-x", "hip"]
+        cmd += DEVICE + PER_FILE.get(os.path.basename(src), []) + ["-x", "hip"]
     else:
         cmd += [f"--offload-arch={ARCH}"]
     cmd += ["-c", src, "-o", obj]

@@ -38,8 +38,8 @@ namespace {
 
 constexpr int kWaves = kBlock / 64;
 
-// Streaming hints and launch width (nontemporal loads and stores and 32 workgroups per compute unit
-// measured fastest on MI355X for these streaming kernels).
+// Streaming hints and launch widths (nontemporal loads and stores, 32 workgroups per compute unit
+// for encode and 96 for the store-heavy decode measured fastest on MI355X).
 #ifndef TQ_LOAD_NT
 #define TQ_LOAD_NT 1
 #endif
@@ -48,6 +48,9 @@ constexpr int kWaves = kBlock / 64;
 #endif
 #ifndef TQ_GRID_PER_CU
 #define TQ_GRID_PER_CU 32
+#endif
+#ifndef TQ_DEC_GRID_PER_CU
+#define TQ_DEC_GRID_PER_CU 96
 #endif
 #ifndef TQ_DEC_LGC
 #define TQ_DEC_LGC 1
@@ -712,7 +715,7 @@ __global__ __launch_bounds__(kBlock) void decode32_mfma_kernel(DecodeArgs a) {
 
 // Workgroups per launch: enough resident waves to cover HBM latency, with a
 // grid-stride loop over the rest (amortises the per-lane set-up).
-int64_t grid_for(int64_t n_groups) {
+int64_t grid_for(int64_t n_groups, int per_cu) {
   static int cus = 0;
   if (!cus) {
     int dev = 0;
@@ -722,13 +725,13 @@ int64_t grid_for(int64_t n_groups) {
     if (cus <= 0) cus = 256;
   }
   int64_t need = (n_groups + kBlock - 1) / kBlock;
-  int64_t cap = (int64_t)cus * TQ_GRID_PER_CU;
+  int64_t cap = (int64_t)cus * per_cu;
   return need < cap ? need : cap;
 }
 
 template <int BITS, int LPU, bool CONTIG>
 hipError_t encode_dispatch_dtype(const tq_config& cfg, const EncodeArgs& a, hipStream_t s) {
-  dim3 grid((unsigned)grid_for(a.n_groups)), block(kBlock);
+  dim3 grid((unsigned)grid_for(a.n_groups, TQ_GRID_PER_CU)), block(kBlock);
   const bool in32 = cfg.x_dtype == TQ_F32, n32 = cfg.norm_dtype == TQ_F32;
   if constexpr (LPU == 1) {
     if (!in32) {
@@ -763,7 +766,7 @@ hipError_t encode_dispatch_lpu(const tq_config& cfg, const EncodeArgs& a, hipStr
 
 template <int BITS, int LPU, bool NC, bool CONTIG>
 hipError_t decode_dispatch_dtype(const tq_config& cfg, const DecodeArgs& a, tq_dtype yt, hipStream_t s) {
-  dim3 grid((unsigned)grid_for(a.n_groups)), block(kBlock);
+  dim3 grid((unsigned)grid_for(a.n_groups, LPU == 1 ? TQ_DEC_GRID_PER_CU : TQ_GRID_PER_CU)), block(kBlock);
   const bool o32 = yt == TQ_F32, n32 = cfg.norm_dtype == TQ_F32;
   if constexpr (LPU == 1) {
     if (!o32 && !n32) hipLaunchKernelGGL((decode32_mfma_kernel<BITS, false, false, NC, CONTIG>), grid, block, 0, s, a);
