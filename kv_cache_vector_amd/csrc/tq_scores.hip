@@ -197,19 +197,28 @@ __global__ __launch_bounds__(256) void prep_keys(ScoreArgs a) {
 
 // ---------------------------------------------------------------------------
 // scores: workgroup = 4 waves x (16*CB keys each), loops over 16-query blocks
+//
+// Keys are the MFMA's A operand and queries its B operand, so each lane's
+// accumulator holds 4 consecutive keys of one query: one 16-byte store per
+// 16-key tile writes them.  The next block's query records are fetched into
+// registers before this block's MFMAs and parked in the other LDS buffer
+// after them, so one barrier per block suffices and the L2 latency of the
+// fetch hides behind the contraction.
 // ---------------------------------------------------------------------------
 template <int NP, int KD, int KM, int CB>
 __global__ __launch_bounds__(256) void scores_kernel(ScoreArgs a) {
   constexpr int Kd = 64 * KD, Km = 64 * KM, RQ = 2 * (Kd + Km), RK = NP * Kd + Km;
-  __shared__ __attribute__((aligned(16))) int8_t qblk[kQB * RQ];
-  __shared__ float qs[kQB * 2];
+  constexpr int QV = kQB * RQ / 16;  // 16-byte vectors per query block
+  constexpr int PER = (QV + 255) / 256;
+  __shared__ __attribute__((aligned(16))) int8_t qblk[2][kQB * RQ];
+  __shared__ float qs[2][kQB * 2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col_l = lane & 15, slot = lane >> 4;
   const int64_t key0 = (int64_t)blockIdx.x * (64 * CB) + wave * (16 * CB);
 
-  // this wave's key-side operands, kept in registers for the whole query chunk
+  // this wave's key-side operands (row col_l of each 16-key tile), kept in registers
   v4i bT[CB][NP][KD], bS[CB][KM];
-  float ncol[CB], nrcol[CB];
+  float nk[CB][4], nrk[CB][4];  // scales of the 4 keys 16 cb + 4 slot + i whose scores this lane writes
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     const int64_t key = key0 + 16 * cb + col_l;
@@ -220,22 +229,48 @@ __global__ __launch_bounds__(256) void scores_kernel(ScoreArgs a) {
       for (int ks = 0; ks < KD; ++ks) bT[cb][t][ks] = *reinterpret_cast<const v4i*>(rec + t * Kd + 64 * ks + 16 * slot);
 #pragma unroll
     for (int ks = 0; ks < KM; ++ks) bS[cb][ks] = *reinterpret_cast<const v4i*>(rec + NP * Kd + 64 * ks + 16 * slot);
-    ncol[cb] = a.kscale[2 * key];
-    nrcol[cb] = a.kscale[2 * key + 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t kk = key0 + 16 * cb + 4 * slot + i;
+      nk[cb][i] = a.kscale[2 * kk];
+      nrk[cb][i] = a.kscale[2 * kk + 1];
+    }
   }
   float w[NP];
 #pragma unroll
   for (int t = 0; t < NP; ++t) w[t] = a.plane_w[t];
+  // 16-byte stores need 16-byte aligned rows
+  const bool vec = ((a.ld_s & 3) == 0) && ((reinterpret_cast<uintptr_t>(a.scores) & 15) == 0);
 
   const int64_t q_begin = (int64_t)blockIdx.y * kQChunk;
   const int64_t q_end = q_begin + kQChunk < a.n_q_pad ? q_begin + kQChunk : a.n_q_pad;
-  for (int64_t r0 = q_begin; r0 < q_end; r0 += kQB) {
-    __syncthreads();
-    // stage the block's query records (16 * RQ bytes) and scales
-    for (int e = tid; e < kQB * RQ / 16; e += 256)
-      reinterpret_cast<v4i*>(qblk)[e] = reinterpret_cast<const v4i*>(a.qrec + r0 * RQ)[e];
-    if (tid < kQB * 2) qs[tid] = a.qscale[r0 * 2 + tid];
-    __syncthreads();
+  const v4i* qrec_v = reinterpret_cast<const v4i*>(a.qrec);
+  v4i pre[PER];
+  float pqs = 0.0f;
+  auto fetch = [&](int64_t r0) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int e = tid + 256 * p;
+      if (e < QV) pre[p] = qrec_v[r0 * (RQ / 16) + e];
+    }
+    if (tid < kQB * 2) pqs = a.qscale[r0 * 2 + tid];
+  };
+  auto park = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int e = tid + 256 * p;
+      if (e < QV) reinterpret_cast<v4i*>(qblk[buf])[e] = pre[p];
+    }
+    if (tid < kQB * 2) qs[buf][tid] = pqs;
+  };
+  fetch(q_begin);
+  park(0);
+  __syncthreads();
+
+  int cur = 0;
+  for (int64_t r0 = q_begin; r0 < q_end; r0 += kQB, cur ^= 1) {
+    const bool more = r0 + kQB < q_end;
+    if (more) fetch(r0 + kQB);
 
     v4i accT[CB][NP], accS[CB];
 #pragma unroll
@@ -244,7 +279,7 @@ __global__ __launch_bounds__(256) void scores_kernel(ScoreArgs a) {
       for (int t = 0; t < NP; ++t) accT[cb][t] = v4i{0, 0, 0, 0};
       accS[cb] = v4i{0, 0, 0, 0};
     }
-    const int8_t* qrow = qblk + col_l * RQ + 16 * slot;
+    const int8_t* qrow = qblk[cur] + col_l * RQ + 16 * slot;
 #pragma unroll
     for (int limb = 0; limb < 2; ++limb) {
       if (limb == 1) {
@@ -257,38 +292,48 @@ __global__ __launch_bounds__(256) void scores_kernel(ScoreArgs a) {
       }
 #pragma unroll
       for (int ks = 0; ks < KD; ++ks) {
-        const v4i aq = *reinterpret_cast<const v4i*>(qrow + limb * Kd + 64 * ks);
+        const v4i bq = *reinterpret_cast<const v4i*>(qrow + limb * Kd + 64 * ks);
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
           for (int t = 0; t < NP; ++t)
-            accT[cb][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq, bT[cb][t][ks], accT[cb][t], 0, 0, 0);
+            accT[cb][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bT[cb][t][ks], bq, accT[cb][t], 0, 0, 0);
       }
 #pragma unroll
       for (int ks = 0; ks < KM; ++ks) {
-        const v4i ap = *reinterpret_cast<const v4i*>(qrow + 2 * Kd + limb * Km + 64 * ks);
+        const v4i bp = *reinterpret_cast<const v4i*>(qrow + 2 * Kd + limb * Km + 64 * ks);
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) accS[cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ap, bS[cb][ks], accS[cb], 0, 0, 0);
+        for (int cb = 0; cb < CB; ++cb) accS[cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bS[cb][ks], bp, accS[cb], 0, 0, 0);
       }
     }
-    // epilogue: lane holds rows 4*slot + i, column col_l of each 16x16 tile
+    if (more) park(cur ^ 1);
+
+    // epilogue: lane holds keys 16 cb + 4 slot + i of query r0 + col_l
+    const float alpha = qs[cur][2 * col_l], beta = qs[cur][2 * col_l + 1];
+    v4f val[CB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = 4 * slot + i;
-      const int64_t row = r0 + rr;
-      const float alpha = qs[2 * rr], beta = qs[2 * rr + 1];
-      if (row >= a.n_q) continue;
-      float* out = a.scores + row * a.ld_s;
+    for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        float s = 0.0f;
+      for (int i = 0; i < 4; ++i) {
+        float sum = 0.0f;
 #pragma unroll
-        for (int t = 0; t < NP; ++t) s = __builtin_fmaf(w[t], (float)accT[cb][t][i], s);
-        const float v = ncol[cb] * (alpha * s) + nrcol[cb] * (beta * (float)accS[cb][i]);
-        const int64_t col = key0 + 16 * cb + col_l;
-        if (col < a.n_k) out[col] = v;
+        for (int t = 0; t < NP; ++t) sum = __builtin_fmaf(w[t], (float)accT[cb][t][i], sum);
+        val[cb][i] = nk[cb][i] * (alpha * sum) + nrk[cb][i] * (beta * (float)accS[cb][i]);
       }
+    const int64_t row = r0 + col_l;
+    float* out = a.scores + row * a.ld_s + key0 + 4 * slot;
+    if (vec && key0 + 16 * CB <= a.n_k && r0 + kQB <= a.n_q) {  // whole tile inside the matrix (wave-uniform)
+      // plain (cached) stores: L2 merges the 64-byte row pieces of the 16 queries into whole lines
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) *reinterpret_cast<v4f*>(out + 16 * cb) = val[cb];
+    } else if (row < a.n_q) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (key0 + 16 * cb + 4 * slot + i < a.n_k) out[16 * cb + i] = val[cb][i];
     }
+    __syncthreads();
   }
 }
 
