@@ -98,10 +98,6 @@ __device__ __forceinline__ uint32_t lut_word(const uint32_t* table, uint32_t w, 
   return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(table) + byte);
 }
 
-// Workgroup barrier for LDS traffic only: this wave's LDS operations have completed, nothing is
-// waited for on the global-memory side, so prefetched tiles stay in flight across it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();

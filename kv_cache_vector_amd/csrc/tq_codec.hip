@@ -297,28 +297,6 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
   }
 }
 
-// Asynchronous copies global -> LDS (global_load_lds): lane l's data lands at m0 + 16 l (12- and
-// 16-byte copies) or m0 + 4 l (4- and 2-byte copies); m0 must be wave-uniform.  Written as inline
-// assembly: the compiler neither waits for them nor orders later LDS reads behind them, so a copy
-// for the next iteration can stay in flight across this iteration's stores; the caller waits by
-// hand (vmcnt counts these copies, loads and stores together, in issue order).
-template <int BYTES>
-__device__ __forceinline__ void lds_copy(const void* g, const void* lds) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
-  if constexpr (BYTES == 16)
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory");
-  else if constexpr (BYTES == 12)
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx3 %0, off" ::"v"(g), "s"(m0) : "memory");
-  else if constexpr (BYTES == 4)
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0) : "memory");
-  else
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_ushort %0, off" ::"v"(g), "s"(m0) : "memory");
-}
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 // Copy the code record and norm of group g (lane's own) into the wave's LDS slots: records at
 // rec_lds + 16 l (BITS = 3, 4) or word planes rec_lds + 256 k + 4 l (BITS = 1, 2), norms at
 // n_lds + 4 l.  Returns the number of copy instructions.

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#pragma clang diagnostic ignored "-Winline-asm"
+
 namespace tq {
 
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
@@ -93,5 +95,31 @@ __device__ __forceinline__ uint32_t get_code(const uint32_t* w, int j) {
   if ((pos & 31) + BITS > 32) c |= w[(pos >> 5) + 1] << (32 - (pos & 31));
   return c & ((1u << BITS) - 1);
 }
+
+// Asynchronous copies global -> LDS (global_load_lds): lane l's data lands at m0 + 16 l (12- and
+// 16-byte copies) or m0 + 4 l (4- and 2-byte copies); m0 must be wave-uniform.  Written as inline
+// assembly: the compiler neither waits for them nor orders later LDS reads behind them, so a copy
+// for the next iteration can stay in flight across this iteration's stores; the caller waits by
+// hand (vmcnt counts these copies, loads and stores together, in issue order).
+template <int BYTES>
+__device__ __forceinline__ void lds_copy(const void* g, const void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+  if constexpr (BYTES == 16)
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory");
+  else if constexpr (BYTES == 12)
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx3 %0, off" ::"v"(g), "s"(m0) : "memory");
+  else if constexpr (BYTES == 4)
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0) : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_ushort %0, off" ::"v"(g), "s"(m0) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier for LDS traffic only: this wave's LDS operations have completed, nothing is
+// waited for on the global-memory side, so prefetched data stays in flight across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 }  // namespace tq

@@ -365,7 +365,8 @@ ScoreLayout score_layout(const tq_config& cfg, int64_t n_q, int64_t n_k) {
   const int64_t kd = (cfg.dt + 63) / 64 * 64, km = (cfg.qjl_m + 63) / 64 * 64;
   const int64_t tile = tq::scores_key_tile(cfg.bits);
   L.planes = (int64_t)1 << (cfg.bits - 1);
-  L.n_q_pad = (n_q + 15) / 16 * 16;
+  const int64_t qb = tq::scores_query_block();
+  L.n_q_pad = (n_q + qb - 1) / qb * qb;
   L.n_k_pad = (n_k + tile - 1) / tile * tile;
   L.rq = 2 * (kd + km);
   L.rk = L.planes * kd + km;

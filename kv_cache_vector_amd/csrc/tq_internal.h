@@ -84,10 +84,11 @@ struct ScoreArgs {
   int64_t n_k, n_k_pad;      // keys, padded to the scores key tile
   float* scores;
   int64_t ld_s;
-  int8_t* qrec;              // [n_q_pad][2*(kd+km)]: qhat hi, qhat lo, p hi, p lo (int8 limbs)
+  int8_t* qrec;              // [n_q_pad / 32] blocks of 32 queries x 2*(kd+km) int8 limbs (qhat hi, qhat lo,
+                             // p hi, p lo), each block laid out as 1 KiB MFMA operand fragments
   float* qscale;             // [n_q_pad][2]: fixed-point scale of qhat / sqrt(dt), of p * sqrt(pi/2)/m
   int8_t* krec;              // [n_k_pad][planes*kd + km]: ternary planes, then the +-1 sign plane
-  float* kscale;             // [n_k_pad][2]: n_j, n_j * rho_j
+  float* kscale;             // [2][n_k_pad]: n_j, then n_j * rho_j
   const float* s_rot32;      // S~ [m][dt] float32
   uint32_t dbits[8];
   float plane_w[8];          // weight of each ternary plane (N(0,1) scale)
@@ -123,6 +124,7 @@ hipError_t launch_qjl_encode(const tq_config& cfg, const QjlEncodeArgs& a, hipSt
 hipError_t launch_qjl_decode(const tq_config& cfg, const QjlDecodeArgs& a, bool nc, tq_dtype y_dtype, hipStream_t s);
 hipError_t launch_qjl_scores(const tq_config& cfg, const ScoreArgs& a, hipStream_t s);
 int64_t scores_key_tile(int bits);
+int64_t scores_query_block();
 hipError_t launch_decode_attn(int kbits, int vbits, const AttnArgs& a, hipStream_t s);
 int64_t attn_tokens_per_wg(int n_kv_heads, int64_t n_tokens);
 

@@ -3,7 +3,8 @@
 //   score[i][j] = n_j * ( <q_i, D H c_j> + rho_j * sqrt(pi/2)/m * <S q_i, sign_j> )
 //
 // Both contractions over all (query, key) pairs run on int8 MFMA
-// (v_mfma_i32_16x16x64_i8) with exact integer accumulation:
+// (v_mfma_i32_32x32x32_i8, the shape that reaches the int8 matrix peak on
+// gfx950) with exact integer accumulation:
 //   * key side, exact small integers: the reconstruction c_j = sgn * C[mag]
 //     is split over the magnitude bits, c = sum_t w_t * T_t with
 //     T_t[d] = sgn_d * [mag_d contains the bits of t] in {0, +-1} and weights
@@ -16,10 +17,11 @@
 // rotated back.  The rounding error is that of 16-bit fixed point for qhat
 // and p (about 1e-5 of ||q|| per element), far inside the 1e-4 tolerance.
 //
-// Kernels: prep_queries (one workgroup per 16 queries: rotation in LDS, S~
-// projection on fp32 MFMA, fixed-point limbs), prep_keys (one lane per key:
-// ternary planes and per-key scalars), scores (each wave keeps the operand
-// planes of 64 keys in registers and streams 16-query blocks through LDS).
+// Kernels: prep_queries (one workgroup per 16 queries: rotation in registers,
+// S~ projection on fp32 MFMA, fixed-point limbs written as MFMA operand
+// fragments), prep_keys (one lane per 16-byte piece of a key's operand
+// record), scores (each wave keeps the operand planes of 32*CB keys in
+// registers and streams 32-query blocks through an LDS ring).
 #include <hip/hip_fp16.h>
 
 #include "tq_device.h"
@@ -29,212 +31,229 @@ namespace tq {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kQB = 16;         // queries per row block
+constexpr int kQB = 32;         // queries per block (the MFMA's N)
 constexpr int kQChunk = 512;    // queries per scores workgroup
 constexpr float kFixed = 32000.0f;
 
+// Byte offset of element idx (of a Kd- or Km-long int8 vector) of query r inside its block's
+// fragment f0 + idx / 32: fragment = 1 KiB, lane 32 h + r holds bytes 16 h .. 16 h + 15 of the
+// 32-byte chunk, which is the operand layout of v_mfma_i32_32x32x32_i8.
+__device__ __forceinline__ int frag_offset(int f0, int r, int idx) {
+  return (f0 + (idx >> 5)) * 1024 + ((((idx >> 4) & 1) * 32 + r) * 16) + (idx & 15);
+}
+
 // ---------------------------------------------------------------------------
-// query preparation
+// query preparation: one workgroup per 16 queries (half of a 32-query block).
+// Thread t owns 8 consecutive coordinates (and 8 projections) of query t / 16:
+// the rotation runs 3 butterfly stages in registers and 4 across the 16 lanes
+// of the query, the maxima are 16-lane reductions, and each thread writes its
+// 8 limbs as 8-byte pieces of the block's operand fragments.  dt, m <= 128.
 // ---------------------------------------------------------------------------
 template <bool Q_F32>
 __global__ __launch_bounds__(256) void prep_queries(ScoreArgs a) {
-  extern __shared__ float smem[];
-  const int dt = a.dt, m = a.m;
-  float* qhat = smem;                // [kQB][dt]
-  float* pbuf = smem + kQB * dt;     // [kQB][m]
-  __shared__ float red[kQB][2];
-  const int row0 = blockIdx.x * kQB;
+  __shared__ float qhat[16][128 + 4];
+  __shared__ float pbuf[16][128 + 4];
+  const int dt = a.dt, m = a.m, Kd = a.kd, Km = a.km, RQ = 2 * (Kd + Km);
+  const int64_t row0 = (int64_t)blockIdx.x * 16;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = tid >> 4, c8 = (tid & 15) * 8;  // query r of the 16, coordinates c8 .. c8 + 7
+  const int64_t row = row0 + r;
 
-  for (int e = tid; e < kQB * dt; e += 256) {
-    const int r = e / dt, d = e % dt;
-    float v = 0.0f;
-    if (row0 + r < a.n_q) {
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int d = c8 + i;
+    float x = 0.0f;
+    if (row < a.n_q && d < dt) {
       if constexpr (Q_F32)
-        v = static_cast<const float*>(a.q)[(int64_t)(row0 + r) * a.ld_q + d];
+        x = static_cast<const float*>(a.q)[row * a.ld_q + d];
       else
-        v = __half2float(static_cast<const __half*>(a.q)[(int64_t)(row0 + r) * a.ld_q + d]);
+        x = __half2float(static_cast<const __half*>(a.q)[row * a.ld_q + d]);
     }
-    qhat[e] = ((a.dbits[d >> 5] >> (d & 31)) & 1u) ? -v : v;
+    v[i] = ((a.dbits[(d >> 5) & 7] >> (d & 31)) & 1u) ? -x : x;
   }
-  __syncthreads();
-  for (int h = 1; h < dt; h <<= 1) {  // unnormalised butterflies, one index bit per pass
-    for (int e = tid; e < kQB * dt / 2; e += 256) {
-      const int r = e / (dt / 2), pidx = e % (dt / 2);
-      const int i = (pidx / h) * 2 * h + (pidx % h);
-      float* row = qhat + r * dt;
-      const float x = row[i], y = row[i + h];
-      row[i] = x + y;
-      row[i + h] = x - y;
+  // unnormalised FWHT over dt coordinates: bits 0..2 in registers, bits 3..6 across lanes 1, 2, 4, 8 apart
+#pragma unroll
+  for (int bit = 1; bit < 8; bit <<= 1)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (!(i & bit)) {
+        const float x = v[i], y = v[i | bit];
+        v[i] = x + y;
+        v[i | bit] = x - y;
+      }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if ((8 << k) >= dt) break;
+    const bool upper = (tid >> k) & 1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float o = __shfl_xor(v[i], 1 << k);
+      v[i] = upper ? o - v[i] : v[i] + o;
     }
-    __syncthreads();
   }
   const float inv_sqrt_dt = a.inv_sqrt_dt;
-  for (int e = tid; e < kQB * dt; e += 256) qhat[e] *= inv_sqrt_dt;
-  __syncthreads();
-
-  // p = S~ qhat on fp32 MFMA: 16 queries x 16 projections per tile, K = 4 per step
-  for (int t = wave; t < m / 16; t += 4) {
-    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    const float* srow = a.s_rot32 + (int64_t)(16 * t + (lane & 15)) * dt;
-    for (int k0 = 0; k0 < dt; k0 += 4) {
-      const float av = qhat[(lane & 15) * dt + k0 + (lane >> 4)];
-      const float bv = srow[k0 + (lane >> 4)];
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
-    }
+  float ma = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pbuf[(4 * (lane >> 4) + i) * m + 16 * t + (lane & 15)] = acc[i];
+  for (int i = 0; i < 8; ++i) {
+    v[i] = c8 + i < dt ? v[i] * inv_sqrt_dt : 0.0f;
+    ma = fmaxf(ma, fabsf(v[i]));
+    qhat[r][c8 + i] = v[i];
   }
   __syncthreads();
 
-  // per-query maxima (wave w handles queries 4w .. 4w+3)
-  for (int r = 4 * wave; r < 4 * wave + 4; ++r) {
-    float ma = 0.0f, mp = 0.0f;
-    for (int d = lane; d < dt; d += 64) ma = fmaxf(ma, fabsf(qhat[r * dt + d]));
-    for (int j = lane; j < m; j += 64) mp = fmaxf(mp, fabsf(pbuf[r * m + j]));
-    for (int off = 32; off >= 1; off >>= 1) {
-      ma = fmaxf(ma, __shfl_xor(ma, off));
-      mp = fmaxf(mp, __shfl_xor(mp, off));
-    }
-    if (lane == 0) {
-      red[r][0] = ma;
-      red[r][1] = mp;
-    }
+  // p = S~ qhat on fp32 MFMA: the 16 queries x 16 projections of tile ct, K = 4 per step
+  for (int ct = wave; ct < m / 16; ct += 4) {
+    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    const float* srow = a.s_rot32 + (int64_t)(16 * ct + (lane & 15)) * dt;
+    for (int k0 = 0; k0 < dt; k0 += 4)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qhat[lane & 15][k0 + (lane >> 4)], srow[k0 + (lane >> 4)], acc, 0, 0,
+                                                 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pbuf[4 * (lane >> 4) + i][16 * ct + (lane & 15)] = acc[i];
   }
   __syncthreads();
+  float pv[8], mp = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    pv[i] = c8 + i < m ? pbuf[r][c8 + i] : 0.0f;
+    mp = fmaxf(mp, fabsf(pv[i]));
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    ma = fmaxf(ma, __shfl_xor(ma, 1 << k));
+    mp = fmaxf(mp, __shfl_xor(mp, 1 << k));
+  }
 
   // fixed-point limbs: Q = rint(x * kFixed / max), hi = floor((Q + 128) / 256), lo = Q - 256 hi
-  const int Kd = a.kd, Km = a.km, RQ = 2 * (Kd + Km);
-  for (int e = tid; e < kQB * (Kd + Km); e += 256) {
-    const int r = e / (Kd + Km), c = e % (Kd + Km);
-    const bool is_p = c >= Kd;
-    const int idx = is_p ? c - Kd : c;
-    const int lim = is_p ? m : dt;
-    const float mx = red[r][is_p ? 1 : 0];
-    float x = 0.0f;
-    if (idx < lim) x = is_p ? pbuf[r * m + idx] : qhat[r * dt + idx];
-    int Q = mx > 0.0f ? (int)rintf(x * (kFixed / mx)) : 0;
-    Q = Q > 32000 ? 32000 : (Q < -32000 ? -32000 : Q);
-    const int hi = (Q + 128) >> 8, lo = Q - 256 * hi;
-    int8_t* rec = a.qrec + (int64_t)(row0 + r) * RQ;
-    const int base = is_p ? 2 * Kd : 0, width = is_p ? Km : Kd;
-    rec[base + idx] = (int8_t)hi;
-    rec[base + width + idx] = (int8_t)lo;
-  }
-  if (tid < kQB) {
-    const float sa = red[tid][0] > 0.0f ? red[tid][0] / kFixed : 0.0f;
-    const float sp = red[tid][1] > 0.0f ? red[tid][1] / kFixed : 0.0f;
-    a.qscale[(row0 + tid) * 2] = sa * inv_sqrt_dt;
-    a.qscale[(row0 + tid) * 2 + 1] = sp * a.qjl_const;
+  int8_t* blk = a.qrec + (row0 & ~(int64_t)(kQB - 1)) * RQ;
+  const int rb = (int)(row0 & (kQB - 1)) + r;  // row within the 32-query block
+  auto put = [&](const float* x, float mx, int idx, int f0, int nks) {
+    uint32_t hw[2] = {0u, 0u}, lw[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      int Q = mx > 0.0f ? (int)rintf(x[i] * (kFixed / mx)) : 0;
+      Q = Q > 32000 ? 32000 : (Q < -32000 ? -32000 : Q);
+      const int hi = (Q + 128) >> 8, lo = Q - 256 * hi;
+      hw[i >> 2] |= (uint32_t)(hi & 0xFF) << (8 * (i & 3));
+      lw[i >> 2] |= (uint32_t)(lo & 0xFF) << (8 * (i & 3));
+    }
+    *reinterpret_cast<uint2*>(blk + frag_offset(f0, rb, idx)) = make_uint2(hw[0], hw[1]);
+    *reinterpret_cast<uint2*>(blk + frag_offset(f0 + nks, rb, idx)) = make_uint2(lw[0], lw[1]);
+  };
+  if (c8 < Kd) put(v, ma, c8, 0, Kd / 32);
+  if (c8 < Km) put(pv, mp, c8, 2 * (Kd / 32), Km / 32);
+  if ((tid & 15) == 0) {
+    a.qscale[row * 2] = (ma > 0.0f ? ma / kFixed : 0.0f) * inv_sqrt_dt;
+    a.qscale[row * 2 + 1] = (mp > 0.0f ? mp / kFixed : 0.0f) * a.qjl_const;
   }
 }
 
 // ---------------------------------------------------------------------------
-// key preparation: one lane per key
+// key preparation: one lane per 16-byte piece of a key's record (NP ternary
+// planes of Kd bytes, then Km bytes of the +-1 sign plane)
 // ---------------------------------------------------------------------------
 template <int BITS, bool NORM_F32>
 __global__ __launch_bounds__(256) void prep_keys(ScoreArgs a) {
   constexpr int NP = 1 << (BITS - 1);
-  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (j >= a.n_k_pad) return;
   const int dt = a.dt, m = a.m, Kd = a.kd, Km = a.km;
-  const int RK = NP * Kd + Km;
-  uint32_t* rec = reinterpret_cast<uint32_t*>(a.krec + j * RK);
+  const int pieces = (NP * Kd + Km) / 16;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t j = gid / pieces;
+  const int c = (int)(gid - j * pieces);
+  if (j >= a.n_k_pad) return;
   const bool live = j < a.n_k;
-  // ternary planes, 4 coordinates per dword
-  for (int d4 = 0; d4 < Kd; d4 += 4) {
-    uint32_t planes[NP];
+  u32x4 out = {0u, 0u, 0u, 0u};
+  if (c < NP * Kd / 16) {
+    const int t = c / (Kd / 16), d0 = (c % (Kd / 16)) * 16;
+    if (live && d0 < dt) {
+      // the key's codes form one little-endian bitstream of dt * BITS bits; take bits BITS*d0 .. +16*BITS
+      const uint32_t* wp = reinterpret_cast<const uint32_t*>(a.codes + j * (dt * BITS / 8));
+      const int pos = BITS * d0, w0 = pos >> 5;
+      const int last = (pos + 16 * BITS - 1) >> 5;
+      uint64_t bits = wp[w0];
+      if (last > w0) bits |= (uint64_t)wp[w0 + 1] << 32;
+      bits >>= (pos & 31);
+      uint32_t b[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int t = 0; t < NP; ++t) planes[t] = 0u;
-    if (live) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int d = d4 + k;
-        if (d >= dt) break;
-        const int pos = BITS * d;  // coordinate d of the unit: group d/32, bit BITS*(d%32) -> same as BITS*d
-        const uint32_t* wp = reinterpret_cast<const uint32_t*>(a.codes + j * (dt * BITS / 8));
-        uint32_t c = wp[pos >> 5] >> (pos & 31);
-        if ((pos & 31) + BITS > 32) c |= wp[(pos >> 5) + 1] << (32 - (pos & 31));
-        c &= (1u << BITS) - 1;
-        const uint32_t mag = c & ((1u << (BITS - 1)) - 1);
-        const uint32_t sgn_byte = (c >> (BITS - 1)) ? 0xFFu : 0x01u;
-#pragma unroll
-        for (int t = 0; t < NP; ++t)
-          if ((mag & (uint32_t)t) == (uint32_t)t) planes[t] |= sgn_byte << (8 * k);
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t code = (uint32_t)(bits >> (BITS * i)) & ((1u << BITS) - 1);
+        const uint32_t mag = code & ((1u << (BITS - 1)) - 1);
+        const uint32_t v = ((mag & (uint32_t)t) == (uint32_t)t) ? ((code >> (BITS - 1)) ? 0xFFu : 0x01u) : 0u;
+        b[i >> 2] |= v << (8 * (i & 3));
       }
+      out = u32x4{b[0], b[1], b[2], b[3]};
     }
+  } else {
+    const int p0 = (c - NP * Kd / 16) * 16;
+    if (live && p0 < m) {
+      const uint32_t sb = reinterpret_cast<const uint16_t*>(a.qjl_bits + j * (m / 8))[p0 >> 4];
+      uint32_t b[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int t = 0; t < NP; ++t) rec[(t * Kd + d4) / 4] = planes[t];
+      for (int i = 0; i < 16; ++i) b[i >> 2] |= (((sb >> i) & 1u) ? 0x01u : 0xFFu) << (8 * (i & 3));  // bit set: +1
+      out = u32x4{b[0], b[1], b[2], b[3]};
+    }
   }
-  // sign plane: +1 where the bit is set, -1 where clear
-  for (int p4 = 0; p4 < Km; p4 += 4) {
-    uint32_t w = 0u;
+  reinterpret_cast<u32x4*>(a.krec + j * (NP * Kd + Km))[c] = out;
+  if (c == 0) {
+    float n = 0.0f, rho = 0.0f;
     if (live) {
-      const uint8_t* sb = a.qjl_bits + j * (m / 8);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int p = p4 + k;
-        if (p >= m) break;
-        const uint32_t bit = (sb[p >> 3] >> (p & 7)) & 1u;
-        w |= (bit ? 0x01u : 0xFFu) << (8 * k);
-      }
+      if constexpr (NORM_F32)
+        n = static_cast<const float*>(a.norms)[j];
+      else
+        n = __half2float(static_cast<const __half*>(a.norms)[j]);
+      rho = __half2float(__ushort_as_half(a.rnorm[j]));
     }
-    rec[(NP * Kd + p4) / 4] = w;
+    a.kscale[j] = n;
+    a.kscale[a.n_k_pad + j] = n * rho;
   }
-  float n = 0.0f, rho = 0.0f;
-  if (live) {
-    if constexpr (NORM_F32)
-      n = static_cast<const float*>(a.norms)[j];
-    else
-      n = __half2float(static_cast<const __half*>(a.norms)[j]);
-    rho = __half2float(__ushort_as_half(a.rnorm[j]));
-  }
-  a.kscale[2 * j] = n;
-  a.kscale[2 * j + 1] = n * rho;
 }
 
 // ---------------------------------------------------------------------------
-// scores: workgroup = 4 waves x (16*CB keys each), loops over 16-query blocks
+// scores: workgroup = 4 waves x (32*CB keys each), loops over 32-query blocks
 //
-// Keys are the MFMA's A operand and queries its B operand, so each lane's
-// accumulator holds 4 consecutive keys of one query: one 16-byte store per
-// 16-key tile writes them.  The next block's query records are fetched into
-// registers before this block's MFMAs and parked in the other LDS buffer
-// after them, so one barrier per block suffices and the L2 latency of the
-// fetch hides behind the contraction.
+// Keys are the MFMA's A operand (rows) and queries its B operand (columns):
+// lane l's accumulator holds, for query l % 32, the keys 8 g + 4 (l / 32) + i
+// (i = 0..3) of each group g, so one 16-byte store writes four scores.
+// Query records are copied straight into a ring of three LDS buffers
+// (global_load_lds) two blocks ahead.  vmcnt counts stores and copies
+// together, in issue order, so the wait that makes block b + 1 resident
+// skips the two youngest blocks of stores: a wave never waits for stores
+// younger than two blocks, and the write stream stays deep enough to keep
+// HBM busy.
 // ---------------------------------------------------------------------------
 template <int NP, int KD, int KM, int CB>
 __global__ __launch_bounds__(256) void scores_kernel(ScoreArgs a) {
-  constexpr int Kd = 64 * KD, Km = 64 * KM, RQ = 2 * (Kd + Km), RK = NP * Kd + Km;
-  constexpr int QV = kQB * RQ / 16;  // 16-byte vectors per query block
-  constexpr int PER = (QV + 255) / 256;
-  __shared__ __attribute__((aligned(16))) int8_t qblk[2][kQB * RQ];
-  __shared__ float qs[2][kQB * 2];
+  constexpr int Kd = 32 * KD, Km = 32 * KM, RQ = 2 * (Kd + Km), RK = NP * Kd + Km;
+  constexpr int KIB = kQB * RQ / 1024;  // 1 KiB copies per block
+  static_assert(KIB % 4 == 0, "every wave copies the same number of 1 KiB pieces");
+  constexpr int KEYS = 128 * CB;        // keys per workgroup
+  __shared__ __attribute__((aligned(1024))) int8_t qblk[3][kQB * RQ];
+  __shared__ __attribute__((aligned(256))) float qs[3][kQB * 2];
+  __shared__ __attribute__((aligned(16))) float ks_n[KEYS], ks_nr[KEYS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int col_l = lane & 15, slot = lane >> 4;
-  const int64_t key0 = (int64_t)blockIdx.x * (64 * CB) + wave * (16 * CB);
+  const int col = lane & 31, half = lane >> 5;
+  const int64_t wg_key0 = (int64_t)blockIdx.x * KEYS;
+  const int64_t key0 = wg_key0 + wave * (32 * CB);
 
-  // this wave's key-side operands (row col_l of each 16-key tile), kept in registers
+  // this wave's key-side operands (row col of each 32-key tile), kept in registers
   v4i bT[CB][NP][KD], bS[CB][KM];
-  float nk[CB][4], nrk[CB][4];  // scales of the 4 keys 16 cb + 4 slot + i whose scores this lane writes
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
-    const int64_t key = key0 + 16 * cb + col_l;
-    const int8_t* rec = a.krec + key * RK;
+    const int8_t* rec = a.krec + (key0 + 32 * cb + col) * RK + 16 * half;
 #pragma unroll
     for (int t = 0; t < NP; ++t)
 #pragma unroll
-      for (int ks = 0; ks < KD; ++ks) bT[cb][t][ks] = *reinterpret_cast<const v4i*>(rec + t * Kd + 64 * ks + 16 * slot);
+      for (int ks = 0; ks < KD; ++ks) bT[cb][t][ks] = *reinterpret_cast<const v4i*>(rec + t * Kd + 32 * ks);
 #pragma unroll
-    for (int ks = 0; ks < KM; ++ks) bS[cb][ks] = *reinterpret_cast<const v4i*>(rec + NP * Kd + 64 * ks + 16 * slot);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t kk = key0 + 16 * cb + 4 * slot + i;
-      nk[cb][i] = a.kscale[2 * kk];
-      nrk[cb][i] = a.kscale[2 * kk + 1];
-    }
+    for (int ks = 0; ks < KM; ++ks) bS[cb][ks] = *reinterpret_cast<const v4i*>(rec + NP * Kd + 32 * ks);
+  }
+  for (int e = tid; e < KEYS; e += 256) {
+    ks_n[e] = a.kscale[wg_key0 + e];
+    ks_nr[e] = a.kscale[a.n_k_pad + wg_key0 + e];
   }
   float w[NP];
 #pragma unroll
@@ -244,42 +263,32 @@ __global__ __launch_bounds__(256) void scores_kernel(ScoreArgs a) {
 
   const int64_t q_begin = (int64_t)blockIdx.y * kQChunk;
   const int64_t q_end = q_begin + kQChunk < a.n_q_pad ? q_begin + kQChunk : a.n_q_pad;
-  const v4i* qrec_v = reinterpret_cast<const v4i*>(a.qrec);
-  v4i pre[PER];
-  float pqs = 0.0f;
-  auto fetch = [&](int64_t r0) {
+  // copy the records (KIB pieces of 1 KiB, KIB / 4 per wave) and scales (wave 0) of block r0 into buffer buf
+  auto fetch = [&](int64_t r0, int buf) {
+    const char* src = reinterpret_cast<const char*>(a.qrec) + r0 * RQ;
 #pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int e = tid + 256 * p;
-      if (e < QV) pre[p] = qrec_v[r0 * (RQ / 16) + e];
-    }
-    if (tid < kQB * 2) pqs = a.qscale[r0 * 2 + tid];
+    for (int k = wave; k < KIB; k += 4) lds_copy<16>(src + 1024 * k + 16 * lane, qblk[buf] + 1024 * k);
+    if (wave == 0) lds_copy<4>(a.qscale + r0 * 2 + lane, qs[buf]);
   };
-  auto park = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int e = tid + 256 * p;
-      if (e < QV) reinterpret_cast<v4i*>(qblk[buf])[e] = pre[p];
-    }
-    if (tid < kQB * 2) qs[buf][tid] = pqs;
-  };
-  fetch(q_begin);
-  park(0);
-  __syncthreads();
+  // blocks b and b + 1 are resident when block b starts; block b + 2 is copied during it
+  fetch(q_begin, 0);
+  if (q_begin + kQB < q_end) fetch(q_begin + kQB, 1);
+  wait_vm<0>();
+  __syncthreads();  // also publishes the key scales
 
   int cur = 0;
-  for (int64_t r0 = q_begin; r0 < q_end; r0 += kQB, cur ^= 1) {
-    const bool more = r0 + kQB < q_end;
-    if (more) fetch(r0 + kQB);
+  for (int64_t r0 = q_begin; r0 < q_end; r0 += kQB, cur = cur == 2 ? 0 : cur + 1) {
+    const bool ahead = r0 + 2 * kQB < q_end;
+    if (ahead) fetch(r0 + 2 * kQB, cur == 0 ? 2 : cur - 1);
 
-    v4i accT[CB][NP], accS[CB];
+    v16i accT[CB][NP], accS[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
-      for (int t = 0; t < NP; ++t) accT[cb][t] = v4i{0, 0, 0, 0};
-      accS[cb] = v4i{0, 0, 0, 0};
+      for (int t = 0; t < NP; ++t) accT[cb][t] = v16i{};
+      accS[cb] = v16i{};
     }
-    const int8_t* qrow = qblk[cur] + col_l * RQ + 16 * slot;
+    const int8_t* qfrag = qblk[cur] + 16 * lane;
 #pragma unroll
     for (int limb = 0; limb < 2; ++limb) {
       if (limb == 1) {
@@ -292,55 +301,78 @@ __global__ __launch_bounds__(256) void scores_kernel(ScoreArgs a) {
       }
 #pragma unroll
       for (int ks = 0; ks < KD; ++ks) {
-        const v4i bq = *reinterpret_cast<const v4i*>(qrow + limb * Kd + 64 * ks);
+        const v4i bq = *reinterpret_cast<const v4i*>(qfrag + 1024 * (limb * KD + ks));
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
           for (int t = 0; t < NP; ++t)
-            accT[cb][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bT[cb][t][ks], bq, accT[cb][t], 0, 0, 0);
+            accT[cb][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bT[cb][t][ks], bq, accT[cb][t], 0, 0, 0);
       }
 #pragma unroll
       for (int ks = 0; ks < KM; ++ks) {
-        const v4i bp = *reinterpret_cast<const v4i*>(qrow + 2 * Kd + limb * Km + 64 * ks);
+        const v4i bp = *reinterpret_cast<const v4i*>(qfrag + 1024 * (2 * KD + limb * KM + ks));
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) accS[cb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bS[cb][ks], bp, accS[cb], 0, 0, 0);
+        for (int cb = 0; cb < CB; ++cb) accS[cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bS[cb][ks], bp, accS[cb], 0, 0, 0);
       }
     }
-    if (more) park(cur ^ 1);
 
-    // epilogue: lane holds keys 16 cb + 4 slot + i of query r0 + col_l
-    const float alpha = qs[cur][2 * col_l], beta = qs[cur][2 * col_l + 1];
-    v4f val[CB];
+    // epilogue: query r0 + col, keys key0 + 32 cb + 8 g + 4 half + i
+    const float alpha = qs[cur][2 * col], beta = qs[cur][2 * col + 1];
+    const int64_t row = r0 + col;
+    float* out = a.scores + row * a.ld_s + key0 + 4 * half;
+    const bool fast = vec && key0 + 32 * CB <= a.n_k && r0 + kQB <= a.n_q;  // wave-uniform
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
+    for (int cb = 0; cb < CB; ++cb) {
+      v4f val[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float sum = 0.0f;
+      for (int g = 0; g < 4; ++g) {
+        const int kl = wave * (32 * CB) + 32 * cb + 8 * g + 4 * half;  // key index within the workgroup
+        const v4f kn = *reinterpret_cast<const v4f*>(ks_n + kl);
+        const v4f knr = *reinterpret_cast<const v4f*>(ks_nr + kl);
 #pragma unroll
-        for (int t = 0; t < NP; ++t) sum = __builtin_fmaf(w[t], (float)accT[cb][t][i], sum);
-        val[cb][i] = nk[cb][i] * (alpha * sum) + nrk[cb][i] * (beta * (float)accS[cb][i]);
+        for (int i = 0; i < 4; ++i) {
+          float sum = 0.0f;
+#pragma unroll
+          for (int t = 0; t < NP; ++t) sum = __builtin_fmaf(w[t], (float)accT[cb][t][4 * g + i], sum);
+          val[g][i] = (kn[i] * alpha) * sum + (knr[i] * beta) * (float)accS[cb][4 * g + i];
+        }
       }
-    const int64_t row = r0 + col_l;
-    float* out = a.scores + row * a.ld_s + key0 + 4 * slot;
-    if (vec && key0 + 16 * CB <= a.n_k && r0 + kQB <= a.n_q) {  // whole tile inside the matrix (wave-uniform)
-      // plain (cached) stores: L2 merges the 64-byte row pieces of the 16 queries into whole lines
+      if (fast) {
+        // plain (cached) stores: L2 merges the 16-byte row pieces into whole lines
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) *reinterpret_cast<v4f*>(out + 16 * cb) = val[cb];
-    } else if (row < a.n_q) {
+        for (int g = 0; g < 4; ++g) *reinterpret_cast<v4f*>(out + 32 * cb + 8 * g) = val[g];
+      } else if (row < a.n_q) {
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
+        for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (key0 + 16 * cb + 4 * slot + i < a.n_k) out[16 * cb + i] = val[cb][i];
+          for (int i = 0; i < 4; ++i)
+            if (key0 + 32 * cb + 8 * g + 4 * half + i < a.n_k) out[32 * cb + 8 * g + i] = val[g][i];
+      }
     }
-    __syncthreads();
+    if (fast) {
+      // the copy of block b + 1 (issued one block ago) must land; younger than it are the previous block's
+      // 4 CB stores, this block's copies and this block's 4 CB stores, none of which are waited for
+      if (!ahead)
+        wait_vm<8 * CB>();
+      else if (wave == 0)
+        wait_vm<8 * CB + KIB / 4 + 1>();
+      else
+        wait_vm<8 * CB + KIB / 4>();
+    } else {
+      wait_vm<0>();  // also completes the copy of block b + 1, whatever follows
+    }
+    lds_barrier();
   }
+  wait_vm<0>();
 }
 
+#ifndef TQ_SCORES_CB2
+#define TQ_SCORES_CB2 2
+#endif
 template <int NP, int KD, int KM>
 hipError_t launch_scores_t(const ScoreArgs& a, hipStream_t s) {
-  constexpr int CB = NP <= 2 ? 4 : 2;
-  dim3 grid((unsigned)(a.n_k_pad / (64 * CB)), (unsigned)((a.n_q_pad + kQChunk - 1) / kQChunk));
+  constexpr int CB = NP <= 2 ? TQ_SCORES_CB2 : 1;
+  dim3 grid((unsigned)(a.n_k_pad / (128 * CB)), (unsigned)((a.n_q_pad + kQChunk - 1) / kQChunk));
   hipLaunchKernelGGL((scores_kernel<NP, KD, KM, CB>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
@@ -348,40 +380,40 @@ hipError_t launch_scores_t(const ScoreArgs& a, hipStream_t s) {
 template <int NP>
 hipError_t launch_scores_np(const ScoreArgs& a, hipStream_t s) {
   const int kd = a.kd / 64, km = a.km / 64;
-  if (kd == 1 && km == 1) return launch_scores_t<NP, 1, 1>(a, s);
-  if (kd == 1 && km == 2) return launch_scores_t<NP, 1, 2>(a, s);
-  if (kd == 2 && km == 1) return launch_scores_t<NP, 2, 1>(a, s);
-  return launch_scores_t<NP, 2, 2>(a, s);
+  if (kd == 1 && km == 1) return launch_scores_t<NP, 2, 2>(a, s);
+  if (kd == 1 && km == 2) return launch_scores_t<NP, 2, 4>(a, s);
+  if (kd == 2 && km == 1) return launch_scores_t<NP, 4, 2>(a, s);
+  return launch_scores_t<NP, 4, 4>(a, s);
+}
+
+template <int BITS>
+void launch_prep_keys(const tq_config& cfg, const ScoreArgs& a, hipStream_t s) {
+  constexpr int NP = 1 << (BITS - 1);
+  const int64_t lanes = a.n_k_pad * ((NP * a.kd + a.km) / 16);
+  dim3 grid((unsigned)((lanes + 255) / 256));
+  if (cfg.norm_dtype == TQ_F32)
+    hipLaunchKernelGGL((prep_keys<BITS, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((prep_keys<BITS, false>), grid, dim3(256), 0, s, a);
 }
 
 }  // namespace
 
 int64_t scores_key_tile(int bits) { return bits <= 2 ? 256 : 128; }
+int64_t scores_query_block() { return kQB; }
 
 hipError_t launch_qjl_scores(const tq_config& cfg, const ScoreArgs& a, hipStream_t s) {
-  const size_t lds = (size_t)kQB * (a.dt + a.m) * sizeof(float);
-  dim3 gq((unsigned)(a.n_q_pad / kQB));
+  dim3 gq((unsigned)(a.n_q_pad / 16));
   if (a.q_f32)
-    hipLaunchKernelGGL((prep_queries<true>), gq, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((prep_queries<true>), gq, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((prep_queries<false>), gq, dim3(256), lds, s, a);
+    hipLaunchKernelGGL((prep_queries<false>), gq, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 gk((unsigned)((a.n_k_pad + 255) / 256));
-  const bool n32 = cfg.norm_dtype == TQ_F32;
   switch (cfg.bits) {
-    case 1:
-      if (n32) hipLaunchKernelGGL((prep_keys<1, true>), gk, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((prep_keys<1, false>), gk, dim3(256), 0, s, a);
-      break;
-    case 2:
-      if (n32) hipLaunchKernelGGL((prep_keys<2, true>), gk, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((prep_keys<2, false>), gk, dim3(256), 0, s, a);
-      break;
-    default:
-      if (n32) hipLaunchKernelGGL((prep_keys<3, true>), gk, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((prep_keys<3, false>), gk, dim3(256), 0, s, a);
-      break;
+    case 1: launch_prep_keys<1>(cfg, a, s); break;
+    case 2: launch_prep_keys<2>(cfg, a, s); break;
+    default: launch_prep_keys<3>(cfg, a, s); break;
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
