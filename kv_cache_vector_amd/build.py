@@ -26,10 +26,10 @@ ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-function"]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-munsafe-fp-atomics", "-ffp-contract=fast"]
-# Per-file code generation options.  The codec and scores kernels feed MFMA
-# results straight into VALU work; keeping them in arch VGPRs instead of AGPRs
-# saves the v_accvgpr moves in between.
-PER_FILE = {name: ["-mllvm", "-amdgpu-mfma-vgpr-form"] for name in ("tq_codec.hip", "tq_scores.hip")}
+# Per-file code generation options.  The codec, scores and attention kernels
+# feed MFMA results straight into VALU work; keeping them in arch VGPRs instead
+# of AGPRs saves the v_accvgpr moves in between.
+PER_FILE = {name: ["-mllvm", "-amdgpu-mfma-vgpr-form"] for name in ("tq_codec.hip", "tq_scores.hip", "tq_attn.hip")}
 
 
 def _compile(src: str) -> str:
