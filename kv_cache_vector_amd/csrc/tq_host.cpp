@@ -368,7 +368,7 @@ ScoreLayout score_layout(const tq_config& cfg, int64_t n_q, int64_t n_k) {
   const int64_t qb = tq::scores_query_block();
   L.n_q_pad = (n_q + qb - 1) / qb * qb;
   L.n_k_pad = (n_k + tile - 1) / tile * tile;
-  L.rq = 2 * (kd + km);
+  L.rq = 2 * (L.planes * kd + km);
   L.rk = L.planes * kd + km;
   L.off_qrec = 0;
   L.off_qscale = round256(L.off_qrec + (size_t)(L.n_q_pad * L.rq));

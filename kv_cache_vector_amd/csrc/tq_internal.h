@@ -84,8 +84,8 @@ struct ScoreArgs {
   int64_t n_k, n_k_pad;      // keys, padded to the scores key tile
   float* scores;
   int64_t ld_s;
-  int8_t* qrec;              // [n_q_pad / 32] blocks of 32 queries x 2*(kd+km) int8 limbs (qhat hi, qhat lo,
-                             // p hi, p lo), each block laid out as 1 KiB MFMA operand fragments
+  int8_t* qrec;              // [n_q_pad / 32] blocks of 32 queries x 2*(planes*kd+km) int8 limbs (per plane
+                             // w_t qhat hi, lo; then p hi, lo), each block laid out as 1 KiB MFMA fragments
   float* qscale;             // [n_q_pad][2]: fixed-point scale of qhat / sqrt(dt), of p * sqrt(pi/2)/m
   int8_t* krec;              // [n_k_pad][planes*kd + km]: ternary planes, then the +-1 sign plane
   float* kscale;             // [2][n_k_pad]: n_j, then n_j * rho_j

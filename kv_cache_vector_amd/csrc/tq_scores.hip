@@ -10,9 +10,11 @@
 //     T_t[d] = sgn_d * [mag_d contains the bits of t] in {0, +-1} and weights
 //     w_t from the Moebius inversion of the positive centroids; the sign
 //     sketch is a +-1 plane.
-//   * query side, fixed point: qhat = H D q and p = S q = S~ qhat (fp32 MFMA)
-//     are scaled per query to 16-bit integers and split into two int8 limbs,
-//     hi * 256 + lo; the accumulator is shifted by 8 between the limb passes.
+//   * query side, fixed point: the plane-weighted copies w_t qhat of qhat =
+//     H D q, and p = S q = S~ qhat (fp32 MFMA), are scaled per query to
+//     16-bit integers and split into two int8 limbs, hi * 256 + lo; since the
+//     weights ride on the query, all planes add into one integer accumulator,
+//     which is shifted by 8 between the limb passes.
 // <q, D H c> = <H D q, c> (H, D symmetric involutions), so keys are never
 // rotated back.  The rounding error is that of 16-bit fixed point for qhat
 // and p (about 1e-5 of ||q|| per element), far inside the 1e-4 tolerance.
@@ -35,7 +37,10 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kQB = 32;         // queries per block (the MFMA's N)
-constexpr int kQChunk = 512;    // queries per scores workgroup
+#ifndef TQ_QCHUNK
+#define TQ_QCHUNK 512
+#endif
+constexpr int kQChunk = TQ_QCHUNK;  // queries per scores workgroup
 constexpr float kFixed = 32000.0f;
 
 // Byte offset of element idx (of a Kd- or Km-long int8 vector) of query r inside its block's
@@ -52,11 +57,11 @@ __device__ __forceinline__ int frag_offset(int f0, int r, int idx) {
 // of the query, the maxima are 16-lane reductions, and each thread writes its
 // 8 limbs as 8-byte pieces of the block's operand fragments.  dt, m <= 128.
 // ---------------------------------------------------------------------------
-template <bool Q_F32>
+template <bool Q_F32, int NP>
 __global__ __launch_bounds__(256) void prep_queries(ScoreArgs a) {
   __shared__ float qhat[16][128 + 4];
   __shared__ float pbuf[16][128 + 4];
-  const int dt = a.dt, m = a.m, Kd = a.kd, Km = a.km, RQ = 2 * (Kd + Km);
+  const int dt = a.dt, m = a.m, Kd = a.kd, Km = a.km, RQ = 2 * (NP * Kd + Km);
   const int64_t row0 = (int64_t)blockIdx.x * 16;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = tid >> 4, c8 = (tid & 15) * 8;  // query r of the 16, coordinates c8 .. c8 + 7
@@ -144,10 +149,23 @@ __global__ __launch_bounds__(256) void prep_queries(ScoreArgs a) {
     *reinterpret_cast<uint2*>(blk + frag_offset(f0, rb, idx)) = make_uint2(hw[0], hw[1]);
     *reinterpret_cast<uint2*>(blk + frag_offset(f0 + nks, rb, idx)) = make_uint2(lw[0], lw[1]);
   };
-  if (c8 < Kd) put(v, ma, c8, 0, Kd / 32);
-  if (c8 < Km) put(pv, mp, c8, 2 * (Kd / 32), Km / 32);
+  // plane t carries w_t qhat; one fixed-point scale over all planes lets them share an accumulator
+  float wmax = 0.0f;
+#pragma unroll
+  for (int t = 0; t < NP; ++t) wmax = fmaxf(wmax, fabsf(a.plane_w[t]));
+  const float mq = ma * wmax;
+  if (c8 < Kd) {
+#pragma unroll
+    for (int t = 0; t < NP; ++t) {
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = v[i] * a.plane_w[t];
+      put(x, mq, c8, 2 * t * (Kd / 32), Kd / 32);
+    }
+  }
+  if (c8 < Km) put(pv, mp, c8, 2 * NP * (Kd / 32), Km / 32);
   if ((tid & 15) == 0) {
-    a.qscale[row * 2] = (ma > 0.0f ? ma / kFixed : 0.0f) * inv_sqrt_dt;
+    a.qscale[row * 2] = (mq > 0.0f ? mq / kFixed : 0.0f) * inv_sqrt_dt;
     a.qscale[row * 2 + 1] = (mp > 0.0f ? mp / kFixed : 0.0f) * a.qjl_const;
   }
 }
@@ -225,15 +243,30 @@ __global__ __launch_bounds__(256) void prep_keys(ScoreArgs a) {
 // younger than two blocks, and the write stream stays deep enough to keep
 // HBM busy.
 // ---------------------------------------------------------------------------
+// Dynamic LDS of one scores workgroup: a ring of three query blocks, their scales, the key scales.
+template <int NP, int KD, int KM, int CB>
+struct ScoresLds {
+  static constexpr int RQ = 2 * (NP * 32 * KD + 32 * KM);  // bytes per query record
+  static constexpr int KIB = kQB * RQ / 1024;               // 1 KiB copies per block
+  static_assert(KIB % 4 == 0, "every wave copies the same number of 1 KiB pieces");
+  static constexpr int KEYS = 128 * CB;                     // keys per workgroup
+  static constexpr int QS = 3 * kQB * RQ;
+  static constexpr int KSN = QS + 3 * kQB * 2 * 4;
+  static constexpr int TOTAL = KSN + 2 * KEYS * 4;
+  static_assert(TOTAL <= 160 * 1024, "fits the LDS of one compute unit");
+};
+
 template <int NP, int KD, int KM, int CB>
 __global__ __launch_bounds__(256) void scores_kernel(ScoreArgs a) {
-  constexpr int Kd = 32 * KD, Km = 32 * KM, RQ = 2 * (Kd + Km), RK = NP * Kd + Km;
-  constexpr int KIB = kQB * RQ / 1024;  // 1 KiB copies per block
-  static_assert(KIB % 4 == 0, "every wave copies the same number of 1 KiB pieces");
-  constexpr int KEYS = 128 * CB;        // keys per workgroup
-  __shared__ __attribute__((aligned(1024))) int8_t qblk[3][kQB * RQ];
-  __shared__ __attribute__((aligned(256))) float qs[3][kQB * 2];
-  __shared__ __attribute__((aligned(16))) float ks_n[KEYS], ks_nr[KEYS];
+  using LY = ScoresLds<NP, KD, KM, CB>;
+  constexpr int Kd = 32 * KD, Km = 32 * KM, RQ = LY::RQ, RK = NP * Kd + Km;
+  constexpr int KIB = LY::KIB;
+  constexpr int KEYS = LY::KEYS;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  int8_t (*qblk)[kQB * RQ] = reinterpret_cast<int8_t (*)[kQB * RQ]>(smem);
+  float (*qs)[kQB * 2] = reinterpret_cast<float (*)[kQB * 2]>(smem + LY::QS);
+  float* ks_n = reinterpret_cast<float*>(smem + LY::KSN);
+  float* ks_nr = ks_n + KEYS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
   const int64_t wg_key0 = (int64_t)blockIdx.x * KEYS;
@@ -255,9 +288,6 @@ __global__ __launch_bounds__(256) void scores_kernel(ScoreArgs a) {
     ks_n[e] = a.kscale[wg_key0 + e];
     ks_nr[e] = a.kscale[a.n_k_pad + wg_key0 + e];
   }
-  float w[NP];
-#pragma unroll
-  for (int t = 0; t < NP; ++t) w[t] = a.plane_w[t];
   // 16-byte stores need 16-byte aligned rows
   const bool vec = ((a.ld_s & 3) == 0) && ((reinterpret_cast<uintptr_t>(a.scores) & 15) == 0);
 
@@ -281,36 +311,32 @@ __global__ __launch_bounds__(256) void scores_kernel(ScoreArgs a) {
     const bool ahead = r0 + 2 * kQB < q_end;
     if (ahead) fetch(r0 + 2 * kQB, cur == 0 ? 2 : cur - 1);
 
-    v16i accT[CB][NP], accS[CB];
+    v16i accT[CB], accS[CB];
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-#pragma unroll
-      for (int t = 0; t < NP; ++t) accT[cb][t] = v16i{};
-      accS[cb] = v16i{};
-    }
+    for (int cb = 0; cb < CB; ++cb) accT[cb] = accS[cb] = v16i{};
     const int8_t* qfrag = qblk[cur] + 16 * lane;
 #pragma unroll
     for (int limb = 0; limb < 2; ++limb) {
       if (limb == 1) {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
-#pragma unroll
-          for (int t = 0; t < NP; ++t) accT[cb][t] <<= 8;
+          accT[cb] <<= 8;
           accS[cb] <<= 8;
         }
       }
 #pragma unroll
       for (int ks = 0; ks < KD; ++ks) {
-        const v4i bq = *reinterpret_cast<const v4i*>(qfrag + 1024 * (limb * KD + ks));
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
+        for (int t = 0; t < NP; ++t) {
+          const v4i bq = *reinterpret_cast<const v4i*>(qfrag + 1024 * ((2 * t + limb) * KD + ks));
 #pragma unroll
-          for (int t = 0; t < NP; ++t)
-            accT[cb][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bT[cb][t][ks], bq, accT[cb][t], 0, 0, 0);
+          for (int cb = 0; cb < CB; ++cb)
+            accT[cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bT[cb][t][ks], bq, accT[cb], 0, 0, 0);
+        }
       }
 #pragma unroll
       for (int ks = 0; ks < KM; ++ks) {
-        const v4i bp = *reinterpret_cast<const v4i*>(qfrag + 1024 * (2 * KD + limb * KM + ks));
+        const v4i bp = *reinterpret_cast<const v4i*>(qfrag + 1024 * (2 * NP * KD + limb * KM + ks));
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) accS[cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bS[cb][ks], bp, accS[cb], 0, 0, 0);
       }
@@ -330,12 +356,8 @@ __global__ __launch_bounds__(256) void scores_kernel(ScoreArgs a) {
         const v4f kn = *reinterpret_cast<const v4f*>(ks_n + kl);
         const v4f knr = *reinterpret_cast<const v4f*>(ks_nr + kl);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float sum = 0.0f;
-#pragma unroll
-          for (int t = 0; t < NP; ++t) sum = __builtin_fmaf(w[t], (float)accT[cb][t][4 * g + i], sum);
-          val[g][i] = (kn[i] * alpha) * sum + (knr[i] * beta) * (float)accS[cb][4 * g + i];
-        }
+        for (int i = 0; i < 4; ++i)
+          val[g][i] = (kn[i] * alpha) * (float)accT[cb][4 * g + i] + (knr[i] * beta) * (float)accS[cb][4 * g + i];
       }
       if (fast) {
         // plain (cached) stores: L2 merges the 16-byte row pieces into whole lines
@@ -372,8 +394,16 @@ __global__ __launch_bounds__(256) void scores_kernel(ScoreArgs a) {
 template <int NP, int KD, int KM>
 hipError_t launch_scores_t(const ScoreArgs& a, hipStream_t s) {
   constexpr int CB = NP <= 2 ? TQ_SCORES_CB2 : 1;
+  constexpr int lds = ScoresLds<NP, KD, KM, CB>::TOTAL;
+  static bool ready = false;  // more than the default 64 KiB of dynamic LDS for the larger records
+  if (!ready) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scores_kernel<NP, KD, KM, CB>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    ready = true;
+  }
   dim3 grid((unsigned)(a.n_k_pad / (128 * CB)), (unsigned)((a.n_q_pad + kQChunk - 1) / kQChunk));
-  hipLaunchKernelGGL((scores_kernel<NP, KD, KM, CB>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((scores_kernel<NP, KD, KM, CB>), grid, dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
@@ -404,10 +434,16 @@ int64_t scores_query_block() { return kQB; }
 
 hipError_t launch_qjl_scores(const tq_config& cfg, const ScoreArgs& a, hipStream_t s) {
   dim3 gq((unsigned)(a.n_q_pad / 16));
-  if (a.q_f32)
-    hipLaunchKernelGGL((prep_queries<true>), gq, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((prep_queries<false>), gq, dim3(256), 0, s, a);
+  const int np = 1 << (cfg.bits - 1);
+  if (a.q_f32) {
+    if (np == 1) hipLaunchKernelGGL((prep_queries<true, 1>), gq, dim3(256), 0, s, a);
+    if (np == 2) hipLaunchKernelGGL((prep_queries<true, 2>), gq, dim3(256), 0, s, a);
+    if (np == 4) hipLaunchKernelGGL((prep_queries<true, 4>), gq, dim3(256), 0, s, a);
+  } else {
+    if (np == 1) hipLaunchKernelGGL((prep_queries<false, 1>), gq, dim3(256), 0, s, a);
+    if (np == 2) hipLaunchKernelGGL((prep_queries<false, 2>), gq, dim3(256), 0, s, a);
+    if (np == 4) hipLaunchKernelGGL((prep_queries<false, 4>), gq, dim3(256), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   switch (cfg.bits) {
