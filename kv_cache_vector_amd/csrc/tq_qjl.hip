@@ -132,7 +132,7 @@ __global__ __launch_bounds__(kBlock) void qjl_encode_kernel(QjlEncodeArgs a, con
 }
 
 // Encode for head_dim = 128 in fp32, with the projection z = S~ e on fp32 MFMA
-// (v_mfma_f32_16x16x4_f32).  A wave encodes 16 keys: lane l holds the 32
+// (v_mfma_f32_16x16x4_f32).  Eight waves share one LDS copy of S~; a wave encodes 16 keys: lane l holds the 32
 // coordinates 32 (l / 16) .. + 31 of key l % 16, so the A operand of k-step s
 // is the lane's coordinate s and each lane packs one whole 32-group.  S~ sits
 // in LDS as B-operand fragments, four k-steps per 16-byte read.  The sign bit
@@ -143,14 +143,17 @@ __global__ __launch_bounds__(kBlock) void qjl_encode_kernel(QjlEncodeArgs a, con
 // the |z| < 1e-6 rho band that the parity contract allows.
 typedef float v4f __attribute__((ext_vector_type(4)));
 
+constexpr int kEncBlock = 512;  // 8 waves share one copy of S~ in LDS
+
 template <int BITS, bool IN_F32, bool NORM_F32>
-__global__ __launch_bounds__(kBlock) void qjl_encode128_kernel(QjlEncodeArgs a, const float* __restrict__ s_rot32) {
+__global__ __launch_bounds__(kEncBlock) void qjl_encode128_kernel(QjlEncodeArgs a, const float* __restrict__ s_rot32) {
+  constexpr int W = kEncBlock / 64;
   extern __shared__ v4f sfrag[];                  // [m/16][8][64]: S~[16 pt + ln%16][32 (ln/16) + 4 s4 + i]
-  __shared__ uint64_t ballots[kBlock / 64][32];   // per wave: [pt * 4 + r]
+  __shared__ uint64_t ballots[W][32];             // per wave: [pt * 4 + r]
   __shared__ float lvl_s[16];
   const int m = a.m, npt = m / 16, words = m / 32;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = tid; e < npt * 512; e += kBlock) {
+  for (int e = tid; e < npt * 512; e += kEncBlock) {
     const int pt = e >> 9, s4 = (e >> 6) & 7, ln = e & 63;
     sfrag[e] = *reinterpret_cast<const v4f*>(s_rot32 + (16 * pt + (ln & 15)) * 128 + 32 * (ln >> 4) + 4 * s4);
   }
@@ -163,7 +166,7 @@ __global__ __launch_bounds__(kBlock) void qjl_encode128_kernel(QjlEncodeArgs a, 
 #pragma unroll
   for (int k = 0; k < 7; ++k) thr[k] = (float)a.thr[k];
   const int64_t n_tiles = (a.n_units + 15) / 16;
-  for (int64_t tile = (int64_t)blockIdx.x * 4 + wave; tile < n_tiles; tile += (int64_t)gridDim.x * 4) {
+  for (int64_t tile = (int64_t)blockIdx.x * W + wave; tile < n_tiles; tile += (int64_t)gridDim.x * W) {
     const int64_t key = tile * 16 + kl;
     const bool valid = key < a.n_units;
     float v[32];
@@ -404,8 +407,8 @@ hipError_t qjl_encode128(const tq_config& cfg, const QjlEncodeArgs& a, hipStream
   const float* s32 = reinterpret_cast<const float*>(a.s_rot + (size_t)a.m * 128);
   const size_t lds = (size_t)a.m * 128 * sizeof(float);
   const int64_t tiles = (a.n_units + 15) / 16;
-  int64_t wgs = (tiles + 3) / 4, cap = 2 * (int64_t)cu_count();
-  dim3 grid((unsigned)(wgs < cap ? wgs : cap)), block(kBlock);
+  int64_t wgs = (tiles + kEncBlock / 64 - 1) / (kEncBlock / 64), cap = 2 * (int64_t)cu_count();
+  dim3 grid((unsigned)(wgs < cap ? wgs : cap)), block(kEncBlock);
   const bool in32 = cfg.x_dtype == TQ_F32, n32 = cfg.norm_dtype == TQ_F32;
   if (!in32 && !n32) hipLaunchKernelGGL((qjl_encode128_kernel<BITS, false, false>), grid, block, lds, s, a, s32);
   if (!in32 && n32) hipLaunchKernelGGL((qjl_encode128_kernel<BITS, false, true>), grid, block, lds, s, a, s32);

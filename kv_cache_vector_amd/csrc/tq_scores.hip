@@ -110,15 +110,29 @@ __global__ __launch_bounds__(256) void prep_queries(ScoreArgs a) {
   }
   __syncthreads();
 
-  // p = S~ qhat on fp32 MFMA: the 16 queries x 16 projections of tile ct, K = 4 per step
+  // p = S~ qhat on fp32 MFMA: the 16 queries x 16 projections of tile ct.  K step s of lane group
+  // q = lane / 16 takes coordinate q dt/4 + s, so each lane's S~ operands are dt/4 contiguous floats
+  // (loaded up front as 16-byte pieces) and its qhat operands a contiguous LDS run.
+  const int q4 = lane >> 4, kq = dt / 4;
   for (int ct = wave; ct < m / 16; ct += 4) {
-    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    const float* srow = a.s_rot32 + (int64_t)(16 * ct + (lane & 15)) * dt;
-    for (int k0 = 0; k0 < dt; k0 += 4)
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qhat[lane & 15][k0 + (lane >> 4)], srow[k0 + (lane >> 4)], acc, 0, 0,
-                                                 0);
+    const float4* srow = reinterpret_cast<const float4*>(a.s_rot32 + (int64_t)(16 * ct + (lane & 15)) * dt + kq * q4);
+    float4 sv[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pbuf[4 * (lane >> 4) + i][16 * ct + (lane & 15)] = acc[i];
+    for (int i = 0; i < 8; ++i)
+      if (4 * i < kq) sv[i] = srow[i];
+    const float* qrow = &qhat[lane & 15][kq * q4];
+    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (4 * i < kq) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qrow[4 * i], sv[i].x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qrow[4 * i + 1], sv[i].y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qrow[4 * i + 2], sv[i].z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qrow[4 * i + 3], sv[i].w, acc, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pbuf[4 * q4 + i][16 * ct + (lane & 15)] = acc[i];
   }
   __syncthreads();
   float pv[8], mp = 0.0f;
@@ -174,14 +188,17 @@ __global__ __launch_bounds__(256) void prep_queries(ScoreArgs a) {
 // key preparation: one lane per 16-byte piece of a key's record (NP ternary
 // planes of Kd bytes, then Km bytes of the +-1 sign plane)
 // ---------------------------------------------------------------------------
-template <int BITS, bool NORM_F32>
+template <int BITS, bool NORM_F32, int KD, int KM>
 __global__ __launch_bounds__(256) void prep_keys(ScoreArgs a) {
   constexpr int NP = 1 << (BITS - 1);
-  const int dt = a.dt, m = a.m, Kd = a.kd, Km = a.km;
-  const int pieces = (NP * Kd + Km) / 16;
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t j = gid / pieces;
-  const int c = (int)(gid - j * pieces);
+  constexpr int Kd = 64 * KD, Km = 64 * KM;
+  constexpr int pieces = (NP * Kd + Km) / 16;
+  const int dt = a.dt, m = a.m;
+  // keys of this workgroup: 256 / pieces (rounded down) whole records per 256 lanes
+  constexpr int KPW = 256 / pieces;
+  const int c = threadIdx.x % pieces, kl = threadIdx.x / pieces;
+  if (kl >= KPW) return;
+  const int64_t j = (int64_t)blockIdx.x * KPW + kl;
   if (j >= a.n_k_pad) return;
   const bool live = j < a.n_k;
   u32x4 out = {0u, 0u, 0u, 0u};
@@ -416,15 +433,24 @@ hipError_t launch_scores_np(const ScoreArgs& a, hipStream_t s) {
   return launch_scores_t<NP, 4, 4>(a, s);
 }
 
+template <int BITS, int KD, int KM>
+void launch_prep_keys_t(const tq_config& cfg, const ScoreArgs& a, hipStream_t s) {
+  constexpr int NP = 1 << (BITS - 1);
+  constexpr int KPW = 256 / ((NP * 64 * KD + 64 * KM) / 16);
+  dim3 grid((unsigned)((a.n_k_pad + KPW - 1) / KPW));
+  if (cfg.norm_dtype == TQ_F32)
+    hipLaunchKernelGGL((prep_keys<BITS, true, KD, KM>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((prep_keys<BITS, false, KD, KM>), grid, dim3(256), 0, s, a);
+}
+
 template <int BITS>
 void launch_prep_keys(const tq_config& cfg, const ScoreArgs& a, hipStream_t s) {
-  constexpr int NP = 1 << (BITS - 1);
-  const int64_t lanes = a.n_k_pad * ((NP * a.kd + a.km) / 16);
-  dim3 grid((unsigned)((lanes + 255) / 256));
-  if (cfg.norm_dtype == TQ_F32)
-    hipLaunchKernelGGL((prep_keys<BITS, true>), grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((prep_keys<BITS, false>), grid, dim3(256), 0, s, a);
+  const int kd = a.kd / 64, km = a.km / 64;
+  if (kd == 1 && km == 1) launch_prep_keys_t<BITS, 1, 1>(cfg, a, s);
+  else if (kd == 1 && km == 2) launch_prep_keys_t<BITS, 1, 2>(cfg, a, s);
+  else if (kd == 2 && km == 1) launch_prep_keys_t<BITS, 2, 1>(cfg, a, s);
+  else launch_prep_keys_t<BITS, 2, 2>(cfg, a, s);
 }
 
 }  // namespace
