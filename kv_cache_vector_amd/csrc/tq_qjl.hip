@@ -172,12 +172,12 @@ __global__ __launch_bounds__(kEncBlock) void qjl_encode128_kernel(QjlEncodeArgs 
     float v[32];
     if (valid) {
       if constexpr (IN_F32) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(a.x) + key * a.ld_x + 32 * q);
+        const v4f* p = reinterpret_cast<const v4f*>(static_cast<const float*>(a.x) + key * a.ld_x + 32 * q);
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          const u32x4 w = p[c];
+          const v4f w = p[c];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[4 * c + i] = __builtin_bit_cast(float, w[i]);
+          for (int i = 0; i < 4; ++i) v[4 * c + i] = w[i];
         }
       } else {
         const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const __half*>(a.x) + key * a.ld_x + 32 * q);

@@ -86,3 +86,40 @@ def test_qjl_keys_full_size_sampled():
     sb = check_sign_bits(sbits.cpu().numpy().reshape(n, 16)[idx], orc, m)
     assert st["in_band"] <= 1e-5 * st["coords"] + 1
     print(st, sb)
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_qjl_encode_head128_f32_zero_keys(bits):
+    """head_dim 128 with fp32 keys and fp32 norms at 3 and 4 bits, including all-zero keys: codes,
+    norms, sign bits and residual norms against the oracle; zero keys store n = 0, the code just
+    below zero for every coordinate, rho of the unit-less residual, and decode to zero."""
+    dt, m, n = 128, 128, 333
+    keys = synth.kv_tensor(bits + 40, 1, 1, 0, n, dt, n_outliers=2).reshape(n, dt).astype(np.float32)
+    keys[[0, 17, 200, n - 1]] = 0.0
+    signs = synth.signs(bits + 40, 2, dt)
+    S = synth.gaussian_matrix(bits + 41, 0, m, dt)
+    qz = tq.Quantizer(dt, dt, bits, signs, flags=tq.TQ_QJL, qjl_m=m, x_dtype=tq.TQ_F32, norm_dtype=tq.TQ_F32)
+    params = torch.empty(tq.tq_qjl_params_size(m, dt), dtype=torch.uint8, device=DEV)
+    tq.tq_qjl_prepare(qz, S, params)
+    x = torch.from_numpy(keys).to(DEV)
+    codes = torch.full((n * dt * bits // 8,), 0x5A, dtype=torch.uint8, device=DEV)
+    norms = torch.full((n,), -1.0, dtype=torch.float32, device=DEV)
+    sbits = torch.full((n * m // 8,), 0x33, dtype=torch.uint8, device=DEV)
+    rnorm = torch.empty(n, dtype=torch.float16, device=DEV)
+    tq.tq_quantize(qz, x, n, dt, codes, norms, sbits, rnorm)
+    torch.cuda.synchronize()
+    cb = Codebook.build(bits, dt)
+    orc = quantize(keys.astype(np.float64), signs, cb, norm_dtype=np.float32, S=S)
+    codes_np, norms_np = codes.cpu().numpy(), norms.cpu().numpy()
+    check_codes(codes_np, orc, cb, bits, dt)
+    check_norms(norms_np, orc["norms"])
+    assert np.all(norms_np[[0, 17, 200, n - 1]] == 0.0)
+    same = np.all(unpack_codes(codes_np.reshape(n, -1), bits, dt) == unpack_codes(orc["codes"], bits, dt), axis=1)
+    assert same[[0, 17, 200, n - 1]].all(), "zero keys must take the code just below zero everywhere"
+    sb = sbits.cpu().numpy().reshape(n, m // 8)
+    check_sign_bits(sb[same], {k: v[same] for k, v in orc.items()}, m)
+    check_norms(rnorm.cpu().numpy()[same], orc["rho"][same])
+    y = torch.empty((n, dt), dtype=torch.float32, device=DEV)
+    tq.tq_dequantize(qz, codes, norms, sbits, rnorm, n, y, tq.TQ_F32, dt)
+    torch.cuda.synchronize()
+    assert np.all(y.cpu().numpy()[[0, 17, 200, n - 1]] == 0.0)

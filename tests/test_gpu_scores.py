@@ -77,7 +77,7 @@ def _check(gpu, orc, q, norms):
                                            (3, 128, 64, np.float16), (2, 64, 128, np.float32),
                                            (3, 64, 64, np.float16)])
 def test_scores_matrix(bits, dt, m, qdt):
-    n_k, n_q = 1000, 70  # ragged against the 16-query blocks and the 128/256-key tiles
+    n_k, n_q = 1000, 70  # ragged against the 32-query blocks and the 128/256-key tiles
     keys = synth.kv_tensor(bits + dt, 1, 1, 0, n_k, dt, n_outliers=0).reshape(n_k, dt)
     signs = synth.signs(bits, 2, dt)
     S = synth.gaussian_matrix(bits + 1, 0, m, dt)
@@ -87,6 +87,22 @@ def test_scores_matrix(bits, dt, m, qdt):
     orc = K.oracle(q)
     worst = _check(gpu, orc, q, K.host()[1][None, :][0])
     print(f"bits={bits} dt={dt} m={m}: worst error {worst:.2e} of n*||q||")
+
+
+@pytest.mark.parametrize("n_k,n_q", [(1000, 70), (4100, 200)])
+def test_scores_dense_rows_ragged(n_k, n_q):
+    """ld_s == n_k (16-byte row pieces where a whole tile fits, element stores on the ragged key tile
+    and query block): every score of the matrix against the oracle."""
+    bits, dt, m = 2, 128, 128
+    keys = synth.kv_tensor(77, 1, 1, 0, n_k, dt, n_outliers=0).reshape(n_k, dt)
+    signs = synth.signs(78, 2, dt)
+    S = synth.gaussian_matrix(79, 0, m, dt)
+    K = Keys(keys, dt, bits, m, signs, S)
+    q = synth.normal_f16(80, 6, n_q * dt).reshape(n_q, dt)
+    gpu = K.scores(q)
+    orc = K.oracle(q)
+    worst = _check(gpu, orc, q, K.host()[1])
+    print(f"n_k={n_k} n_q={n_q}: worst error {worst:.2e} of n*||q||")
 
 
 def test_scores_full_size_sampled():
