@@ -234,6 +234,24 @@ def batch_ms(torch, fn, reps):
     return e0.elapsed_time(e1) / reps
 
 
+def graph_ms(torch, fn, outputs, reps):
+    """Average device duration (ms) of fn() from `reps` replays of a HIP graph holding one call,
+    between two HIP events (the host cost of the Python call is not timed).  The replay is checked
+    against an eager call first; falls back to back-to-back eager calls if it differs."""
+    graph = capture_step(torch, fn, outputs)
+    if graph is None:
+        return batch_ms(torch, fn, reps)
+    torch.cuda.synchronize()
+    graph.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
 def bench_qjl(tq, torch, dev, reps):
     """QJL workload: encode 65536 keys (2-bit MSE + QJL, m = 128), score 4096 queries against them."""
     from synth import workloads
@@ -263,8 +281,9 @@ def bench_qjl(tq, torch, dev, reps):
     for _ in range(2):
         enc()
         score()
-    enc_ms = batch_ms(torch, enc, reps)
-    sc_ms = batch_ms(torch, score, reps)
+    # device time: one call per graph replay (the kernels are far shorter than the host cost of a call)
+    enc_ms = graph_ms(torch, enc, [codes, norms, sbits, rnorm], reps)
+    sc_ms = graph_ms(torch, score, [scores], reps)
     key_bytes = n * (d * 2 + d * bits // 8 + 2 + m // 8 + 2)  # fp16 key in; codes, norm, signs, rho out
     n_scores = nq * n
     # int8 MFMA work of the scoring kernel: per score, hi and lo limbs of the rotated query against
