@@ -129,7 +129,11 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   // l % C, so the random lookups of one instruction fall in distinct LDS banks.
   constexpr int LGCK = KB == 3 ? 5 : 3, LGCV = VB == 3 ? 5 : 3;
   constexpr int CK = 1 << LGCK, CV = 1 << LGCV;
-  __shared__ uint32_t kth[KL * KL * CK], ktl[KL * KL * CK];
+  // hi and lo tables one word apart from a 256-byte multiple: their lookups at the same entry stay
+  // two ds_read_b32 into the operand registers instead of one ds_read2st64 into a register pair
+  __shared__ uint32_t ktab[2 * KL * KL * CK + 1];
+  uint32_t* kth = ktab;
+  uint32_t* ktl = ktab + KL * KL * CK + 1;
   __shared__ uint32_t vtab[VL * VL * CV];
   __shared__ __attribute__((aligned(16))) _Float16 vt[kWaves][kTile * VROW];
   __shared__ __attribute__((aligned(16))) _Float16 pt[kWaves][GP * kTile];
