@@ -31,7 +31,7 @@ Sources (cited by short tag in every docstring):
 Every function here is pinned by ``tests/test_oracle_*.py`` against values
 the pages print, closed forms, invariants or brute force.
 """
-from .codebook import Codebook, lloyd_max_gaussian, gaussian_distortion  # noqa: F401
+from .codebook import Codebook, lloyd_max_gaussian, gaussian_distortion, lloyd_max_beta, beta_distortion  # noqa: F401
 from .quantizer import (  # noqa: F401
     fwht, hadamard_matrix, index_to_code, code_to_index, pack_codes, unpack_codes, pack_sign_bits,
     unpack_sign_bits, encode_indices, quantize, dequantize, qjl_scores, QJL_CONST,
