@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0
 LAYERS, KV_HEADS, TOKENS, HEAD_DIM, DT = 36, 8, 16384, 128, 32
+CODEBOOK = "gaussian"  # set from --codebook
 
 
 def log(msg: str) -> None:
@@ -65,8 +66,8 @@ def make_cache(tq, torch, dev):
 class Codec:
     def __init__(self, tq, torch, dev, rows, bits, signs_k, signs_v):
         self.tq, self.rows, self.bits = tq, rows, bits
-        self.qk = tq.Quantizer(HEAD_DIM, DT, bits, signs_k)
-        self.qv = tq.Quantizer(HEAD_DIM, DT, bits, signs_v)
+        self.qk = tq.Quantizer(HEAD_DIM, DT, bits, signs_k, codebook=CODEBOOK)
+        self.qv = tq.Quantizer(HEAD_DIM, DT, bits, signs_v, codebook=CODEBOOK)
         units = rows * HEAD_DIM // DT
         self.units = units
         cb = units * DT * bits // 8
@@ -259,7 +260,7 @@ def bench_qjl(tq, torch, dev, reps):
     w = workloads.qjl_keys()
     n, d, m, bits = w["keys"].shape[0], 128, 128, 2
     nq = w["q"].shape[0]
-    qz = tq.Quantizer(d, d, bits, w["signs"], flags=tq.TQ_QJL, qjl_m=m)
+    qz = tq.Quantizer(d, d, bits, w["signs"], flags=tq.TQ_QJL, qjl_m=m, codebook=CODEBOOK)
     params = torch.empty(tq.tq_qjl_params_size(m, d), dtype=torch.uint8, device=dev)
     tq.tq_qjl_prepare(qz, w["S"], params)
     x = torch.from_numpy(w["keys"]).to(dev)
@@ -310,8 +311,8 @@ def bench_attn(tq, torch, dev, reps):
     H, T, hd = w["k"].shape[1], w["k"].shape[2], w["k"].shape[3]
     hq = w["q"].shape[0]
     rows = H * T
-    kq = tq.Quantizer(hd, 32, 3, w["signs_k"])
-    vq = tq.Quantizer(hd, 32, 3, w["signs_v"])
+    kq = tq.Quantizer(hd, 32, 3, w["signs_k"], codebook=CODEBOOK)
+    vq = tq.Quantizer(hd, 32, 3, w["signs_v"], codebook=CODEBOOK)
     units = rows * hd // 32
     plane = {}
     for name, qz in (("k", kq), ("v", vq)):
@@ -357,7 +358,11 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a captured step")
     ap.add_argument("--only", choices=("all", "codec", "qjl", "attn"), default="all",
                     help="run one workload (for profiling runs); the JSON line needs 'all'")
+    ap.add_argument("--codebook", choices=("gaussian", "beta"), default="gaussian",
+                    help="Lloyd-Max codebook for N(0,1/d) (default) or for the exact Beta marginal")
     args = ap.parse_args()
+    global CODEBOOK
+    CODEBOOK = args.codebook
     if args.gpus != 1:
         print("bench.py measures one GPU: this quantizer's hot path has no cross-GPU step, and runs on more "
               "than one GPU are not part of this build (use --gpus 1)", file=sys.stderr)
@@ -434,6 +439,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "qwen3_8b_kv_block32_turbo3", "layers": LAYERS, "kv_heads": KV_HEADS,
                    "tokens": TOKENS, "head_dim": HEAD_DIM, "block": DT, "bits": 3, "kv_dtype": "f16",
+                   "codebook": CODEBOOK,
                    "step": "quantize K, quantize V, dequantize K, dequantize V",
                    "launch": "hip graph of the step's four launches" if results[3]["graphed"] else "eager launches"},
         "roofline": {"bound": "hbm", "kernel": f"{dom} (turbo3, one K half-cache per launch)",

@@ -73,10 +73,12 @@ enum {
 enum { TQ_OP_QJL_SCORES = 1, TQ_OP_DECODE_ATTN = 2 };
 
 /*
- * Lloyd-Max codebook for a coordinate distributed N(0, 1/dim) ([Scratch] §2
- * step 3: computed once per bit width, no calibration).  Plain host data.
- * unit_* are the N(0,1) values; the N(0,1/dim) values are unit_* / sqrt(dim).
- * Only the first 2^bits centroids and 2^bits - 1 bounds are meaningful.
+ * Lloyd-Max codebook for one rotated coordinate, whose variance is 1/dim
+ * ([Scratch] §2 step 3: computed once per bit width, no calibration).  Plain
+ * host data.  unit_* are the values for the unit-variance variable
+ * sqrt(dim) * coordinate; the codebook proper is unit_* / sqrt(dim).  Only the
+ * first 2^bits centroids and 2^bits - 1 bounds are meaningful.  Every kernel
+ * reads only these fields, so either solver below can feed any entry point.
  */
 typedef struct {
   int bits;                     /* 1..4 */
@@ -85,7 +87,7 @@ typedef struct {
   double unit_bounds[15];       /* midpoints of neighbouring centroids */
   float centroids[16];          /* fp32(unit_centroids / sqrt(dim)) */
   float bounds[15];             /* fp32(unit_bounds / sqrt(dim)) */
-  double distortion;            /* E[(X - Q(X))^2] for X ~ N(0,1) */
+  double distortion;            /* E[(X - Q(X))^2] for the unit-variance X the codebook was solved for */
 } tq_codebook;
 
 /*
@@ -94,6 +96,22 @@ typedef struct {
  * in 2..4096.  Errors: TQ_ERR_INVALID_ARG.
  */
 tq_status tq_codebook_init(tq_codebook* out, int bits, int dim);
+
+/*
+ * Fill *out with the Lloyd-Max quantizer of the exact marginal of a rotated
+ * unit vector ([Fork] "How it works": centroids solved for the
+ * Beta((dim-1)/2, (dim-1)/2) law of one coordinate, i.e. density proportional
+ * to (1 - t^2)^((dim-3)/2) on [-1, 1]; [README], stage 1 of its two-stage
+ * description: the Gaussian N(0, 1/dim) of tq_codebook_init is its large-dim
+ * limit).  It differs from
+ * the Gaussian codebook most at small dim, e.g. the 32-coordinate blocks of
+ * [Scratch] §7.  Same fields and scaling as tq_codebook_init (X = sqrt(dim) T
+ * has unit variance); distortion is the MSE under this law.  Host only,
+ * float64.  bits in 1..4, dim a power of two in 4..4096 (the law is
+ * log-concave there, so the fixed point is unique).  Errors:
+ * TQ_ERR_INVALID_ARG.
+ */
+tq_status tq_codebook_init_beta(tq_codebook* out, int bits, int dim);
 
 /*
  * One quantizer (e.g. the key quantizer or the value quantizer of a cache).

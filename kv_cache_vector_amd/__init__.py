@@ -23,7 +23,7 @@ TQ_F16, TQ_F32 = 0, 1
 TQ_NORM_CORRECT, TQ_QJL = 1, 2
 TQ_OP_QJL_SCORES, TQ_OP_DECODE_ATTN = 1, 2
 
-EXPORTED = ("tq_codebook_init", "tq_qjl_params_size", "tq_qjl_prepare", "tq_quantize", "tq_dequantize",
+EXPORTED = ("tq_codebook_init", "tq_codebook_init_beta", "tq_qjl_params_size", "tq_qjl_prepare", "tq_quantize", "tq_dequantize",
             "tq_qjl_scores", "tq_decode_attn", "tq_workspace_size", "tq_status_str", "tq_last_error")
 
 
@@ -61,6 +61,7 @@ def lib():
     vp, i64, c_int, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     cfgp = ctypes.POINTER(tq_config)
     L.tq_codebook_init.argtypes = [ctypes.POINTER(tq_codebook), c_int, c_int]
+    L.tq_codebook_init_beta.argtypes = [ctypes.POINTER(tq_codebook), c_int, c_int]
     L.tq_qjl_params_size.argtypes = [c_int, c_int]
     L.tq_qjl_params_size.restype = sz
     L.tq_qjl_prepare.argtypes = [cfgp, vp, vp, sz, vp]
@@ -74,7 +75,7 @@ def lib():
     L.tq_status_str.argtypes = [c_int]
     L.tq_status_str.restype = ctypes.c_char_p
     L.tq_last_error.restype = ctypes.c_char_p
-    for name in ("tq_codebook_init", "tq_qjl_prepare", "tq_quantize", "tq_dequantize", "tq_qjl_scores",
+    for name in ("tq_codebook_init", "tq_codebook_init_beta", "tq_qjl_prepare", "tq_quantize", "tq_dequantize", "tq_qjl_scores",
                  "tq_decode_attn"):
         getattr(L, name).restype = c_int
     _lib = L
@@ -111,12 +112,21 @@ def tq_codebook_init(bits: int, dim: int) -> tq_codebook:
     return cb
 
 
+def tq_codebook_init_beta(bits: int, dim: int) -> tq_codebook:
+    cb = tq_codebook()
+    _check(lib().tq_codebook_init_beta(ctypes.byref(cb), bits, dim))
+    return cb
+
+
+CODEBOOKS = {"gaussian": tq_codebook_init, "beta": tq_codebook_init_beta}
+
+
 class Quantizer:
     """A ``tq_config`` plus the host data it points to (kept alive here)."""
 
     def __init__(self, head_dim: int, dt: int, bits: int, signs, flags: int = 0, qjl_m: int = 0,
-                 x_dtype: int = TQ_F16, norm_dtype: int = TQ_F16):
-        self.codebook = tq_codebook_init(bits, dt)
+                 x_dtype: int = TQ_F16, norm_dtype: int = TQ_F16, codebook: str = "gaussian"):
+        self.codebook = CODEBOOKS[codebook](bits, dt)
         self.signs = np.ascontiguousarray(np.asarray(signs, dtype=np.float32))
         self.params = None
         self.cfg = tq_config(head_dim, dt, bits, flags, qjl_m, x_dtype, norm_dtype, ctypes.pointer(self.codebook),

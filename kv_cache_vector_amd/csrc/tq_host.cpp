@@ -51,17 +51,97 @@ double std_mass(double a, double b) {
   return 1.0 - 0.5 * std::erfc(-a * M_SQRT1_2) - 0.5 * std::erfc(b * M_SQRT1_2);
 }
 
-void solve_lloyd_max(int bits, double* levels, double* edges, double* distortion) {
+struct GaussCell {
+  // mass and first moment of N(0,1) over (a, b)
+  void operator()(double a, double b, double* m0, double* m1) const {
+    *m0 = std_mass(a, b);
+    *m1 = std_pdf(a) - std_pdf(b);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Exact marginal of a rotated unit vector ([Fork] "How it works": the
+// codebook is solved for Beta((d-1)/2, (d-1)/2); [README], stage 1: the Gaussian
+// is its large-d limit).  A coordinate T of a uniform unit vector in d
+// dimensions has density proportional to (1 - t^2)^((d-3)/2) on [-1, 1].
+// With t = sin(theta) the mass element becomes cos^(d-2)(theta) d theta, a
+// smooth bell of width about 1/sqrt(d) with no end-point singularity, which
+// composite 16-point Gauss-Legendre integrates to rounding.  Cells are given
+// in the unit-variance scale u = sqrt(d) t; the first moment is returned in
+// that scale too.  Masses are not normalised (the Lloyd step only needs
+// ratios; the distortion divides by their sum).
+// ---------------------------------------------------------------------------
+struct GaussLegendre16 {
+  double x[16], w[16];
+  GaussLegendre16() {
+    const int n = 16;
+    for (int i = 0; i < n; ++i) {
+      double z = std::cos(M_PI * (i + 0.75) / (n + 0.5));  // Newton on P_16 from the usual initial guess
+      double dp = 1.0;
+      for (int it = 0; it < 100; ++it) {
+        double p0 = 1.0, p1 = z;
+        for (int k = 2; k <= n; ++k) {
+          double p2 = ((2 * k - 1) * z * p1 - (k - 1) * p0) / k;
+          p0 = p1;
+          p1 = p2;
+        }
+        dp = n * (z * p1 - p0) / (z * z - 1.0);
+        double dz = p1 / dp;
+        z -= dz;
+        if (std::fabs(dz) < 1e-17) break;
+      }
+      x[i] = z;
+      w[i] = 2.0 / ((1.0 - z * z) * dp * dp);
+    }
+  }
+};
+
+struct SphereCell {
+  int dim;
+  void operator()(double a, double b, double* m0, double* m1) const {
+    static const GaussLegendre16 gl;
+    const double sd = std::sqrt((double)dim), n = dim - 2;
+    // beyond |theta| = acos(exp(-745/n)) the integrand is below the smallest double
+    const double lim = std::acos(std::exp(-745.0 / n));
+    double lo = std::max(-lim, std::asin(std::max(-1.0, std::min(1.0, a / sd))));
+    double hi = std::min(lim, std::asin(std::max(-1.0, std::min(1.0, b / sd))));
+    double s0 = 0.0, s1 = 0.0;
+    if (hi > lo) {
+      const double h = 1.0 / std::sqrt(n);  // panel no wider than the bell
+      const int panels = std::min(100000, std::max(1, (int)std::ceil((hi - lo) / h)));
+      const double pw = (hi - lo) / panels;
+      for (int p = 0; p < panels; ++p) {
+        const double mid = lo + (p + 0.5) * pw;
+        for (int k = 0; k < 16; ++k) {
+          const double th = mid + 0.5 * pw * gl.x[k];
+          const double sn = std::sin(th);
+          const double f = 0.5 * pw * gl.w[k] * std::exp(0.5 * n * std::log1p(-sn * sn));  // cos^n, cos >= 0
+          s0 += f;
+          s1 += f * sn;
+        }
+      }
+    }
+    *m0 = s0;
+    *m1 = sd * s1;
+  }
+};
+
+// Jacobi iteration of Lloyd's two conditions for the symmetric law whose
+// cell moments `cell` returns, starting from a uniform grid on [-r, r].
+template <typename Cell>
+void solve_lloyd_max(int bits, const Cell& cell, double r, double* levels, double* edges, double* distortion) {
   const int L = 1 << bits;
   std::vector<double> c(L), t(L - 1), nc(L);
-  for (int i = 0; i < L; ++i) c[i] = -3.0 + 6.0 * (i + 0.5) / L;
+  for (int i = 0; i < L; ++i) c[i] = -r + 2.0 * r * (i + 0.5) / L;
   for (int it = 0; it < 1000000; ++it) {
     for (int k = 0; k + 1 < L; ++k) t[k] = 0.5 * (c[k] + c[k + 1]);
     double moved = 0.0;
     for (int i = 0; i < L; ++i) {
       double a = i == 0 ? -INFINITY : t[i - 1];
       double b = i == L - 1 ? INFINITY : t[i];
-      nc[i] = (std_pdf(a) - std_pdf(b)) / std_mass(a, b);
+      double m0, m1;
+      cell(a, b, &m0, &m1);
+      nc[i] = m1 / m0;
       moved = std::max(moved, std::fabs(nc[i] - c[i]));
     }
     c = nc;
@@ -72,17 +152,21 @@ void solve_lloyd_max(int bits, double* levels, double* edges, double* distortion
     c[i] = -m;
     c[L - 1 - i] = m;
   }
-  double sum = 0.0;
+  double sum = 0.0, total = 0.0;
   for (int k = 0; k + 1 < L; ++k) t[k] = 0.5 * (c[k] + c[k + 1]);
   t[L / 2 - 1] = 0.0;
   for (int i = 0; i < L; ++i) {
     double a = i == 0 ? -INFINITY : t[i - 1];
     double b = i == L - 1 ? INFINITY : t[i];
-    sum += std_mass(a, b) * c[i] * c[i];
+    double m0, m1;
+    cell(a, b, &m0, &m1);
+    sum += m0 * c[i] * c[i];
+    total += m0;
   }
   for (int i = 0; i < L; ++i) levels[i] = c[i];
   for (int k = 0; k + 1 < L; ++k) edges[k] = t[k];
-  *distortion = 1.0 - sum;
+  // E[(X - Q X)^2] = E[X^2] - sum_i P_i c_i^2 at a Lloyd fixed point, E[X^2] = 1
+  *distortion = 1.0 - sum / total;
 }
 
 bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
@@ -196,6 +280,18 @@ const char* tq_status_str(tq_status s) {
 
 const char* tq_last_error(void) { return g_last_error.c_str(); }
 
+}  // extern "C"
+
+namespace {
+void scale_codebook(tq_codebook* out) {
+  const double s = 1.0 / std::sqrt((double)out->dim);
+  for (int i = 0; i < (1 << out->bits); ++i) out->centroids[i] = (float)(out->unit_centroids[i] * s);
+  for (int i = 0; i + 1 < (1 << out->bits); ++i) out->bounds[i] = (float)(out->unit_bounds[i] * s);
+}
+}  // namespace
+
+extern "C" {
+
 tq_status tq_codebook_init(tq_codebook* out, int bits, int dim) {
   if (!out) return fail(TQ_ERR_INVALID_ARG, "tq_codebook_init: out is NULL");
   if (bits < 1 || bits > 4) return fail(TQ_ERR_INVALID_ARG, "tq_codebook_init: bits must be 1..4 (got %d)", bits);
@@ -204,10 +300,24 @@ tq_status tq_codebook_init(tq_codebook* out, int bits, int dim) {
   std::memset(out, 0, sizeof(*out));
   out->bits = bits;
   out->dim = dim;
-  solve_lloyd_max(bits, out->unit_centroids, out->unit_bounds, &out->distortion);
-  const double s = 1.0 / std::sqrt((double)dim);
-  for (int i = 0; i < (1 << bits); ++i) out->centroids[i] = (float)(out->unit_centroids[i] * s);
-  for (int i = 0; i + 1 < (1 << bits); ++i) out->bounds[i] = (float)(out->unit_bounds[i] * s);
+  solve_lloyd_max(bits, GaussCell{}, 3.0, out->unit_centroids, out->unit_bounds, &out->distortion);
+  scale_codebook(out);
+  return ok();
+}
+
+tq_status tq_codebook_init_beta(tq_codebook* out, int bits, int dim) {
+  if (!out) return fail(TQ_ERR_INVALID_ARG, "tq_codebook_init_beta: out is NULL");
+  if (bits < 1 || bits > 4)
+    return fail(TQ_ERR_INVALID_ARG, "tq_codebook_init_beta: bits must be 1..4 (got %d)", bits);
+  if (!is_pow2(dim) || dim < 4 || dim > 4096)
+    return fail(TQ_ERR_INVALID_ARG, "tq_codebook_init_beta: dim must be a power of two in 4..4096 (got %d)", dim);
+  std::memset(out, 0, sizeof(*out));
+  out->bits = bits;
+  out->dim = dim;
+  // start inside the support |u| < sqrt(dim)
+  const double r = std::min(3.0, 0.9 * std::sqrt((double)dim));
+  solve_lloyd_max(bits, SphereCell{dim}, r, out->unit_centroids, out->unit_bounds, &out->distortion);
+  scale_codebook(out);
   return ok();
 }
 

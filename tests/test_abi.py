@@ -47,6 +47,33 @@ def test_host_codebook_matches_oracle(bits, dim):
     assert cb.distortion == pytest.approx(orc.distortion, abs=1e-12)
 
 
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("dim", [4, 32, 64, 128, 256, 4096])
+def test_host_beta_codebook_matches_oracle(bits, dim):
+    """The host solver (theta-substitution quadrature) against the oracle (incomplete beta function)."""
+    cb = tq.tq_codebook_init_beta(bits, dim)
+    orc = Codebook.build_beta(bits, dim)
+    L = 1 << bits
+    tol = 1e-11 if dim > 256 else 1e-12  # Lloyd's contraction slows at large d and 4 bits
+    np.testing.assert_allclose(np.array(cb.unit_centroids[:L]), orc.unit_levels, atol=tol, rtol=0)
+    np.testing.assert_allclose(np.array(cb.unit_bounds[:L - 1]), orc.unit_bounds, atol=tol, rtol=0)
+    np.testing.assert_array_equal(np.array(cb.centroids[:L], dtype=np.float32), orc.levels.astype(np.float32))
+    np.testing.assert_array_equal(np.array(cb.bounds[:L - 1], dtype=np.float32), orc.bounds.astype(np.float32))
+    assert cb.distortion == pytest.approx(orc.distortion, abs=1e-12)
+    assert (cb.bits, cb.dim) == (bits, dim)
+
+
+def test_beta_codebook_init_rejects_bad_arguments():
+    cb = tq.tq_codebook()
+    L = tq.lib()
+    assert L.tq_codebook_init_beta(ctypes.byref(cb), 0, 32) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_codebook_init_beta(ctypes.byref(cb), 5, 32) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_codebook_init_beta(ctypes.byref(cb), 3, 2) == tq.TQ_ERR_INVALID_ARG  # below 4: not log-concave
+    assert L.tq_codebook_init_beta(ctypes.byref(cb), 3, 48) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_codebook_init_beta(ctypes.byref(cb), 3, 8192) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_codebook_init_beta(None, 3, 32) == tq.TQ_ERR_INVALID_ARG
+
+
 def test_codebook_init_rejects_bad_arguments():
     cb = tq.tq_codebook()
     L = tq.lib()

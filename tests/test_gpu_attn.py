@@ -39,12 +39,13 @@ U16 = 2.0 ** -11
 class Cache:
     """n_kv_heads x n_tokens x head_dim K and V, encoded on the GPU in the block-32 layout."""
 
-    def __init__(self, k, v, kbits, vbits, signs_k, signs_v):
+    def __init__(self, k, v, kbits, vbits, signs_k, signs_v, codebook="gaussian"):
         self.H, self.T, self.hd = k.shape
         self.kbits, self.vbits = kbits, vbits
         self.signs_k, self.signs_v = signs_k, signs_v
-        self.kq = tq.Quantizer(self.hd, 32, kbits, signs_k)
-        self.vq = tq.Quantizer(self.hd, 32, vbits, signs_v)
+        self.codebook = codebook
+        self.kq = tq.Quantizer(self.hd, 32, kbits, signs_k, codebook=codebook)
+        self.vq = tq.Quantizer(self.hd, 32, vbits, signs_v, codebook=codebook)
         self.kc, self.kn = self._encode(self.kq, k, kbits)
         self.vc, self.vn = self._encode(self.vq, v, vbits)
 
@@ -87,7 +88,8 @@ class Cache:
         G = q.shape[0] // self.H
         qs = np.concatenate([q[g * G:(g + 1) * G] for g in sel])
         kc, kn, vc, vn = self.host(sel)
-        kcb, vcb = Codebook.build(self.kbits, 32), Codebook.build(self.vbits, 32)
+        build = Codebook.build_beta if self.codebook == "beta" else Codebook.build
+        kcb, vcb = build(self.kbits, 32), build(self.vbits, 32)
         out = decode_attention(qs.astype(np.float64), kc, kn, vc, vn, self.signs_k, self.signs_v, kcb, vcb, len(sel),
                                self.T, self.hd, scale)
         bound = self._bound(qs.astype(np.float64), kc, kn, vc, vn, kcb, vcb, len(sel), G,
@@ -149,6 +151,17 @@ def test_attn_matrix(hd, H, G, T, kbits, vbits, qdt):
     gpu = c.attend(q)
     orc, bound = c.oracle(q)
     _check(gpu, orc, bound, f"hd={hd} H={H} G={G} T={T} K{kbits}V{vbits}")
+
+
+@pytest.mark.parametrize("kbits,vbits", [(3, 3), (4, 3)])
+def test_attn_beta_codebook(kbits, vbits):
+    """K and V block-32 codebooks solved for the exact marginal of a 32-long unit block."""
+    k, v, sk, sv = _data(31, 2, 1500, 128)
+    c = Cache(k, v, kbits, vbits, sk, sv, codebook="beta")
+    q = synth.normal_f16(31, 6, 8 * 128).reshape(8, 128)
+    gpu = c.attend(q)
+    orc, bound = c.oracle(q)
+    _check(gpu, orc, bound, f"beta codebook K{kbits}V{vbits}")
 
 
 def test_attn_explicit_scale():

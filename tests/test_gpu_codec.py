@@ -53,12 +53,13 @@ def _run_decode(qz, codes_np, norms_np, n_rows, y_dtype, ld=None):
     return out[:, :hd]
 
 
-def _roundtrip(x_np, dt, bits, seed, x_dtype, norm_dtype, nc=False, ld=None, y_dtypes=(tq.TQ_F32, tq.TQ_F16)):
+def _roundtrip(x_np, dt, bits, seed, x_dtype, norm_dtype, nc=False, ld=None, y_dtypes=(tq.TQ_F32, tq.TQ_F16),
+               codebook="gaussian"):
     n_rows, hd = x_np.shape
     signs = synth.signs(seed, 2, dt)
     qz = tq.Quantizer(hd, dt, bits, signs, flags=tq.TQ_NORM_CORRECT if nc else 0, x_dtype=x_dtype,
-                      norm_dtype=norm_dtype)
-    cb = Codebook.build(bits, dt)
+                      norm_dtype=norm_dtype, codebook=codebook)
+    cb = Codebook.build_beta(bits, dt) if codebook == "beta" else Codebook.build(bits, dt)
     codes, norms = _run_encode(qz, x_np, ld)
     orc = quantize(x_np.astype(np.float64), signs, cb, norm_dtype=np.float32 if norm_dtype == tq.TQ_F32 else np.float16)
     stats = check_codes(codes, orc, cb, bits, dt)
@@ -89,6 +90,17 @@ def test_matrix_f32_strided(dt, bits):
     hd, n_rows = 256, 129
     x = synth.normal_f32(7, 0, n_rows * hd).reshape(n_rows, hd) * 3.0
     stats, *_ = _roundtrip(x, dt, bits, seed=5, x_dtype=tq.TQ_F32, norm_dtype=tq.TQ_F32, ld=hd + 8)
+    print(stats)
+
+
+@pytest.mark.parametrize("dt", [32, 128])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_beta_codebook(dt, bits):
+    """Codebook solved for the exact marginal (tq_codebook_init_beta): the same kernels, other centroids."""
+    hd, n_rows = 256, 301
+    x = synth.kv_tensor(100 + dt + bits, 1, 1, 0, n_rows, hd).reshape(n_rows, hd)
+    stats, *_ = _roundtrip(x, dt, bits, seed=3 * dt + bits, x_dtype=tq.TQ_F16, norm_dtype=tq.TQ_F16,
+                           nc=bits == 3, codebook="beta")
     print(stats)
 
 

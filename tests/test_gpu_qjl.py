@@ -14,11 +14,12 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _encode(keys, dt, bits, m, seed, nc=False):
+def _encode(keys, dt, bits, m, seed, nc=False, codebook="gaussian"):
     n = keys.shape[0]
     signs = synth.signs(seed, 2, dt)
     S = synth.gaussian_matrix(seed + 1, 0, m, dt)
-    qz = tq.Quantizer(dt, dt, bits, signs, flags=tq.TQ_QJL | (tq.TQ_NORM_CORRECT if nc else 0), qjl_m=m)
+    qz = tq.Quantizer(dt, dt, bits, signs, flags=tq.TQ_QJL | (tq.TQ_NORM_CORRECT if nc else 0), qjl_m=m,
+                      codebook=codebook)
     params = torch.empty(tq.tq_qjl_params_size(m, dt), dtype=torch.uint8, device=DEV)
     tq.tq_qjl_prepare(qz, S, params)
     x = torch.from_numpy(keys).to(DEV)
@@ -31,12 +32,15 @@ def _encode(keys, dt, bits, m, seed, nc=False):
     return qz, signs, S, codes, norms, sbits, rnorm
 
 
-@pytest.mark.parametrize("dt,m,bits", [(128, 128, 2), (128, 64, 1), (64, 128, 3), (64, 64, 2), (128, 96, 2)])
-def test_qjl_encode_decode(dt, m, bits):
+@pytest.mark.parametrize("dt,m,bits,codebook", [(128, 128, 2, "gaussian"), (128, 64, 1, "gaussian"),
+                                                 (64, 128, 3, "gaussian"), (64, 64, 2, "gaussian"),
+                                                 (128, 96, 2, "gaussian"), (128, 128, 3, "beta"),
+                                                 (64, 64, 2, "beta")])
+def test_qjl_encode_decode(dt, m, bits, codebook):
     n = 1000  # several workgroups plus a ragged tail
     keys = synth.kv_tensor(dt + m + bits, 1, 1, 0, n, dt, n_outliers=0).reshape(n, dt)
-    qz, signs, S, codes, norms, sbits, rnorm = _encode(keys, dt, bits, m, seed=dt + bits)
-    cb = Codebook.build(bits, dt)
+    qz, signs, S, codes, norms, sbits, rnorm = _encode(keys, dt, bits, m, seed=dt + bits, codebook=codebook)
+    cb = Codebook.build_beta(bits, dt) if codebook == "beta" else Codebook.build(bits, dt)
     orc = quantize(keys.astype(np.float64), signs, cb, S=S)
     codes_np, norms_np = codes.cpu().numpy(), norms.cpu().numpy()
     stats = check_codes(codes_np, orc, cb, bits, dt)

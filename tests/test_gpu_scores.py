@@ -21,11 +21,11 @@ TOL = 1e-4
 
 
 class Keys:
-    def __init__(self, keys, dt, bits, m, signs, S):
+    def __init__(self, keys, dt, bits, m, signs, S, codebook="gaussian"):
         n = keys.shape[0]
         self.n, self.dt, self.bits, self.m = n, dt, bits, m
-        self.signs, self.S = signs, S
-        self.qz = tq.Quantizer(dt, dt, bits, signs, flags=tq.TQ_QJL, qjl_m=m)
+        self.signs, self.S, self.codebook = signs, S, codebook
+        self.qz = tq.Quantizer(dt, dt, bits, signs, flags=tq.TQ_QJL, qjl_m=m, codebook=codebook)
         self.params = torch.empty(tq.tq_qjl_params_size(m, dt), dtype=torch.uint8, device=DEV)
         tq.tq_qjl_prepare(self.qz, S, self.params)
         x = torch.from_numpy(keys).to(DEV)
@@ -60,7 +60,7 @@ class Keys:
         codes, norms, sb, rn = self.host()
         cols = np.arange(self.n) if cols is None else cols
         q = q_np if rows is None else q_np[rows]
-        cb = Codebook.build(self.bits, self.dt)
+        cb = Codebook.build_beta(self.bits, self.dt) if self.codebook == "beta" else Codebook.build(self.bits, self.dt)
         return qjl_scores(q.astype(np.float64), codes[cols], norms[cols], sb[cols], rn[cols], self.signs, cb, self.S)
 
 
@@ -87,6 +87,21 @@ def test_scores_matrix(bits, dt, m, qdt):
     orc = K.oracle(q)
     worst = _check(gpu, orc, q, K.host()[1][None, :][0])
     print(f"bits={bits} dt={dt} m={m}: worst error {worst:.2e} of n*||q||")
+
+
+@pytest.mark.parametrize("bits,dt", [(2, 128), (3, 64)])
+def test_scores_beta_codebook(bits, dt):
+    """Keys encoded with the exact-marginal codebook: QJL residuals and scores use its centroids."""
+    n_k, n_q, m = 700, 40, 128
+    keys = synth.kv_tensor(90 + bits, 1, 1, 0, n_k, dt, n_outliers=0).reshape(n_k, dt)
+    signs = synth.signs(91, 2, dt)
+    S = synth.gaussian_matrix(92, 0, m, dt)
+    K = Keys(keys, dt, bits, m, signs, S, codebook="beta")
+    q = synth.normal_f16(93, 6, n_q * dt).reshape(n_q, dt)
+    gpu = K.scores(q)
+    orc = K.oracle(q)
+    worst = _check(gpu, orc, q, K.host()[1])
+    print(f"beta bits={bits} dt={dt}: worst error {worst:.2e} of n*||q||")
 
 
 @pytest.mark.parametrize("n_k,n_q", [(1000, 70), (4100, 200)])
