@@ -23,7 +23,7 @@ Sources (cited by short tag in every docstring):
 [Fork]     "TurboQuant KV Cache Quantization (Experimental)"
            (llama.cpp-turboquant docs/turboquant.md): "How it works",
            "GGML Types", "KV Cache Memory", "Fused tile path: K and V decoded
-           inside attention".
+           inside attention".  ``blocks.py`` holds its 32-value record format.
 [Blog]     "TurboQuant: 3-Bit Compression with Zero Overhead"
            (cneuralnets.xyz/blog/turboquant): "Part 2: Quantized
            Johnson-Lindenstrauss", "Part 3: TurboQuant Synthesis".
@@ -37,3 +37,4 @@ from .quantizer import (  # noqa: F401
     unpack_sign_bits, encode_indices, quantize, dequantize, qjl_scores, QJL_CONST,
 )
 from .attention import decode_attention  # noqa: F401
+from .blocks import to_blocks, from_blocks, dequantize_blocks, record_bytes  # noqa: F401
