@@ -12,6 +12,10 @@ tq_dequantize(K), tq_dequantize(V) through the C ABI.
 Prints one JSON line.  `value` is fp16 KV GB/s encoded+decoded: fp16 bytes
 read by the encodes plus fp16 bytes written by the decodes, per second.
 
+The same cache is also run in the fork's production layout (128-value
+chunks, the chunk norm copied into each 14/18-byte 32-value record, Beta
+codebook for d = 128), reported as `fork_layout` (not part of `value`).
+
 Two more workloads are timed and reported beside it (not part of `value`):
   qjl   65536 keys x 128 fp16 encoded at 2 bits + the 1-bit QJL residual
         (dense Gaussian S, m = 128), then scored against 4096 queries
@@ -64,25 +68,40 @@ def make_cache(tq, torch, dev):
 
 
 class Codec:
-    def __init__(self, tq, torch, dev, rows, bits, signs_k, signs_v):
+    """K and V encode/decode buffers for the cache: block-32 units in two planes (codes, fp16 norms),
+    or with records=True the fork's 32-value records over dt-long chunks (norms inside the records)."""
+
+    def __init__(self, tq, torch, dev, rows, bits, signs_k, signs_v, dt=DT, records=False, codebook=None):
         self.tq, self.rows, self.bits = tq, rows, bits
-        self.qk = tq.Quantizer(HEAD_DIM, DT, bits, signs_k, codebook=CODEBOOK)
-        self.qv = tq.Quantizer(HEAD_DIM, DT, bits, signs_v, codebook=CODEBOOK)
-        units = rows * HEAD_DIM // DT
-        self.units = units
-        cb = units * DT * bits // 8
-        self.ck = torch.empty(cb, dtype=torch.uint8, device=dev)
-        self.cv = torch.empty(cb, dtype=torch.uint8, device=dev)
-        self.nk = torch.empty(units, dtype=torch.float16, device=dev)
-        self.nv = torch.empty(units, dtype=torch.float16, device=dev)
+        flags = tq.TQ_BLOCKS if records else 0
+        cbk = codebook or CODEBOOK
+        self.qk = tq.Quantizer(HEAD_DIM, dt, bits, signs_k, flags=flags, codebook=cbk)
+        self.qv = tq.Quantizer(HEAD_DIM, dt, bits, signs_v, flags=flags, codebook=cbk)
+        groups = rows * HEAD_DIM // 32
+        self.units = groups  # 32-value groups (the unit of the byte accounting)
+        if records:
+            nb = groups * (2 + 4 * bits)
+            self.ck = torch.empty(nb, dtype=torch.uint8, device=dev)
+            self.cv = torch.empty(nb, dtype=torch.uint8, device=dev)
+            self.nk = self.nv = None
+        else:
+            units = rows * HEAD_DIM // dt
+            cb = units * dt * bits // 8
+            self.ck = torch.empty(cb, dtype=torch.uint8, device=dev)
+            self.cv = torch.empty(cb, dtype=torch.uint8, device=dev)
+            self.nk = torch.empty(units, dtype=torch.float16, device=dev)
+            self.nv = torch.empty(units, dtype=torch.float16, device=dev)
 
-    def encode(self, k, v):
-        self.tq.tq_quantize(self.qk, k, self.rows, HEAD_DIM, self.ck, self.nk)
-        self.tq.tq_quantize(self.qv, v, self.rows, HEAD_DIM, self.cv, self.nv)
+    def outputs(self):
+        return [t for t in (self.ck, self.cv, self.nk, self.nv) if t is not None]
 
-    def decode(self, ok, ov):
-        self.tq.tq_dequantize(self.qk, self.ck, self.nk, None, None, self.rows, ok, self.tq.TQ_F16, HEAD_DIM)
-        self.tq.tq_dequantize(self.qv, self.cv, self.nv, None, None, self.rows, ov, self.tq.TQ_F16, HEAD_DIM)
+    def launches(self, k, v, ok, ov):
+        """The step's four launches: quantize K, quantize V, dequantize K, dequantize V."""
+        tq = self.tq
+        return [lambda: tq.tq_quantize(self.qk, k, self.rows, HEAD_DIM, self.ck, self.nk),
+                lambda: tq.tq_quantize(self.qv, v, self.rows, HEAD_DIM, self.cv, self.nv),
+                lambda: tq.tq_dequantize(self.qk, self.ck, self.nk, None, None, self.rows, ok, tq.TQ_F16, HEAD_DIM),
+                lambda: tq.tq_dequantize(self.qv, self.cv, self.nv, None, None, self.rows, ov, tq.TQ_F16, HEAD_DIM)]
 
 
 def time_steps(torch, fn, steps, warmup):
@@ -134,11 +153,7 @@ def per_kernel_ms(torch, codec, k, v, ok, ov, reps):
     step), from HIP events recorded between the launches on the stream they run on (torch's
     current stream).  One untimed step first keeps the GPU busy, so host launch latency is not
     timed; each interval also holds the launch gap before its kernel."""
-    tq = codec.tq
-    launches = [lambda: tq.tq_quantize(codec.qk, k, codec.rows, HEAD_DIM, codec.ck, codec.nk),
-                lambda: tq.tq_quantize(codec.qv, v, codec.rows, HEAD_DIM, codec.cv, codec.nv),
-                lambda: tq.tq_dequantize(codec.qk, codec.ck, codec.nk, None, None, codec.rows, ok, tq.TQ_F16, HEAD_DIM),
-                lambda: tq.tq_dequantize(codec.qv, codec.cv, codec.nv, None, None, codec.rows, ov, tq.TQ_F16, HEAD_DIM)]
+    launches = codec.launches(k, v, ok, ov)
     torch.cuda.synchronize()
     for f in launches:
         f()
@@ -386,26 +401,34 @@ def main():
     copy_gbs = 2 * k.numel() * 2 / (copy_ms * 1e-3) / 1e9
     log(f"device copy of one half-cache: {copy_ms:.3f} ms ({copy_gbs:.0f} GB/s read+write)")
 
-    results = {}
-    for bits in (3, 4):
-        codec = Codec(tq, torch, dev, rows, bits, signs_k, signs_v)
+    def run_codec(bits, tag, sk, sv, **kw):
+        codec = Codec(tq, torch, dev, rows, bits, sk, sv, **kw)
+        launches = codec.launches(k, v, ok, ov)
 
         def step():
-            codec.encode(k, v)
-            codec.decode(ok, ov)
+            for f in launches:
+                f()
 
-        graph = None if args.no_graph else capture_step(torch, step, [codec.ck, codec.cv, codec.nk, codec.nv, ok, ov])
+        graph = None if args.no_graph else capture_step(torch, step, codec.outputs() + [ok, ov])
         ms = time_steps(torch, graph.replay if graph is not None else step, args.steps, args.warmup)
         graphed = graph is not None
         del graph
         enc_ms, dec_ms = per_kernel_ms(torch, codec, k, v, ok, ov, max(5, args.steps // 2))
         ab = algorithmic_bytes(codec.units, bits)
-        results[bits] = {"ms": ms, "enc_ms": enc_ms, "dec_ms": dec_ms, "bytes": ab, "units": codec.units,
-                         "graphed": graphed}
-        log(f"{bits}-bit: step {ms:.3f} ms, encode {enc_ms:.3f} ms ({ab['per_launch'] / enc_ms / 1e6:.0f} GB/s), "
+        log(f"{tag} {bits}-bit: step {ms:.3f} ms, encode {enc_ms:.3f} ms ({ab['per_launch'] / enc_ms / 1e6:.0f} GB/s), "
             f"decode {dec_ms:.3f} ms ({ab['per_launch'] / dec_ms / 1e6:.0f} GB/s)")
         del codec
         torch.cuda.empty_cache()
+        return {"ms": ms, "enc_ms": enc_ms, "dec_ms": dec_ms, "bytes": ab, "units": ab["fp16"] // 64,
+                "graphed": graphed}
+
+    results = {bits: run_codec(bits, "block-32", signs_k, signs_v) for bits in (3, 4)}
+    # the fork's production layout: 128-value chunks, norm copied into 14/18-byte records, Beta codebook
+    import synth
+
+    sk128, sv128 = synth.signs(0, synth.STREAM_SIGNS_K, 128), synth.signs(0, synth.STREAM_SIGNS_V, 128)
+    fork = {bits: run_codec(bits, "fork records", sk128, sv128, dt=128, records=True, codebook="beta")
+            for bits in (3, 4)}
 
     if args.only == "codec":
         return
@@ -456,6 +479,15 @@ def main():
                    "turbo3_blocks_per_s": round(r["units"] / (r["dec_ms"] * 1e-3)),
                    "turbo3_ms": round(r["dec_ms"], 4), "turbo4_ms": round(r4["dec_ms"], 4)},
         "turbo4_value": round(2 * 2 * r4["bytes"]["fp16"] / (r4["ms"] * 1e-3) / 1e9, 1),
+        "fork_layout": {
+            "workload": "same cache as 128-value chunks stored as the fork's records (fp16 chunk norm in each "
+                        "32-value record + packed codes: 14 B turbo3, 18 B turbo4), Beta codebook for d=128",
+            **{f"turbo{b}": {"GBs": round(2 * 2 * fork[b]["bytes"]["fp16"] / (fork[b]["ms"] * 1e-3) / 1e9, 1),
+                             "step_ms": round(fork[b]["ms"], 4),
+                             "encode_ms": round(fork[b]["enc_ms"], 4), "decode_ms": round(fork[b]["dec_ms"], 4),
+                             "encode_GBs": round(fork[b]["bytes"]["per_launch"] / fork[b]["enc_ms"] / 1e6, 1),
+                             "decode_GBs": round(fork[b]["bytes"]["per_launch"] / fork[b]["dec_ms"] / 1e6, 1)}
+               for b in (3, 4)}},
         "copy_reference_GBs": round(copy_gbs, 1),
         "qjl": qjl,
         "attn": attn,

@@ -44,6 +44,16 @@
  *   qjl_bits: [units][m / 8] bytes, projection i at bit i%8 of byte i/8,
  *             1 meaning sign(+), i.e. (S r)_i >= 0.
  *   qjl_rnorm: [units] binary16, the residual norm ||r||.
+ *
+ * Records (flag TQ_BLOCKS; [Fork] "GGML Types" and "How it works"): instead of
+ *   the two planes above, one array of 32-coordinate records in coordinate
+ *   order, record g = the binary16 norm of the unit that group g belongs to,
+ *   then group g's 4 * bits code bytes (14 bytes per 32 values at 3 bits, 18
+ *   at 4).  With dt = 128 this is the fork's turbo3/turbo4 layout: rows walked
+ *   in 128-value chunks, each its own unit, the chunk norm copied into each of
+ *   its four records.  Decode scales each group by the norm in its own record.
+ *   Requires norm_dtype TQ_F16, no TQ_QJL; the record array is passed as
+ *   `codes` (16-byte aligned) and `norms` must be NULL.
  */
 #ifndef TQ_H_
 #define TQ_H_
@@ -67,7 +77,8 @@ typedef enum { TQ_F16 = 0, TQ_F32 = 1 } tq_dtype;
 
 enum {
   TQ_NORM_CORRECT = 1u, /* rescale the reconstructed direction to unit length ([Scratch] §6) */
-  TQ_QJL = 2u           /* add the 1-bit QJL residual stage ([Scratch] §2, [README]) */
+  TQ_QJL = 2u,          /* add the 1-bit QJL residual stage ([Scratch] §2, [README]) */
+  TQ_BLOCKS = 4u        /* codes and norms as the fork's 32-value records (see "Records" above) */
 };
 
 enum { TQ_OP_QJL_SCORES = 1, TQ_OP_DECODE_ATTN = 2 };
@@ -163,8 +174,9 @@ tq_status tq_qjl_prepare(const tq_config* cfg, const float* S_host, void* params
  * r = u - D H c[idx], qjl_rnorm = ||r|| and qjl_bits = [S r >= 0].
  *   x        device, rows of ld_x elements (ld_x >= head_dim); 16-byte
  *            aligned, ld_x * element size a multiple of 16 bytes
- *   codes    device, 4-byte aligned, n_rows * head_dim/dt units
- *   norms    device, aligned to norm_dtype
+ *   codes    device, 4-byte aligned, n_rows * head_dim/dt units (TQ_BLOCKS:
+ *            the records, 16-byte aligned)
+ *   norms    device, aligned to norm_dtype (TQ_BLOCKS: NULL)
  *   qjl_bits, qjl_rnorm  device (TQ_QJL), otherwise ignored
  * A zero unit stores norm 0 and the codes of idx = 2^(b-1) - 1.
  */
@@ -176,7 +188,8 @@ tq_status tq_quantize(const tq_config* cfg, const void* x, int64_t n_rows, int64
  * [Fork] "How it works"): c = centroid(code), optional QJL correction
  * c += sqrt(pi/2) * rnorm / m * S~^T sign (in the rotated domain), optional
  * norm correction c /= ||c||, then x~ = n * D H c written as y_dtype rows of
- * stride ld_y (16-byte aligned like x).
+ * stride ld_y (16-byte aligned like x).  codes and norms as for tq_quantize
+ * (TQ_BLOCKS: records in codes, norms NULL).
  */
 tq_status tq_dequantize(const tq_config* cfg, const uint8_t* codes, const void* norms, const uint8_t* qjl_bits,
                         const void* qjl_rnorm, int64_t n_rows, void* y, tq_dtype y_dtype, int64_t ld_y,

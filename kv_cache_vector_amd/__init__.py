@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libtq.so")
 
 TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE, TQ_ERR_HIP = range(5)
 TQ_F16, TQ_F32 = 0, 1
-TQ_NORM_CORRECT, TQ_QJL = 1, 2
+TQ_NORM_CORRECT, TQ_QJL, TQ_BLOCKS = 1, 2, 4
 TQ_OP_QJL_SCORES, TQ_OP_DECODE_ATTN = 1, 2
 
 EXPORTED = ("tq_codebook_init", "tq_codebook_init_beta", "tq_qjl_params_size", "tq_qjl_prepare", "tq_quantize", "tq_dequantize",
@@ -139,6 +139,10 @@ class Quantizer:
     def code_bytes(self) -> int:
         """Bytes of packed codes per unit."""
         return self.cfg.dt * self.cfg.bits // 8
+
+    def record_bytes(self) -> int:
+        """Bytes of one 32-value record of the TQ_BLOCKS format (fp16 norm + codes)."""
+        return 2 + 4 * self.cfg.bits
 
     def attach_params(self, params_tensor):
         self.params = params_tensor

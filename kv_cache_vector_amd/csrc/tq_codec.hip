@@ -214,8 +214,38 @@ __device__ __forceinline__ void fwht32_from(float* v) {
   }
 }
 
-template <int BITS, int LPU, bool IN_F32, bool NORM_F32, bool CONTIG>
+// Records of the fork's block format ([Fork] "GGML Types"): per 32-coordinate
+// group the fp16 norm of its unit, then the group's 4*BITS code bytes, so
+// R = 2 + 4*BITS bytes (14 at 3 bits, 18 at 4).  R is even, so a record is a
+// run of 16-bit words.  A full wave's 64 records are 64 R = 16 (4 R) bytes,
+// 16-byte aligned (wave starts are multiples of 64 groups), and move between
+// LDS and memory as 4 R whole 16-byte chunks.
+template <int BITS>
+struct Record {
+  static constexpr int kBytes = 2 + 4 * BITS;
+  static constexpr int kChunks = 4 * kBytes;
+};
+
+template <int BITS>
+__device__ __forceinline__ void put_record(uint16_t* r, uint16_t norm_bits, const uint32_t* word) {
+  r[0] = norm_bits;
+#pragma unroll
+  for (int k = 0; k < BITS; ++k) {
+    r[1 + 2 * k] = (uint16_t)word[k];
+    r[2 + 2 * k] = (uint16_t)(word[k] >> 16);
+  }
+}
+
+template <int BITS>
+__device__ __forceinline__ float get_record(const uint16_t* r, uint32_t* word) {
+#pragma unroll
+  for (int k = 0; k < BITS; ++k) word[k] = (uint32_t)r[1 + 2 * k] | ((uint32_t)r[2 + 2 * k] << 16);
+  return __half2float(__ushort_as_half(r[0]));
+}
+
+template <int BITS, int LPU, bool IN_F32, bool NORM_F32, bool CONTIG, bool AOS>
 __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
+  static_assert(!(AOS && NORM_F32), "records carry fp16 norms");
   constexpr int CH = IN_F32 ? 8 : 4;  // 16-byte chunks per group
   constexpr int PITCH = 16 * CH + 16;  // LDS bytes per staged group (padded against bank conflicts)
   __shared__ __attribute__((aligned(16))) uint8_t stage[kWaves][64 * PITCH];
@@ -282,7 +312,22 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
 #pragma unroll
       for (int k = 0; k < BITS; ++k) word[k] = zero_unit_word<BITS>(k);
     }
-    if (valid) {
+    if constexpr (AOS) {
+      // every group of a unit carries the unit's norm (each lane of the unit holds n)
+      constexpr int R = Record<BITS>::kBytes;
+      const uint16_t nb = __half_as_ushort(__float2half_rn(n));
+      if (w0 + 64 <= a.n_groups) {
+        put_record<BITS>(reinterpret_cast<uint16_t*>(tile + R * lane), nb, word);
+        __builtin_amdgcn_wave_barrier();
+        u32x4* out = reinterpret_cast<u32x4*>(a.codes + w0 * R);
+#pragma unroll
+        for (int c = lane; c < Record<BITS>::kChunks; c += 64)
+          store_stream(*reinterpret_cast<const u32x4*>(tile + 16 * c), out + c);
+        __builtin_amdgcn_wave_barrier();
+      } else if (valid) {
+        put_record<BITS>(reinterpret_cast<uint16_t*>(a.codes + g * R), nb, word);
+      }
+    } else if (valid) {
       uint32_t* cp = reinterpret_cast<uint32_t*>(a.codes + g * (4 * BITS));
 #pragma unroll
       for (int k = 0; k < BITS; ++k) __builtin_nontemporal_store(word[k], cp + k);
@@ -456,8 +501,9 @@ __device__ __forceinline__ uint32_t pair_key8(const uint32_t* word, int i) {
   return key << 3;
 }
 
-template <int BITS, int LPU, bool OUT_F32, bool NORM_F32, bool NC, bool CONTIG>
+template <int BITS, int LPU, bool OUT_F32, bool NORM_F32, bool NC, bool CONTIG, bool AOS>
 __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs a) {
+  static_assert(!(AOS && NORM_F32), "records carry fp16 norms");
   constexpr int L = 1 << BITS;
   constexpr int CH = OUT_F32 ? 8 : 4;
   constexpr int PITCH = 16 * CH + 16;
@@ -479,7 +525,28 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs a) {
     const bool valid = g < a.n_groups;
     uint32_t word[BITS];
     float n = 0.0f;
-    if (valid) {
+    if constexpr (AOS) {
+      // each group is scaled by the norm its own record carries
+      constexpr int R = Record<BITS>::kBytes;
+      if (w0 + 64 <= a.n_groups) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(a.codes + w0 * R);
+        u32x4 t[(Record<BITS>::kChunks + 63) / 64];
+#pragma unroll
+        for (int i = 0; i * 64 < Record<BITS>::kChunks; ++i)
+          if (lane + 64 * i < Record<BITS>::kChunks) t[i] = load_stream(src + lane + 64 * i);
+#pragma unroll
+        for (int i = 0; i * 64 < Record<BITS>::kChunks; ++i)
+          if (lane + 64 * i < Record<BITS>::kChunks) *reinterpret_cast<u32x4*>(tile + 16 * (lane + 64 * i)) = t[i];
+        __builtin_amdgcn_wave_barrier();
+        n = get_record<BITS>(reinterpret_cast<const uint16_t*>(tile + R * lane), word);
+        __builtin_amdgcn_wave_barrier();
+      } else if (valid) {
+        n = get_record<BITS>(reinterpret_cast<const uint16_t*>(a.codes + g * R), word);
+      } else {
+#pragma unroll
+        for (int k = 0; k < BITS; ++k) word[k] = 0u;
+      }
+    } else if (valid) {
       const uint32_t* cp = reinterpret_cast<const uint32_t*>(a.codes + g * (4 * BITS));
 #pragma unroll
       for (int k = 0; k < BITS; ++k) word[k] = __builtin_nontemporal_load(cp + k);
@@ -711,6 +778,13 @@ template <int BITS, int LPU, bool CONTIG>
 hipError_t encode_dispatch_dtype(const tq_config& cfg, const EncodeArgs& a, hipStream_t s) {
   dim3 grid((unsigned)grid_for(a.n_groups, TQ_GRID_PER_CU)), block(kBlock);
   const bool in32 = cfg.x_dtype == TQ_F32, n32 = cfg.norm_dtype == TQ_F32;
+  if (cfg.flags & TQ_BLOCKS) {  // fp16 norms (checked on the host)
+    if (in32)
+      hipLaunchKernelGGL((encode_kernel<BITS, LPU, true, false, CONTIG, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((encode_kernel<BITS, LPU, false, false, CONTIG, true>), grid, block, 0, s, a);
+    return hipGetLastError();
+  }
   if constexpr (LPU == 1) {
     if (!in32) {
       if (n32)
@@ -720,10 +794,10 @@ hipError_t encode_dispatch_dtype(const tq_config& cfg, const EncodeArgs& a, hipS
       return hipGetLastError();
     }
   }
-  if (!in32 && !n32) hipLaunchKernelGGL((encode_kernel<BITS, LPU, false, false, CONTIG>), grid, block, 0, s, a);
-  if (!in32 && n32) hipLaunchKernelGGL((encode_kernel<BITS, LPU, false, true, CONTIG>), grid, block, 0, s, a);
-  if (in32 && !n32) hipLaunchKernelGGL((encode_kernel<BITS, LPU, true, false, CONTIG>), grid, block, 0, s, a);
-  if (in32 && n32) hipLaunchKernelGGL((encode_kernel<BITS, LPU, true, true, CONTIG>), grid, block, 0, s, a);
+  if (!in32 && !n32) hipLaunchKernelGGL((encode_kernel<BITS, LPU, false, false, CONTIG, false>), grid, block, 0, s, a);
+  if (!in32 && n32) hipLaunchKernelGGL((encode_kernel<BITS, LPU, false, true, CONTIG, false>), grid, block, 0, s, a);
+  if (in32 && !n32) hipLaunchKernelGGL((encode_kernel<BITS, LPU, true, false, CONTIG, false>), grid, block, 0, s, a);
+  if (in32 && n32) hipLaunchKernelGGL((encode_kernel<BITS, LPU, true, true, CONTIG, false>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
@@ -746,6 +820,13 @@ template <int BITS, int LPU, bool NC, bool CONTIG>
 hipError_t decode_dispatch_dtype(const tq_config& cfg, const DecodeArgs& a, tq_dtype yt, hipStream_t s) {
   dim3 grid((unsigned)grid_for(a.n_groups, LPU == 1 ? TQ_DEC_GRID_PER_CU : TQ_GRID_PER_CU)), block(kBlock);
   const bool o32 = yt == TQ_F32, n32 = cfg.norm_dtype == TQ_F32;
+  if (cfg.flags & TQ_BLOCKS) {  // fp16 norms (checked on the host)
+    if (o32)
+      hipLaunchKernelGGL((decode_kernel<BITS, LPU, true, false, NC, CONTIG, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<BITS, LPU, false, false, NC, CONTIG, true>), grid, block, 0, s, a);
+    return hipGetLastError();
+  }
   if constexpr (LPU == 1) {
     if (!o32 && !n32) hipLaunchKernelGGL((decode32_mfma_kernel<BITS, false, false, NC, CONTIG>), grid, block, 0, s, a);
     if (!o32 && n32) hipLaunchKernelGGL((decode32_mfma_kernel<BITS, false, true, NC, CONTIG>), grid, block, 0, s, a);
@@ -753,10 +834,10 @@ hipError_t decode_dispatch_dtype(const tq_config& cfg, const DecodeArgs& a, tq_d
     if (o32 && n32) hipLaunchKernelGGL((decode32_mfma_kernel<BITS, true, true, NC, CONTIG>), grid, block, 0, s, a);
     return hipGetLastError();
   }
-  if (!o32 && !n32) hipLaunchKernelGGL((decode_kernel<BITS, LPU, false, false, NC, CONTIG>), grid, block, 0, s, a);
-  if (!o32 && n32) hipLaunchKernelGGL((decode_kernel<BITS, LPU, false, true, NC, CONTIG>), grid, block, 0, s, a);
-  if (o32 && !n32) hipLaunchKernelGGL((decode_kernel<BITS, LPU, true, false, NC, CONTIG>), grid, block, 0, s, a);
-  if (o32 && n32) hipLaunchKernelGGL((decode_kernel<BITS, LPU, true, true, NC, CONTIG>), grid, block, 0, s, a);
+  if (!o32 && !n32) hipLaunchKernelGGL((decode_kernel<BITS, LPU, false, false, NC, CONTIG, false>), grid, block, 0, s, a);
+  if (!o32 && n32) hipLaunchKernelGGL((decode_kernel<BITS, LPU, false, true, NC, CONTIG, false>), grid, block, 0, s, a);
+  if (o32 && !n32) hipLaunchKernelGGL((decode_kernel<BITS, LPU, true, false, NC, CONTIG, false>), grid, block, 0, s, a);
+  if (o32 && n32) hipLaunchKernelGGL((decode_kernel<BITS, LPU, true, true, NC, CONTIG, false>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 

@@ -190,10 +190,15 @@ tq_status check_config(const tq_config* cfg, const char* who) {
   for (int i = 0; i < cfg->dt; ++i)
     if (cfg->signs[i] != 1.0f && cfg->signs[i] != -1.0f)
       return fail(TQ_ERR_INVALID_ARG, "%s: signs[%d] = %g is not +1 or -1", who, i, (double)cfg->signs[i]);
-  if (cfg->flags & ~(unsigned)(TQ_NORM_CORRECT | TQ_QJL))
+  if (cfg->flags & ~(unsigned)(TQ_NORM_CORRECT | TQ_QJL | TQ_BLOCKS))
     return fail(TQ_ERR_INVALID_ARG, "%s: unknown flag bits 0x%x", who, cfg->flags);
   if ((cfg->x_dtype != TQ_F16 && cfg->x_dtype != TQ_F32) || (cfg->norm_dtype != TQ_F16 && cfg->norm_dtype != TQ_F32))
     return fail(TQ_ERR_INVALID_ARG, "%s: dtype must be TQ_F16 or TQ_F32", who);
+  if (cfg->flags & TQ_BLOCKS) {
+    if (cfg->norm_dtype != TQ_F16)
+      return fail(TQ_ERR_INVALID_ARG, "%s: TQ_BLOCKS records carry fp16 norms (norm_dtype must be TQ_F16)", who);
+    if (cfg->flags & TQ_QJL) return fail(TQ_ERR_UNSUPPORTED, "%s: TQ_BLOCKS does not combine with TQ_QJL", who);
+  }
   if (cfg->flags & TQ_QJL) {
     if (cfg->head_dim != cfg->dt)
       return fail(TQ_ERR_UNSUPPORTED, "%s: QJL needs one unit per row (dt == head_dim)", who);
@@ -222,6 +227,20 @@ tq_status check_rows(const char* who, const char* name, const void* p, int64_t n
                 who, name);
   if (n_rows > (int64_t)(INT64_MAX / 4) / (ld * (int64_t)es))
     return fail(TQ_ERR_INVALID_ARG, "%s: %s size overflows", who, name);
+  return TQ_OK;
+}
+
+// codes / norms of tq_quantize and tq_dequantize: two planes, or records (TQ_BLOCKS)
+tq_status check_code_planes(const tq_config* cfg, const char* who, const void* codes, const void* norms) {
+  if (cfg->flags & TQ_BLOCKS) {
+    if (!codes || !aligned(codes, 16))
+      return fail(TQ_ERR_INVALID_ARG, "%s: TQ_BLOCKS records (codes) must be non-NULL, 16-byte aligned", who);
+    if (norms) return fail(TQ_ERR_INVALID_ARG, "%s: with TQ_BLOCKS the norms live in the records; pass NULL", who);
+    return TQ_OK;
+  }
+  if (!codes || !aligned(codes, 4)) return fail(TQ_ERR_INVALID_ARG, "%s: codes must be non-NULL, 4-byte aligned", who);
+  if (!norms || !aligned(norms, esize(cfg->norm_dtype)))
+    return fail(TQ_ERR_INVALID_ARG, "%s: norms must be non-NULL and aligned to its element size", who);
   return TQ_OK;
 }
 
@@ -364,9 +383,7 @@ tq_status tq_quantize(const tq_config* cfg, const void* x, int64_t n_rows, int64
   if (n_rows < 0) return fail(TQ_ERR_INVALID_ARG, "%s: n_rows < 0", who);
   if (n_rows == 0) return ok();
   if ((st = check_rows(who, "x", x, n_rows, ld_x, cfg->head_dim, esize(cfg->x_dtype)))) return st;
-  if (!codes || !aligned(codes, 4)) return fail(TQ_ERR_INVALID_ARG, "%s: codes must be non-NULL, 4-byte aligned", who);
-  if (!norms || !aligned(norms, esize(cfg->norm_dtype)))
-    return fail(TQ_ERR_INVALID_ARG, "%s: norms must be non-NULL and aligned to its element size", who);
+  if ((st = check_code_planes(cfg, who, codes, norms))) return st;
   hipStream_t s = (hipStream_t)stream;
   if (cfg->flags & TQ_QJL) {
     if ((st = check_params(cfg, who))) return st;
@@ -414,9 +431,7 @@ tq_status tq_dequantize(const tq_config* cfg, const uint8_t* codes, const void* 
   if (n_rows < 0) return fail(TQ_ERR_INVALID_ARG, "%s: n_rows < 0", who);
   if (n_rows == 0) return ok();
   if ((st = check_rows(who, "y", y, n_rows, ld_y, cfg->head_dim, esize(y_dtype)))) return st;
-  if (!codes || !aligned(codes, 4)) return fail(TQ_ERR_INVALID_ARG, "%s: codes must be non-NULL, 4-byte aligned", who);
-  if (!norms || !aligned(norms, esize(cfg->norm_dtype)))
-    return fail(TQ_ERR_INVALID_ARG, "%s: norms must be non-NULL and aligned to its element size", who);
+  if ((st = check_code_planes(cfg, who, codes, norms))) return st;
   hipStream_t s = (hipStream_t)stream;
   const bool nc = (cfg->flags & TQ_NORM_CORRECT) != 0;
   if (cfg->flags & TQ_QJL) {

@@ -7,6 +7,8 @@ models the pages measure on (their weights and corpora are not available):
   vectors_fp32   4096 random vectors, d = 128, fp32, N(0,1) entries, seed 0
   llama_1b_kv    16 layers x 8 KV heads x 2048 tokens x head_dim 64, fp16
   qwen3_8b_kv    36 layers x 8 KV heads x 16384 tokens x head_dim 128, fp16
+                 (sign vectors for 32-value blocks; qwen3_8b_kv_chunk128: the
+                 same tensors with sign vectors for 128-value chunks)
   qjl_keys       65536 keys x 128 fp16 (per-channel log-normal, no outliers),
                  4096 queries (32 heads x 128) ~ N(0,1) fp16, S: 128 x 128 N(0,1), seed 1
   decode_cache   1 layer x 4 KV heads x 131072 tokens x head_dim 256 fp16,
@@ -49,6 +51,10 @@ def llama_1b_kv(layers: int = 16, heads: int = 8, tokens: int = 2048, head_dim: 
 def qwen3_8b_kv(layers: int = 36, heads: int = 8, tokens: int = 16384, head_dim: int = 128, seed: int = SEED,
                 out_k=None, out_v=None):
     return kv_pair(layers, heads, tokens, head_dim, dt=32, seed=seed, out_k=out_k, out_v=out_v)
+
+
+def qwen3_8b_kv_chunk128(layers: int = 36, heads: int = 8, tokens: int = 16384, seed: int = SEED):
+    return kv_pair(layers, heads, tokens, 128, dt=128, seed=seed)
 
 
 def qjl_keys(n_keys: int = 65536, d: int = 128, n_queries: int = 4096, m: int = 128, seed: int = SEED):

@@ -132,6 +132,28 @@ def test_quantize_validation():
     assert "qjl_m" in tq.lib().tq_last_error().decode()
 
 
+def test_blocks_validation():
+    """TQ_BLOCKS: fp16 norms only, no QJL, 16-byte aligned records, norms must be NULL."""
+    E, U = tq.TQ_ERR_INVALID_ARG, tq.TQ_ERR_UNSUPPORTED
+    L = tq.lib()
+    qz = _q(dt=128, signs=np.ones(128), flags=tq.TQ_BLOCKS)
+    q = lambda codes=FAKE, norms=None: L.tq_quantize(ctypes.byref(qz.cfg), FAKE, 4, 128, codes, norms, None, None,
+                                                      None)
+    d = lambda codes=FAKE, norms=None: L.tq_dequantize(ctypes.byref(qz.cfg), codes, norms, None, None, 4, FAKE,
+                                                        tq.TQ_F16, 128, None)
+    assert q(norms=FAKE) == E and d(norms=FAKE) == E  # the norms live in the records
+    assert q(codes=FAKE + 4) == E and d(codes=FAKE + 8) == E  # records are 16-byte aligned
+    assert q(codes=None) == E and d(codes=None) == E
+    assert "NULL" in L.tq_last_error().decode()
+    bad = _q(dt=128, signs=np.ones(128), flags=tq.TQ_BLOCKS, norm_dtype=tq.TQ_F32)
+    assert L.tq_quantize(ctypes.byref(bad.cfg), FAKE, 4, 128, FAKE, None, None, None, None) == E
+    qj = _q(head_dim=128, dt=128, bits=2, signs=np.ones(128), flags=tq.TQ_QJL | tq.TQ_BLOCKS, qjl_m=128)
+    assert L.tq_quantize(ctypes.byref(qj.cfg), FAKE, 4, 128, FAKE, None, FAKE, FAKE, None) == U
+    # records are not an attention cache format
+    assert L.tq_decode_attn(ctypes.byref(qz.cfg), ctypes.byref(qz.cfg), FAKE, tq.TQ_F16, 4, 1, 8, FAKE, FAKE, FAKE,
+                            FAKE, 0.0, FAKE, FAKE, 1 << 20, None) == U
+
+
 def test_dequantize_validation():
     E, OK = tq.TQ_ERR_INVALID_ARG, tq.TQ_OK
     qz = _q()
