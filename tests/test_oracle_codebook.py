@@ -5,7 +5,11 @@ What pins it, besides itself:
   * the distortions printed in [Scratch] §3 (0.118 / 0.0345 / 0.0095 at 2/3/4 bits);
   * brute force: grid search (b = 1, 2) and direct numerical minimisation (b = 3)
     of the closed-form distortion land on the Lloyd fixed point;
-  * the closed-form distortion equals adaptive quadrature of the same integral.
+  * the closed-form distortion equals adaptive quadrature of the same integral;
+  * at 5-8 bits (root finding instead of the slow iteration): agreement with the
+    iteration at 5 bits, the conditional-mean fixed point, the approach of the
+    distortion to the high-resolution (Panter-Dite) limit, sampling, and local
+    optimality against random moves of the levels.
 
 The Beta-marginal codebook (exact law of a rotated unit vector's coordinate) is
 pinned by the uniform law at d = 3, the one-bit closed form E|T|, a Lloyd step
@@ -114,6 +118,58 @@ def test_scaling_to_dimension():
     cb = Codebook.build(3, 128)
     np.testing.assert_allclose(cb.levels * math.sqrt(128), cb.unit_levels, rtol=0, atol=1e-15)
     np.testing.assert_allclose(cb.bounds * math.sqrt(128), cb.unit_bounds, rtol=0, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# Many levels (8-bit keys of [Scratch] §10): the conditions solved by root finding.
+# ---------------------------------------------------------------------------
+from oracle.codebook import _lloyd_max_gaussian_iter, _lloyd_max_gaussian_root  # noqa: E402
+
+
+def test_root_solver_matches_the_iteration_at_five_bits():
+    lv_i, ed_i = _lloyd_max_gaussian_iter(5)
+    lv_r, ed_r = _lloyd_max_gaussian_root(5)
+    np.testing.assert_allclose(lv_r, lv_i, atol=1e-11)
+    np.testing.assert_allclose(ed_r, ed_i, atol=1e-11)
+
+
+@pytest.mark.parametrize("bits", [5, 6, 7, 8])
+def test_many_level_fixed_point(bits):
+    levels, edges = lloyd_max_gaussian(bits)
+    L = 1 << bits
+    assert levels.shape == (L,) and edges.shape == (L - 1,)
+    assert np.all(np.diff(levels) > 0)
+    np.testing.assert_array_equal(levels, -levels[::-1])
+    np.testing.assert_allclose(edges, 0.5 * (levels[:-1] + levels[1:]), atol=1e-15)
+    bnd = np.concatenate([[-np.inf], edges, [np.inf]])
+    mass = norm.sf(bnd[:-1]) - norm.sf(bnd[1:])
+    cond_mean = (norm.pdf(bnd[:-1]) - norm.pdf(bnd[1:])) / mass
+    np.testing.assert_allclose(cond_mean, levels, atol=1e-11)
+
+
+def test_distortion_tends_to_the_high_resolution_limit():
+    """Lloyd-Max distortion over the Panter-Dite value sqrt(3) pi / 2 * 4^-b (the [README]
+    bound column) rises monotonically towards 1 as the codebook grows."""
+    ratios = [Codebook.build(b, 128).distortion / (math.sqrt(3) * math.pi / 2 * 4.0 ** -b) for b in range(1, 9)]
+    assert all(b > a for a, b in zip(ratios, ratios[1:]))
+    assert 0.985 < ratios[-1] < 1.0
+
+
+def test_eight_bit_distortion_by_sampling_and_local_optimality():
+    """8 bits: the MSE of 2^21 N(0,1) samples matches the closed form within 4 standard errors,
+    and random small moves of the levels (edges kept at midpoints) never lower the distortion."""
+    import synth
+
+    cb = Codebook.build(8, 128)
+    x = synth.normal(3, 0, 1 << 21)
+    q = cb.unit_levels[np.searchsorted(cb.unit_bounds, x, side="left")]
+    err = (x - q) ** 2
+    assert abs(err.mean() - cb.distortion) < 4 * err.std(ddof=1) / math.sqrt(len(err))
+    rng = np.random.default_rng(8)
+    half = cb.unit_levels[128:]
+    for _ in range(20):
+        pos = np.sort(half + rng.normal(scale=1e-3, size=half.size) * np.diff(np.concatenate([[0.0], half])))
+        assert _sym_distortion(pos) >= cb.distortion - 1e-15
 
 
 # ---------------------------------------------------------------------------
