@@ -92,19 +92,21 @@ enum { TQ_OP_QJL_SCORES = 1, TQ_OP_DECODE_ATTN = 2 };
  * reads only these fields, so either solver below can feed any entry point.
  */
 typedef struct {
-  int bits;                     /* 1..4 */
+  int bits;                     /* 1..8 */
   int dim;                      /* transform length the codebook is scaled for */
-  double unit_centroids[16];    /* ascending, symmetric about 0 */
-  double unit_bounds[15];       /* midpoints of neighbouring centroids */
-  float centroids[16];          /* fp32(unit_centroids / sqrt(dim)) */
-  float bounds[15];             /* fp32(unit_bounds / sqrt(dim)) */
+  double unit_centroids[256];   /* ascending, symmetric about 0 */
+  double unit_bounds[255];      /* midpoints of neighbouring centroids */
+  float centroids[256];         /* fp32(unit_centroids / sqrt(dim)) */
+  float bounds[255];            /* fp32(unit_bounds / sqrt(dim)) */
   double distortion;            /* E[(X - Q(X))^2] for the unit-variance X the codebook was solved for */
 } tq_codebook;
 
 /*
  * Fill *out with the Lloyd-Max quantizer of N(0,1/dim) at `bits` bits.
- * Host only, float64 fixed-point iteration.  bits in 1..4, dim a power of two
- * in 2..4096.  Errors: TQ_ERR_INVALID_ARG.
+ * Host only, float64: Lloyd's fixed-point iteration up to 4 bits, Newton's
+ * method on the same conditions above (the 8-bit keys of [Scratch] §10;
+ * the quantize/dequantize kernels take 1..4 and 8 bits).  bits in 1..8, dim a
+ * power of two in 2..4096.  Errors: TQ_ERR_INVALID_ARG.
  */
 tq_status tq_codebook_init(tq_codebook* out, int bits, int dim);
 

@@ -34,9 +34,9 @@ class TqError(RuntimeError):
 
 
 class tq_codebook(ctypes.Structure):
-    _fields_ = [("bits", ctypes.c_int), ("dim", ctypes.c_int), ("unit_centroids", ctypes.c_double * 16),
-                ("unit_bounds", ctypes.c_double * 15), ("centroids", ctypes.c_float * 16),
-                ("bounds", ctypes.c_float * 15), ("distortion", ctypes.c_double)]
+    _fields_ = [("bits", ctypes.c_int), ("dim", ctypes.c_int), ("unit_centroids", ctypes.c_double * 256),
+                ("unit_bounds", ctypes.c_double * 255), ("centroids", ctypes.c_float * 256),
+                ("bounds", ctypes.c_float * 255), ("distortion", ctypes.c_double)]
 
 
 class tq_config(ctypes.Structure):

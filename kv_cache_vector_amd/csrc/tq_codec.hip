@@ -246,6 +246,23 @@ __device__ __forceinline__ float get_record(const uint16_t* r, uint32_t* word) {
 template <int BITS, int LPU, bool IN_F32, bool NORM_F32, bool CONTIG, bool AOS>
 __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
   static_assert(!(AOS && NORM_F32), "records carry fp16 norms");
+  static_assert(BITS <= 4 || BITS == 8, "1..4 or 8 bits");
+  constexpr bool B8 = BITS == 8;
+  // 8 bits: edges t_0 = -1 (sentinel below |u|), t_1..t_127, t_128 = +inf, and the number of
+  // edges below each bin of |u| (bins a third of the narrowest cell, so two neighbouring bins
+  // hold at most one edge)
+  __shared__ float edge8[B8 ? 132 : 1];
+  __shared__ uint8_t bin8[B8 ? kMaxBins8 : 1];
+  if constexpr (B8) {
+    for (int i = threadIdx.x; i < 129; i += kBlock) edge8[i] = i == 0 ? -1.0f : a.thr[i - 1];
+    for (int b = threadIdx.x; b < a.n_bins; b += kBlock) {
+      const float lo = (float)b / a.bin_scale;
+      int c = 0;
+      for (int i = 0; i < 127; ++i) c += a.thr[i] < lo ? 1 : 0;
+      bin8[b] = (uint8_t)c;
+    }
+    __syncthreads();
+  }
   constexpr int CH = IN_F32 ? 8 : 4;  // 16-byte chunks per group
   constexpr int PITCH = 16 * CH + 16;  // LDS bytes per staged group (padded against bank conflicts)
   __shared__ __attribute__((aligned(16))) uint8_t stage[kWaves][64 * PITCH];
@@ -306,8 +323,24 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
     uint32_t word[BITS];
 #pragma unroll
     for (int k = 0; k < BITS; ++k) word[k] = 0u;
+    if constexpr (B8) {
+      // bin of |u| = |yhat| / n (may be one off), then the two edges around the bin's count:
+      // magnitude = #{t_i < |u|} exactly, compared as |yhat| against t n like the narrow codes
+      const float kb = n > 0.0f ? a.bin_scale / n : 0.0f;
+      const float top = (float)(a.n_bins - 1);
 #pragma unroll
-    for (int j = 31; j >= 0; --j) code_chain<BITS>(word, j, v[j], T);
+      for (int j = 0; j < 32; ++j) {
+        const float ay = __builtin_fabsf(v[j]);
+        const int m0 = bin8[(int)__builtin_fminf(ay * kb, top)];
+        const float lo = edge8[m0], hi = edge8[m0 + 1];
+        const uint32_t mag = (uint32_t)(m0 + (ay > hi * n ? 1 : 0) - (ay <= lo * n ? 1 : 0));
+        const uint32_t code = ((__builtin_bit_cast(uint32_t, v[j]) >> 31) << 7) | (mag & 127u);
+        word[j >> 2] |= code << (8 * (j & 3));
+      }
+    } else {
+#pragma unroll
+      for (int j = 31; j >= 0; --j) code_chain<BITS>(word, j, v[j], T);
+    }
     if (n == 0.0f) {
 #pragma unroll
       for (int k = 0; k < BITS; ++k) word[k] = zero_unit_word<BITS>(k);
@@ -504,12 +537,20 @@ __device__ __forceinline__ uint32_t pair_key8(const uint32_t* word, int i) {
 template <int BITS, int LPU, bool OUT_F32, bool NORM_F32, bool NC, bool CONTIG, bool AOS>
 __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs a) {
   static_assert(!(AOS && NORM_F32), "records carry fp16 norms");
+  static_assert(BITS <= 4 || BITS == 8, "1..4 or 8 bits");
+  constexpr bool B8 = BITS == 8;
   constexpr int L = 1 << BITS;
   constexpr int CH = OUT_F32 ? 8 : 4;
   constexpr int PITCH = 16 * CH + 16;
   __shared__ __attribute__((aligned(16))) uint8_t stage[kWaves][64 * PITCH];
-  __shared__ float2 ptab[L * L];
-  fill_pair_table<BITS>(ptab, a.level);
+  // pair table (two codes -> first butterfly) for narrow codes; 8 bits: one level per code
+  __shared__ float2 ptab[B8 ? 1 : L * L];
+  __shared__ float lvl8[B8 ? 256 : 1];
+  if constexpr (B8) {
+    for (int e = threadIdx.x; e < 256; e += kBlock) lvl8[e] = a.level[e];
+  } else {
+    fill_pair_table<BITS>(ptab, a.level);
+  }
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint8_t* tile = stage[wave];
@@ -562,9 +603,16 @@ __global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs a) {
     float v[32];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float2 e = *reinterpret_cast<const float2*>(tabp + pair_key8<BITS>(word, i));
-      v[2 * i] = e.x;
-      v[2 * i + 1] = e.y;
+      if constexpr (B8) {
+        const uint32_t w = word[i >> 1] >> (16 * (i & 1));
+        const float ca = lvl8[w & 255u], cb = lvl8[(w >> 8) & 255u];
+        v[2 * i] = ca + cb;
+        v[2 * i + 1] = ca - cb;
+      } else {
+        const float2 e = *reinterpret_cast<const float2*>(tabp + pair_key8<BITS>(word, i));
+        v[2 * i] = e.x;
+        v[2 * i + 1] = e.y;
+      }
     }
     float scale;
     if constexpr (NC) {
@@ -785,7 +833,7 @@ hipError_t encode_dispatch_dtype(const tq_config& cfg, const EncodeArgs& a, hipS
       hipLaunchKernelGGL((encode_kernel<BITS, LPU, false, false, CONTIG, true>), grid, block, 0, s, a);
     return hipGetLastError();
   }
-  if constexpr (LPU == 1) {
+  if constexpr (LPU == 1 && BITS <= 4) {
     if (!in32) {
       if (n32)
         hipLaunchKernelGGL((encode32_mfma_kernel<BITS, true, CONTIG>), grid, block, 0, s, a);
@@ -827,7 +875,7 @@ hipError_t decode_dispatch_dtype(const tq_config& cfg, const DecodeArgs& a, tq_d
       hipLaunchKernelGGL((decode_kernel<BITS, LPU, false, false, NC, CONTIG, true>), grid, block, 0, s, a);
     return hipGetLastError();
   }
-  if constexpr (LPU == 1) {
+  if constexpr (LPU == 1 && BITS <= 4) {
     if (!o32 && !n32) hipLaunchKernelGGL((decode32_mfma_kernel<BITS, false, false, NC, CONTIG>), grid, block, 0, s, a);
     if (!o32 && n32) hipLaunchKernelGGL((decode32_mfma_kernel<BITS, false, true, NC, CONTIG>), grid, block, 0, s, a);
     if (o32 && !n32) hipLaunchKernelGGL((decode32_mfma_kernel<BITS, true, false, NC, CONTIG>), grid, block, 0, s, a);
@@ -867,7 +915,8 @@ hipError_t launch_encode(const tq_config& cfg, const EncodeArgs& a, hipStream_t 
     case 1: return encode_dispatch_lpu<1>(cfg, a, s);
     case 2: return encode_dispatch_lpu<2>(cfg, a, s);
     case 3: return encode_dispatch_lpu<3>(cfg, a, s);
-    default: return encode_dispatch_lpu<4>(cfg, a, s);
+    case 4: return encode_dispatch_lpu<4>(cfg, a, s);
+    default: return encode_dispatch_lpu<8>(cfg, a, s);
   }
 }
 
@@ -876,7 +925,8 @@ hipError_t launch_decode(const tq_config& cfg, const DecodeArgs& a, bool nc, tq_
     case 1: return decode_dispatch_lpu<1>(cfg, a, nc, y_dtype, s);
     case 2: return decode_dispatch_lpu<2>(cfg, a, nc, y_dtype, s);
     case 3: return decode_dispatch_lpu<3>(cfg, a, nc, y_dtype, s);
-    default: return decode_dispatch_lpu<4>(cfg, a, nc, y_dtype, s);
+    case 4: return decode_dispatch_lpu<4>(cfg, a, nc, y_dtype, s);
+    default: return decode_dispatch_lpu<8>(cfg, a, nc, y_dtype, s);
   }
 }
 

@@ -51,6 +51,95 @@ double std_mass(double a, double b) {
   return 1.0 - 0.5 * std::erfc(-a * M_SQRT1_2) - 0.5 * std::erfc(b * M_SQRT1_2);
 }
 
+// Lloyd-Max for N(0,1) at many levels (5..8 bits).  Lloyd's iteration contracts
+// ever more slowly as L grows, so the fixed point of the non-negative half is
+// found by Newton's method on G_i(c) = c_i - E[X | e_i < X < e_{i+1}], with
+// e_0 = 0, e_i = (c_{i-1} + c_i)/2 and e_h = +inf.  The Jacobian is
+// tridiagonal: with m_i the conditional mean and P_i the cell mass,
+//   dm_i/de_i = phi(e_i)(m_i - e_i)/P_i,  dm_i/de_{i+1} = phi(e_{i+1})(e_{i+1} - m_i)/P_i.
+// Start: the high-resolution point density, proportional to phi^(1/3), i.e.
+// edges at the quantiles of N(0, 3) (inverse normal CDF by bisection on erfc).
+// Steps are halved while they would break the ordering or raise the residual.
+bool solve_lloyd_max_newton(int bits, double* levels, double* edges, double* distortion) {
+  const int h = 1 << (bits - 1), L = 2 * h;
+  auto upper_tail = [](double x) { return std::isinf(x) ? 0.0 : 0.5 * std::erfc(x * M_SQRT1_2); };
+  auto inv_upper_tail = [&](double p) {  // x >= 0 with P(X > x) = p, p in (0, 1/2]
+    double lo = 0.0, hi = 40.0;
+    for (int it = 0; it < 200; ++it) {
+      const double mid = 0.5 * (lo + hi);
+      (upper_tail(mid) > p ? lo : hi) = mid;
+    }
+    return 0.5 * (lo + hi);
+  };
+  std::vector<double> c(h), e(h + 1), m(h), P(h), G(h), a(h), b(h), d(h), rhs(h), nc(h);
+  auto edges_of = [&](const std::vector<double>& cc) {
+    e[0] = 0.0;
+    for (int i = 1; i < h; ++i) e[i] = 0.5 * (cc[i - 1] + cc[i]);
+    e[h] = INFINITY;
+  };
+  auto residual = [&](const std::vector<double>& cc) {
+    edges_of(cc);
+    double worst = 0.0;
+    for (int i = 0; i < h; ++i) {
+      P[i] = upper_tail(e[i]) - upper_tail(e[i + 1]);
+      m[i] = (std_pdf(e[i]) - std_pdf(e[i + 1])) / P[i];
+      G[i] = cc[i] - m[i];
+      worst = std::max(worst, std::fabs(G[i]));
+    }
+    return worst;
+  };
+  for (int i = 0; i <= h; ++i) e[i] = i == h ? INFINITY : std::sqrt(3.0) * inv_upper_tail(0.5 * (1.0 - (double)i / h));
+  for (int i = 0; i < h; ++i) c[i] = (std_pdf(e[i]) - std_pdf(e[i + 1])) / (upper_tail(e[i]) - upper_tail(e[i + 1]));
+  double res = residual(c);
+  for (int it = 0; it < 100 && res > 1e-15; ++it) {
+    // tridiagonal J: sub a[i] = dG_i/dc_{i-1}, diag d[i], super b[i] = dG_i/dc_{i+1}
+    for (int i = 0; i < h; ++i) {
+      const double dlo = i >= 1 ? std_pdf(e[i]) * (m[i] - e[i]) / P[i] : 0.0;
+      const double dhi = i + 1 < h ? std_pdf(e[i + 1]) * (e[i + 1] - m[i]) / P[i] : 0.0;
+      a[i] = -0.5 * dlo;
+      b[i] = -0.5 * dhi;
+      d[i] = 1.0 - 0.5 * dlo - 0.5 * dhi;
+      rhs[i] = -G[i];
+    }
+    for (int i = 1; i < h; ++i) {  // Thomas algorithm
+      const double w = a[i] / d[i - 1];
+      d[i] -= w * b[i - 1];
+      rhs[i] -= w * rhs[i - 1];
+    }
+    std::vector<double> delta(h);
+    delta[h - 1] = rhs[h - 1] / d[h - 1];
+    for (int i = h - 2; i >= 0; --i) delta[i] = (rhs[i] - b[i] * delta[i + 1]) / d[i];
+    double step = 1.0, new_res = INFINITY;
+    for (int tries = 0; tries < 60; ++tries, step *= 0.5) {
+      bool ordered = true;
+      for (int i = 0; i < h; ++i) {
+        nc[i] = c[i] + step * delta[i];
+        if (nc[i] <= (i ? nc[i - 1] : 0.0)) ordered = false;
+      }
+      if (!ordered) continue;
+      new_res = residual(nc);
+      if (new_res < res || new_res <= 1e-15) break;
+    }
+    if (!(new_res < INFINITY)) return false;
+    const bool progress = new_res < res;
+    c = nc;
+    res = residual(c);
+    if (!progress) break;  // at the rounding floor
+  }
+  if (!(res < 1e-12)) return false;
+  edges_of(c);
+  double sum = 0.0;
+  for (int i = 0; i < h; ++i) {
+    levels[h + i] = c[i];
+    levels[h - 1 - i] = -c[i];
+    sum += 2.0 * (upper_tail(e[i]) - upper_tail(e[i + 1])) * c[i] * c[i];
+  }
+  for (int k = 0; k + 1 < L; ++k) edges[k] = 0.5 * (levels[k] + levels[k + 1]);
+  edges[h - 1] = 0.0;
+  *distortion = 1.0 - sum;
+  return true;
+}
+
 struct GaussCell {
   // mass and first moment of N(0,1) over (a, b)
   void operator()(double a, double b, double* m0, double* m1) const {
@@ -180,8 +269,8 @@ tq_status check_config(const tq_config* cfg, const char* who) {
   if (cfg->head_dim <= 0 || cfg->head_dim % cfg->dt || cfg->head_dim > 65536)
     return fail(TQ_ERR_INVALID_ARG, "%s: head_dim (%d) must be a positive multiple of dt (%d), <= 65536", who,
                 cfg->head_dim, cfg->dt);
-  if (cfg->bits < 1 || cfg->bits > 4)
-    return fail(TQ_ERR_UNSUPPORTED, "%s: bits must be 1..4 (got %d)", who, cfg->bits);
+  if ((cfg->bits < 1 || cfg->bits > 4) && cfg->bits != 8)
+    return fail(TQ_ERR_UNSUPPORTED, "%s: bits must be 1..4 or 8 (got %d)", who, cfg->bits);
   if (!cfg->cb) return fail(TQ_ERR_INVALID_ARG, "%s: codebook is NULL", who);
   if (cfg->cb->bits != cfg->bits || cfg->cb->dim != cfg->dt)
     return fail(TQ_ERR_INVALID_ARG, "%s: codebook (bits %d, dim %d) does not match config (bits %d, dt %d)", who,
@@ -200,6 +289,7 @@ tq_status check_config(const tq_config* cfg, const char* who) {
     if (cfg->flags & TQ_QJL) return fail(TQ_ERR_UNSUPPORTED, "%s: TQ_BLOCKS does not combine with TQ_QJL", who);
   }
   if (cfg->flags & TQ_QJL) {
+    if (cfg->bits > 4) return fail(TQ_ERR_UNSUPPORTED, "%s: QJL takes a 1..4-bit MSE stage (got %d)", who, cfg->bits);
     if (cfg->head_dim != cfg->dt)
       return fail(TQ_ERR_UNSUPPORTED, "%s: QJL needs one unit per row (dt == head_dim)", who);
     if (cfg->qjl_m < 32 || cfg->qjl_m > 256 || cfg->qjl_m % 32)
@@ -252,22 +342,39 @@ void fill_dbits(const tq_config& cfg, uint32_t* dbits) {
 
 // N(0,1) centroid of each stored code: code = s << (b-1) | m, with the
 // positive half's m-th level for s = 0 and its negative for s = 1.
-template <typename T>
-void fill_levels(const tq_codebook& cb, T* level) {
+template <typename T, int N>
+void fill_levels(const tq_codebook& cb, T (&level)[N]) {
   const int L = 1 << cb.bits, h = L / 2;
-  for (int code = 0; code < 16; ++code) level[code] = 0;
-  for (int code = 0; code < L; ++code) {
+  for (int code = 0; code < N; ++code) level[code] = 0;
+  for (int code = 0; code < L && code < N; ++code) {
     int s = code >> (cb.bits - 1), m = code & (h - 1);
     int idx = s ? h - 1 - m : h + m;
     level[code] = (T)cb.unit_centroids[idx];
   }
 }
 
-template <typename T>
-void fill_thr(const tq_codebook& cb, T* thr) {
+template <typename T, int N>
+void fill_thr(const tq_codebook& cb, T (&thr)[N]) {
   const int L = 1 << cb.bits, h = L / 2;
-  for (int k = 0; k < 8; ++k) thr[k] = (T)INFINITY;
-  for (int k = 0; k + 1 < h; ++k) thr[k] = (T)cb.unit_bounds[h + k];  // edges above 0, ascending
+  for (int k = 0; k < N; ++k) thr[k] = (T)INFINITY;
+  for (int k = 0; k + 1 < h && k < N; ++k) thr[k] = (T)cb.unit_bounds[h + k];  // edges above 0, ascending
+}
+
+// Bucket index of the 8-bit encoder: |u| (unit scale) is binned uniformly with
+// bins a third of the narrowest cell, so that any two neighbouring bins hold at
+// most one cell edge; a table gives the number of edges below each bin, and two
+// comparisons against the edges next to that count fix the exact cell even if
+// the bin was computed one off.
+void fill_bins(const tq_codebook& cb, tq::EncodeArgs& a) {
+  a.bin_scale = 0.0f;
+  a.n_bins = 0;
+  if (cb.bits != 8) return;
+  const int h = 128;
+  double w = cb.unit_bounds[h];  // the cell [0, t_1]
+  for (int k = 1; k + 1 < h; ++k) w = std::min(w, cb.unit_bounds[h + k] - cb.unit_bounds[h + k - 1]);
+  const double scale = 3.0 / w;
+  a.bin_scale = (float)scale;
+  a.n_bins = (int32_t)std::ceil((cb.unit_bounds[2 * h - 2] + w) * scale) + 1;
 }
 
 void fwht_inplace(double* v, int d) {
@@ -313,13 +420,17 @@ extern "C" {
 
 tq_status tq_codebook_init(tq_codebook* out, int bits, int dim) {
   if (!out) return fail(TQ_ERR_INVALID_ARG, "tq_codebook_init: out is NULL");
-  if (bits < 1 || bits > 4) return fail(TQ_ERR_INVALID_ARG, "tq_codebook_init: bits must be 1..4 (got %d)", bits);
+  if (bits < 1 || bits > 8) return fail(TQ_ERR_INVALID_ARG, "tq_codebook_init: bits must be 1..8 (got %d)", bits);
   if (!is_pow2(dim) || dim < 2 || dim > 4096)
     return fail(TQ_ERR_INVALID_ARG, "tq_codebook_init: dim must be a power of two in 2..4096 (got %d)", dim);
   std::memset(out, 0, sizeof(*out));
   out->bits = bits;
   out->dim = dim;
-  solve_lloyd_max(bits, GaussCell{}, 3.0, out->unit_centroids, out->unit_bounds, &out->distortion);
+  if (bits <= 4) {
+    solve_lloyd_max(bits, GaussCell{}, 3.0, out->unit_centroids, out->unit_bounds, &out->distortion);
+  } else if (!solve_lloyd_max_newton(bits, out->unit_centroids, out->unit_bounds, &out->distortion)) {
+    return fail(TQ_ERR_INVALID_ARG, "tq_codebook_init: the %d-bit Lloyd-Max solve did not converge", bits);
+  }
   scale_codebook(out);
   return ok();
 }
@@ -416,6 +527,10 @@ tq_status tq_quantize(const tq_config* cfg, const void* x, int64_t n_rows, int64
   a.contiguous = ld_x == cfg->head_dim;
   fill_dbits(*cfg, a.dbits);
   fill_thr(*cfg->cb, a.thr);
+  fill_bins(*cfg->cb, a);
+  if (a.n_bins > tq::kMaxBins8)
+    return fail(TQ_ERR_INVALID_ARG, "%s: the 8-bit codebook's narrowest cell needs %d bins (max %d)", who, a.n_bins,
+                tq::kMaxBins8);
   hipError_t e = tq::launch_encode(*cfg, a, s);
   if (e != hipSuccess) return hip_fail(e, who);
   return ok();

@@ -21,8 +21,12 @@ struct EncodeArgs {
   int32_t groups_per_row;  // head_dim / 32
   int32_t contiguous;      // ld_x == head_dim
   uint32_t dbits[8];       // D: bit c%32 of word c/32 set when D_c = -1
-  float thr[8];            // positive N(0,1) cell edges t_1 < t_2 < ... (the edge at 0 is implicit)
+  float thr[128];          // positive N(0,1) cell edges t_1 < t_2 < ... (the edge at 0 is implicit), then +inf
+  float bin_scale;         // 8 bits: bins per unit of |u| (N(0,1) scale)
+  int32_t n_bins;          // 8 bits: number of bins (<= kMaxBins8)
 };
+
+constexpr int kMaxBins8 = 1024;
 
 // Arguments of the decode kernel.
 struct DecodeArgs {
@@ -34,7 +38,7 @@ struct DecodeArgs {
   int32_t groups_per_row;
   int32_t contiguous;
   uint32_t dbits[8];
-  float level[16];   // N(0,1) centroid of each stored code (sign-magnitude order)
+  float level[256];  // N(0,1) centroid of each stored code (sign-magnitude order)
   float inv_dt;      // 1 / dt
   float inv_sqrt_dt; // 1 / sqrt(dt)
 };
@@ -113,7 +117,7 @@ struct AttnArgs {
   int32_t wg_per_head;
   int64_t tokens_per_wg;
   uint32_t kdbits, vdbits;   // D_K, D_V of the 32-long blocks
-  float klevel[16], vlevel[16];
+  float klevel[256], vlevel[16];
   float kscale;              // softmax scale / sqrt(32): score = kscale * sum_b n_b <H D q_b, c_b>
 };
 

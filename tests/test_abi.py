@@ -34,14 +34,17 @@ def test_library_exports_every_declared_symbol():
     assert names == set(tq.EXPORTED)
 
 
-@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("dim", [32, 64, 128, 256])
 def test_host_codebook_matches_oracle(bits, dim):
+    """Up to 4 bits both sides iterate Lloyd's conditions; above, the host runs Newton's method and
+    the oracle MINPACK's hybrid root finder on them (agreement limited by the conditioning)."""
     cb = tq.tq_codebook_init(bits, dim)
     orc = Codebook.build(bits, dim)
     L = 1 << bits
-    np.testing.assert_allclose(np.array(cb.unit_centroids[:L]), orc.unit_levels, atol=1e-12, rtol=0)
-    np.testing.assert_allclose(np.array(cb.unit_bounds[:L - 1]), orc.unit_bounds, atol=1e-12, rtol=0)
+    tol = 1e-12 if bits <= 4 else 1e-10
+    np.testing.assert_allclose(np.array(cb.unit_centroids[:L]), orc.unit_levels, atol=tol, rtol=0)
+    np.testing.assert_allclose(np.array(cb.unit_bounds[:L - 1]), orc.unit_bounds, atol=tol, rtol=0)
     np.testing.assert_array_equal(np.array(cb.centroids[:L], dtype=np.float32), orc.levels.astype(np.float32))
     np.testing.assert_array_equal(np.array(cb.bounds[:L - 1], dtype=np.float32), orc.bounds.astype(np.float32))
     assert cb.distortion == pytest.approx(orc.distortion, abs=1e-12)
@@ -78,7 +81,7 @@ def test_codebook_init_rejects_bad_arguments():
     cb = tq.tq_codebook()
     L = tq.lib()
     assert L.tq_codebook_init(ctypes.byref(cb), 0, 32) == tq.TQ_ERR_INVALID_ARG
-    assert L.tq_codebook_init(ctypes.byref(cb), 5, 32) == tq.TQ_ERR_INVALID_ARG
+    assert L.tq_codebook_init(ctypes.byref(cb), 9, 32) == tq.TQ_ERR_INVALID_ARG
     assert L.tq_codebook_init(ctypes.byref(cb), 3, 48) == tq.TQ_ERR_INVALID_ARG
     assert L.tq_codebook_init(None, 3, 32) == tq.TQ_ERR_INVALID_ARG
 
@@ -130,6 +133,13 @@ def test_quantize_validation():
     qj.cfg.qjl_m = 100
     assert _quantize(qj, bits=FAKE, rnorm=FAKE) == E
     assert "qjl_m" in tq.lib().tq_last_error().decode()
+    qj8 = _q(head_dim=128, dt=128, bits=8, signs=np.ones(128), flags=tq.TQ_QJL, qjl_m=128)
+    qj8.cfg.qjl_params = FAKE
+    assert _quantize(qj8, bits=FAKE, rnorm=FAKE) == U  # the QJL stage takes a 1..4-bit MSE stage
+    for b in (5, 6, 7):
+        bad = _q()
+        bad.cfg.bits = b
+        assert _quantize(bad) == U
 
 
 def test_blocks_validation():

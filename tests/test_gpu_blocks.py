@@ -77,7 +77,7 @@ def _case(x, dt, bits, seed, nc=False, ld=None, codebook="gaussian"):
     return stats, qz, rec, orc, signs, cb
 
 
-@pytest.mark.parametrize("hd,bits", [(128, 3), (128, 4), (256, 3), (256, 4), (128, 1), (128, 2)])
+@pytest.mark.parametrize("hd,bits", [(128, 3), (128, 4), (256, 3), (256, 4), (128, 1), (128, 2), (128, 8)])
 def test_fork_layout_chunk128(hd, bits):
     """dt = 128: the fork's turbo layout (a 256 head is two chunks, each with its own norm)."""
     n_rows = 333  # 333 * hd/32 records: full waves plus a partial one
@@ -86,7 +86,7 @@ def test_fork_layout_chunk128(hd, bits):
     print(stats)
 
 
-@pytest.mark.parametrize("dt,bits", [(32, 3), (32, 4), (64, 2), (256, 3)])
+@pytest.mark.parametrize("dt,bits", [(32, 3), (32, 4), (64, 2), (256, 3), (32, 8)])
 def test_records_other_units(dt, bits):
     hd, n_rows = 256, 201
     x = synth.kv_tensor(dt * bits, 1, 1, 1, n_rows, hd).reshape(n_rows, hd)
