@@ -53,6 +53,7 @@ typedef __attribute__((address_space(3))) short lds_short;
 constexpr int kWaves = 4;
 constexpr int kTile = 64;     // tokens per tile
 constexpr int kMergeLanes = 8;
+constexpr float kSlack = 8.0f;  // softmax weights relative to the running reference stay below e^8
 
 __device__ __forceinline__ uint32_t pack_h2(_Float16 lo, _Float16 hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
@@ -109,7 +110,7 @@ template <int NBW, int KB, int VB, int NC>
 struct TileRegs {
   uint32_t kw[NBW][4][2];  // K: 2 words covering this lane's 8 coordinates, per owned block and subtile
   uint32_t kn[NC];         // K norms (fp16) of the token this lane scales, per accumulator; NBW halves
-  uint32_t vw[NBW][VB];    // V: whole record of token `lane`, per owned block
+  uint32_t vw[NBW * VB];   // V: whole records of token `lane`, owned blocks in order
   uint32_t vn;             // V norms (fp16) of token `lane`, NBW halves
 };
 
@@ -207,10 +208,9 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   const int b0 = NBW * wave;  // first owned block
 
   // this lane's K window: bits [24g, 24g + 24) of a 3-bit record, from the 8 bytes at word
-  // kword (0, 0, 1, 1 for g = 0..3) by a funnel shift of 0, 24, 16 or 40 bits (the last one
-  // takes the high word alone), or word g of a 4-bit record
+  // kword (0, 0, 1, 1 for g = 0..3) shifted right by 0, 24, 16 or 40 bits, or word g of a 4-bit record
   const int kword = KB == 4 ? g : (g >= 2 ? 1 : 0);
-  const int kshift = KB == 4 ? 0 : (24 * g) & 31;
+  const int kshift = KB == 4 ? 0 : 24 * g - 32 * kword;
   // token (within the tile) whose K norm scales accumulator cc in this lane
   auto ktok = [&](int cc) { return 16 * (cc * S + (4 * g) / GP) + row; };
 
@@ -220,39 +220,60 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   const int64_t t_step = (int64_t)a.wg_per_head * kTile;
 
   using Regs = TileRegs<NBW, KB, VB, NC>;
+  // Loads address a tile through uniform base pointers plus 32-bit per-lane offsets; the token of
+  // an offset is clamped to the last token of the head (only the final tile has tokens past it).
+  constexpr uint32_t KREC = NB * 4 * KB, VREC = NB * 4 * VB;  // bytes per token
   auto load = [&](Regs& r, int64_t tb) {
+    const int64_t rem = T - 1 - tb;
+    const uint32_t last = rem < kTile ? (uint32_t)rem : (uint32_t)(kTile - 1);
+    const uint8_t* kt = kbase + tb * KREC;
+    const uint8_t* vt8 = vbase + tb * VREC;
+    const uint16_t* knt = knb + tb * NB;
+    const uint16_t* vnt = vnb + tb * NB;
 #pragma unroll
-    for (int bl = 0; bl < NBW; ++bl) {
+    for (int st = 0; st < 4; ++st) {
+      const uint32_t t = min((uint32_t)(16 * st + row), last);
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        int64_t t = tb + 16 * st + row;
-        t = t < T ? t : T - 1;
-        const uint32_t* rp = reinterpret_cast<const uint32_t*>(kbase + (t * NB + b0 + bl) * (4 * KB)) + kword;
+      for (int bl = 0; bl < NBW; ++bl) {
+        const uint32_t off = t * KREC + (uint32_t)((b0 + bl) * 4 * KB + 4 * kword);
         if (KB == 4) {
-          r.kw[bl][st][0] = rp[0];
+          r.kw[bl][st][0] = *reinterpret_cast<const uint32_t*>(kt + off);
           r.kw[bl][st][1] = 0u;
         } else {
-          const uint2 w = *reinterpret_cast<const uint2*>(rp);
-          r.kw[bl][st][0] = g == 3 ? w.y : w.x;
+          const uint2 w = *reinterpret_cast<const uint2*>(kt + off);
+          r.kw[bl][st][0] = w.x;  // raw words: nothing computed from a load before its use
           r.kw[bl][st][1] = w.y;
         }
       }
     }
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
-      int64_t t = tb + ktok(cc);
-      t = t < T ? t : T - 1;
-      r.kn[cc] = NBW == 2 ? *reinterpret_cast<const uint32_t*>(knb + t * NB + b0) : (uint32_t)knb[t * NB + b0];
+      const uint32_t t = min((uint32_t)ktok(cc), last);
+      r.kn[cc] = NBW == 2 ? *reinterpret_cast<const uint32_t*>(knt + t * NB + b0) : (uint32_t)knt[t * NB + b0];
     }
-    int64_t t = tb + lane;
-    t = t < T ? t : T - 1;
+    const uint32_t t = min((uint32_t)lane, last);
+    const uint32_t* rp = reinterpret_cast<const uint32_t*>(vt8 + t * VREC + (uint32_t)(b0 * 4 * VB));
+    if constexpr (NBW * VB % 4 == 0) {  // 16-byte aligned whole quads
 #pragma unroll
-    for (int bl = 0; bl < NBW; ++bl) {
-      const uint32_t* rp = reinterpret_cast<const uint32_t*>(vbase + (t * NB + b0 + bl) * (4 * VB));
+      for (int q = 0; q < NBW * VB / 4; ++q) {
+        const uint4 w = reinterpret_cast<const uint4*>(rp)[q];
+        r.vw[4 * q] = w.x;
+        r.vw[4 * q + 1] = w.y;
+        r.vw[4 * q + 2] = w.z;
+        r.vw[4 * q + 3] = w.w;
+      }
+    } else if constexpr (NBW * VB % 2 == 0) {  // 8-byte aligned pairs (24 B per token at 3 bits)
 #pragma unroll
-      for (int q = 0; q < VB; ++q) r.vw[bl][q] = rp[q];
+      for (int q = 0; q < NBW * VB / 2; ++q) {
+        const uint2 w = reinterpret_cast<const uint2*>(rp)[q];
+        r.vw[2 * q] = w.x;
+        r.vw[2 * q + 1] = w.y;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < NBW * VB; ++q) r.vw[q] = rp[q];
     }
-    r.vn = NBW == 2 ? *reinterpret_cast<const uint32_t*>(vnb + t * NB + b0) : (uint32_t)vnb[t * NB + b0];
+    r.vn = NBW == 2 ? *reinterpret_cast<const uint32_t*>(vnt + t * NB + b0) : (uint32_t)vnt[t * NB + b0];
   };
 
   float m_run[4], lsum[4];
@@ -267,13 +288,11 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
 
   _Float16* vtile = vt[wave];
   _Float16* ptile = pt[wave];
-  // three register sets in rotation keep two tiles of loads in flight behind the one in use
-  Regs ra, rb, rc;
-  if (t_begin < T) load(ra, t_begin);
-  if (t_begin + t_step < T) load(rb, t_begin + t_step);
+  // two register sets: the next tile's loads are in flight while the current one is consumed
+  Regs rs[2];
+  if (t_begin < T) load(rs[0], t_begin);
   int parity = 0;
-  auto tile = [&](const Regs& cur, Regs& fill, int64_t tb) {
-    if (tb + 2 * t_step < T) load(fill, tb + 2 * t_step);
+  auto tile = [&](const Regs& cur, int64_t tb) {
 
     // ---- value records of token `lane` -> V tile row `lane` (norm folded in, chunks swizzled)
 #pragma unroll
@@ -284,7 +303,8 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int pp = 0; pp < 16; ++pp) {
         const int pos = 2 * VB * pp, wi = pos >> 5, sh = pos & 31;
-        const uint32_t w = sh + 2 * VB <= 32 ? cur.vw[bl][wi] : __builtin_amdgcn_alignbit(cur.vw[bl][wi + 1], cur.vw[bl][wi], sh);
+        const uint32_t w = sh + 2 * VB <= 32 ? cur.vw[bl * VB + wi]
+                                             : __builtin_amdgcn_alignbit(cur.vw[bl * VB + wi + 1], cur.vw[bl * VB + wi], sh);
         const int s2 = sh + 2 * VB <= 32 ? sh : 0;
         const v2h c = __builtin_bit_cast(v2h, lut_word(vtab, w, s2, 2 * VB, LGCV, voff));
         o[pp] = __builtin_bit_cast(uint32_t, c * nv2);
@@ -313,8 +333,9 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int sv = 0; sv < S; ++sv) {
           const int st = cc * S + sv;
-          const uint32_t win = KB == 4 ? cur.kw[bl][st][0]
-                                       : __builtin_amdgcn_alignbit(cur.kw[bl][st][1], cur.kw[bl][st][0], kshift);
+          const uint32_t win =
+              KB == 4 ? cur.kw[bl][st][0]
+                      : (uint32_t)((((uint64_t)cur.kw[bl][st][1] << 32) | cur.kw[bl][st][0]) >> kshift);
           uint32_t bh[4], bo[4];
 #pragma unroll
           for (int pp = 0; pp < 4; ++pp) {
@@ -360,29 +381,43 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
       s[cc][3] = live ? v.w * a.kscale : -INFINITY;
     }
 
-    // ---- online softmax; register i of this lane belongs to head (4g + i) % GP
+    // ---- online softmax; register i of this lane belongs to head (4g + i) % GP.  The reference
+    // m_run of a head only moves when some score of the tile exceeds it by more than kSlack (always
+    // on the first tile): the weights exp(s - m_run) then stay below e^kSlack, well inside fp16, and
+    // most tiles skip the cross-lane maximum and the rescaling.  lsum holds this lane's share of the
+    // weight sum; the lanes of a head are summed once, after the last tile.
+    bool grow = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float mt = s[0][i];
 #pragma unroll
-      for (int cc = 1; cc < NC; ++cc) mt = fmaxf(mt, s[cc][i]);
-      mt = head_reduce<S, true>(mt);
-      const float m_new = fmaxf(m_run[i], mt);  // finite: every tile holds a live token
-      const float alpha = m_run[i] == -INFINITY ? 0.0f : __expf(m_run[i] - m_new);
-      float ps = 0.0f;
+      for (int cc = 0; cc < NC; ++cc) grow |= s[cc][i] > m_run[i] + kSlack;
+    }
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float mt = s[0][i];
+#pragma unroll
+        for (int cc = 1; cc < NC; ++cc) mt = fmaxf(mt, s[cc][i]);
+        mt = head_reduce<S, true>(mt);
+        const float m_new = fmaxf(m_run[i], mt);  // finite: every tile holds a live token
+        const float alpha = m_run[i] == -INFINITY ? 0.0f : __expf(m_run[i] - m_new);
+        lsum[i] *= alpha;
+        m_run[i] = m_new;
+#pragma unroll
+        for (int bl = 0; bl < NBW; ++bl) {
+          acc[bl][0][i] *= alpha;
+          acc[bl][1][i] *= alpha;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
       const int r = 4 * g + i, h = r % GP, sub = r / GP;
 #pragma unroll
       for (int cc = 0; cc < NC; ++cc) {
-        const float p = __expf(s[cc][i] - m_new);
-        ps += p;
+        const float p = __expf(s[cc][i] - m_run[i]);
+        lsum[i] += p;
         ptile[h * kTile + 16 * (cc * S + sub) + row] = (_Float16)p;
-      }
-      lsum[i] = lsum[i] * alpha + head_reduce<S, false>(ps);
-      m_run[i] = m_new;
-#pragma unroll
-      for (int bl = 0; bl < NBW; ++bl) {
-        acc[bl][0][i] *= alpha;
-        acc[bl][1][i] *= alpha;
       }
     }
     wave_sync();
@@ -412,12 +447,16 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
     wave_sync();
     parity ^= 1;
   };
-  for (int64_t tb = t_begin; tb < T; tb += 3 * t_step) {
-    tile(ra, rc, tb);
-    if (tb + t_step >= T) break;
-    tile(rb, ra, tb + t_step);
-    if (tb + 2 * t_step >= T) break;
-    tile(rc, rb, tb + 2 * t_step);
+  // Tiles go in pairs with no exit between them: a workgroup with an odd number of tiles ends on a
+  // tile past the end, whose tokens are all masked.  The prefetch is unconditional (a load aimed
+  // past the end reloads an earlier tile), so the same loads are in flight on every path into a
+  // tile and the wait for the current register set leaves the next one pending.
+  for (int64_t tb = t_begin; tb < T; tb += 2 * t_step) {
+    const int64_t t1 = tb + t_step, t2 = tb + 2 * t_step;
+    load(rs[1], t1 < T ? t1 : tb);
+    tile(rs[0], tb);
+    load(rs[0], t2 < T ? t2 : tb);
+    tile(rs[1], t1);
   }
 
   // ---- partial of this workgroup: part[kvh][wg][head][HD coordinates, max, sum]
@@ -433,6 +472,8 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
     }
   }
   // running max / sum of head h are held in register h % 4 of the lanes whose row group maps to h
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lsum[i] = head_reduce<S, false>(lsum[i]);
   if (wave == 0 && row == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
