@@ -132,14 +132,24 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   constexpr int CK = 1 << LGCK, CV = 1 << LGCV;
   // hi and lo tables one word apart from a 256-byte multiple: their lookups at the same entry stay
   // two ds_read_b32 into the operand registers instead of one ds_read2st64 into a register pair
-  __shared__ uint32_t ktab[2 * KL * KL * CK + 1];
+  constexpr int XSTR = kWaves * NC * 4 + 4;  // per-lane row of the score exchange (+4 breaks bank aliasing)
+  // One LDS block with the lookup tables first, so that their addresses fit the 16-bit immediate
+  // offset of ds_read and a lookup address is one and-or of the shifted code bits with the copy offset.
+  struct Smem {
+    uint32_t ktab[2 * KL * KL * CK + 1];
+    uint32_t vtab[VL * VL * CV];
+    __attribute__((aligned(16))) _Float16 vt[kWaves][kTile * VROW];
+    __attribute__((aligned(16))) _Float16 pt[kWaves][GP * kTile];
+    __attribute__((aligned(16))) float xs[2][64][XSTR];
+  };
+  __shared__ Smem sm;
+  uint32_t* ktab = sm.ktab;
   uint32_t* kth = ktab;
   uint32_t* ktl = ktab + KL * KL * CK + 1;
-  __shared__ uint32_t vtab[VL * VL * CV];
-  __shared__ __attribute__((aligned(16))) _Float16 vt[kWaves][kTile * VROW];
-  __shared__ __attribute__((aligned(16))) _Float16 pt[kWaves][GP * kTile];
-  constexpr int XSTR = kWaves * NC * 4 + 4;  // per-lane row of the score exchange (+4 breaks bank aliasing)
-  __shared__ __attribute__((aligned(16))) float xs[2][64][XSTR];
+  uint32_t* vtab = sm.vtab;
+  auto& vt = sm.vt;
+  auto& pt = sm.pt;
+  auto& xs = sm.xs;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = lane & 15, g = lane >> 4;
@@ -185,17 +195,21 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
     __syncthreads();
   }
 
-  // query operands of this lane: row `row` of subtile slot sv is head row % GP when row / GP == sv
-  // (the masked copies are formed at each use, which keeps 16/GP - 1 copies out of the registers)
-  v8h qh8[NBW], ql8[NBW];
+  // query operands of this lane, one masked copy per stacked subtile slot: row `row` of slot sv
+  // is head row % GP when row / GP == sv and zero otherwise
+  v8h qh8[NBW][S], ql8[NBW][S];
 #pragma unroll
   for (int bl = 0; bl < NBW; ++bl) {
     const int b = NBW * wave + bl;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float v = qf[(row % GP) * HD + 32 * b + 8 * g + j] * 0.17677669529663688f;  // 1/sqrt(32)
-      qh8[bl][j] = (_Float16)v;
-      ql8[bl][j] = (_Float16)(v - (float)qh8[bl][j]);
+      const _Float16 h = (_Float16)v, l = (_Float16)(v - (float)h);
+#pragma unroll
+      for (int sv = 0; sv < S; ++sv) {
+        qh8[bl][sv][j] = row / GP == sv ? h : (_Float16)0.0f;
+        ql8[bl][sv][j] = row / GP == sv ? l : (_Float16)0.0f;
+      }
     }
   }
   __syncthreads();  // query staging is overwritten by the V tiles below
@@ -344,10 +358,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
           }
           const v8h bhi = __builtin_bit_cast(v8h, make_uint4(bh[0], bh[1], bh[2], bh[3]));
           const v8h blo = __builtin_bit_cast(v8h, make_uint4(bo[0], bo[1], bo[2], bo[3]));
-          uint32_t on = row / GP == sv ? 0xFFFFFFFFu : 0u;
-          asm volatile("" : "+v"(on));  // opaque: the masked operands are not hoisted out of the loop
-          const v8h ah = __builtin_bit_cast(v8h, __builtin_bit_cast(u32x4, qh8[bl]) & on);
-          const v8h al = __builtin_bit_cast(v8h, __builtin_bit_cast(u32x4, ql8[bl]) & on);
+          const v8h ah = qh8[bl][sv], al = ql8[bl][sv];
           c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bhi, c, 0, 0, 0);
           c = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bhi, c, 0, 0, 0);
           c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, blo, c, 0, 0, 0);
