@@ -157,63 +157,6 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   const int G = a.group;
   const uint32_t koff = (uint32_t)(lane & (CK - 1)) * 4u, voff = (uint32_t)(lane & (CV - 1)) * 4u;
 
-  for (int x = tid; x < KL * KL * CK; x += 256) {
-    const int e = x / CK;
-    const float ca = a.klevel[e & (KL - 1)], cb = a.klevel[e >> KB];
-    const _Float16 ha = (_Float16)ca, hb = (_Float16)cb;
-    kth[x] = pack_h2(ha, hb);
-    ktl[x] = pack_h2((_Float16)(ca - (float)ha), (_Float16)(cb - (float)hb));
-  }
-  for (int x = tid; x < VL * VL * CV; x += 256) {
-    const int e = x / CV;
-    vtab[x] = pack_h2((_Float16)a.vlevel[e & (VL - 1)], (_Float16)a.vlevel[e >> VB]);
-  }
-
-  // rotated query blocks qhat_b = H D_K q_b / sqrt(32) of the group's heads (rows >= G zero),
-  // FWHT staged in fp32 over the V tile area
-  float* qf = reinterpret_cast<float*>(&vt[0][0]);
-  static_assert(sizeof(vt) >= sizeof(float) * GP * HD, "query staging fits the V tiles");
-  for (int e = tid; e < GP * HD; e += 256) {
-    const int r = e / HD, d = e % HD;
-    float v = 0.0f;
-    if (r < G) {
-      const int64_t off = (int64_t)(kvh * G + r) * HD + d;
-      v = a.q_f32 ? static_cast<const float*>(a.q)[off] : __half2float(static_cast<const __half*>(a.q)[off]);
-    }
-    qf[e] = ((a.kdbits >> (d & 31)) & 1u) ? -v : v;
-  }
-  __syncthreads();
-  for (int hb = 1; hb < 32; hb <<= 1) {
-    for (int e = tid; e < GP * HD / 2; e += 256) {
-      const int r = e / (HD / 2), rem = e % (HD / 2), b = rem / 16, p = rem % 16;
-      const int i = (p / hb) * 2 * hb + (p % hb);
-      float* blk = qf + r * HD + 32 * b;
-      const float x = blk[i], y = blk[i + hb];
-      blk[i] = x + y;
-      blk[i + hb] = x - y;
-    }
-    __syncthreads();
-  }
-
-  // query operands of this lane, one masked copy per stacked subtile slot: row `row` of slot sv
-  // is head row % GP when row / GP == sv and zero otherwise
-  v8h qh8[NBW][S], ql8[NBW][S];
-#pragma unroll
-  for (int bl = 0; bl < NBW; ++bl) {
-    const int b = NBW * wave + bl;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float v = qf[(row % GP) * HD + 32 * b + 8 * g + j] * 0.17677669529663688f;  // 1/sqrt(32)
-      const _Float16 h = (_Float16)v, l = (_Float16)(v - (float)h);
-#pragma unroll
-      for (int sv = 0; sv < S; ++sv) {
-        qh8[bl][sv][j] = row / GP == sv ? h : (_Float16)0.0f;
-        ql8[bl][sv][j] = row / GP == sv ? l : (_Float16)0.0f;
-      }
-    }
-  }
-  __syncthreads();  // query staging is overwritten by the V tiles below
-
   const int64_t T = a.n_tokens;
   const uint8_t* kbase = a.k_codes + (int64_t)kvh * T * NB * (4 * KB);
   const uint8_t* vbase = a.v_codes + (int64_t)kvh * T * NB * (4 * VB);
@@ -290,6 +233,68 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
     r.vn = NBW == 2 ? *reinterpret_cast<const uint32_t*>(vnt + t * NB + b0) : (uint32_t)vnt[t * NB + b0];
   };
 
+  // the first tile's loads go out before the tables and the query are set up, hiding their latency
+  Regs rs[2];
+  if (t_begin < T) load(rs[0], t_begin);
+
+
+  for (int x = tid; x < KL * KL * CK; x += 256) {
+    const int e = x / CK;
+    const float ca = a.klevel[e & (KL - 1)], cb = a.klevel[e >> KB];
+    const _Float16 ha = (_Float16)ca, hb = (_Float16)cb;
+    kth[x] = pack_h2(ha, hb);
+    ktl[x] = pack_h2((_Float16)(ca - (float)ha), (_Float16)(cb - (float)hb));
+  }
+  for (int x = tid; x < VL * VL * CV; x += 256) {
+    const int e = x / CV;
+    vtab[x] = pack_h2((_Float16)a.vlevel[e & (VL - 1)], (_Float16)a.vlevel[e >> VB]);
+  }
+
+  // rotated query blocks qhat_b = H D_K q_b / sqrt(32) of the group's heads (rows >= G zero),
+  // FWHT staged in fp32 over the V tile area
+  float* qf = reinterpret_cast<float*>(&vt[0][0]);
+  static_assert(sizeof(vt) >= sizeof(float) * GP * HD, "query staging fits the V tiles");
+  for (int e = tid; e < GP * HD; e += 256) {
+    const int r = e / HD, d = e % HD;
+    float v = 0.0f;
+    if (r < G) {
+      const int64_t off = (int64_t)(kvh * G + r) * HD + d;
+      v = a.q_f32 ? static_cast<const float*>(a.q)[off] : __half2float(static_cast<const __half*>(a.q)[off]);
+    }
+    qf[e] = ((a.kdbits >> (d & 31)) & 1u) ? -v : v;
+  }
+  __syncthreads();
+  for (int hb = 1; hb < 32; hb <<= 1) {
+    for (int e = tid; e < GP * HD / 2; e += 256) {
+      const int r = e / (HD / 2), rem = e % (HD / 2), b = rem / 16, p = rem % 16;
+      const int i = (p / hb) * 2 * hb + (p % hb);
+      float* blk = qf + r * HD + 32 * b;
+      const float x = blk[i], y = blk[i + hb];
+      blk[i] = x + y;
+      blk[i + hb] = x - y;
+    }
+    __syncthreads();
+  }
+
+  // query operands of this lane, one masked copy per stacked subtile slot: row `row` of slot sv
+  // is head row % GP when row / GP == sv and zero otherwise
+  v8h qh8[NBW][S], ql8[NBW][S];
+#pragma unroll
+  for (int bl = 0; bl < NBW; ++bl) {
+    const int b = NBW * wave + bl;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float v = qf[(row % GP) * HD + 32 * b + 8 * g + j] * 0.17677669529663688f;  // 1/sqrt(32)
+      const _Float16 h = (_Float16)v, l = (_Float16)(v - (float)h);
+#pragma unroll
+      for (int sv = 0; sv < S; ++sv) {
+        qh8[bl][sv][j] = row / GP == sv ? h : (_Float16)0.0f;
+        ql8[bl][sv][j] = row / GP == sv ? l : (_Float16)0.0f;
+      }
+    }
+  }
+  __syncthreads();  // query staging is overwritten by the V tiles below
+
   float m_run[4], lsum[4];
   v4f acc[NBW][2];
 #pragma unroll
@@ -302,9 +307,6 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
 
   _Float16* vtile = vt[wave];
   _Float16* ptile = pt[wave];
-  // two register sets: the next tile's loads are in flight while the current one is consumed
-  Regs rs[2];
-  if (t_begin < T) load(rs[0], t_begin);
   int parity = 0;
   auto tile = [&](const Regs& cur, int64_t tb) {
 
@@ -505,33 +507,39 @@ __global__ __launch_bounds__(256) void attn_merge(AttnArgs a) {
   const int n_part = a.wg_per_head;
   const int64_t stride = (int64_t)G * (HD + 2);
   const float* base = a.part + (int64_t)kvh * n_part * stride + (int64_t)r * (HD + 2);
-  __shared__ float red[kMergeLanes][33];
-  __shared__ float wmax[4];
-  float m = -INFINITY;
-  for (int p = tid; p < n_part; p += 256) m = fmaxf(m, base[p * stride + HD]);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  if ((tid & 63) == 0) wmax[tid >> 6] = m;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-  float acc = 0.0f, l = 0.0f;
+  __shared__ float red[kMergeLanes][34];
+  // one pass over this lane's partials with a running reference (the partials' own references
+  // differ; a larger one rescales what was summed so far)
+  float m = -INFINITY, acc = 0.0f, l = 0.0f;
 #pragma unroll 4
   for (int p = pl; p < n_part; p += kMergeLanes) {
     const float* pb = base + p * stride;
-    const float mp = pb[HD];
-    const float f = mp == -INFINITY ? 0.0f : __expf(mp - M);
-    acc = __builtin_fmaf(pb[32 * b + dl], f, acc);
-    l = __builtin_fmaf(pb[HD + 1], f, l);
+    const float mp = pb[HD], lp = pb[HD + 1], xp = pb[32 * b + dl];
+    // branch-free, so the loads of the unrolled iterations go out together (every partial has a
+    // finite reference: each workgroup scores at least one live token)
+    const float m_new = fmaxf(m, mp);
+    const float f_old = m == -INFINITY ? 0.0f : __expf(m - m_new), f_new = __expf(mp - m_new);
+    acc = __builtin_fmaf(xp, f_new, acc * f_old);
+    l = __builtin_fmaf(lp, f_new, l * f_old);
+    m = m_new;
   }
   red[pl][dl] = acc;
-  if (dl == 0) red[pl][32] = l;
+  if (dl == 0) {
+    red[pl][32] = l;
+    red[pl][33] = m;
+  }
   __syncthreads();
   if (pl == 0) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < kMergeLanes; ++q) M = fmaxf(M, red[q][33]);
     float s = 0.0f, ls = 0.0f;
 #pragma unroll
     for (int q = 0; q < kMergeLanes; ++q) {
-      s += red[q][dl];
-      ls += red[q][32];
+      const float mq = red[q][33];
+      const float f = mq == -INFINITY ? 0.0f : __expf(mq - M);
+      s = __builtin_fmaf(red[q][dl], f, s);
+      ls = __builtin_fmaf(red[q][32], f, ls);
     }
     // out = D_V * H_unnorm(acc) / (32 * l): butterflies across the 32 lanes of the first wave
     float v = s;
