@@ -123,6 +123,13 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   constexpr int KL = 1 << KB, VL = 1 << VB;
   constexpr int VROW = NBW * 32;    // fp16 per V tile row (one token, the wave's blocks)
   constexpr int NCH = 2 * NBW;      // 16-coordinate chunks per V tile row
+  // fp16 offset of 16-byte half k of chunk c in V tile row t.  Chunks are permuted by token bits
+  // above the rows that share 256 bytes of banks, and the halves by bit 3, so the 16 rows written
+  // by 16 consecutive lanes, and the rows read together by the transposing loads, use distinct banks.
+  constexpr int RB = NBW == 2 ? 1 : 2;
+  auto vslot = [](int t, int c, int k) {
+    return t * VROW + 8 * (2 * (c ^ ((t >> RB) & (NCH - 1))) + (k ^ ((t >> 3) & 1)));
+  };
   static_assert(NBW == 1 || NBW == 2, "head_dim 128 or 256");
 
   // Pair tables (two codes -> two fp16 levels, N(0,1) scale): K hi part, K lo part, V.  Each
@@ -328,9 +335,10 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int c = 2 * bl + half;
-        _Float16* dst = vtile + lane * VROW + 16 * (c ^ ((lane >> 1) & (NCH - 1)));
-        reinterpret_cast<uint4*>(dst)[0] = make_uint4(o[8 * half], o[8 * half + 1], o[8 * half + 2], o[8 * half + 3]);
-        reinterpret_cast<uint4*>(dst)[1] = make_uint4(o[8 * half + 4], o[8 * half + 5], o[8 * half + 6], o[8 * half + 7]);
+        *reinterpret_cast<uint4*>(vtile + vslot(lane, c, 0)) =
+            make_uint4(o[8 * half], o[8 * half + 1], o[8 * half + 2], o[8 * half + 3]);
+        *reinterpret_cast<uint4*>(vtile + vslot(lane, c, 1)) =
+            make_uint4(o[8 * half + 4], o[8 * half + 5], o[8 * half + 6], o[8 * half + 7]);
       }
     }
 
@@ -448,9 +456,9 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
           const int c = 2 * bl + nh;
           lds_short* base = (lds_short*)vtile;
           const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4s*)(base + t1 * VROW + 16 * (c ^ ((t1 >> 1) & (NCH - 1))) + 4 * (row & 3)));
+              (lds_v4s*)(base + vslot(t1, c, (row & 3) >> 1) + 4 * (row & 1)));
           const v4s r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4s*)(base + t2 * VROW + 16 * (c ^ ((t2 >> 1) & (NCH - 1))) + 4 * (row & 3)));
+              (lds_v4s*)(base + vslot(t2, c, (row & 3) >> 1) + 4 * (row & 1)));
           const v4h h1 = __builtin_bit_cast(v4h, r1), h2 = __builtin_bit_cast(v4h, r2);
           const v8h bv = {h1[0], h1[1], h1[2], h1[3], h2[0], h2[1], h2[2], h2[3]};
           acc[bl][nh] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc[bl][nh], 0, 0, 0);
