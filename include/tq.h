@@ -221,8 +221,10 @@ tq_status tq_qjl_scores(const tq_config* cfg, const void* q, tq_dtype q_dtype, i
  * with query head h reading KV head h / (n_q_heads / n_kv_heads) and k~, v~
  * the tq_dequantize reconstructions of the cached units.
  *   kcfg, vcfg  formats of K and V: block-32 layout (dt = 32), fp16 norms,
- *               3 or 4 bits each (K and V may differ), equal head_dim of 128
- *               or 256, no flags (TQ_ERR_UNSUPPORTED otherwise)
+ *               K at 3, 4 or 8 bits and V at 3 or 4 bits (K and V may differ;
+ *               8-bit keys with 4-bit values is the asymmetric allocation of
+ *               [Scratch] §4 "Finding 1" and §10 "Takeaways"), equal head_dim
+ *               of 128 or 256, no flags (TQ_ERR_UNSUPPORTED otherwise)
  *   q           device, [n_q_heads][head_dim] of q_dtype, contiguous
  *   n_q_heads   a multiple of n_kv_heads, at most 16 query heads per KV head
  *   k_codes, v_codes  device, 4-byte aligned, units in (kv head, token,

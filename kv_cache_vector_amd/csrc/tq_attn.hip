@@ -15,10 +15,11 @@
 // w*NB/4 ..), so each wave reads only its blocks' codes and keeps only their
 // accumulators.  Per tile:
 //   loads    next tile's K windows, K/V norms and V records go straight to
-//            registers one tile ahead (no staging buffer);
+//            registers one tile ahead (two register sets, no staging buffer);
 //   K side   per owned block, the 64 tokens form 4 subtiles of 16; each lane
 //            expands 8 coordinates of one token through an LDS pair table
-//            into fp16 hi/lo operands, and three v_mfma_f32_16x16x32_f16
+//            (8-bit keys: a one-code table, two lookups per pair) into fp16
+//            hi/lo operands, and three v_mfma_f32_16x16x32_f16
 //            (q_hi c_hi + q_lo c_hi + q_hi c_lo) give the block dot products
 //            to ~2^-22.  The query operand of subtile st is non-zero only in
 //            rows st*GP .. st*GP+GP-1 (GP = query heads padded to 4, 8 or 16),
@@ -26,7 +27,8 @@
 //            lane holding live scores; block norms scale it in fp32;
 //   exchange the waves' partial scores (over their own blocks) are summed
 //            through LDS, after which every wave holds the full scores;
-//   softmax  online (running max and sum) per query head;
+//   softmax  online per query head against a running reference that only
+//            moves when a score passes it by more than kSlack;
 //   V side   each lane expands one token's records (pair table, scaled by
 //            the block norm with one packed fp16 multiply per pair) into a
 //            wave-private LDS tile; ds_read_b64_tr_b16 returns four tokens of
@@ -135,7 +137,8 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   // Pair tables (two codes -> two fp16 levels, N(0,1) scale): K hi part, K lo part, V.  Each
   // entry is replicated in CK / CV copies interleaved at word granularity; lane l reads copy
   // l % C, so the random lookups of one instruction fall in distinct LDS banks.
-  constexpr int LGCK = KB == 3 ? 5 : 3, LGCV = VB == 3 ? 5 : 3;
+  constexpr bool K8 = KB == 8;  // 8-bit keys: one-code table of (hi, lo) pairs instead of pair tables
+  constexpr int LGCK = K8 ? 4 : (KB == 3 ? 5 : 3), LGCV = VB == 3 ? 5 : 3;
   constexpr int CK = 1 << LGCK, CV = 1 << LGCV;
   // hi and lo tables one word apart from a 256-byte multiple: their lookups at the same entry stay
   // two ds_read_b32 into the operand registers instead of one ds_read2st64 into a register pair
@@ -143,7 +146,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   // One LDS block with the lookup tables first, so that their addresses fit the 16-bit immediate
   // offset of ds_read and a lookup address is one and-or of the shifted code bits with the copy offset.
   struct Smem {
-    uint32_t ktab[2 * KL * KL * CK + 1];
+    uint32_t ktab[K8 ? KL * CK : 2 * KL * KL * CK + 1];
     uint32_t vtab[VL * VL * CV];
     __attribute__((aligned(16))) _Float16 vt[kWaves][kTile * VROW];
     __attribute__((aligned(16))) _Float16 pt[kWaves][GP * kTile];
@@ -152,7 +155,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   __shared__ Smem sm;
   uint32_t* ktab = sm.ktab;
   uint32_t* kth = ktab;
-  uint32_t* ktl = ktab + KL * KL * CK + 1;
+  uint32_t* ktl = ktab + (K8 ? 0 : KL * KL * CK + 1);
   uint32_t* vtab = sm.vtab;
   auto& vt = sm.vt;
   auto& pt = sm.pt;
@@ -172,9 +175,10 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   const int b0 = NBW * wave;  // first owned block
 
   // this lane's K window: bits [24g, 24g + 24) of a 3-bit record, from the 8 bytes at word
-  // kword (0, 0, 1, 1 for g = 0..3) shifted right by 0, 24, 16 or 40 bits, or word g of a 4-bit record
-  const int kword = KB == 4 ? g : (g >= 2 ? 1 : 0);
-  const int kshift = KB == 4 ? 0 : 24 * g - 32 * kword;
+  // kword (0, 0, 1, 1 for g = 0..3) shifted right by 0, 24, 16 or 40 bits; word g of a 4-bit
+  // record; words 2g, 2g + 1 (one byte per code) of an 8-bit record
+  const int kword = KB == 8 ? 2 * g : KB == 4 ? g : (g >= 2 ? 1 : 0);
+  const int kshift = KB == 3 ? 24 * g - 32 * kword : 0;
   // token (within the tile) whose K norm scales accumulator cc in this lane
   auto ktok = [&](int cc) { return 16 * (cc * S + (4 * g) / GP) + row; };
 
@@ -200,7 +204,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int bl = 0; bl < NBW; ++bl) {
         const uint32_t off = t * KREC + (uint32_t)((b0 + bl) * 4 * KB + 4 * kword);
-        if (KB == 4) {
+        if constexpr (KB == 4) {
           r.kw[bl][st][0] = *reinterpret_cast<const uint32_t*>(kt + off);
           r.kw[bl][st][1] = 0u;
         } else {
@@ -245,12 +249,20 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   if (t_begin < T) load(rs[0], t_begin);
 
 
-  for (int x = tid; x < KL * KL * CK; x += 256) {
-    const int e = x / CK;
-    const float ca = a.klevel[e & (KL - 1)], cb = a.klevel[e >> KB];
-    const _Float16 ha = (_Float16)ca, hb = (_Float16)cb;
-    kth[x] = pack_h2(ha, hb);
-    ktl[x] = pack_h2((_Float16)(ca - (float)ha), (_Float16)(cb - (float)hb));
+  if constexpr (K8) {
+    for (int x = tid; x < KL * CK; x += 256) {  // code -> (fp16 hi part, fp16 lo part)
+      const float c = a.klevel[x / CK];
+      const _Float16 h = (_Float16)c;
+      kth[x] = pack_h2(h, (_Float16)(c - (float)h));
+    }
+  } else {
+    for (int x = tid; x < KL * KL * CK; x += 256) {
+      const int e = x / CK;
+      const float ca = a.klevel[e & (KL - 1)], cb = a.klevel[e >> KB];
+      const _Float16 ha = (_Float16)ca, hb = (_Float16)cb;
+      kth[x] = pack_h2(ha, hb);
+      ktl[x] = pack_h2((_Float16)(ca - (float)ha), (_Float16)(cb - (float)hb));
+    }
   }
   for (int x = tid; x < VL * VL * CV; x += 256) {
     const int e = x / CV;
@@ -357,14 +369,26 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int sv = 0; sv < S; ++sv) {
           const int st = cc * S + sv;
-          const uint32_t win =
-              KB == 4 ? cur.kw[bl][st][0]
-                      : (uint32_t)((((uint64_t)cur.kw[bl][st][1] << 32) | cur.kw[bl][st][0]) >> kshift);
           uint32_t bh[4], bo[4];
+          if constexpr (K8) {
+            // two one-code lookups per pair; byte permutes gather the two hi and the two lo halves
 #pragma unroll
-          for (int pp = 0; pp < 4; ++pp) {
-            bh[pp] = lut_word(kth, win, 2 * KB * pp, 2 * KB, LGCK, koff);
-            bo[pp] = lut_word(ktl, win, 2 * KB * pp, 2 * KB, LGCK, koff);
+            for (int pp = 0; pp < 4; ++pp) {
+              const uint32_t w = cur.kw[bl][st][pp >> 1];
+              const uint32_t e0 = lut_word(kth, w, 16 * (pp & 1), 8, LGCK, koff);
+              const uint32_t e1 = lut_word(kth, w, 16 * (pp & 1) + 8, 8, LGCK, koff);
+              bh[pp] = __builtin_amdgcn_perm(e1, e0, 0x05040100u);
+              bo[pp] = __builtin_amdgcn_perm(e1, e0, 0x07060302u);
+            }
+          } else {
+            const uint32_t win =
+                KB == 4 ? cur.kw[bl][st][0]
+                        : (uint32_t)((((uint64_t)cur.kw[bl][st][1] << 32) | cur.kw[bl][st][0]) >> kshift);
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) {
+              bh[pp] = lut_word(kth, win, 2 * KB * pp, 2 * KB, LGCK, koff);
+              bo[pp] = lut_word(ktl, win, 2 * KB * pp, 2 * KB, LGCK, koff);
+            }
           }
           const v8h bhi = __builtin_bit_cast(v8h, make_uint4(bh[0], bh[1], bh[2], bh[3]));
           const v8h blo = __builtin_bit_cast(v8h, make_uint4(bo[0], bo[1], bo[2], bo[3]));
@@ -599,7 +623,9 @@ hipError_t launch_decode_attn(int kbits, int vbits, const AttnArgs& a, hipStream
   if (kbits == 3 && vbits == 3) return launch_bits<3, 3>(a, s);
   if (kbits == 4 && vbits == 4) return launch_bits<4, 4>(a, s);
   if (kbits == 3 && vbits == 4) return launch_bits<3, 4>(a, s);
-  return launch_bits<4, 3>(a, s);
+  if (kbits == 4 && vbits == 3) return launch_bits<4, 3>(a, s);
+  if (kbits == 8 && vbits == 3) return launch_bits<8, 3>(a, s);
+  return launch_bits<8, 4>(a, s);
 }
 
 }  // namespace tq

@@ -630,8 +630,9 @@ tq_status check_scores_config(const tq_config* cfg, const char* who) {
   return TQ_OK;
 }
 
-// Decode attention: block-32 K and V (fp16 norms, 3 or 4 bits, no QJL or norm
-// correction), head_dim 128 or 256, up to 16 query heads per KV head.
+// Decode attention: block-32 K and V (fp16 norms, K at 3, 4 or 8 bits, V at 3 or
+// 4 bits, no QJL or norm correction), head_dim 128 or 256, up to 16 query heads
+// per KV head.
 tq_status check_attn_config(const tq_config* kcfg, const tq_config* vcfg, int n_q_heads, int n_kv_heads,
                             int64_t n_tokens, const char* who) {
   tq_status st = check_config(kcfg, who);
@@ -642,8 +643,8 @@ tq_status check_attn_config(const tq_config* kcfg, const tq_config* vcfg, int n_
   if (kcfg->head_dim != vcfg->head_dim) return fail(TQ_ERR_INVALID_ARG, "%s: K and V head_dim differ", who);
   if (kcfg->dt != 32 || vcfg->dt != 32 || (kcfg->head_dim != 128 && kcfg->head_dim != 256))
     return fail(TQ_ERR_UNSUPPORTED, "%s: needs the block-32 layout (dt = 32) with head_dim 128 or 256", who);
-  if ((kcfg->bits != 3 && kcfg->bits != 4) || (vcfg->bits != 3 && vcfg->bits != 4))
-    return fail(TQ_ERR_UNSUPPORTED, "%s: K and V must be 3- or 4-bit", who);
+  if ((kcfg->bits != 3 && kcfg->bits != 4 && kcfg->bits != 8) || (vcfg->bits != 3 && vcfg->bits != 4))
+    return fail(TQ_ERR_UNSUPPORTED, "%s: K must be 3-, 4- or 8-bit and V 3- or 4-bit", who);
   if (kcfg->flags || vcfg->flags)
     return fail(TQ_ERR_UNSUPPORTED, "%s: QJL and norm correction are not supported in attention", who);
   if (kcfg->norm_dtype != TQ_F16 || vcfg->norm_dtype != TQ_F16)

@@ -143,6 +143,9 @@ def _data(seed, H, T, hd):
     (256, 2, 3, 1, 4, 3, np.float32),      # a single token, a group that is not a power of two
     (128, 1, 8, 5000, 4, 4, np.float16),   # several token ranges per KV head
     (256, 4, 4, 3000, 3, 3, np.float16),   # the decode workload's head layout at a short length
+    (128, 2, 4, 1000, 8, 4, np.float16),   # 8-bit keys, 4-bit values
+    (256, 2, 4, 2100, 8, 3, np.float32),   # 8-bit keys, 3-bit values, ragged tail
+    (256, 1, 16, 70, 8, 4, np.float16),    # 8-bit keys with 16 query heads, one tile and a bit
 ])
 def test_attn_matrix(hd, H, G, T, kbits, vbits, qdt):
     k, v, sk, sv = _data(hd + T, H, T, hd)
@@ -210,6 +213,11 @@ def test_attn_rejects_bad_args():
     with pytest.raises(tq.TqError) as e:  # 32 query heads per KV head
         tq.tq_decode_attn(c.kq, c.vq, q, tq.TQ_F16, 32, 1, 32, c.kc, c.kn, c.vc, c.vn, 0.0, out, None, 0)
     assert e.value.status == 2
+    v8 = tq.Quantizer(128, 32, 8, sv)
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=DEV)
+    with pytest.raises(tq.TqError) as e:  # 8-bit values are not an attention format
+        tq.tq_decode_attn(c.kq, v8, q, tq.TQ_F16, 4, 1, 32, c.kc, c.kn, c.vc, c.vn, 0.0, out, ws, 1 << 20)
+    assert e.value.status == 2
 
 
 def test_attn_full_size_sampled():
@@ -223,3 +231,16 @@ def test_attn_full_size_sampled():
     gpu = c.attend(w["q"])
     orc, bound = c.oracle(w["q"], kv_heads=[2])
     _check(gpu[8:12], orc, bound, "131072 tokens, KV head 2")
+
+
+def test_attn_full_size_k8v4_sampled():
+    """The same 131072-token cache with 8-bit keys and 4-bit values (the asymmetric allocation); the
+    oracle on KV head 1."""
+    from synth.workloads import decode_cache
+
+    w = decode_cache()
+    c = Cache(w["k"][0], w["v"][0], 8, 4, w["signs_k"], w["signs_v"])
+    del w["k"], w["v"]
+    gpu = c.attend(w["q"])
+    orc, bound = c.oracle(w["q"], kv_heads=[1])
+    _check(gpu[4:8], orc, bound, "131072 tokens, K8V4, KV head 1")
