@@ -14,16 +14,18 @@ read by the encodes plus fp16 bytes written by the decodes, per second.
 
 The same cache is also run in the fork's production layout (128-value
 chunks, the chunk norm copied into each 14/18-byte 32-value record, Beta
-codebook for d = 128), reported as `fork_layout` (not part of `value`).
+codebook for d = 128), reported as `fork_layout`, and with 8-bit keys and
+4-bit values (block-32), reported as `k8v4` (neither is part of `value`).
 
 Two more workloads are timed and reported beside it (not part of `value`):
   qjl   65536 keys x 128 fp16 encoded at 2 bits + the 1-bit QJL residual
         (dense Gaussian S, m = 128), then scored against 4096 queries
         (32 heads x 128 tokens): keys/s and scores/s;
   attn  single-token decode attention over a 131072-token cache, head_dim
-        256, 4 KV heads, 16 query heads, 3-bit block-32 K and V: time per
-        call and compressed bytes read per second, with the cache warm in the
-        last-level cache and with it flushed before each call.
+        256, 4 KV heads, 16 query heads, 3-bit block-32 K and V (and, as
+        attn.k8v4, 8-bit K with 4-bit V): time per call and compressed bytes
+        read per second, with the cache warm in the last-level cache and with
+        it flushed before each call.
 """
 from __future__ import annotations
 
@@ -71,24 +73,24 @@ class Codec:
     """K and V encode/decode buffers for the cache: block-32 units in two planes (codes, fp16 norms),
     or with records=True the fork's 32-value records over dt-long chunks (norms inside the records)."""
 
-    def __init__(self, tq, torch, dev, rows, bits, signs_k, signs_v, dt=DT, records=False, codebook=None):
-        self.tq, self.rows, self.bits = tq, rows, bits
+    def __init__(self, tq, torch, dev, rows, bits, signs_k, signs_v, dt=DT, records=False, codebook=None,
+                 vbits=None):
+        vbits = vbits or bits  # V may take fewer bits than K (8-bit keys with 4-bit values)
+        self.tq, self.rows, self.bits, self.vbits = tq, rows, bits, vbits
         flags = tq.TQ_BLOCKS if records else 0
         cbk = codebook or CODEBOOK
         self.qk = tq.Quantizer(HEAD_DIM, dt, bits, signs_k, flags=flags, codebook=cbk)
-        self.qv = tq.Quantizer(HEAD_DIM, dt, bits, signs_v, flags=flags, codebook=cbk)
+        self.qv = tq.Quantizer(HEAD_DIM, dt, vbits, signs_v, flags=flags, codebook=cbk)
         groups = rows * HEAD_DIM // 32
         self.units = groups  # 32-value groups (the unit of the byte accounting)
         if records:
-            nb = groups * (2 + 4 * bits)
-            self.ck = torch.empty(nb, dtype=torch.uint8, device=dev)
-            self.cv = torch.empty(nb, dtype=torch.uint8, device=dev)
+            self.ck = torch.empty(groups * (2 + 4 * bits), dtype=torch.uint8, device=dev)
+            self.cv = torch.empty(groups * (2 + 4 * vbits), dtype=torch.uint8, device=dev)
             self.nk = self.nv = None
         else:
             units = rows * HEAD_DIM // dt
-            cb = units * dt * bits // 8
-            self.ck = torch.empty(cb, dtype=torch.uint8, device=dev)
-            self.cv = torch.empty(cb, dtype=torch.uint8, device=dev)
+            self.ck = torch.empty(units * dt * bits // 8, dtype=torch.uint8, device=dev)
+            self.cv = torch.empty(units * dt * vbits // 8, dtype=torch.uint8, device=dev)
             self.nk = torch.empty(units, dtype=torch.float16, device=dev)
             self.nv = torch.empty(units, dtype=torch.float16, device=dev)
 
@@ -147,7 +149,7 @@ def capture_step(torch, step, outputs):
     return graph
 
 
-def per_kernel_ms(torch, codec, k, v, ok, ov, reps):
+def per_kernel_ms(torch, codec, k, v, ok, ov, reps, split=False):
     """Average duration (ms) of one encode launch and one decode launch inside the step sequence
     (quantize K, quantize V, dequantize K, dequantize V, so every launch streams from HBM as in the
     step), from HIP events recorded between the launches on the stream they run on (torch's
@@ -169,6 +171,8 @@ def per_kernel_ms(torch, codec, k, v, ok, ov, reps):
     ev.append(end)
     torch.cuda.synchronize()
     d = [ev[i].elapsed_time(ev[i + 1]) for i in range(len(ev) - 1)]
+    if split:  # K encode, V encode, K decode, V decode separately
+        return tuple(sum(d[i] for i in range(len(d)) if i % 4 == j) / reps for j in range(4))
     enc = [d[i] for i in range(len(d)) if i % 4 in (0, 1)]
     dec = [d[i] for i in range(len(d)) if i % 4 in (2, 3)]
     return sum(enc) / len(enc), sum(dec) / len(dec)
@@ -216,6 +220,32 @@ def cpu_baseline(rows_total: int, bits: int, target_s: float = 15.0) -> dict:
     return {"value": fp16_bytes / dt_s / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{done_rows} head vectors ({done_rows * HEAD_DIM // DT} blocks) of layer 0 / head 0 K, "
                       f"encode+decode at {bits} bits, {dt_s:.1f} s single-threaded numpy float64"}
+
+
+def run_k8v4(tq, torch, dev, rows, k, v, ok, ov, signs_k, signs_v, args):
+    """The cache with 8-bit keys and 4-bit values (block-32): the same four-launch step."""
+    codec = Codec(tq, torch, dev, rows, 8, signs_k, signs_v, vbits=4)
+    launches = codec.launches(k, v, ok, ov)
+
+    def step():
+        for f in launches:
+            f()
+
+    graph = None if args.no_graph else capture_step(torch, step, codec.outputs() + [ok, ov])
+    ms = time_steps(torch, graph.replay if graph is not None else step, args.steps, args.warmup)
+    del graph
+    ek, ev, dk, dv = per_kernel_ms(torch, codec, k, v, ok, ov, max(5, args.steps // 2), split=True)
+    b8, b4 = algorithmic_bytes(codec.units, 8), algorithmic_bytes(codec.units, 4)
+    out = {"workload": "same cache, 8-bit keys and 4-bit values, block-32 (fp16 norm per 32 values)",
+           "step_ms": round(ms, 4), "GBs": round(2 * 2 * b8["fp16"] / (ms * 1e-3) / 1e9, 1),
+           "encode_k8_ms": round(ek, 4), "encode_k8_GBs": round(b8["per_launch"] / ek / 1e6, 1),
+           "decode_k8_ms": round(dk, 4), "decode_k8_GBs": round(b8["per_launch"] / dk / 1e6, 1),
+           "encode_v4_ms": round(ev, 4), "decode_v4_ms": round(dv, 4)}
+    log(f"k8v4: step {ms:.3f} ms, K encode {ek:.3f} ms ({out['encode_k8_GBs']} GB/s), K decode {dk:.3f} ms "
+        f"({out['decode_k8_GBs']} GB/s), V encode {ev:.3f} ms, V decode {dv:.3f} ms")
+    del codec
+    torch.cuda.empty_cache()
+    return out
 
 
 def event_ms(torch, fn, reps, before=None):
@@ -318,21 +348,22 @@ def bench_qjl(tq, torch, dev, reps):
     return out
 
 
-def bench_attn(tq, torch, dev, reps):
-    """Decode attention: 16 query heads over a 131072-token, 4-KV-head, head_dim-256 turbo3 cache."""
+def bench_attn(tq, torch, dev, reps, kbits=3, vbits=3):
+    """Decode attention: 16 query heads over a 131072-token, 4-KV-head, head_dim-256 cache, K and V in
+    the block-32 layout (turbo3 by default; kbits=8, vbits=4 is the asymmetric 8-bit-key cache)."""
     from synth import workloads
 
     w = workloads.decode_cache()
     H, T, hd = w["k"].shape[1], w["k"].shape[2], w["k"].shape[3]
     hq = w["q"].shape[0]
     rows = H * T
-    kq = tq.Quantizer(hd, 32, 3, w["signs_k"], codebook=CODEBOOK)
-    vq = tq.Quantizer(hd, 32, 3, w["signs_v"], codebook=CODEBOOK)
+    kq = tq.Quantizer(hd, 32, kbits, w["signs_k"], codebook=CODEBOOK)
+    vq = tq.Quantizer(hd, 32, vbits, w["signs_v"], codebook=CODEBOOK)
     units = rows * hd // 32
     plane = {}
-    for name, qz in (("k", kq), ("v", vq)):
+    for name, qz, b in (("k", kq, kbits), ("v", vq, vbits)):
         x = torch.from_numpy(w[name].reshape(rows, hd)).to(dev)
-        plane[name] = (torch.empty(units * 12, dtype=torch.uint8, device=dev),
+        plane[name] = (torch.empty(units * 4 * b, dtype=torch.uint8, device=dev),
                        torch.empty(units, dtype=torch.float16, device=dev))
         tq.tq_quantize(qz, x, rows, hd, plane[name][0], plane[name][1])
         del x
@@ -352,15 +383,17 @@ def bench_attn(tq, torch, dev, reps):
         attn()
     warm_ms = batch_ms(torch, attn, reps)
     cold_ms, cold_min = event_ms(torch, attn, reps, before=lambda: flush.sum())
-    nbytes = 2 * units * (12 + 2)  # K and V codes and norms
-    res = {"workload": "decode attention, head_dim 256, 4 KV heads, 16 query heads, 131072 tokens, turbo3 K/V",
+    nbytes = units * (4 * kbits + 2 + 4 * vbits + 2)  # K and V codes and norms
+    fmt = "turbo3 K/V" if kbits == vbits == 3 else f"{kbits}-bit K, {vbits}-bit V"
+    res = {"workload": f"decode attention, head_dim 256, 4 KV heads, 16 query heads, 131072 tokens, {fmt}",
            "us_flushed": round(cold_ms * 1e3, 2), "us_warm": round(warm_ms * 1e3, 2),
            "us_min_flushed": round(cold_min * 1e3, 2), "compressed_bytes": nbytes,
            "GBs_flushed": round(nbytes / (cold_ms * 1e-3) / 1e9, 1),
            "GBs_warm": round(nbytes / (warm_ms * 1e-3) / 1e9, 1),
            "frac_hbm_flushed": round(nbytes / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
            "tokens_per_s_flushed": round(H * T / (cold_ms * 1e-3))}
-    log(f"attn: {cold_ms * 1e3:.1f} us flushed ({res['GBs_flushed']} GB/s), {warm_ms * 1e3:.1f} us warm")
+    log(f"attn K{kbits}V{vbits}: {cold_ms * 1e3:.1f} us flushed ({res['GBs_flushed']} GB/s), "
+        f"{warm_ms * 1e3:.1f} us warm")
     return res
 
 
@@ -429,6 +462,7 @@ def main():
     sk128, sv128 = synth.signs(0, synth.STREAM_SIGNS_K, 128), synth.signs(0, synth.STREAM_SIGNS_V, 128)
     fork = {bits: run_codec(bits, "fork records", sk128, sv128, dt=128, records=True, codebook="beta")
             for bits in (3, 4)}
+    k8v4 = run_k8v4(tq, torch, dev, rows, k, v, ok, ov, signs_k, signs_v, args)
 
     if args.only == "codec":
         return
@@ -437,6 +471,8 @@ def main():
     qjl = bench_qjl(tq, torch, dev, reps)
     torch.cuda.empty_cache()
     attn = bench_attn(tq, torch, dev, reps)
+    torch.cuda.empty_cache()
+    attn["k8v4"] = bench_attn(tq, torch, dev, reps, kbits=8, vbits=4)
     torch.cuda.empty_cache()
 
     r = results[3]
@@ -488,6 +524,7 @@ def main():
                              "encode_GBs": round(fork[b]["bytes"]["per_launch"] / fork[b]["enc_ms"] / 1e6, 1),
                              "decode_GBs": round(fork[b]["bytes"]["per_launch"] / fork[b]["dec_ms"] / 1e6, 1)}
                for b in (3, 4)}},
+        "k8v4": k8v4,
         "copy_reference_GBs": round(copy_gbs, 1),
         "qjl": qjl,
         "attn": attn,
