@@ -36,5 +36,5 @@ from .quantizer import (  # noqa: F401
     fwht, hadamard_matrix, index_to_code, code_to_index, pack_codes, unpack_codes, pack_sign_bits,
     unpack_sign_bits, encode_indices, quantize, dequantize, qjl_scores, QJL_CONST,
 )
-from .attention import decode_attention  # noqa: F401
+from .attention import decode_attention, multi_attention  # noqa: F401
 from .blocks import to_blocks, from_blocks, dequantize_blocks, record_bytes  # noqa: F401

@@ -2,6 +2,8 @@
 
   * equals a per-token pure-Python loop (exp, sum, weighted sum) on tiny inputs;
   * special cases: one token gives v~_0; a zero query gives the mean of v~;
+  * several query tokens (with and without the causal mask) against a loop over the visible
+    tokens, against decode calls over the visible prefix, and the first causal row = v~_0;
   * the rotated-domain identities of [Fork] "Fused tile path"
     (<D H c, q> = <c, H D q> and sum_j p_j D H c_j = D H sum_j p_j c_j), in float64.
 """
@@ -64,3 +66,55 @@ def test_rotated_domain_identities():
     p = rng.random(7)
     np.testing.assert_allclose((fwht(c) * D) @ q, c @ fwht(q * D), rtol=1e-13)
     np.testing.assert_allclose(p @ (fwht(c) * D), fwht(p @ c) * D, rtol=1e-13)
+
+
+def _multi(q, cache, n_kv, tokens, hd, causal):
+    from oracle import multi_attention
+
+    cb, dk, dv, ek, ev = cache
+    return multi_attention(q, ek["codes"], ek["norms"], ev["codes"], ev["norms"], dk, dv, cb, cb, n_kv, tokens, hd,
+                           causal=causal)
+
+
+def test_multi_query_matches_per_token_loop_with_mask():
+    """Several query tokens with the causal mask against a pure-Python loop over the visible tokens."""
+    n_kv, G, n_q, tokens, hd = 2, 2, 3, 6, 32
+    cache = _cache(n_kv, tokens, hd, seed=5)
+    cb, dk, dv, ek, ev = cache
+    q = synth.normal_f16(5, 6, n_q * n_kv * G * hd).reshape(n_q, n_kv * G, hd)
+    out = _multi(q, cache, n_kv, tokens, hd, causal=True)
+    kd = dequantize(ek["codes"], ek["norms"], dk, cb).reshape(n_kv, tokens, hd)
+    vd = dequantize(ev["codes"], ev["norms"], dv, cb).reshape(n_kv, tokens, hd)
+    for i in range(n_q):
+        visible = tokens - n_q + i + 1
+        for h in range(n_kv * G):
+            g = h // G
+            logits = [sum(float(q[i, h, c]) * kd[g, j, c] for c in range(hd)) / math.sqrt(hd) for j in range(visible)]
+            mx = max(logits)
+            w = [math.exp(s - mx) for s in logits]
+            ref = [sum(w[j] * vd[g, j, c] for j in range(visible)) / sum(w) for c in range(hd)]
+            np.testing.assert_allclose(out[i, h], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_multi_query_reduces_to_decode():
+    """Without the mask every query token is a decode call; with it, row i is a decode call over the
+    first n_tokens - n_q + i + 1 tokens; a causal chunk as long as the cache starts with v~_0."""
+    n_kv, G, n_q, tokens, hd = 1, 4, 5, 40, 64
+    cache = _cache(n_kv, tokens, hd, seed=6)
+    cb, dk, dv, ek, ev = cache
+    q = synth.normal_f16(6, 6, n_q * G * hd).reshape(n_q, G, hd)
+    full = _multi(q, cache, n_kv, tokens, hd, causal=False)
+    masked = _multi(q, cache, n_kv, tokens, hd, causal=True)
+    upt = hd // 32
+    for i in range(n_q):
+        dec = decode_attention(q[i], ek["codes"], ek["norms"], ev["codes"], ev["norms"], dk, dv, cb, cb, n_kv, tokens,
+                               hd)
+        np.testing.assert_allclose(full[i], dec, rtol=1e-13, atol=1e-15)
+        t = tokens - n_q + i + 1
+        dec = decode_attention(q[i], ek["codes"][:t * upt], ek["norms"][:t * upt], ev["codes"][:t * upt],
+                               ev["norms"][:t * upt], dk, dv, cb, cb, n_kv, t, hd)
+        np.testing.assert_allclose(masked[i], dec, rtol=1e-13, atol=1e-15)
+    q = synth.normal_f16(7, 6, tokens * G * hd).reshape(tokens, G, hd)
+    first = _multi(q, cache, n_kv, tokens, hd, causal=True)[0]
+    vd = dequantize(ev["codes"][:upt], ev["norms"][:upt], dv, cb).reshape(hd)
+    np.testing.assert_allclose(first, np.repeat(vd[None], G, axis=0), rtol=1e-14)
