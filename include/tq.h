@@ -81,7 +81,7 @@ enum {
   TQ_BLOCKS = 4u        /* codes and norms as the fork's 32-value records (see "Records" above) */
 };
 
-enum { TQ_OP_QJL_SCORES = 1, TQ_OP_DECODE_ATTN = 2 };
+enum { TQ_OP_QJL_SCORES = 1, TQ_OP_DECODE_ATTN = 2, TQ_OP_MULTI_ATTN = 3 };
 
 /*
  * Lloyd-Max codebook for one rotated coordinate, whose variance is 1/dim
@@ -226,7 +226,8 @@ tq_status tq_qjl_scores(const tq_config* cfg, const void* q, tq_dtype q_dtype, i
  *               [Scratch] §4 "Finding 1" and §10 "Takeaways"), equal head_dim
  *               of 128 or 256, no flags (TQ_ERR_UNSUPPORTED otherwise)
  *   q           device, [n_q_heads][head_dim] of q_dtype, contiguous
- *   n_q_heads   a multiple of n_kv_heads, at most 16 query heads per KV head
+ *   n_q_heads   a multiple of n_kv_heads (up to 16 heads share each K and V
+ *               read; more are processed in groups of 16)
  *   k_codes, v_codes  device, 4-byte aligned, units in (kv head, token,
  *               block) order, i.e. rows of tq_quantize over
  *               [n_kv_heads][n_tokens][head_dim]
@@ -246,6 +247,32 @@ tq_status tq_decode_attn(const tq_config* kcfg, const tq_config* vcfg, const voi
                          int n_q_heads, int n_kv_heads, int64_t n_tokens, const uint8_t* k_codes, const void* k_norms,
                          const uint8_t* v_codes, const void* v_norms, float scale, float* out, void* ws,
                          size_t ws_bytes, void* stream);
+
+/*
+ * Attention of several query tokens over the same quantized cache (the
+ * [Fork] "Fused tile path" with more than one query column: a prefill chunk
+ * or a batch of draft tokens).  Query token i (0 <= i < n_q) with head h:
+ *   out[i][h] = sum_{j in S_i} softmax_j(scale * <q_ih, k~_j>) v~_j
+ * over KV head h / (n_q_heads / n_kv_heads), where S_i is every cached token,
+ * or with causal != 0 the tokens j <= n_tokens - n_q + i (the n_q queries are
+ * the last n_q positions of the cache, whose K and V are already in it).
+ *   kcfg, vcfg, k_codes, k_norms, v_codes, v_norms, scale: as tq_decode_attn
+ *   q     device, [n_q][n_q_heads][head_dim] of q_dtype, contiguous
+ *   out   device fp32 [n_q][n_q_heads][head_dim]
+ *   ws    256-byte aligned device workspace of
+ *         tq_workspace_size(TQ_OP_MULTI_ATTN, kcfg, n_q * n_q_heads,
+ *         n_kv_heads, n_tokens) bytes (contents are scratch)
+ * The (query token, head) rows of one KV head are processed in groups of up
+ * to 16 that share each K and V read.  n_q = 1 without a mask is
+ * tq_decode_attn.  Errors: causal with n_q > n_tokens is TQ_ERR_INVALID_ARG;
+ * more than 65535 (KV head, 16-row group) pairs or 2^31 rows is
+ * TQ_ERR_UNSUPPORTED; n_q = 0 or n_tokens = 0 leaves out untouched.
+ * Precision as tq_decode_attn.
+ */
+tq_status tq_multi_attn(const tq_config* kcfg, const tq_config* vcfg, const void* q, tq_dtype q_dtype, int64_t n_q,
+                        int n_q_heads, int n_kv_heads, int64_t n_tokens, const uint8_t* k_codes, const void* k_norms,
+                        const uint8_t* v_codes, const void* v_norms, int causal, float scale, float* out, void* ws,
+                        size_t ws_bytes, void* stream);
 
 /* Workspace bytes for op (TQ_OP_*) with sizes (a, b, c) as described per op; 0 if none. */
 size_t tq_workspace_size(int op, const tq_config* cfg, int64_t a, int64_t b, int64_t c);

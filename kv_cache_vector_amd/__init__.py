@@ -21,10 +21,11 @@ LIB_PATH = os.path.join(_HERE, "libtq.so")
 TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE, TQ_ERR_HIP = range(5)
 TQ_F16, TQ_F32 = 0, 1
 TQ_NORM_CORRECT, TQ_QJL, TQ_BLOCKS = 1, 2, 4
-TQ_OP_QJL_SCORES, TQ_OP_DECODE_ATTN = 1, 2
+TQ_OP_QJL_SCORES, TQ_OP_DECODE_ATTN, TQ_OP_MULTI_ATTN = 1, 2, 3
 
 EXPORTED = ("tq_codebook_init", "tq_codebook_init_beta", "tq_qjl_params_size", "tq_qjl_prepare", "tq_quantize", "tq_dequantize",
-            "tq_qjl_scores", "tq_decode_attn", "tq_workspace_size", "tq_status_str", "tq_last_error")
+            "tq_qjl_scores", "tq_decode_attn", "tq_multi_attn", "tq_workspace_size", "tq_status_str",
+            "tq_last_error")
 
 
 class TqError(RuntimeError):
@@ -70,13 +71,15 @@ def lib():
     L.tq_qjl_scores.argtypes = [cfgp, vp, c_int, i64, i64, vp, vp, vp, vp, i64, vp, i64, vp, sz, vp]
     L.tq_decode_attn.argtypes = [cfgp, cfgp, vp, c_int, c_int, c_int, i64, vp, vp, vp, vp, ctypes.c_float, vp, vp, sz,
                                  vp]
+    L.tq_multi_attn.argtypes = [cfgp, cfgp, vp, c_int, i64, c_int, c_int, i64, vp, vp, vp, vp, c_int, ctypes.c_float,
+                                vp, vp, sz, vp]
     L.tq_workspace_size.argtypes = [c_int, cfgp, i64, i64, i64]
     L.tq_workspace_size.restype = sz
     L.tq_status_str.argtypes = [c_int]
     L.tq_status_str.restype = ctypes.c_char_p
     L.tq_last_error.restype = ctypes.c_char_p
     for name in ("tq_codebook_init", "tq_codebook_init_beta", "tq_qjl_prepare", "tq_quantize", "tq_dequantize", "tq_qjl_scores",
-                 "tq_decode_attn"):
+                 "tq_decode_attn", "tq_multi_attn"):
         getattr(L, name).restype = c_int
     _lib = L
     return L
@@ -187,6 +190,14 @@ def tq_decode_attn(kq: Quantizer, vq: Quantizer, q, q_dtype: int, n_q_heads: int
     _check(lib().tq_decode_attn(ctypes.byref(kq.cfg), ctypes.byref(vq.cfg), _ptr(q), q_dtype, n_q_heads, n_kv_heads,
                                 n_tokens, _ptr(k_codes), _ptr(k_norms), _ptr(v_codes), _ptr(v_norms), scale,
                                 _ptr(out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def tq_multi_attn(kq: Quantizer, vq: Quantizer, q, q_dtype: int, n_q: int, n_q_heads: int, n_kv_heads: int,
+                  n_tokens: int, k_codes, k_norms, v_codes, v_norms, causal: bool, scale: float, out, ws=None,
+                  ws_bytes: int = 0, stream=None):
+    _check(lib().tq_multi_attn(ctypes.byref(kq.cfg), ctypes.byref(vq.cfg), _ptr(q), q_dtype, n_q, n_q_heads,
+                               n_kv_heads, n_tokens, _ptr(k_codes), _ptr(k_norms), _ptr(v_codes), _ptr(v_norms),
+                               1 if causal else 0, scale, _ptr(out), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def default_scale(head_dim: int) -> float:

@@ -56,6 +56,9 @@ constexpr int kWaves = 4;
 constexpr int kTile = 64;     // tokens per tile
 constexpr int kMergeLanes = 8;
 constexpr float kSlack = 8.0f;  // softmax weights relative to the running reference stay below e^8
+// Initial softmax reference: finite, so a row whose tokens are all masked so far gets weights
+// exp(-inf - kNoRef) = 0 rather than NaN, and any live score moves it.
+constexpr float kNoRef = -1e30f;
 
 __device__ __forceinline__ uint32_t pack_h2(_Float16 lo, _Float16 hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
@@ -163,8 +166,10 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = lane & 15, g = lane >> 4;
-  const int kvh = blockIdx.y;
+  const int kvh = blockIdx.y / a.n_rg, rg = blockIdx.y % a.n_rg;
   const int G = a.group;
+  const int64_t row0 = (int64_t)rg * a.grp;                                 // first row of the group
+  const int grows = (int)(a.rows - row0 < a.grp ? a.rows - row0 : a.grp);  // live rows in the group
   const uint32_t koff = (uint32_t)(lane & (CK - 1)) * 4u, voff = (uint32_t)(lane & (CV - 1)) * 4u;
 
   const int64_t T = a.n_tokens;
@@ -269,15 +274,16 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
     vtab[x] = pack_h2((_Float16)a.vlevel[e & (VL - 1)], (_Float16)a.vlevel[e >> VB]);
   }
 
-  // rotated query blocks qhat_b = H D_K q_b / sqrt(32) of the group's heads (rows >= G zero),
-  // FWHT staged in fp32 over the V tile area
+  // rotated query blocks qhat_b = H D_K q_b / sqrt(32) of the group's rows (rows past the live
+  // ones zero), FWHT staged in fp32 over the V tile area
   float* qf = reinterpret_cast<float*>(&vt[0][0]);
   static_assert(sizeof(vt) >= sizeof(float) * GP * HD, "query staging fits the V tiles");
   for (int e = tid; e < GP * HD; e += 256) {
     const int r = e / HD, d = e % HD;
     float v = 0.0f;
-    if (r < G) {
-      const int64_t off = (int64_t)(kvh * G + r) * HD + d;
+    if (r < grows) {
+      const int64_t rr = row0 + r, i = rr / G;  // query token and head of the row
+      const int64_t off = (i * a.n_q_heads + (int64_t)kvh * G + rr % G) * HD + d;
       v = a.q_f32 ? static_cast<const float*>(a.q)[off] : __half2float(static_cast<const __half*>(a.q)[off]);
     }
     qf[e] = ((a.kdbits >> (d & 31)) & 1u) ? -v : v;
@@ -314,11 +320,20 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   }
   __syncthreads();  // query staging is overwritten by the V tiles below
 
+  // last token each register's row may see: all tokens, or with a causal mask the row's query
+  // position n_tokens - n_q + i (register i of this lane holds row (4g + i) % GP of the group)
+  int64_t lim[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t rr = row0 + (4 * g + i) % GP;
+    lim[i] = a.causal && rr < a.rows ? T - a.n_q + rr / G : T - 1;
+  }
+  const int64_t all_live = T - (a.causal ? a.n_q : 1);  // last token every row sees
   float m_run[4], lsum[4];
   v4f acc[NBW][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    m_run[i] = -INFINITY;
+    m_run[i] = kNoRef;
     lsum[i] = 0.0f;
   }
 #pragma unroll
@@ -410,7 +425,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
     lds_barrier();
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
-      const bool live = tb + ktok(cc) < T;
+      const int64_t tok = tb + ktok(cc);
       float4 v = *reinterpret_cast<const float4*>(&xs[parity][lane][cc * 4]);
 #pragma unroll
       for (int w = 1; w < kWaves; ++w) {
@@ -420,10 +435,17 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
         v.z += u.z;
         v.w += u.w;
       }
-      s[cc][0] = live ? v.x * a.kscale : -INFINITY;
-      s[cc][1] = live ? v.y * a.kscale : -INFINITY;
-      s[cc][2] = live ? v.z * a.kscale : -INFINITY;
-      s[cc][3] = live ? v.w * a.kscale : -INFINITY;
+      if (tb + kTile - 1 <= all_live) {  // every row sees the whole tile: no per-row test
+        s[cc][0] = v.x * a.kscale;
+        s[cc][1] = v.y * a.kscale;
+        s[cc][2] = v.z * a.kscale;
+        s[cc][3] = v.w * a.kscale;
+      } else {
+        s[cc][0] = tok <= lim[0] ? v.x * a.kscale : -INFINITY;
+        s[cc][1] = tok <= lim[1] ? v.y * a.kscale : -INFINITY;
+        s[cc][2] = tok <= lim[2] ? v.z * a.kscale : -INFINITY;
+        s[cc][3] = tok <= lim[3] ? v.w * a.kscale : -INFINITY;
+      }
     }
 
     // ---- online softmax; register i of this lane belongs to head (4g + i) % GP.  The reference
@@ -444,8 +466,8 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int cc = 1; cc < NC; ++cc) mt = fmaxf(mt, s[cc][i]);
         mt = head_reduce<S, true>(mt);
-        const float m_new = fmaxf(m_run[i], mt);  // finite: every tile holds a live token
-        const float alpha = m_run[i] == -INFINITY ? 0.0f : __expf(m_run[i] - m_new);
+        const float m_new = fmaxf(m_run[i], mt);  // >= kNoRef, so alpha below is never NaN
+        const float alpha = __expf(m_run[i] - m_new);
         lsum[i] *= alpha;
         m_run[i] = m_new;
 #pragma unroll
@@ -471,7 +493,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int half = 0; half < kTile / 32; ++half) {
       const v8h z = {0, 0, 0, 0, 0, 0, 0, 0};
-      const v8h av = row < G ? *reinterpret_cast<const v8h*>(ptile + (row % GP) * kTile + 32 * half + 8 * g) : z;
+      const v8h av = row < grows ? *reinterpret_cast<const v8h*>(ptile + (row % GP) * kTile + 32 * half + 8 * g) : z;
       const int t1 = 32 * half + 8 * g + (row >> 2), t2 = t1 + 4;
 #pragma unroll
       for (int bl = 0; bl < NBW; ++bl) {
@@ -504,12 +526,12 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
     tile(rs[1], t1);
   }
 
-  // ---- partial of this workgroup: part[kvh][wg][head][HD coordinates, max, sum]
-  float* pbase = a.part + ((int64_t)kvh * a.wg_per_head + blockIdx.x) * G * (HD + 2);
+  // ---- partial of this workgroup: part[kvh][rg][wg][row][HD coordinates, reference, sum]
+  float* pbase = a.part + ((int64_t)blockIdx.y * a.wg_per_head + blockIdx.x) * a.grp * (HD + 2);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int h = 4 * g + i;  // accumulator row = query head
-    if (h >= G) continue;
+    const int h = 4 * g + i;  // accumulator row = row of the group
+    if (h >= grows) continue;
 #pragma unroll
     for (int bl = 0; bl < NBW; ++bl) {
       pbase[h * (HD + 2) + 32 * (b0 + bl) + row] = acc[bl][0][i];
@@ -523,7 +545,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * g + i, h = r % GP;
-      if (r < GP && h < G) {
+      if (r < GP && h < grows) {
         pbase[h * (HD + 2) + HD] = m_run[i];
         pbase[h * (HD + 2) + HD + 1] = lsum[i];
       }
@@ -531,14 +553,18 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   }
 }
 
-// Merge: one workgroup per (query head, 32-block); kMergeLanes x 32 threads (partial lane, coordinate).
+// Merge: one workgroup per (output row, 32-block); kMergeLanes x 32 threads (partial lane, coordinate).
+// Output row o = (query token i, query head h) reads row i * group + h % group of KV head h / group.
 __global__ __launch_bounds__(256) void attn_merge(AttnArgs a) {
-  const int h = blockIdx.x, b = blockIdx.y, HD = a.head_dim, G = a.group;
-  const int kvh = h / G, r = h % G;
+  const int64_t o = blockIdx.x;
+  const int b = blockIdx.y, HD = a.head_dim, G = a.group;
+  const int64_t i = o / a.n_q_heads;
+  const int h = (int)(o % a.n_q_heads), kvh = h / G;
+  const int64_t rr = i * G + h % G, rg = rr / a.grp, r = rr % a.grp;
   const int tid = threadIdx.x, pl = tid >> 5, dl = tid & 31;
   const int n_part = a.wg_per_head;
-  const int64_t stride = (int64_t)G * (HD + 2);
-  const float* base = a.part + (int64_t)kvh * n_part * stride + (int64_t)r * (HD + 2);
+  const int64_t stride = (int64_t)a.grp * (HD + 2);
+  const float* base = a.part + ((int64_t)kvh * a.n_rg + rg) * n_part * stride + r * (HD + 2);
   __shared__ float red[kMergeLanes][34];
   // one pass over this lane's partials with a running reference (the partials' own references
   // differ; a larger one rescales what was summed so far)
@@ -548,7 +574,7 @@ __global__ __launch_bounds__(256) void attn_merge(AttnArgs a) {
     const float* pb = base + p * stride;
     const float mp = pb[HD], lp = pb[HD + 1], xp = pb[32 * b + dl];
     // branch-free, so the loads of the unrolled iterations go out together (every partial has a
-    // finite reference: each workgroup scores at least one live token)
+    // finite reference; a row with no live token in a workgroup has reference kNoRef and sum 0)
     const float m_new = fmaxf(m, mp);
     const float f_old = m == -INFINITY ? 0.0f : __expf(m - m_new), f_new = __expf(mp - m_new);
     acc = __builtin_fmaf(xp, f_new, acc * f_old);
@@ -582,22 +608,23 @@ __global__ __launch_bounds__(256) void attn_merge(AttnArgs a) {
     }
     v = v / (32.0f * ls);
     if ((a.vdbits >> dl) & 1u) v = -v;
-    a.out[(int64_t)h * HD + 32 * b + dl] = v;
+    a.out[o * HD + 32 * b + dl] = v;
   }
 }
 
 template <int NB, int KB, int VB>
 hipError_t launch_nb(const AttnArgs& a, hipStream_t s) {
-  dim3 grid((unsigned)a.wg_per_head, (unsigned)a.n_kv_heads);
-  if (a.group <= 4)
+  dim3 grid((unsigned)a.wg_per_head, (unsigned)(a.n_kv_heads * a.n_rg));
+  if (a.grp <= 4)
     hipLaunchKernelGGL((attn_kernel<NB, KB, VB, 4>), grid, dim3(256), 0, s, a);
-  else if (a.group <= 8)
+  else if (a.grp <= 8)
     hipLaunchKernelGGL((attn_kernel<NB, KB, VB, 8>), grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((attn_kernel<NB, KB, VB, 16>), grid, dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_merge, dim3((unsigned)a.n_q_heads, (unsigned)(a.head_dim / 32)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(attn_merge, dim3((unsigned)(a.n_q * a.n_q_heads), (unsigned)(a.head_dim / 32)), dim3(256), 0, s,
+                     a);
   return hipGetLastError();
 }
 
@@ -609,10 +636,11 @@ hipError_t launch_bits(const AttnArgs& a, hipStream_t s) {
 }  // namespace
 
 // Token range per workgroup: a multiple of the 64-token tile that spreads the
-// cache over about 512 workgroups (two per compute unit), 64 .. 8192 tokens.
-int64_t attn_tokens_per_wg(int n_kv_heads, int64_t n_tokens) {
+// cache over about 512 workgroups (two per compute unit), 64 .. 8192 tokens;
+// `columns` = KV heads x row groups, the workgroup columns that each walk it.
+int64_t attn_tokens_per_wg(int64_t columns, int64_t n_tokens) {
   const int64_t target = 512;
-  int64_t per = (n_tokens * n_kv_heads + target - 1) / target;
+  int64_t per = (n_tokens * columns + target - 1) / target;
   per = (per + kTile - 1) / kTile * kTile;
   if (per < kTile) per = kTile;
   if (per > 8192) per = 8192;

@@ -630,9 +630,8 @@ tq_status check_scores_config(const tq_config* cfg, const char* who) {
   return TQ_OK;
 }
 
-// Decode attention: block-32 K and V (fp16 norms, K at 3, 4 or 8 bits, V at 3 or
-// 4 bits, no QJL or norm correction), head_dim 128 or 256, up to 16 query heads
-// per KV head.
+// Attention: block-32 K and V (fp16 norms, K at 3, 4 or 8 bits, V at 3 or 4
+// bits, no QJL or norm correction), head_dim 128 or 256.
 tq_status check_attn_config(const tq_config* kcfg, const tq_config* vcfg, int n_q_heads, int n_kv_heads,
                             int64_t n_tokens, const char* who) {
   tq_status st = check_config(kcfg, who);
@@ -649,18 +648,92 @@ tq_status check_attn_config(const tq_config* kcfg, const tq_config* vcfg, int n_
     return fail(TQ_ERR_UNSUPPORTED, "%s: QJL and norm correction are not supported in attention", who);
   if (kcfg->norm_dtype != TQ_F16 || vcfg->norm_dtype != TQ_F16)
     return fail(TQ_ERR_UNSUPPORTED, "%s: K and V norms must be fp16", who);
-  if (n_q_heads / n_kv_heads > 16) return fail(TQ_ERR_UNSUPPORTED, "%s: at most 16 query heads per KV head", who);
   if (n_kv_heads > 65535 || n_tokens > ((int64_t)1 << 40))
     return fail(TQ_ERR_UNSUPPORTED, "%s: at most 65535 KV heads and 2^40 tokens", who);
   return TQ_OK;
 }
 
-// one fp32 partial (head_dim sums, running max, running sum) per query head and token range
-size_t attn_workspace(const tq_config& kcfg, int n_q_heads, int n_kv_heads, int64_t n_tokens) {
-  const int64_t per_wg = tq::attn_tokens_per_wg(n_kv_heads, n_tokens);
-  const int64_t wgs = (n_tokens + per_wg - 1) / per_wg;
-  const int64_t parts = (int64_t)n_kv_heads * wgs * (n_q_heads / n_kv_heads);
+// Row groups of attention: rows = n_q * group (query token, head) pairs per KV head, cut into
+// groups of at most 16 rows.
+struct AttnShape {
+  int64_t rows, n_rg, grp, per_wg, wgs;
+};
+AttnShape attn_shape(int n_q_heads, int n_kv_heads, int64_t n_q, int64_t n_tokens) {
+  AttnShape sh{};
+  sh.rows = n_q * (n_q_heads / n_kv_heads);
+  sh.grp = sh.rows <= 16 ? sh.rows : 16;
+  sh.n_rg = (sh.rows + sh.grp - 1) / sh.grp;
+  sh.per_wg = tq::attn_tokens_per_wg((int64_t)n_kv_heads * sh.n_rg, n_tokens);
+  sh.wgs = (n_tokens + sh.per_wg - 1) / sh.per_wg;
+  return sh;
+}
+
+// one fp32 partial (head_dim sums, softmax reference, weight sum) per row and token range
+size_t attn_workspace(const tq_config& kcfg, int n_q_heads, int n_kv_heads, int64_t n_q, int64_t n_tokens) {
+  const AttnShape sh = attn_shape(n_q_heads, n_kv_heads, n_q, n_tokens);
+  const int64_t parts = (int64_t)n_kv_heads * sh.n_rg * sh.wgs * sh.grp;
   return round256((size_t)parts * (size_t)(kcfg.head_dim + 2) * sizeof(float));
+}
+
+tq_status run_attn(const char* who, const tq_config* kcfg, const tq_config* vcfg, const void* q, tq_dtype q_dtype,
+                   int64_t n_q, int n_q_heads, int n_kv_heads, int64_t n_tokens, const uint8_t* k_codes,
+                   const void* k_norms, const uint8_t* v_codes, const void* v_norms, int causal, float scale,
+                   float* out, void* ws, size_t ws_bytes, void* stream) {
+  tq_status st = check_attn_config(kcfg, vcfg, n_q_heads, n_kv_heads, n_tokens, who);
+  if (st) return st;
+  if (q_dtype != TQ_F16 && q_dtype != TQ_F32) return fail(TQ_ERR_INVALID_ARG, "%s: bad q_dtype", who);
+  if (!(scale <= 0.0f || std::isfinite(scale))) return fail(TQ_ERR_INVALID_ARG, "%s: scale is not finite", who);
+  if (n_q < 0) return fail(TQ_ERR_INVALID_ARG, "%s: n_q < 0", who);
+  if (causal && n_q > n_tokens)
+    return fail(TQ_ERR_INVALID_ARG, "%s: a causal call needs n_q <= n_tokens (the queries are the last positions)",
+                who);
+  if (n_tokens == 0 || n_q == 0) return ok();
+  if (n_q > ((int64_t)1 << 31) / n_q_heads) return fail(TQ_ERR_UNSUPPORTED, "%s: at most 2^31 query rows", who);
+  if (!q || !aligned(q, esize(q_dtype)) || !out || !aligned(out, 4))
+    return fail(TQ_ERR_INVALID_ARG, "%s: q and out must be non-NULL and element-aligned", who);
+  if (!k_codes || !aligned(k_codes, 4) || !v_codes || !aligned(v_codes, 4) || !k_norms || !aligned(k_norms, 2) ||
+      !v_norms || !aligned(v_norms, 2))
+    return fail(TQ_ERR_INVALID_ARG, "%s: codes must be 4-byte and norms 2-byte aligned, non-NULL", who);
+  const AttnShape sh = attn_shape(n_q_heads, n_kv_heads, n_q, n_tokens);
+  if ((int64_t)n_kv_heads * sh.n_rg > 65535)
+    return fail(TQ_ERR_UNSUPPORTED, "%s: at most 65535 (KV head, 16-row group) columns", who);
+  const size_t need = attn_workspace(*kcfg, n_q_heads, n_kv_heads, n_q, n_tokens);
+  if (!ws || !aligned(ws, 256) || ws_bytes < need)
+    return fail(TQ_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned with %zu bytes (got %zu)", who, need,
+                ws_bytes);
+  tq::AttnArgs a{};
+  a.q = q;
+  a.q_f32 = q_dtype == TQ_F32;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.group = n_q_heads / n_kv_heads;
+  a.head_dim = kcfg->head_dim;
+  a.n_tokens = n_tokens;
+  a.n_q = n_q;
+  a.rows = sh.rows;
+  a.grp = (int32_t)sh.grp;
+  a.n_rg = (int32_t)sh.n_rg;
+  a.causal = causal ? 1 : 0;
+  a.k_codes = k_codes;
+  a.k_norms = (const uint16_t*)k_norms;
+  a.v_codes = v_codes;
+  a.v_norms = (const uint16_t*)v_norms;
+  a.out = out;
+  a.part = (float*)ws;
+  a.tokens_per_wg = sh.per_wg;
+  a.wg_per_head = (int32_t)sh.wgs;
+  uint32_t db[8];
+  fill_dbits(*kcfg, db);
+  a.kdbits = db[0];
+  fill_dbits(*vcfg, db);
+  a.vdbits = db[0];
+  fill_levels(*kcfg->cb, a.klevel);
+  fill_levels(*vcfg->cb, a.vlevel);
+  const double sc = scale > 0.0f ? (double)scale : 1.0 / std::sqrt((double)kcfg->head_dim);
+  a.kscale = (float)(sc / std::sqrt(32.0));
+  hipError_t e = tq::launch_decode_attn(kcfg->bits, vcfg->bits, a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, who);
+  return ok();
 }
 
 }  // namespace
@@ -737,49 +810,16 @@ tq_status tq_decode_attn(const tq_config* kcfg, const tq_config* vcfg, const voi
                          int n_q_heads, int n_kv_heads, int64_t n_tokens, const uint8_t* k_codes, const void* k_norms,
                          const uint8_t* v_codes, const void* v_norms, float scale, float* out, void* ws,
                          size_t ws_bytes, void* stream) {
-  const char* who = "tq_decode_attn";
-  tq_status st = check_attn_config(kcfg, vcfg, n_q_heads, n_kv_heads, n_tokens, who);
-  if (st) return st;
-  if (q_dtype != TQ_F16 && q_dtype != TQ_F32) return fail(TQ_ERR_INVALID_ARG, "%s: bad q_dtype", who);
-  if (!(scale <= 0.0f || std::isfinite(scale))) return fail(TQ_ERR_INVALID_ARG, "%s: scale is not finite", who);
-  if (n_tokens == 0) return ok();
-  if (!q || !aligned(q, esize(q_dtype)) || !out || !aligned(out, 4))
-    return fail(TQ_ERR_INVALID_ARG, "%s: q and out must be non-NULL and element-aligned", who);
-  if (!k_codes || !aligned(k_codes, 4) || !v_codes || !aligned(v_codes, 4) || !k_norms || !aligned(k_norms, 2) ||
-      !v_norms || !aligned(v_norms, 2))
-    return fail(TQ_ERR_INVALID_ARG, "%s: codes must be 4-byte and norms 2-byte aligned, non-NULL", who);
-  const size_t need = attn_workspace(*kcfg, n_q_heads, n_kv_heads, n_tokens);
-  if (!ws || !aligned(ws, 256) || ws_bytes < need)
-    return fail(TQ_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned with %zu bytes (got %zu)", who, need,
-                ws_bytes);
-  tq::AttnArgs a{};
-  a.q = q;
-  a.q_f32 = q_dtype == TQ_F32;
-  a.n_q_heads = n_q_heads;
-  a.n_kv_heads = n_kv_heads;
-  a.group = n_q_heads / n_kv_heads;
-  a.head_dim = kcfg->head_dim;
-  a.n_tokens = n_tokens;
-  a.k_codes = k_codes;
-  a.k_norms = (const uint16_t*)k_norms;
-  a.v_codes = v_codes;
-  a.v_norms = (const uint16_t*)v_norms;
-  a.out = out;
-  a.part = (float*)ws;
-  a.tokens_per_wg = tq::attn_tokens_per_wg(n_kv_heads, n_tokens);
-  a.wg_per_head = (int32_t)((n_tokens + a.tokens_per_wg - 1) / a.tokens_per_wg);
-  uint32_t db[8];
-  fill_dbits(*kcfg, db);
-  a.kdbits = db[0];
-  fill_dbits(*vcfg, db);
-  a.vdbits = db[0];
-  fill_levels(*kcfg->cb, a.klevel);
-  fill_levels(*vcfg->cb, a.vlevel);
-  const double sc = scale > 0.0f ? (double)scale : 1.0 / std::sqrt((double)kcfg->head_dim);
-  a.kscale = (float)(sc / std::sqrt(32.0));
-  hipError_t e = tq::launch_decode_attn(kcfg->bits, vcfg->bits, a, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, who);
-  return ok();
+  return run_attn("tq_decode_attn", kcfg, vcfg, q, q_dtype, 1, n_q_heads, n_kv_heads, n_tokens, k_codes, k_norms,
+                  v_codes, v_norms, 0, scale, out, ws, ws_bytes, stream);
+}
+
+tq_status tq_multi_attn(const tq_config* kcfg, const tq_config* vcfg, const void* q, tq_dtype q_dtype, int64_t n_q,
+                        int n_q_heads, int n_kv_heads, int64_t n_tokens, const uint8_t* k_codes, const void* k_norms,
+                        const uint8_t* v_codes, const void* v_norms, int causal, float scale, float* out, void* ws,
+                        size_t ws_bytes, void* stream) {
+  return run_attn("tq_multi_attn", kcfg, vcfg, q, q_dtype, n_q, n_q_heads, n_kv_heads, n_tokens, k_codes, k_norms,
+                  v_codes, v_norms, causal, scale, out, ws, ws_bytes, stream);
 }
 
 size_t tq_workspace_size(int op, const tq_config* cfg, int64_t a, int64_t b, int64_t c) {
@@ -790,7 +830,11 @@ size_t tq_workspace_size(int op, const tq_config* cfg, int64_t a, int64_t b, int
   }
   if (op == TQ_OP_DECODE_ATTN) {
     if (a <= 0 || b <= 0 || a > 65536 || a % b || c < 0 || check_config(cfg, "tq_workspace_size")) return 0;
-    return attn_workspace(*cfg, (int)a, (int)b, c);
+    return attn_workspace(*cfg, (int)a, (int)b, 1, c);
+  }
+  if (op == TQ_OP_MULTI_ATTN) {  // a = n_q * n_q_heads query rows, b = n_kv_heads, c = n_tokens
+    if (a <= 0 || b <= 0 || b > 65535 || a % b || c < 0 || check_config(cfg, "tq_workspace_size")) return 0;
+    return attn_workspace(*cfg, (int)b, (int)b, a / b, c);
   }
   return 0;
 }

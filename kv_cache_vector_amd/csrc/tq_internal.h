@@ -101,19 +101,26 @@ struct ScoreArgs {
   float inv_sqrt_dt, qjl_const;
 };
 
-// Decode attention (tq_decode_attn), block-32 K and V with fp16 norms.
+// Attention over a block-32 K/V cache with fp16 norms (tq_decode_attn, tq_multi_attn).  The
+// rows of a KV head are its (query token, query head) pairs, row = token * group + head in group;
+// they are cut into row groups of at most 16, one workgroup column per (KV head, row group).
 struct AttnArgs {
-  const void* q;
+  const void* q;             // [n_q][n_q_heads][head_dim]
   int32_t q_f32;
-  int32_t n_q_heads, n_kv_heads, group;  // group = n_q_heads / n_kv_heads, <= 16
+  int32_t n_q_heads, n_kv_heads, group;  // group = n_q_heads / n_kv_heads
   int32_t head_dim;
   int64_t n_tokens;
+  int64_t n_q;               // query tokens (1 for decode)
+  int64_t rows;              // n_q * group rows per KV head
+  int32_t grp;               // rows per row group: rows if rows <= 16, else 16
+  int32_t n_rg;              // row groups per KV head
+  int32_t causal;            // row of query token i sees tokens j <= n_tokens - n_q + i
   const uint8_t* k_codes;
   const uint16_t* k_norms;
   const uint8_t* v_codes;
   const uint16_t* v_norms;
-  float* out;
-  float* part;               // [n_kv_heads][wg_per_head][group][head_dim + 2] partial (acc, max, sum)
+  float* out;                // [n_q][n_q_heads][head_dim]
+  float* part;               // [n_kv_heads][n_rg][wg_per_head][grp][head_dim + 2] partial (acc, ref, sum)
   int32_t wg_per_head;
   int64_t tokens_per_wg;
   uint32_t kdbits, vdbits;   // D_K, D_V of the 32-long blocks
@@ -130,6 +137,6 @@ hipError_t launch_qjl_scores(const tq_config& cfg, const ScoreArgs& a, hipStream
 int64_t scores_key_tile(int bits);
 int64_t scores_query_block();
 hipError_t launch_decode_attn(int kbits, int vbits, const AttnArgs& a, hipStream_t s);
-int64_t attn_tokens_per_wg(int n_kv_heads, int64_t n_tokens);
+int64_t attn_tokens_per_wg(int64_t columns, int64_t n_tokens);
 
 }  // namespace tq
