@@ -348,6 +348,33 @@ def bench_qjl(tq, torch, dev, reps):
     return out
 
 
+def bench_multi(tq, torch, dev, reps, w, kq, vq, plane, H, T, hd, hq, flush):
+    """Several query tokens over the same cache: causal chunks of n_q tokens at the end of it (a
+    prefill chunk or a batch of draft tokens), n_q x 16 query rows."""
+    import synth
+
+    out = {}
+    for n_q in (4, 16, 64):
+        q = torch.from_numpy(synth.normal_f16(7, 6, n_q * hq * hd).reshape(n_q, hq, hd)).to(dev)
+        o = torch.empty((n_q, hq, hd), dtype=torch.float32, device=dev)
+        wsb = tq.tq_workspace_size(tq.TQ_OP_MULTI_ATTN, kq, n_q * hq, H, T)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+        def call():
+            tq.tq_multi_attn(kq, vq, q, tq.TQ_F16, n_q, hq, H, T, plane["k"][0], plane["k"][1], plane["v"][0],
+                             plane["v"][1], True, 0.0, o, ws, wsb)
+
+        call()
+        ms, _ = event_ms(torch, call, max(5, reps // 2), before=lambda: flush.sum())
+        rows = n_q * hq
+        out[f"n_q{n_q}"] = {"us_flushed": round(ms * 1e3, 2), "query_rows": rows,
+                            "row_tokens_per_s": round(rows * T / (ms * 1e-3)),
+                            "us_per_query_token": round(ms * 1e3 / n_q, 3)}
+        log(f"multi-query attention, causal chunk of {n_q} tokens: {ms * 1e3:.1f} us flushed "
+            f"({ms * 1e3 / n_q:.2f} us per query token)")
+    return out
+
+
 def bench_attn(tq, torch, dev, reps, kbits=3, vbits=3):
     """Decode attention: 16 query heads over a 131072-token, 4-KV-head, head_dim-256 cache, K and V in
     the block-32 layout (turbo3 by default; kbits=8, vbits=4 is the asymmetric 8-bit-key cache)."""
@@ -381,6 +408,9 @@ def bench_attn(tq, torch, dev, reps, kbits=3, vbits=3):
 
     for _ in range(3):
         attn()
+    multi = {}
+    if kbits == 3 and vbits == 3:
+        multi = bench_multi(tq, torch, dev, reps, w, kq, vq, plane, H, T, hd, hq, flush)
     warm_ms = batch_ms(torch, attn, reps)
     cold_ms, cold_min = event_ms(torch, attn, reps, before=lambda: flush.sum())
     nbytes = units * (4 * kbits + 2 + 4 * vbits + 2)  # K and V codes and norms
@@ -392,6 +422,8 @@ def bench_attn(tq, torch, dev, reps, kbits=3, vbits=3):
            "GBs_warm": round(nbytes / (warm_ms * 1e-3) / 1e9, 1),
            "frac_hbm_flushed": round(nbytes / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
            "tokens_per_s_flushed": round(H * T / (cold_ms * 1e-3))}
+    if multi:
+        res["multi_query"] = multi
     log(f"attn K{kbits}V{vbits}: {cold_ms * 1e3:.1f} us flushed ({res['GBs_flushed']} GB/s), "
         f"{warm_ms * 1e3:.1f} us warm")
     return res
