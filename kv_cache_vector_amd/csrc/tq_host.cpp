@@ -653,17 +653,18 @@ tq_status check_attn_config(const tq_config* kcfg, const tq_config* vcfg, int n_
   return TQ_OK;
 }
 
-// Row groups of attention: rows = n_q * group (query token, head) pairs per KV head, cut into
-// groups of at most 16 rows.
+// Row groups of attention: rows = n_q * group (query token, head) pairs per KV head.  Up to 16
+// rows go to the decode kernel as one group; more go to the prefill kernel in groups of 128.
 struct AttnShape {
   int64_t rows, n_rg, grp, per_wg, wgs;
 };
 AttnShape attn_shape(int n_q_heads, int n_kv_heads, int64_t n_q, int64_t n_tokens) {
   AttnShape sh{};
   sh.rows = n_q * (n_q_heads / n_kv_heads);
-  sh.grp = sh.rows <= 16 ? sh.rows : 16;
+  const bool prefill = sh.rows > 16;
+  sh.grp = prefill ? tq::attn_prefill_rows() : sh.rows;
   sh.n_rg = (sh.rows + sh.grp - 1) / sh.grp;
-  sh.per_wg = tq::attn_tokens_per_wg((int64_t)n_kv_heads * sh.n_rg, n_tokens);
+  sh.per_wg = tq::attn_tokens_per_wg((int64_t)n_kv_heads * sh.n_rg, n_tokens, prefill);
   sh.wgs = (n_tokens + sh.per_wg - 1) / sh.per_wg;
   return sh;
 }
@@ -696,7 +697,7 @@ tq_status run_attn(const char* who, const tq_config* kcfg, const tq_config* vcfg
     return fail(TQ_ERR_INVALID_ARG, "%s: codes must be 4-byte and norms 2-byte aligned, non-NULL", who);
   const AttnShape sh = attn_shape(n_q_heads, n_kv_heads, n_q, n_tokens);
   if ((int64_t)n_kv_heads * sh.n_rg > 65535)
-    return fail(TQ_ERR_UNSUPPORTED, "%s: at most 65535 (KV head, 16-row group) columns", who);
+    return fail(TQ_ERR_UNSUPPORTED, "%s: at most 65535 (KV head, row group) columns", who);
   const size_t need = attn_workspace(*kcfg, n_q_heads, n_kv_heads, n_q, n_tokens);
   if (!ws || !aligned(ws, 256) || ws_bytes < need)
     return fail(TQ_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned with %zu bytes (got %zu)", who, need,

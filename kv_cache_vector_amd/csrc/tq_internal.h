@@ -112,7 +112,7 @@ struct AttnArgs {
   int64_t n_tokens;
   int64_t n_q;               // query tokens (1 for decode)
   int64_t rows;              // n_q * group rows per KV head
-  int32_t grp;               // rows per row group: rows if rows <= 16, else 16
+  int32_t grp;               // rows per row group: rows if rows <= 16, else the prefill kernel's 128
   int32_t n_rg;              // row groups per KV head
   int32_t causal;            // row of query token i sees tokens j <= n_tokens - n_q + i
   const uint8_t* k_codes;
@@ -137,6 +137,8 @@ hipError_t launch_qjl_scores(const tq_config& cfg, const ScoreArgs& a, hipStream
 int64_t scores_key_tile(int bits);
 int64_t scores_query_block();
 hipError_t launch_decode_attn(int kbits, int vbits, const AttnArgs& a, hipStream_t s);
-int64_t attn_tokens_per_wg(int64_t columns, int64_t n_tokens);
+int64_t attn_tokens_per_wg(int64_t columns, int64_t n_tokens, bool prefill);
+int attn_prefill_rows();  // rows per workgroup of the many-row (prefill) attention kernel
+hipError_t launch_prefill(int kbits, int vbits, const AttnArgs& a, hipStream_t s);  // its main kernel (no merge)
 
 }  // namespace tq

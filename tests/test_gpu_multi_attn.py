@@ -2,7 +2,8 @@
 against the oracle's multi_attention run on the GPU's own codes and norms.
 
 The tolerance is the one derived for tq_decode_attn (see test_gpu_attn.py), evaluated per
-(query token, head) row over the tokens that row sees.
+(query token, head) row over the tokens that row sees.  KV heads with up to 16 rows run the decode
+kernel; more rows run the prefill kernel in groups of 128 (both are covered below).
 """
 import math
 
@@ -77,6 +78,8 @@ def oracle_multi(c: Cache, q, causal):
     (256, 4, 4, 200, 64, True, 3, 3, np.float16),    # a 64-token chunk: 16 row groups, masks crossing tiles
     (128, 1, 8, 130, 3, True, 8, 4, np.float16),     # 8-bit keys
     (128, 3, 1, 70, 70, True, 4, 4, np.float32),     # chunk as long as the cache: row 0 sees one token
+    (256, 2, 4, 1500, 128, True, 3, 3, np.float16),  # 512 rows per KV head: four 128-row prefill groups
+    (256, 1, 8, 700, 40, False, 8, 4, np.float32),   # 320 rows, a partial prefill group, 8-bit keys
 ])
 def test_multi_attn_matrix(hd, H, G, T, n_q, causal, kbits, vbits, qdt):
     k, v, sk, sv = _data(hd + T + n_q, H, T, hd)
