@@ -243,26 +243,47 @@ __device__ __forceinline__ float get_record(const uint16_t* r, uint32_t* word) {
   return __half2float(__ushort_as_half(r[0]));
 }
 
+// 8-bit bucketize tables in LDS: edges t_0 = -1 (sentinel below |u|), t_1..t_127, t_128 = +inf,
+// and for each bin of |u| (bins a third of the narrowest cell, so two neighbouring bins hold at
+// most one edge) the number of edges below the bin's lower end, found by binary search.
+__device__ __forceinline__ void setup_bins8(const EncodeArgs& a, float* edge8, uint8_t* bin8) {
+  for (int i = threadIdx.x; i < 129; i += kBlock) edge8[i] = i == 0 ? -1.0f : a.thr[i - 1];
+  __syncthreads();
+  for (int b = threadIdx.x; b < a.n_bins; b += kBlock) {
+    const float x = (float)b / a.bin_scale;
+    int lo = 0, hi = 127;  // count of t_1..t_127 below x
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (edge8[mid + 1] < x)
+        lo = mid + 1;
+      else
+        hi = mid;
+    }
+    bin8[b] = (uint8_t)lo;
+  }
+  __syncthreads();
+}
+
+// 8-bit code of rotated coordinate y of a unit with norm n (kb = bins per unit of |y|):
+// the bin of |u| = |y| / n (possibly one off), then the two edges around the bin's count
+// give magnitude = #{t_i < |u|} exactly, compared as |y| against t n like the narrow codes.
+__device__ __forceinline__ uint32_t code8(float y, float n, float kb, float top, const float* edge8,
+                                          const uint8_t* bin8) {
+  const float ay = __builtin_fabsf(y);
+  const int m0 = bin8[(int)__builtin_fminf(ay * kb, top)];
+  const float lo = edge8[m0], hi = edge8[m0 + 1];
+  const uint32_t mag = (uint32_t)(m0 + (ay > hi * n ? 1 : 0) - (ay <= lo * n ? 1 : 0));
+  return ((__builtin_bit_cast(uint32_t, y) >> 31) << 7) | (mag & 127u);
+}
+
 template <int BITS, int LPU, bool IN_F32, bool NORM_F32, bool CONTIG, bool AOS>
 __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
   static_assert(!(AOS && NORM_F32), "records carry fp16 norms");
   static_assert(BITS <= 4 || BITS == 8, "1..4 or 8 bits");
   constexpr bool B8 = BITS == 8;
-  // 8 bits: edges t_0 = -1 (sentinel below |u|), t_1..t_127, t_128 = +inf, and the number of
-  // edges below each bin of |u| (bins a third of the narrowest cell, so two neighbouring bins
-  // hold at most one edge)
   __shared__ float edge8[B8 ? 132 : 1];
   __shared__ uint8_t bin8[B8 ? kMaxBins8 : 1];
-  if constexpr (B8) {
-    for (int i = threadIdx.x; i < 129; i += kBlock) edge8[i] = i == 0 ? -1.0f : a.thr[i - 1];
-    for (int b = threadIdx.x; b < a.n_bins; b += kBlock) {
-      const float lo = (float)b / a.bin_scale;
-      int c = 0;
-      for (int i = 0; i < 127; ++i) c += a.thr[i] < lo ? 1 : 0;
-      bin8[b] = (uint8_t)c;
-    }
-    __syncthreads();
-  }
+  if constexpr (B8) setup_bins8(a, edge8, bin8);
   constexpr int CH = IN_F32 ? 8 : 4;  // 16-byte chunks per group
   constexpr int PITCH = 16 * CH + 16;  // LDS bytes per staged group (padded against bank conflicts)
   __shared__ __attribute__((aligned(16))) uint8_t stage[kWaves][64 * PITCH];
@@ -324,19 +345,10 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
 #pragma unroll
     for (int k = 0; k < BITS; ++k) word[k] = 0u;
     if constexpr (B8) {
-      // bin of |u| = |yhat| / n (may be one off), then the two edges around the bin's count:
-      // magnitude = #{t_i < |u|} exactly, compared as |yhat| against t n like the narrow codes
       const float kb = n > 0.0f ? a.bin_scale / n : 0.0f;
       const float top = (float)(a.n_bins - 1);
 #pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        const float ay = __builtin_fabsf(v[j]);
-        const int m0 = bin8[(int)__builtin_fminf(ay * kb, top)];
-        const float lo = edge8[m0], hi = edge8[m0 + 1];
-        const uint32_t mag = (uint32_t)(m0 + (ay > hi * n ? 1 : 0) - (ay <= lo * n ? 1 : 0));
-        const uint32_t code = ((__builtin_bit_cast(uint32_t, v[j]) >> 31) << 7) | (mag & 127u);
-        word[j >> 2] |= code << (8 * (j & 3));
-      }
+      for (int j = 0; j < 32; ++j) word[j >> 2] |= code8(v[j], n, kb, top, edge8, bin8) << (8 * (j & 3));
     } else {
 #pragma unroll
       for (int j = 31; j >= 0; --j) code_chain<BITS>(word, j, v[j], T);
@@ -407,8 +419,9 @@ __device__ __forceinline__ uint32_t join_halves(const uint32_t* lo, const uint32
     return k == 0 ? lo[0] : hi[0];
   } else if constexpr (BITS == 3) {
     return k == 0 ? lo[0] : k == 1 ? (lo[1] & 0xFFFFu) | (hi[0] << 16) : (hi[0] >> 16) | (hi[1] << 16);
-  } else {
-    return k < 2 ? lo[k] : hi[k - 2];
+  } else {  // 4 or 8 bits: whole words per half
+    constexpr int W = 16 * BITS / 32;
+    return k < W ? lo[k] : hi[k - W];
   }
 }
 
@@ -427,7 +440,11 @@ template <int BITS, bool NORM_F32, bool CONTIG>
 __global__ __launch_bounds__(kBlock) void encode32_mfma_kernel(EncodeArgs a) {
   constexpr int CH = 4, PITCH = 16 * CH + 16;
   constexpr int SEGW = (16 * BITS + 31) / 32;  // words of one lane's 16-code segment
+  constexpr bool B8 = BITS == 8;
   __shared__ __attribute__((aligned(16))) uint8_t stage[kWaves][64 * PITCH];
+  __shared__ float edge8[B8 ? 132 : 1];
+  __shared__ uint8_t bin8[B8 ? kMaxBins8 : 1];
+  if constexpr (B8) setup_bins8(a, edge8, bin8);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n32 = lane & 31, h = lane >> 5;
   uint8_t* tile = stage[wave];
@@ -477,13 +494,20 @@ __global__ __launch_bounds__(kBlock) void encode32_mfma_kernel(EncodeArgs a) {
       const float n = __builtin_sqrtf(__builtin_bit_cast(float, (uint32_t)r[0]) +
                                       __builtin_bit_cast(float, (uint32_t)r[1]));
       nrm[s] = n;
-      float T[7];
-#pragma unroll
-      for (int k = 0; k < 7; ++k) T[k] = thr[k] * n;
 #pragma unroll
       for (int k = 0; k < SEGW; ++k) seg[s][k] = 0u;
+      if constexpr (B8) {
+        const float kb = n > 0.0f ? a.bin_scale / n : 0.0f;
+        const float top = (float)(a.n_bins - 1);
 #pragma unroll
-      for (int j = 15; j >= 0; --j) code_chain<BITS>(seg[s], j, y[j], T);
+        for (int j = 0; j < 16; ++j) seg[s][j >> 2] |= code8(y[j], n, kb, top, edge8, bin8) << (8 * (j & 3));
+      } else {
+        float T[7];
+#pragma unroll
+        for (int k = 0; k < 7; ++k) T[k] = thr[k] * n;
+#pragma unroll
+        for (int j = 15; j >= 0; --j) code_chain<BITS>(seg[s], j, y[j], T);
+      }
     }
     __builtin_amdgcn_wave_barrier();
     // lanes < 32 store group n32 (set 0), lanes >= 32 group 32 + n32 (set 1): the swap leaves the
@@ -499,9 +523,19 @@ __global__ __launch_bounds__(kBlock) void encode32_mfma_kernel(EncodeArgs a) {
     const int64_t g = w0 + lane;
     if (g < a.n_groups) {
       uint32_t* cp = reinterpret_cast<uint32_t*>(a.codes + g * (4 * BITS));
+      if constexpr (B8) {  // 32 bytes per group: two 16-byte stores
 #pragma unroll
-      for (int k = 0; k < BITS; ++k)
-        __builtin_nontemporal_store(n == 0.0f ? zero_unit_word<BITS>(k) : join_halves<BITS>(lo, hi, k), cp + k);
+        for (int c = 0; c < 2; ++c) {
+          u32x4 w;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) w[k] = n == 0.0f ? zero_unit_word<BITS>(4 * c + k) : join_halves<BITS>(lo, hi, 4 * c + k);
+          __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(cp) + c);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < BITS; ++k)
+          __builtin_nontemporal_store(n == 0.0f ? zero_unit_word<BITS>(k) : join_halves<BITS>(lo, hi, k), cp + k);
+      }
       if constexpr (NORM_F32)
         static_cast<float*>(a.norms)[g] = n;
       else
@@ -833,7 +867,7 @@ hipError_t encode_dispatch_dtype(const tq_config& cfg, const EncodeArgs& a, hipS
       hipLaunchKernelGGL((encode_kernel<BITS, LPU, false, false, CONTIG, true>), grid, block, 0, s, a);
     return hipGetLastError();
   }
-  if constexpr (LPU == 1 && BITS <= 4) {
+  if constexpr (LPU == 1) {
     if (!in32) {
       if (n32)
         hipLaunchKernelGGL((encode32_mfma_kernel<BITS, true, CONTIG>), grid, block, 0, s, a);
