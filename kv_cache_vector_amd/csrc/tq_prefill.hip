@@ -35,6 +35,7 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(AttnArgs a) {
   constexpr int CK = 1 << LGCK, CV = 1 << LGCV;
   constexpr int SLOTS = HD / 8;  // 16-byte slots per decoded token row
   constexpr int NCT = HD / 16;   // 16-coordinate output tiles
+  constexpr int PSTR = kTile + 8;  // fp16 per weight row (144 bytes: rows 4 apart land 64 banks apart)
   constexpr int NT = 64 * kPWaves;
   struct Smem {
     uint32_t ktab[K8 ? KL * CK : 2 * KL * KL * CK + 1];
@@ -43,14 +44,15 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(AttnArgs a) {
     __attribute__((aligned(16))) _Float16 khi[kTile * HD];
     __attribute__((aligned(16))) _Float16 klo[kTile * HD];
     __attribute__((aligned(16))) _Float16 vt[kTile * HD];
-    __attribute__((aligned(16))) _Float16 pt[kPWaves][kPRT * 16 * kTile];
+    __attribute__((aligned(16))) _Float16 pt[kPWaves][kPRT * 16 * PSTR];
   };
   __shared__ Smem sm;
   uint32_t* kth = sm.ktab;
   uint32_t* ktl = sm.ktab + (K8 ? 0 : KL * KL * CK + 1);
   // K rows: slot 4b + g (8 coordinates) of token t at slot ^ (t & 15), so the 16 tokens of a
-  // subtile read one slot each from distinct banks.  V rows: slot 2c + k (half k of 16-coordinate
-  // chunk c) at slot ^ vsw(t), distinct over the 16 tokens one transposing load reads.
+  // subtile read one slot each from distinct banks, and 16 consecutive tokens written by 16
+  // lanes (one block each) do too.  V rows: slot 2c + k (half k of 16-coordinate chunk c) at
+  // slot ^ vsw(t), distinct over the 16 tokens one transposing load reads.
   auto kslot = [](int t, int slot) { return t * HD + 8 * (slot ^ (t & 15)); };
   auto vsw = [](int t) { return (2 * ((((t >> 3) & 3) << 2) | (t & 3))) & (SLOTS - 1); };
   auto vslot = [&](int t, int c, int k) { return t * HD + 8 * ((2 * c + k) ^ vsw(t)); };
@@ -84,8 +86,8 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(AttnArgs a) {
 #pragma unroll
     for (int k = 0; k < UPT; ++k) {
       const int u0 = tid + NT * k;
-      const uint32_t t = min((uint32_t)(u0 / NB), last);
-      const uint32_t u = t * NB + (uint32_t)(u0 % NB);
+      const uint32_t t = min((uint32_t)(u0 % kTile), last);
+      const uint32_t u = t * NB + (uint32_t)(u0 / kTile);
 #pragma unroll
       for (int q = 0; q < KB; ++q) r.kw[k][q] = kp0[u * KB + q];
 #pragma unroll
@@ -186,7 +188,7 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(AttnArgs a) {
     // (8 coordinates) at a time, which keeps few decoded words live
 #pragma unroll
     for (int k = 0; k < (decoder ? UPT : 0); ++k) {
-      const int u0 = tid + NT * k, ut = u0 / NB, ub = u0 % NB;
+      const int u0 = tid + NT * k, ut = u0 % kTile, ub = u0 / kTile;  // a wave decodes one block of all 64 tokens
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         uint32_t hi[4], lo[4];
@@ -326,7 +328,7 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(AttnArgs a) {
         for (int st = 0; st < 4; ++st) {
           const float p = __expf(s[rt][st][i] - m_run[rt][i]);
           lsum[rt][i] += p;
-          ptile[(16 * rt + 4 * g + i) * kTile + 16 * st + row] = (_Float16)p;
+          ptile[(16 * rt + 4 * g + i) * PSTR + 16 * st + row] = (_Float16)p;
         }
       }
     }
@@ -338,7 +340,7 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(AttnArgs a) {
       v8h av[kPRT];
 #pragma unroll
       for (int rt = 0; rt < kPRT; ++rt)
-        av[rt] = *reinterpret_cast<const v8h*>(ptile + (16 * rt + row) * kTile + 32 * half + 8 * g);
+        av[rt] = *reinterpret_cast<const v8h*>(ptile + (16 * rt + row) * PSTR + 32 * half + 8 * g);
       const int t1 = 32 * half + 8 * g + (row >> 2), t2 = t1 + 4;
       lds_short* base = (lds_short*)sm.vt;
 #pragma unroll
