@@ -843,14 +843,7 @@ __global__ __launch_bounds__(kBlock) void decode32_mfma_kernel(DecodeArgs a) {
 // Workgroups per launch: enough resident waves to cover HBM latency, with a
 // grid-stride loop over the rest (amortises the per-lane set-up).
 int64_t grid_for(int64_t n_groups, int per_cu) {
-  static int cus = 0;
-  if (!cus) {
-    int dev = 0;
-    hipDeviceProp_t prop;
-    if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
-      cus = prop.multiProcessorCount;
-    if (cus <= 0) cus = 256;
-  }
+  const int cus = device_cu_count();
   int64_t need = (n_groups + kBlock - 1) / kBlock;
   int64_t cap = (int64_t)cus * per_cu;
   return need < cap ? need : cap;

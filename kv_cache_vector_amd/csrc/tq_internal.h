@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "tq.h"
 
 namespace tq {
@@ -127,6 +129,23 @@ struct AttnArgs {
   float klevel[256], vlevel[16];
   float kscale;              // softmax scale / sqrt(32): score = kscale * sum_b n_b <H D q_b, c_b>
 };
+
+// Compute units of the current device, cached per device (relaxed atomics: concurrent first calls
+// store the same value).  Launch sizing only; 256 if the query fails.
+inline int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  hipDeviceProp_t prop;
+  int cus = 256;
+  if (hipGetDeviceProperties(&prop, dev) == hipSuccess && prop.multiProcessorCount > 0) cus = prop.multiProcessorCount;
+  if (dev >= 0 && dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
 
 // launchers (return hipGetLastError() of the launch)
 hipError_t launch_encode(const tq_config& cfg, const EncodeArgs& a, hipStream_t s);

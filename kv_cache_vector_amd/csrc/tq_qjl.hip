@@ -371,17 +371,7 @@ __global__ __launch_bounds__(kBlock) void qjl_decode_kernel(QjlDecodeArgs a) {
   }
 }
 
-int cu_count() {
-  static int cus = 0;
-  if (!cus) {
-    int dev = 0;
-    hipDeviceProp_t prop;
-    if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
-      cus = prop.multiProcessorCount;
-    if (cus <= 0) cus = 256;
-  }
-  return cus;
-}
+int cu_count() { return device_cu_count(); }
 
 int64_t qjl_grid(int64_t n_groups) {
   int64_t need = (n_groups + kBlock - 1) / kBlock;

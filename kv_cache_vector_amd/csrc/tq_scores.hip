@@ -412,12 +412,14 @@ template <int NP, int KD, int KM>
 hipError_t launch_scores_t(const ScoreArgs& a, hipStream_t s) {
   constexpr int CB = NP <= 2 ? TQ_SCORES_CB2 : 1;
   constexpr int lds = ScoresLds<NP, KD, KM, CB>::TOTAL;
-  static bool ready = false;  // more than the default 64 KiB of dynamic LDS for the larger records
-  if (!ready) {
+  // more than the default 64 KiB of dynamic LDS for the larger records; setting it twice from
+  // racing first calls is harmless
+  static std::atomic<bool> ready{false};
+  if (!ready.load(std::memory_order_acquire)) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scores_kernel<NP, KD, KM, CB>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
-    ready = true;
+    ready.store(true, std::memory_order_release);
   }
   dim3 grid((unsigned)(a.n_k_pad / (128 * CB)), (unsigned)((a.n_q_pad + kQChunk - 1) / kQChunk));
   hipLaunchKernelGGL((scores_kernel<NP, KD, KM, CB>), grid, dim3(256), lds, s, a);
