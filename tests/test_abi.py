@@ -183,3 +183,56 @@ def test_status_strings():
     assert L.tq_status_str(tq.TQ_OK) == b"ok"
     assert L.tq_status_str(tq.TQ_ERR_WORKSPACE).startswith(b"workspace")
     assert L.tq_status_str(99) == b"unknown status"
+
+
+def _attn_ws(qz, rows, n_kv, tokens, op=None):
+    return tq.lib().tq_workspace_size(tq.TQ_OP_MULTI_ATTN if op is None else op, ctypes.byref(qz.cfg), rows, n_kv,
+                                      tokens)
+
+
+def test_attention_validation():
+    """tq_decode_attn / tq_multi_attn reject bad formats and arguments before any launch."""
+    E, U, W, OK = tq.TQ_ERR_INVALID_ARG, tq.TQ_ERR_UNSUPPORTED, tq.TQ_ERR_WORKSPACE, tq.TQ_OK
+    L = tq.lib()
+    k3 = _q(head_dim=256, signs=np.ones(32))
+    v3 = _q(head_dim=256, signs=np.ones(32))
+    big = 1 << 24
+
+    def multi(kq=k3, vq=v3, q=FAKE, qt=tq.TQ_F16, n_q=4, hq=8, hkv=2, T=1000, codes=FAKE, causal=1, scale=0.0,
+              out=FAKE, ws=FAKE, wsb=big):
+        return L.tq_multi_attn(ctypes.byref(kq.cfg), ctypes.byref(vq.cfg), q, qt, n_q, hq, hkv, T, codes, FAKE, codes,
+                               FAKE, causal, scale, out, ws, wsb, None)
+
+    assert multi(n_q=0) == OK and multi(T=0, causal=0) == OK  # nothing to do
+    assert multi(T=0) == E  # a causal chunk longer than the (empty) cache
+    assert multi(n_q=-1) == E
+    assert multi(n_q=1001) == E  # a causal chunk longer than the cache
+    assert multi(hq=6, hkv=4) == E  # query heads not a multiple of KV heads
+    assert multi(qt=5) == E
+    assert multi(q=None) == E and multi(out=FAKE + 2) == E
+    assert multi(codes=FAKE + 2) == E
+    assert multi(scale=float("nan")) == E
+    assert multi(ws=None) == W and multi(wsb=256) == W and multi(ws=FAKE + 64) == W
+    assert multi(vq=_q(head_dim=256, bits=8, signs=np.ones(32))) == U  # 8-bit values
+    assert multi(kq=_q(head_dim=256, bits=2, signs=np.ones(32))) == U  # 2-bit keys
+    assert multi(kq=_q(head_dim=64, dt=32, signs=np.ones(32)), vq=_q(head_dim=64, dt=32, signs=np.ones(32))) == U
+    assert multi(kq=_q(head_dim=256, dt=64, signs=np.ones(64)), vq=_q(head_dim=256, dt=64, signs=np.ones(64))) == U
+    assert multi(vq=_q(head_dim=128, signs=np.ones(32))) == E  # K and V head_dim differ
+    nc = _q(head_dim=256, signs=np.ones(32), flags=tq.TQ_NORM_CORRECT)
+    assert multi(kq=nc) == U
+    assert L.tq_decode_attn(ctypes.byref(k3.cfg), ctypes.byref(v3.cfg), FAKE, tq.TQ_F16, 8, 2, 1000, FAKE, FAKE, FAKE,
+                            FAKE, 0.0, FAKE, None, 0, None) == W
+
+
+def test_attention_workspace_sizes():
+    """Partials: one (head_dim + 2)-float record per row and token range; up to 16 rows per KV head
+    form one group (decode kernel), more go in 128-row groups (prefill kernel)."""
+    qz = _q(head_dim=256, signs=np.ones(32))
+    dec = tq.lib().tq_workspace_size(tq.TQ_OP_DECODE_ATTN, ctypes.byref(qz.cfg), 16, 4, 131072)
+    assert dec > 0 and dec == _attn_ws(qz, 16, 4, 131072)  # one query token = the decode call
+    assert dec % 256 == 0 and dec >= 16 * 258 * 4
+    # more rows never shrink the workspace, and a 128-row group holds every row it serves
+    sizes = [_attn_ws(qz, 16 * n_q, 4, 131072) for n_q in (1, 2, 4, 8, 64)]
+    assert all(b >= a for a, b in zip(sizes, sizes[1:]))
+    assert _attn_ws(qz, 16 * 64, 4, 131072) >= 16 * 64 * 258 * 4
+    assert _attn_ws(qz, 0, 4, 100) == 0 and _attn_ws(qz, 6, 4, 100) == 0  # no rows / not a multiple
