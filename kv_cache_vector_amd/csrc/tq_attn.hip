@@ -510,7 +510,7 @@ __global__ __launch_bounds__(256) void attn_merge(AttnArgs a) {
   // one pass over this lane's partials with a running reference (the partials' own references
   // differ; a larger one rescales what was summed so far)
   float m = -INFINITY, acc = 0.0f, l = 0.0f;
-#pragma unroll 4
+#pragma unroll 16
   for (int p = pl; p < n_part; p += kMergeLanes) {
     const float* pb = base + p * stride;
     const float mp = pb[HD], lp = pb[HD + 1], xp = pb[32 * b + dl];
