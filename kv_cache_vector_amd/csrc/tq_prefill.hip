@@ -40,7 +40,7 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(AttnArgs a) {
   struct Smem {
     uint32_t ktab[K8 ? KL * CK : 2 * KL * KL * CK + 1];
     uint32_t vtab[VL * VL * CV];
-    float kn[kTile][NB];
+    float kn[kTile][NB + 1];  // +1: the 16 tokens of a subtile read distinct banks
     __attribute__((aligned(16))) _Float16 khi[kTile * HD];
     __attribute__((aligned(16))) _Float16 klo[kTile * HD];
     __attribute__((aligned(16))) _Float16 vt[kTile * HD];
