@@ -217,3 +217,47 @@ def test_deterministic_repeat():
         outs.append((codes.clone(), norms.clone()))
     torch.cuda.synchronize()
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+@pytest.fixture(scope="module")
+def qwen_full():
+    from synth.workloads import qwen3_8b_kv
+
+    return qwen3_8b_kv()
+
+
+@pytest.mark.parametrize("kbits,vbits", [(3, 3), (4, 4), (8, 4)])
+def test_block32_full_size_sampled(qwen_full, kbits, vbits):
+    """The Qwen3-8B-shaped cache at full size (36 x 8 x 16384 x 128, K and V fp16) in block-32
+    planes, each half encoded and decoded by one call as the step timing launches it (turbo3,
+    turbo4, and 8-bit keys with 4-bit values): codes, norms and decoded rows of sampled rows
+    (the first and last row among them) against the oracle."""
+    w = qwen_full
+    rows = w["k"].shape[0] * w["k"].shape[1] * w["k"].shape[2]
+    rng = np.random.default_rng(11 + kbits)
+    sample = np.unique(np.concatenate([rng.integers(0, rows, 3000), [0, rows - 1]]))
+    sidx = torch.from_numpy(sample).to(DEV)
+    for half, s, bits in (("k", "signs_k", kbits), ("v", "signs_v", vbits)):
+        x_np = w[half].reshape(rows, 128)
+        qz = tq.Quantizer(128, 32, bits, w[s])
+        x = torch.from_numpy(x_np).to(DEV)
+        rb = 4 * 4 * bits  # code bytes of one row: four 32-value groups
+        codes = torch.empty(rows * rb, dtype=torch.uint8, device=DEV)
+        norms = torch.empty(rows * 4, dtype=torch.float16, device=DEV)
+        tq.tq_quantize(qz, x, rows, 128, codes, norms)
+        del x
+        y = torch.empty((rows, 128), dtype=torch.float16, device=DEV)
+        tq.tq_dequantize(qz, codes, norms, None, None, rows, y, tq.TQ_F16, 128)
+        torch.cuda.synchronize()
+        c = codes.view(rows, rb)[sidx].cpu().numpy()
+        n = norms.view(rows, 4)[sidx].cpu().numpy().reshape(-1)
+        ys = y[sidx].cpu().numpy()
+        del codes, norms, y
+        cb = Codebook.build(bits, 32)
+        orc = quantize(x_np[sample].astype(np.float64), w[s], cb)
+        stats = check_codes(c, orc, cb, bits, 32)
+        stats.update(check_norms(n, orc["norms"]))
+        ref = dequantize(c.reshape(-1, 4 * bits), n, w[s], cb)
+        stats["f16_ulp_off"] = check_decoded_f16(ys, ref, n, 32)
+        print(half, bits, stats)
+        assert stats["in_band_mismatch"] <= 1e-5 * stats["coords"]
