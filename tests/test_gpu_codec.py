@@ -261,3 +261,37 @@ def test_block32_full_size_sampled(qwen_full, kbits, vbits):
         stats["f16_ulp_off"] = check_decoded_f16(ys, ref, n, 32)
         print(half, bits, stats)
         assert stats["in_band_mismatch"] <= 1e-5 * stats["coords"]
+
+
+def test_llama_full_size_sampled():
+    """The Llama-3.2-1B-shaped cache at full size (16 x 8 x 2048 vectors of 64 per half, fp16),
+    4 bits with a per-vector norm and norm correction, one call per half: codes, norms and
+    decoded rows of sampled rows against the oracle."""
+    from synth.workloads import llama_1b_kv
+
+    w = llama_1b_kv()
+    rows = w["k"].shape[0] * w["k"].shape[1] * w["k"].shape[2]
+    rng = np.random.default_rng(5)
+    sample = np.unique(np.concatenate([rng.integers(0, rows, 4000), [0, rows - 1]]))
+    sidx = torch.from_numpy(sample).to(DEV)
+    cb = Codebook.build(4, 64)
+    for half, s in (("k", "signs_k"), ("v", "signs_v")):
+        x_np = w[half].reshape(rows, 64)
+        qz = tq.Quantizer(64, 64, 4, w[s], flags=tq.TQ_NORM_CORRECT)
+        x = torch.from_numpy(x_np).to(DEV)
+        codes = torch.empty(rows * 32, dtype=torch.uint8, device=DEV)
+        norms = torch.empty(rows, dtype=torch.float16, device=DEV)
+        tq.tq_quantize(qz, x, rows, 64, codes, norms)
+        y = torch.empty((rows, 64), dtype=torch.float32, device=DEV)
+        tq.tq_dequantize(qz, codes, norms, None, None, rows, y, tq.TQ_F32, 64)
+        torch.cuda.synchronize()
+        c = codes.view(rows, 32)[sidx].cpu().numpy()
+        n = norms[sidx].cpu().numpy()
+        ys = y[sidx].cpu().numpy()
+        orc = quantize(x_np[sample].astype(np.float64), w[s], cb)
+        stats = check_codes(c, orc, cb, 4, 64)
+        stats.update(check_norms(n, orc["norms"]))
+        ref = dequantize(c, n, w[s], cb, nc=True)
+        stats["decode_err"] = check_decoded_f32(ys, ref, n, 64)
+        print(half, stats)
+        assert stats["in_band_mismatch"] <= 1e-5 * stats["coords"]
