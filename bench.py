@@ -41,6 +41,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0
 LAYERS, KV_HEADS, TOKENS, HEAD_DIM, DT = 36, 8, 16384, 128, 32
+SAMPLE_ROWS = 4096  # head vectors of the oracle's sample (layer 0, head 0 K)
 CODEBOOK = "gaussian"  # set from --codebook
 
 
@@ -198,18 +199,24 @@ def measured_traffic(tag: str):
     return int(v) if v else None
 
 
-def cpu_baseline(rows_total: int, bits: int, target_s: float = 15.0) -> dict:
+def cpu_baseline(rows_total: int, bits: int, target_s: float = 15.0, x_rows=None, gpu_codes=None,
+                 gpu_norms=None) -> dict:
     """The fp64 oracle (as it stands) on a bounded sample of the same cache: encode + decode of
-    a slice of whole head vectors, timed on the host; reported in the same unit (fp16 GB/s)."""
+    a slice of whole head vectors, timed on the host; reported in the same unit (fp16 GB/s).
+    With the GPU's codes and norms of that slice, also the parity counts of the sample: coordinates
+    within 1e-6 (unit-variance scale, i.e. 1e-6/sqrt(d) for the N(0, 1/d) cells) of a cell edge,
+    codes that differ from the oracle's, those outside that band, and norms that differ."""
     import numpy as np
 
     import synth
-    from oracle import Codebook, dequantize, quantize
+    from oracle import Codebook, code_to_index, dequantize, quantize, unpack_codes
 
     cb = Codebook.build(bits, DT)
     signs = synth.signs(0, synth.STREAM_SIGNS_K, DT)
-    rows = 4096
-    x = synth.kv_tensor(0, 1, 1, 0, rows, HEAD_DIM).reshape(rows, HEAD_DIM).astype(np.float64)
+    rows = SAMPLE_ROWS
+    if x_rows is None:
+        x_rows = synth.kv_tensor(0, 1, 1, 0, rows, HEAD_DIM).reshape(rows, HEAD_DIM)
+    x = np.asarray(x_rows[:rows], dtype=np.float64)
     done_rows, t0 = 0, time.perf_counter()
     while time.perf_counter() - t0 < target_s:
         q = quantize(x, signs, cb)
@@ -217,9 +224,19 @@ def cpu_baseline(rows_total: int, bits: int, target_s: float = 15.0) -> dict:
         done_rows += rows
     dt_s = time.perf_counter() - t0
     fp16_bytes = done_rows * HEAD_DIM * 2 * 2  # encoded in + decoded out
-    return {"value": fp16_bytes / dt_s / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done_rows} head vectors ({done_rows * HEAD_DIM // DT} blocks) of layer 0 / head 0 K, "
-                      f"encode+decode at {bits} bits, {dt_s:.1f} s single-threaded numpy float64"}
+    out = {"value": fp16_bytes / dt_s / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": f"{done_rows} head vectors ({done_rows * HEAD_DIM // DT} blocks) of layer 0 / head 0 K, "
+                     f"encode+decode at {bits} bits, {dt_s:.1f} s single-threaded numpy float64"}
+    if gpu_codes is not None:
+        g = code_to_index(unpack_codes(np.asarray(gpu_codes).reshape(-1, DT * bits // 8), bits, DT), bits)
+        o = code_to_index(unpack_codes(q["codes"], bits, DT), bits)
+        dist = np.min(np.abs(q["y_unit"][..., None] - np.asarray(cb.unit_bounds)), axis=-1)
+        near, diff = dist < 1e-6, g != o
+        nd = np.asarray(gpu_norms).astype(np.float16).view(np.uint16) != q["norms"].astype(np.float16).view(np.uint16)
+        out["parity"] = {"rows": rows, "coords": int(g.size), "near_edge": int(near.sum()),
+                         "code_mismatch": int(diff.sum()), "code_mismatch_off_edge": int((diff & ~near).sum()),
+                         "norm_mismatch": int(nd.sum())}
+    return out
 
 
 def run_k8v4(tq, torch, dev, rows, k, v, ok, ov, signs_k, signs_v, args):
@@ -466,7 +483,7 @@ def main():
     copy_gbs = 2 * k.numel() * 2 / (copy_ms * 1e-3) / 1e9
     log(f"device copy of one half-cache: {copy_ms:.3f} ms ({copy_gbs:.0f} GB/s read+write)")
 
-    def run_codec(bits, tag, sk, sv, **kw):
+    def run_codec(bits, tag, sk, sv, keep=None, **kw):
         codec = Codec(tq, torch, dev, rows, bits, sk, sv, **kw)
         launches = codec.launches(k, v, ok, ov)
 
@@ -479,6 +496,10 @@ def main():
         graphed = graph is not None
         del graph
         enc_ms, dec_ms = per_kernel_ms(torch, codec, k, v, ok, ov, max(5, args.steps // 2))
+        if keep is not None:  # the K codes and norms of the first rows, for the oracle's sample
+            keep["codes"] = codec.ck[:SAMPLE_ROWS * HEAD_DIM // DT * DT * bits // 8].cpu().numpy()
+            keep["norms"] = codec.nk[:SAMPLE_ROWS * HEAD_DIM // DT].cpu().numpy()
+            keep["x"] = k[:SAMPLE_ROWS].cpu().numpy()
         ab = algorithmic_bytes(codec.units, bits)
         log(f"{tag} {bits}-bit: step {ms:.3f} ms, encode {enc_ms:.3f} ms ({ab['per_launch'] / enc_ms / 1e6:.0f} GB/s), "
             f"decode {dec_ms:.3f} ms ({ab['per_launch'] / dec_ms / 1e6:.0f} GB/s)")
@@ -487,7 +508,9 @@ def main():
         return {"ms": ms, "enc_ms": enc_ms, "dec_ms": dec_ms, "bytes": ab, "units": ab["fp16"] // 64,
                 "graphed": graphed}
 
-    results = {bits: run_codec(bits, "block-32", signs_k, signs_v) for bits in (3, 4)}
+    kept = {}
+    results = {bits: run_codec(bits, "block-32", signs_k, signs_v, keep=kept if bits == 3 else None)
+               for bits in (3, 4)}
     # the fork's production layout: 128-value chunks, norm copied into 14/18-byte records, Beta codebook
     import synth
 
@@ -563,7 +586,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
-        out["cpu_baseline"] = cpu_baseline(rows, 3)
+        out["cpu_baseline"] = cpu_baseline(rows, 3, x_rows=kept.get("x"), gpu_codes=kept.get("codes"),
+                                           gpu_norms=kept.get("norms"))
     print(json.dumps(out), flush=True)
 
 
