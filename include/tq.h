@@ -226,8 +226,9 @@ tq_status tq_qjl_scores(const tq_config* cfg, const void* q, tq_dtype q_dtype, i
  *               [Scratch] §4 "Finding 1" and §10 "Takeaways"), equal head_dim
  *               of 128 or 256, no flags (TQ_ERR_UNSUPPORTED otherwise)
  *   q           device, [n_q_heads][head_dim] of q_dtype, contiguous
- *   n_q_heads   a multiple of n_kv_heads (up to 16 heads share each K and V
- *               read; more are processed in groups of 16)
+ *   n_q_heads   a multiple of n_kv_heads (all heads of a KV head share each
+ *               K and V read: up to 16 in the decode kernel, more in row
+ *               groups of 128 of the multi-row kernel)
  *   k_codes, v_codes  device, 4-byte aligned, units in (kv head, token,
  *               block) order, i.e. rows of tq_quantize over
  *               [n_kv_heads][n_tokens][head_dim]
@@ -262,11 +263,12 @@ tq_status tq_decode_attn(const tq_config* kcfg, const tq_config* vcfg, const voi
  *   ws    256-byte aligned device workspace of
  *         tq_workspace_size(TQ_OP_MULTI_ATTN, kcfg, n_q * n_q_heads,
  *         n_kv_heads, n_tokens) bytes (contents are scratch)
- * The (query token, head) rows of one KV head are processed in groups of up
- * to 16 that share each K and V read.  n_q = 1 without a mask is
- * tq_decode_attn.  Errors: causal with n_q > n_tokens is TQ_ERR_INVALID_ARG;
- * more than 65535 (KV head, 16-row group) pairs or 2^31 rows is
- * TQ_ERR_UNSUPPORTED; n_q = 0 or n_tokens = 0 leaves out untouched.
+ * The (query token, head) rows of one KV head are processed in row groups
+ * that share each K and V read: one group when there are at most 16 rows,
+ * otherwise groups of 128 rows.  n_q = 1 without a mask is tq_decode_attn.
+ * Errors: causal with n_q > n_tokens is TQ_ERR_INVALID_ARG; more than 65535
+ * (KV head, row group) pairs or 2^31 rows is TQ_ERR_UNSUPPORTED; n_q = 0 or
+ * n_tokens = 0 leaves out untouched.
  * Precision as tq_decode_attn.
  */
 tq_status tq_multi_attn(const tq_config* kcfg, const tq_config* vcfg, const void* q, tq_dtype q_dtype, int64_t n_q,
