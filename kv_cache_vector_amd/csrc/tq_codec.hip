@@ -116,6 +116,34 @@ __device__ __forceinline__ void stage_in(uint8_t* tile, const char* base, int64_
   }
 }
 
+// stage_in in two halves, for a loop that loads one tile ahead: the loads into registers ...
+template <int CH, int ES, bool CONTIG>
+__device__ __forceinline__ void stage_load(u32x4* t, const char* base, int64_t w0, int64_t n_groups, int32_t gpr,
+                                           int64_t ld, int lane) {
+#pragma unroll
+  for (int k = 0; k < CH; ++k) {
+    const int ci = 64 * k + lane;
+    const int grp = ci / CH, c = ci % CH;
+    if (w0 + 64 <= n_groups) {
+      t[k] = load_stream(reinterpret_cast<const u32x4*>(base + ES * group_offset<CONTIG>(w0 + grp, gpr, ld) + 16 * c));
+    } else {
+      t[k] = u32x4{0u, 0u, 0u, 0u};
+      if (w0 + grp < n_groups)
+        t[k] = load_stream(reinterpret_cast<const u32x4*>(base + ES * group_offset<CONTIG>(w0 + grp, gpr, ld) + 16 * c));
+    }
+  }
+}
+
+// ... and their copy into the wave's LDS tile
+template <int CH, int PITCH>
+__device__ __forceinline__ void stage_put(uint8_t* tile, const u32x4* t, int lane) {
+#pragma unroll
+  for (int k = 0; k < CH; ++k) {
+    const int ci = 64 * k + lane;
+    *reinterpret_cast<u32x4*>(tile + (ci / CH) * PITCH + 16 * (ci % CH)) = t[k];
+  }
+}
+
 // Write the wave's 64 staged groups from the LDS tile to global memory, one
 // contiguous 1 KiB span per store instruction (the mirror of stage_in).
 template <int CH, int PITCH, int ES, bool CONTIG>
@@ -445,7 +473,11 @@ __global__ __launch_bounds__(kBlock) void encode32_mfma_kernel(EncodeArgs a) {
   __shared__ float edge8[B8 ? 132 : 1];
   __shared__ uint8_t bin8[B8 ? kMaxBins8 : 1];
   if constexpr (B8) setup_bins8(a, edge8, bin8);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // 4 bits: the next tile's loads go out before this tile's compute and stores (measured faster at
+  // 4 bits, slower at 3)
+  constexpr bool PIPE = BITS == 4;
+  const int lane = threadIdx.x & 63;
+  const int wave = PIPE ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : threadIdx.x >> 6;
   const int n32 = lane & 31, h = lane >> 5;
   uint8_t* tile = stage[wave];
   const uint32_t dword = a.dbits[0];
@@ -468,8 +500,19 @@ __global__ __launch_bounds__(kBlock) void encode32_mfma_kernel(EncodeArgs a) {
   const char* xbase = static_cast<const char*>(a.x);
 
   const int64_t stride = (int64_t)gridDim.x * kBlock;
+  u32x4 pre[PIPE ? CH : 1];
+  if constexpr (PIPE) {
+    const int64_t f0 = (int64_t)blockIdx.x * kBlock + wave * 64;
+    if (f0 < a.n_groups) stage_load<CH, 2, CONTIG>(pre, xbase, f0, a.n_groups, a.groups_per_row, a.ld_x, lane);
+  }
   for (int64_t w0 = (int64_t)blockIdx.x * kBlock + wave * 64; w0 < a.n_groups; w0 += stride) {
-    stage_in<CH, PITCH, 2, CONTIG>(tile, xbase, w0, a.n_groups, a.groups_per_row, a.ld_x, lane);
+    if constexpr (PIPE) {
+      stage_put<CH, PITCH>(tile, pre, lane);
+      if (w0 + stride < a.n_groups)
+        stage_load<CH, 2, CONTIG>(pre, xbase, w0 + stride, a.n_groups, a.groups_per_row, a.ld_x, lane);
+    } else {
+      stage_in<CH, PITCH, 2, CONTIG>(tile, xbase, w0, a.n_groups, a.groups_per_row, a.ld_x, lane);
+    }
     __builtin_amdgcn_wave_barrier();
     uint32_t seg[2][SEGW];
     float nrm[2];
@@ -521,7 +564,7 @@ __global__ __launch_bounds__(kBlock) void encode32_mfma_kernel(EncodeArgs a) {
     }
     const float n = h ? nrm[1] : nrm[0];
     const int64_t g = w0 + lane;
-    if (g < a.n_groups) {
+    if (PIPE ? (w0 + 64 <= a.n_groups || g < a.n_groups) : g < a.n_groups) {
       uint32_t* cp = reinterpret_cast<uint32_t*>(a.codes + g * (4 * BITS));
       if constexpr (B8) {  // 32 bytes per group: two 16-byte stores
 #pragma unroll
