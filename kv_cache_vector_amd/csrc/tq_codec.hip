@@ -473,9 +473,9 @@ __global__ __launch_bounds__(kBlock) void encode32_mfma_kernel(EncodeArgs a) {
   __shared__ float edge8[B8 ? 132 : 1];
   __shared__ uint8_t bin8[B8 ? kMaxBins8 : 1];
   if constexpr (B8) setup_bins8(a, edge8, bin8);
-  // 4 bits: the next tile's loads go out before this tile's compute and stores (measured faster at
-  // 4 bits, slower at 3)
-  constexpr bool PIPE = BITS == 4;
+  // 4 and 8 bits: the next tile's loads go out before this tile's compute and stores (measured
+  // faster at 4 and 8 bits, slower at 3)
+  constexpr bool PIPE = BITS == 4 || BITS == 8;
   const int lane = threadIdx.x & 63;
   const int wave = PIPE ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : threadIdx.x >> 6;
   const int n32 = lane & 31, h = lane >> 5;
