@@ -17,7 +17,13 @@ chunks, the chunk norm copied into each 14/18-byte 32-value record, Beta
 codebook for d = 128), reported as `fork_layout`, and with 8-bit keys and
 4-bit values (block-32), reported as `k8v4` (neither is part of `value`).
 
-Two more workloads are timed and reported beside it (not part of `value`):
+More workloads are timed and reported beside it (not part of `value`):
+  vectors_fp32  4096 vectors x 128 fp32, 3 bits, one fp32 norm per vector
+        (whole-vector units): device time per encode and decode call;
+  llama_1b      the Llama-3.2-1B-shaped cache, 16 layers x 8 KV heads x 2048
+        tokens x head_dim 64 per half, fp16, 4 bits with a per-vector norm and
+        norm correction: the same four-launch step, flushed and warm (the
+        cache fits the 256 MB last-level cache);
   qjl   65536 keys x 128 fp16 encoded at 2 bits + the 1-bit QJL residual
         (dense Gaussian S, m = 128), then scored against 4096 queries
         (32 heads x 128 tokens): keys/s and scores/s;
@@ -26,6 +32,11 @@ Two more workloads are timed and reported beside it (not part of `value`):
         attn.k8v4, 8-bit K with 4-bit V): time per call and compressed bytes
         read per second, with the cache warm in the last-level cache and with
         it flushed before each call.
+
+`cpu_baseline` times the CPU oracle (unchanged, float64 numpy) on the host:
+encode + decode of whole layers of the same cache in worker processes, one
+per core of this GPU's CPU share and then a single one, and the oracle's QJL
+scores and decode attention on the other two workloads.
 """
 from __future__ import annotations
 
@@ -199,41 +210,212 @@ def measured_traffic(tag: str):
     return int(v) if v else None
 
 
-def cpu_baseline(rows_total: int, bits: int, target_s: float = 15.0, x_rows=None, gpu_codes=None,
-                 gpu_norms=None) -> dict:
-    """The fp64 oracle (as it stands) on a bounded sample of the same cache: encode + decode of
-    a slice of whole head vectors, timed on the host; reported in the same unit (fp16 GB/s).
-    With the GPU's codes and norms of that slice, also the parity counts of the sample: coordinates
-    within 1e-6 (unit-variance scale, i.e. 1e-6/sqrt(d) for the N(0, 1/d) cells) of a cell edge,
-    codes that differ from the oracle's, those outside that band, and norms that differ."""
+# ---- CPU oracle baseline ---------------------------------------------------------------------------------
+# The oracle as it stands, split over rows (or queries, or KV heads) across worker processes started fresh
+# (spawn) with one BLAS thread each; inputs reach the workers through shared memory and are generated
+# before the timed region.  Only this leg of the bench runs the oracle.
+
+_SHM = {}
+
+
+def _cpu_worker_init():
+    import numpy  # noqa: F401  (imported before the timed region)
+
+    import oracle  # noqa: F401
+
+
+def _shm_view(name, shape, dtype):
+    from multiprocessing import shared_memory
+
+    import numpy as np
+
+    if name not in _SHM:
+        _SHM[name] = shared_memory.SharedMemory(name=name)
+    return np.ndarray(shape, dtype=dtype, buffer=_SHM[name].buf)
+
+
+def _cpu_codec_task(t):
+    """Encode + decode rows [r0, r1) of the shared fp16 array with the oracle; returns seconds spent."""
     import numpy as np
 
     import synth
-    from oracle import Codebook, code_to_index, dequantize, quantize, unpack_codes
+    from oracle import Codebook, dequantize, quantize
 
-    cb = Codebook.build(bits, DT)
-    signs = synth.signs(0, synth.STREAM_SIGNS_K, DT)
-    rows = SAMPLE_ROWS
-    if x_rows is None:
-        x_rows = synth.kv_tensor(0, 1, 1, 0, rows, HEAD_DIM).reshape(rows, HEAD_DIM)
-    x = np.asarray(x_rows[:rows], dtype=np.float64)
-    done_rows, t0 = 0, time.perf_counter()
-    while time.perf_counter() - t0 < target_s:
-        q = quantize(x, signs, cb)
-        dequantize(q["codes"], q["norms"], signs, cb)
-        done_rows += rows
-    dt_s = time.perf_counter() - t0
-    fp16_bytes = done_rows * HEAD_DIM * 2 * 2  # encoded in + decoded out
-    out = {"value": fp16_bytes / dt_s / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-           "sample": f"{done_rows} head vectors ({done_rows * HEAD_DIM // DT} blocks) of layer 0 / head 0 K, "
-                     f"encode+decode at {bits} bits, {dt_s:.1f} s single-threaded numpy float64"}
-    if gpu_codes is not None:
+    name, shape, r0, r1, bits, dt = t
+    x = np.array(_shm_view(name, shape, np.float16)[r0:r1], dtype=np.float64)
+    cb = Codebook.build(bits, dt)
+    signs = synth.signs(0, synth.STREAM_SIGNS_K, dt)
+    t0 = time.perf_counter()
+    q = quantize(x, signs, cb)
+    dequantize(q["codes"], q["norms"], signs, cb)
+    return time.perf_counter() - t0
+
+
+def _cpu_scores_task(t):
+    """The oracle's QJL scores of queries [q0, q1) against every key; returns seconds spent."""
+    import numpy as np
+
+    from oracle import qjl_scores
+
+    (qn, qs), (cn, cs), (nn, ns), (bn, bs), (rn, rs), q0, q1, signs, cb, S = t
+    q = np.array(_shm_view(qn, qs, np.float16)[q0:q1])
+    args = [np.array(_shm_view(n_, s_, dt_)) for (n_, s_), dt_ in
+            (((cn, cs), np.uint8), ((nn, ns), np.float16), ((bn, bs), np.uint8), ((rn, rs), np.float16))]
+    t0 = time.perf_counter()
+    qjl_scores(q.astype(np.float64), args[0], args[1], args[2], args[3], signs, cb, S)
+    return time.perf_counter() - t0
+
+
+def _cpu_attn_task(t):
+    """The oracle's decode attention of one KV head (its query heads over every token); returns seconds."""
+    import numpy as np
+
+    from oracle import decode_attention
+
+    q, kc, kn, vc, vn, sk, sv, kcb, vcb, T, hd = t
+    t0 = time.perf_counter()
+    decode_attention(q, kc, kn, vc, vn, sk, sv, kcb, vcb, 1, T, hd)
+    return time.perf_counter() - t0
+
+
+def _cpu_share() -> int:
+    """Worker processes: the CPUs this process may run on, at most 16 (one GPU's share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _timed_map(pool, fn, tasks):
+    t0 = time.perf_counter()
+    busy = pool.map(fn, tasks, chunksize=1)
+    return time.perf_counter() - t0, sum(busy)
+
+
+def cpu_baseline(bits: int, layers: int = 4, x_rows=None, gpu_codes=None, gpu_norms=None) -> dict:
+    """The float64 oracle on the host, timed on `layers` whole layers of the Qwen3-8B-shaped cache (K and V,
+    fp16): encode + decode split over rows across one worker per core of this GPU's CPU share, and again
+    in one worker; the same fp16-bytes-per-second unit as `value`.  Then the oracle's QJL scores (65536
+    keys, 4096 queries; one core on a 1/16 strided sample of the queries) and its decode attention (131072
+    tokens, per KV head).  With the GPU's codes and norms of layer 0 / head 0 K's first rows, also the parity
+    counts of that sample: coordinates within 1e-6 (unit-variance scale, i.e. 1e-6/sqrt(d) for the
+    N(0, 1/d) cells) of a cell edge, codes that differ from the oracle's, those outside that band, and
+    norms that differ."""
+    import multiprocessing as mp
+    from multiprocessing import shared_memory
+
+    import numpy as np
+
+    import synth
+    from synth import workloads
+
+    n_cores = _cpu_share()
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"  # one BLAS thread per worker (the spawned workers inherit this)
+    ctx = mp.get_context("spawn")
+    shms = []
+
+    def share(a):
+        m = shared_memory.SharedMemory(create=True, size=max(1, a.nbytes))
+        np.ndarray(a.shape, dtype=a.dtype, buffer=m.buf)[...] = a
+        shms.append(m)
+        return m.name, a.shape
+
+    out = {"unit": "GB/s", "cores": n_cores, "kind": "oracle"}
+    try:
+        # --- encode + decode of whole layers -------------------------------------------------------------
+        rows_half = layers * KV_HEADS * TOKENS
+        kv = workloads.qwen3_8b_kv(layers=layers)
+        x = np.concatenate([kv["k"].reshape(rows_half, HEAD_DIM), kv["v"].reshape(rows_half, HEAD_DIM)])
+        del kv
+        name, shape = share(x)
+        rows = x.shape[0]
+        del x
+        chunk = 4096
+        tasks = [(name, shape, r, min(rows, r + chunk), bits, DT) for r in range(0, rows, chunk)]
+        fp16_bytes = rows * HEAD_DIM * 2 * 2  # encoded in + decoded out
+        with ctx.Pool(n_cores, initializer=_cpu_worker_init) as pool:
+            pool.map(_cpu_codec_task, tasks[:n_cores], chunksize=1)  # every worker up and warm
+            wall_n, busy_n = _timed_map(pool, _cpu_codec_task, tasks)
+        with ctx.Pool(1, initializer=_cpu_worker_init) as pool:
+            pool.map(_cpu_codec_task, tasks[:1])
+            wall_1, busy_1 = _timed_map(pool, _cpu_codec_task, tasks)
+        out["value"] = fp16_bytes / wall_n / 1e9
+        out["sample"] = (f"layers 0-{layers - 1} of the cache, K and V ({rows} head vectors, {rows * HEAD_DIM // DT} "
+                         f"blocks), encode+decode at {bits} bits: {wall_n:.2f} s on {n_cores} worker processes "
+                         f"({busy_n:.1f} s of worker time), {wall_1:.2f} s on one")
+        out["single_core"] = {"value": fp16_bytes / wall_1 / 1e9, "unit": "GB/s", "cores": 1,
+                              "blocks_per_s": round(rows * HEAD_DIM // DT / wall_1)}
+        out["blocks_per_s"] = round(rows * HEAD_DIM // DT / wall_n)
+        log(f"cpu oracle codec: {out['value']:.3f} GB/s on {n_cores} cores, "
+            f"{out['single_core']['value']:.3f} GB/s on one")
+
+        # --- QJL scores ----------------------------------------------------------------------------------
+        from oracle import Codebook, quantize
+
+        w = workloads.qjl_keys()
+        cbq = Codebook.build(2, 128)
+        enc = quantize(w["keys"].astype(np.float64), w["signs"], cbq, S=w["S"])
+        qsh = share(w["q"])
+        parts = [share(enc["codes"]), share(enc["norms"]), share(enc["qjl_bits"]), share(enc["rho"])]
+        nq, nk = w["q"].shape[0], w["keys"].shape[0]
+        blk = 128
+        sc_tasks = [(qsh, *parts, q0, min(nq, q0 + blk), w["signs"], cbq, w["S"]) for q0 in range(0, nq, blk)]
+        with ctx.Pool(n_cores, initializer=_cpu_worker_init) as pool:
+            pool.map(_cpu_scores_task, sc_tasks[:n_cores], chunksize=1)
+            wall_sn, _ = _timed_map(pool, _cpu_scores_task, sc_tasks)
+        one = [(qsh, *parts, q0, q0 + 16, w["signs"], cbq, w["S"]) for q0 in range(0, nq, 512)]
+        with ctx.Pool(1, initializer=_cpu_worker_init) as pool:
+            pool.map(_cpu_scores_task, one[:1])
+            wall_s1, _ = _timed_map(pool, _cpu_scores_task, one)
+        out["qjl_scores"] = {"scores_per_s": round(nq * nk / wall_sn), "cores": n_cores,
+                             "scores_per_s_single_core": round(16 * len(one) * nk / wall_s1),
+                             "sample": f"{nq} queries x {nk} keys on {n_cores} cores ({wall_sn:.2f} s); "
+                                       f"{16 * len(one)} queries (16 of every 512) x {nk} keys on one ({wall_s1:.2f} s)"}
+        log(f"cpu oracle scores: {out['qjl_scores']['scores_per_s']:.3g} scores/s on {n_cores} cores")
+
+        # --- decode attention ----------------------------------------------------------------------------
+        c = workloads.decode_cache()
+        H, T, hd = c["k"].shape[1], c["k"].shape[2], c["k"].shape[3]
+        cba = Codebook.build(3, 32)
+        G = c["q"].shape[0] // H
+        at_tasks = []
+        for g in range(H):
+            ek = quantize(c["k"][0, g].astype(np.float64), c["signs_k"], cba)
+            ev = quantize(c["v"][0, g].astype(np.float64), c["signs_v"], cba)
+            at_tasks.append((c["q"][g * G:(g + 1) * G].astype(np.float64), ek["codes"], ek["norms"], ev["codes"],
+                             ev["norms"], c["signs_k"], c["signs_v"], cba, cba, T, hd))
+        with ctx.Pool(min(n_cores, H), initializer=_cpu_worker_init) as pool:
+            wall_an, _ = _timed_map(pool, _cpu_attn_task, at_tasks)
+        with ctx.Pool(1, initializer=_cpu_worker_init) as pool:
+            wall_a1, _ = _timed_map(pool, _cpu_attn_task, at_tasks[:1])
+        out["attn"] = {"us_per_call": round(wall_an * 1e6), "cores": min(n_cores, H),
+                       "kv_head_tokens_per_s": round(H * T / wall_an),
+                       "kv_head_tokens_per_s_single_core": round(T / wall_a1),
+                       "sample": f"the whole call ({H} KV heads x {T} tokens, {c['q'].shape[0]} query heads, one "
+                                 f"worker per KV head) in {wall_an:.2f} s; one KV head on one core in {wall_a1:.2f} s"}
+        log(f"cpu oracle attention: {wall_an:.2f} s per call on {min(n_cores, H)} cores")
+    finally:
+        for m in shms:
+            m.close()
+            m.unlink()
+
+    if gpu_codes is not None and x_rows is not None:
+        from oracle import Codebook, code_to_index, quantize, unpack_codes
+
+        cb = Codebook.build(bits, DT)
+        signs = synth.signs(0, synth.STREAM_SIGNS_K, DT)
+        q = quantize(np.asarray(x_rows, dtype=np.float64), signs, cb)
         g = code_to_index(unpack_codes(np.asarray(gpu_codes).reshape(-1, DT * bits // 8), bits, DT), bits)
         o = code_to_index(unpack_codes(q["codes"], bits, DT), bits)
-        dist = np.min(np.abs(q["y_unit"][..., None] - np.asarray(cb.unit_bounds)), axis=-1)
+        edges = np.asarray(cb.unit_bounds)
+        i = np.searchsorted(edges, q["y_unit"])
+        dist = np.minimum(np.abs(q["y_unit"] - edges[np.clip(i - 1, 0, len(edges) - 1)]),
+                          np.abs(q["y_unit"] - edges[np.clip(i, 0, len(edges) - 1)]))
         near, diff = dist < 1e-6, g != o
         nd = np.asarray(gpu_norms).astype(np.float16).view(np.uint16) != q["norms"].astype(np.float16).view(np.uint16)
-        out["parity"] = {"rows": rows, "coords": int(g.size), "near_edge": int(near.sum()),
+        out["parity"] = {"rows": len(x_rows), "coords": int(g.size), "near_edge": int(near.sum()),
                          "code_mismatch": int(diff.sum()), "code_mismatch_off_edge": int((diff & ~near).sum()),
                          "norm_mismatch": int(nd.sum())}
     return out
@@ -257,7 +439,11 @@ def run_k8v4(tq, torch, dev, rows, k, v, ok, ov, signs_k, signs_v, args):
            "step_ms": round(ms, 4), "GBs": round(2 * 2 * b8["fp16"] / (ms * 1e-3) / 1e9, 1),
            "encode_k8_ms": round(ek, 4), "encode_k8_GBs": round(b8["per_launch"] / ek / 1e6, 1),
            "decode_k8_ms": round(dk, 4), "decode_k8_GBs": round(b8["per_launch"] / dk / 1e6, 1),
-           "encode_v4_ms": round(ev, 4), "decode_v4_ms": round(dv, 4)}
+           "encode_k8_frac": round(b8["per_launch"] / ek / 1e6 / HBM_PEAK_GBS, 4),
+           "decode_k8_frac": round(b8["per_launch"] / dk / 1e6 / HBM_PEAK_GBS, 4),
+           "encode_v4_ms": round(ev, 4), "decode_v4_ms": round(dv, 4),
+           "encode_v4_frac": round(b4["per_launch"] / ev / 1e6 / HBM_PEAK_GBS, 4),
+           "decode_v4_frac": round(b4["per_launch"] / dv / 1e6 / HBM_PEAK_GBS, 4)}
     log(f"k8v4: step {ms:.3f} ms, K encode {ek:.3f} ms ({out['encode_k8_GBs']} GB/s), K decode {dk:.3f} ms "
         f"({out['decode_k8_GBs']} GB/s), V encode {ev:.3f} ms, V decode {dv:.3f} ms")
     del codec
@@ -313,6 +499,114 @@ def graph_ms(torch, fn, outputs, reps):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / reps
+
+
+def bench_vectors_fp32(tq, torch, dev, reps):
+    """4096 random vectors x 128 fp32 (N(0,1), seed 0), 3 bits, whole-vector units with one fp32 norm each:
+    encode and decode of the whole set, device time per call from HIP-graph replays (the set is 2 MiB
+    and stays in L2, so this is a latency figure)."""
+    from synth import workloads
+
+    w = workloads.vectors_fp32()
+    n, d, bits = w["x"].shape[0], w["x"].shape[1], 3
+    qz = tq.Quantizer(d, d, bits, w["signs"], x_dtype=tq.TQ_F32, norm_dtype=tq.TQ_F32, codebook=CODEBOOK)
+    x = torch.from_numpy(w["x"]).to(dev)
+    codes = torch.empty(n * d * bits // 8, dtype=torch.uint8, device=dev)
+    norms = torch.empty(n, dtype=torch.float32, device=dev)
+    y = torch.empty((n, d), dtype=torch.float32, device=dev)
+
+    def enc():
+        tq.tq_quantize(qz, x, n, d, codes, norms)
+
+    def dec():
+        tq.tq_dequantize(qz, codes, norms, None, None, n, y, tq.TQ_F32, d)
+
+    enc()
+    dec()
+    enc_ms = graph_ms(torch, enc, [codes, norms], reps)
+    dec_ms = graph_ms(torch, dec, [y], reps)
+    nbytes = n * (4 * d + d * bits // 8 + 4)  # fp32 vectors + codes + fp32 norms, per direction
+    out = {"workload": "4096 vectors x 128 fp32 N(0,1), 3 bits, whole-vector units, fp32 norm per vector",
+           "encode_us": round(enc_ms * 1e3, 2), "decode_us": round(dec_ms * 1e3, 2),
+           "encode_vectors_per_s": round(n / (enc_ms * 1e-3)), "decode_vectors_per_s": round(n / (dec_ms * 1e-3)),
+           "bytes_per_direction": nbytes, "encode_GBs": round(nbytes / (enc_ms * 1e-3) / 1e9, 1),
+           "decode_GBs": round(nbytes / (dec_ms * 1e-3) / 1e9, 1)}
+    log(f"vectors fp32: encode {enc_ms * 1e3:.2f} us, decode {dec_ms * 1e3:.2f} us per 4096 vectors")
+    return out
+
+
+def bench_llama(tq, torch, dev, reps, flush):
+    """The Llama-3.2-1B-shaped cache (16 layers x 8 KV heads x 2048 tokens x head_dim 64 per half, fp16),
+    4 bits, one fp16 norm per head vector and norm correction: the four-launch step (quantize K, V,
+    dequantize K, V to fp16) timed warm (graph replays back to back; the 170 MB working set stays in the
+    last-level cache) and flushed (a 1 GiB read before each step); per-launch times from events between
+    the launches of warm steps and of single flushed launches."""
+    from synth import workloads
+
+    w = workloads.llama_1b_kv()
+    L, H, T, d = w["k"].shape
+    rows, bits = L * H * T, 4
+    qk = tq.Quantizer(d, d, bits, w["signs_k"], flags=tq.TQ_NORM_CORRECT, codebook=CODEBOOK)
+    qv = tq.Quantizer(d, d, bits, w["signs_v"], flags=tq.TQ_NORM_CORRECT, codebook=CODEBOOK)
+    k = torch.from_numpy(w["k"].reshape(rows, d)).to(dev)
+    v = torch.from_numpy(w["v"].reshape(rows, d)).to(dev)
+    ck = torch.empty(rows * d * bits // 8, dtype=torch.uint8, device=dev)
+    cv = torch.empty_like(ck)
+    nk = torch.empty(rows, dtype=torch.float16, device=dev)
+    nv = torch.empty_like(nk)
+    ok, ov = torch.empty_like(k), torch.empty_like(v)
+    launches = [lambda: tq.tq_quantize(qk, k, rows, d, ck, nk), lambda: tq.tq_quantize(qv, v, rows, d, cv, nv),
+                lambda: tq.tq_dequantize(qk, ck, nk, None, None, rows, ok, tq.TQ_F16, d),
+                lambda: tq.tq_dequantize(qv, cv, nv, None, None, rows, ov, tq.TQ_F16, d)]
+
+    def step():
+        for f in launches:
+            f()
+
+    step()
+    graph = capture_step(torch, step, [ck, cv, nk, nv, ok, ov])
+    run = graph.replay if graph is not None else step
+    warm_ms = time_steps(torch, run, reps, 3)
+    cold_ms, _ = event_ms(torch, run, reps, before=lambda: flush.sum())
+    del graph
+    # per launch, warm: events between the launches of back-to-back steps
+    torch.cuda.synchronize()
+    step()
+    ev = []
+    for _ in range(reps):
+        for f in launches:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            ev.append(e)
+            f()
+    ev.append(torch.cuda.Event(enable_timing=True))
+    ev[-1].record()
+    torch.cuda.synchronize()
+    dd = [ev[i].elapsed_time(ev[i + 1]) for i in range(len(ev) - 1)]
+    enc_w = sum(dd[i] for i in range(len(dd)) if i % 4 in (0, 1)) / (2 * reps)
+    dec_w = sum(dd[i] for i in range(len(dd)) if i % 4 in (2, 3)) / (2 * reps)
+    # per launch, flushed
+    enc_c, _ = event_ms(torch, launches[0], reps, before=lambda: flush.sum())
+    dec_c, _ = event_ms(torch, launches[2], reps, before=lambda: flush.sum())
+    per_launch = rows * (2 * d + d * bits // 8 + 2)  # one half: fp16 rows + codes + fp16 norms
+    fp16_step = 2 * 2 * rows * d * 2
+    res = {"workload": "Llama-3.2-1B-shaped KV, 16 x 8 x 2048 x 64 per half, fp16, 4 bits, per-vector norm + "
+                       "norm correction",
+           "step_ms_warm": round(warm_ms, 4), "step_ms_flushed": round(cold_ms, 4),
+           "GBs_warm": round(fp16_step / (warm_ms * 1e-3) / 1e9, 1),
+           "GBs_flushed": round(fp16_step / (cold_ms * 1e-3) / 1e9, 1),
+           "algorithmic_bytes_per_launch": per_launch,
+           "encode_us_warm": round(enc_w * 1e3, 2), "decode_us_warm": round(dec_w * 1e3, 2),
+           "encode_us_flushed": round(enc_c * 1e3, 2), "decode_us_flushed": round(dec_c * 1e3, 2),
+           "encode_frac_flushed": round(per_launch / (enc_c * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "decode_frac_flushed": round(per_launch / (dec_c * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "encode_frac_warm": round(per_launch / (enc_w * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "decode_frac_warm": round(per_launch / (dec_w * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "vectors_per_s_flushed": round(2 * 2 * rows / (cold_ms * 1e-3)),
+           "vectors_per_s_warm": round(2 * 2 * rows / (warm_ms * 1e-3))}
+    log(f"llama-1b 4-bit nc: step {cold_ms * 1e3:.1f} us flushed / {warm_ms * 1e3:.1f} us warm; encode "
+        f"{enc_c * 1e3:.1f} / {enc_w * 1e3:.1f} us, decode {dec_c * 1e3:.1f} / {dec_w * 1e3:.1f} us (flushed / warm)")
+    return res
 
 
 def bench_qjl(tq, torch, dev, reps):
@@ -453,7 +747,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a captured step")
-    ap.add_argument("--only", choices=("all", "codec", "qjl", "attn"), default="all",
+    ap.add_argument("--only", choices=("all", "codec", "qjl", "attn", "llama", "vectors"), default="all",
                     help="run one workload (for profiling runs); the JSON line needs 'all'")
     ap.add_argument("--codebook", choices=("gaussian", "beta"), default="gaussian",
                     help="Lloyd-Max codebook for N(0,1/d) (default) or for the exact Beta marginal")
@@ -474,6 +768,12 @@ def main():
     reps = max(5, args.steps)
     if args.only in ("qjl", "attn"):
         (bench_qjl if args.only == "qjl" else bench_attn)(tq, torch, dev, reps)
+        return
+    if args.only == "vectors":
+        bench_vectors_fp32(tq, torch, dev, reps)
+        return
+    if args.only == "llama":
+        bench_llama(tq, torch, dev, reps, torch.zeros(1 << 28, dtype=torch.float32, device=dev))
         return
     k, v, signs_k, signs_v, rows = make_cache(tq, torch, dev)
     ok, ov = torch.empty_like(k), torch.empty_like(v)
@@ -523,6 +823,9 @@ def main():
         return
     del k, v, ok, ov
     torch.cuda.empty_cache()
+    vectors = bench_vectors_fp32(tq, torch, dev, reps)
+    llama = bench_llama(tq, torch, dev, reps, torch.zeros(1 << 28, dtype=torch.float32, device=dev))
+    torch.cuda.empty_cache()
     qjl = bench_qjl(tq, torch, dev, reps)
     torch.cuda.empty_cache()
     attn = bench_attn(tq, torch, dev, reps)
@@ -563,11 +866,17 @@ def main():
         "fraction_of_hbm_peak": round((2 * 2 * r["bytes"]["per_launch"]) / (r["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "encode": {"turbo3_GBs": round(r["bytes"]["per_launch"] / r["enc_ms"] / 1e6, 1),
                    "turbo4_GBs": round(r4["bytes"]["per_launch"] / r4["enc_ms"] / 1e6, 1),
+                   "turbo3_frac": round(r["bytes"]["per_launch"] / r["enc_ms"] / 1e6 / HBM_PEAK_GBS, 4),
+                   "turbo4_frac": round(r4["bytes"]["per_launch"] / r4["enc_ms"] / 1e6 / HBM_PEAK_GBS, 4),
                    "turbo3_blocks_per_s": round(r["units"] / (r["enc_ms"] * 1e-3)),
+                   "turbo4_blocks_per_s": round(r4["units"] / (r4["enc_ms"] * 1e-3)),
                    "turbo3_ms": round(r["enc_ms"], 4), "turbo4_ms": round(r4["enc_ms"], 4)},
         "decode": {"turbo3_GBs": round(r["bytes"]["per_launch"] / r["dec_ms"] / 1e6, 1),
                    "turbo4_GBs": round(r4["bytes"]["per_launch"] / r4["dec_ms"] / 1e6, 1),
+                   "turbo3_frac": round(r["bytes"]["per_launch"] / r["dec_ms"] / 1e6 / HBM_PEAK_GBS, 4),
+                   "turbo4_frac": round(r4["bytes"]["per_launch"] / r4["dec_ms"] / 1e6 / HBM_PEAK_GBS, 4),
                    "turbo3_blocks_per_s": round(r["units"] / (r["dec_ms"] * 1e-3)),
+                   "turbo4_blocks_per_s": round(r4["units"] / (r4["dec_ms"] * 1e-3)),
                    "turbo3_ms": round(r["dec_ms"], 4), "turbo4_ms": round(r4["dec_ms"], 4)},
         "turbo4_value": round(2 * 2 * r4["bytes"]["fp16"] / (r4["ms"] * 1e-3) / 1e9, 1),
         "fork_layout": {
@@ -577,16 +886,22 @@ def main():
                              "step_ms": round(fork[b]["ms"], 4),
                              "encode_ms": round(fork[b]["enc_ms"], 4), "decode_ms": round(fork[b]["dec_ms"], 4),
                              "encode_GBs": round(fork[b]["bytes"]["per_launch"] / fork[b]["enc_ms"] / 1e6, 1),
-                             "decode_GBs": round(fork[b]["bytes"]["per_launch"] / fork[b]["dec_ms"] / 1e6, 1)}
+                             "decode_GBs": round(fork[b]["bytes"]["per_launch"] / fork[b]["dec_ms"] / 1e6, 1),
+                             "encode_frac": round(fork[b]["bytes"]["per_launch"] / fork[b]["enc_ms"] / 1e6
+                                                  / HBM_PEAK_GBS, 4),
+                             "decode_frac": round(fork[b]["bytes"]["per_launch"] / fork[b]["dec_ms"] / 1e6
+                                                  / HBM_PEAK_GBS, 4)}
                for b in (3, 4)}},
         "k8v4": k8v4,
         "copy_reference_GBs": round(copy_gbs, 1),
+        "vectors_fp32": vectors,
+        "llama_1b": llama,
         "qjl": qjl,
         "attn": attn,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
-        out["cpu_baseline"] = cpu_baseline(rows, 3, x_rows=kept.get("x"), gpu_codes=kept.get("codes"),
+        out["cpu_baseline"] = cpu_baseline(3, x_rows=kept.get("x"), gpu_codes=kept.get("codes"),
                                            gpu_norms=kept.get("norms"))
     print(json.dumps(out), flush=True)
 

@@ -130,8 +130,9 @@ tq_status tq_codebook_init_beta(tq_codebook* out, int bits, int dim);
  * One quantizer (e.g. the key quantizer or the value quantizer of a cache).
  *   head_dim   elements per input row, a multiple of dt
  *   dt         transform / normalisation length: 32, 64, 128 or 256
- *   bits       1..4, must equal cb->bits; cb->dim must equal dt
- *   flags      TQ_NORM_CORRECT and/or TQ_QJL
+ *   bits       1..4 or 8, must equal cb->bits; cb->dim must equal dt (QJL
+ *              takes a 1..4-bit first stage)
+ *   flags      any of TQ_NORM_CORRECT, TQ_QJL, TQ_BLOCKS (TQ_BLOCKS excludes TQ_QJL)
  *   qjl_m      number of QJL projections (TQ_QJL only): 32..256, multiple of 32
  *   x_dtype    element type of the input rows (TQ_F16 or TQ_F32)
  *   norm_dtype type of the stored norms (TQ_F16 or TQ_F32)
@@ -170,10 +171,18 @@ tq_status tq_qjl_prepare(const tq_config* cfg, const float* S_host, void* params
 
 /*
  * Encode n_rows rows ([Scratch] §2 steps 1-3, [Fork] "How it works"):
- * per unit n = ||x||, u = x / n, y = H D u, idx_i = #{bounds < y_i} (a value
- * on an edge goes to the lower cell), codes packed as described above, n
- * stored as norm_dtype.  With TQ_QJL (dt == head_dim required) also
- * r = u - D H c[idx], qjl_rnorm = ||r|| and qjl_bits = [S r >= 0].
+ * per unit n = ||x||, u = x / n, y = H D u, idx_i = #{bounds < y_i}, codes
+ * packed as described above, n stored as norm_dtype.  With TQ_QJL
+ * (dt == head_dim required) also r = u - D H c[idx], qjl_rnorm = ||r|| and
+ * qjl_bits = [S r >= 0].
+ * Exact ties: a coordinate that lies exactly on a cell edge is equally near
+ * both neighbouring centroids, and either cell may be stored.  The encoders
+ * pick the half (idx >= 2^(b-1) or below) from y's sign and then the cell
+ * nearer zero within it: without TQ_QJL by the float's sign bit (+0.0 takes
+ * idx 2^(b-1), -0.0 takes 2^(b-1) - 1), with TQ_QJL by y > 0 (both zeros take
+ * 2^(b-1) - 1).  A value on any other edge thus goes to the lower cell when
+ * positive and to the upper one when negative.  (The rounded y a kernel
+ * compares differs from the exact y in the last bits anyway.)
  *   x        device, rows of ld_x elements (ld_x >= head_dim); 16-byte
  *            aligned, ld_x * element size a multiple of 16 bytes
  *   codes    device, 4-byte aligned, n_rows * head_dim/dt units (TQ_BLOCKS:

@@ -10,7 +10,6 @@ binding's functions raises.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 
 import numpy as np
@@ -198,7 +197,3 @@ def tq_multi_attn(kq: Quantizer, vq: Quantizer, q, q_dtype: int, n_q: int, n_q_h
     _check(lib().tq_multi_attn(ctypes.byref(kq.cfg), ctypes.byref(vq.cfg), _ptr(q), q_dtype, n_q, n_q_heads,
                                n_kv_heads, n_tokens, _ptr(k_codes), _ptr(k_norms), _ptr(v_codes), _ptr(v_norms),
                                1 if causal else 0, scale, _ptr(out), _ptr(ws), ws_bytes, _stream(stream)))
-
-
-def default_scale(head_dim: int) -> float:
-    return 1.0 / math.sqrt(head_dim)

@@ -2,12 +2,14 @@
 // dequantize with the QJL correction ([Scratch] §2 "QJL residual";
 // [README] two-stage description and combined estimator).
 //
-// Encode works in float64 so that the bucket indices and sign bits it
-// decides are exact except within ~1e-15 of an edge: the residual's sign
-// bits sign((S r)_p) are only meaningful to the estimator if they agree
-// with the exact projection.  S~ = S D H (host-prepared) is staged in LDS;
-// because H and D are symmetric involutions, S (u - D H c) = S~ (y - c),
-// so the residual never leaves the rotated domain.
+// The residual's sign bits sign((S r)_p) are only meaningful to the
+// estimator if they agree with the exact projection.  head_dim 128 encodes in
+// fp32 with the projection on fp32 MFMA, whose error (about 2e-7 of the
+// residual norm) stays inside the 1e-6-of-rho band around z = 0; the other
+// head sizes encode in float64, exact except within ~1e-15 of an edge.
+// S~ = S D H (host-prepared) is staged in LDS; because H and D are symmetric
+// involutions, S (u - D H c) = S~ (y - c), so the residual never leaves the
+// rotated domain.
 #include <hip/hip_fp16.h>
 
 #include "tq_device.h"

@@ -221,25 +221,27 @@ def test_attn_rejects_bad_args():
 
 def test_attn_full_size_sampled():
     """head_dim 256, 4 KV heads, 16 query heads, 131072 tokens, 3-bit K and V: the full call on the GPU,
-    the oracle on KV head 2 (its 4 query heads over all 131072 tokens)."""
+    the oracle on every KV head (all 16 query heads over all 131072 tokens)."""
     from synth.workloads import decode_cache
 
     w = decode_cache()
     c = Cache(w["k"][0], w["v"][0], 3, 3, w["signs_k"], w["signs_v"])
     del w["k"], w["v"]
     gpu = c.attend(w["q"])
-    orc, bound = c.oracle(w["q"], kv_heads=[2])
-    _check(gpu[8:12], orc, bound, "131072 tokens, KV head 2")
+    for g in range(c.H):
+        orc, bound = c.oracle(w["q"], kv_heads=[g])
+        _check(gpu[4 * g:4 * g + 4], orc, bound, f"131072 tokens, KV head {g}")
 
 
 def test_attn_full_size_k8v4_sampled():
     """The same 131072-token cache with 8-bit keys and 4-bit values (the asymmetric allocation); the
-    oracle on KV head 1."""
+    oracle on every KV head."""
     from synth.workloads import decode_cache
 
     w = decode_cache()
     c = Cache(w["k"][0], w["v"][0], 8, 4, w["signs_k"], w["signs_v"])
     del w["k"], w["v"]
     gpu = c.attend(w["q"])
-    orc, bound = c.oracle(w["q"], kv_heads=[1])
-    _check(gpu[4:8], orc, bound, "131072 tokens, K8V4, KV head 1")
+    for g in range(c.H):
+        orc, bound = c.oracle(w["q"], kv_heads=[g])
+        _check(gpu[4 * g:4 * g + 4], orc, bound, f"131072 tokens, K8V4, KV head {g}")

@@ -12,7 +12,7 @@ import pytest
 
 import synth
 from oracle import Codebook, dequantize, quantize
-from tests.parity import check_codes, check_decoded_f16, check_decoded_f32, check_norms
+from tests.parity import assert_band_rate, check_codes, check_decoded_f16, check_decoded_f32, check_norms
 
 torch = pytest.importorskip("torch")
 import kv_cache_vector_amd as tq  # noqa: E402
@@ -63,10 +63,14 @@ def _roundtrip(x_np, dt, bits, seed, x_dtype, norm_dtype, nc=False, ld=None, y_d
     codes, norms = _run_encode(qz, x_np, ld)
     orc = quantize(x_np.astype(np.float64), signs, cb, norm_dtype=np.float32 if norm_dtype == tq.TQ_F32 else np.float16)
     stats = check_codes(codes, orc, cb, bits, dt)
+    assert_band_rate(stats, cb)
     stats.update(check_norms(norms, orc["norms"]))
     ref = dequantize(codes.reshape(-1, dt * bits // 8), norms, signs, cb, nc=nc)
     for yt in y_dtypes:
-        y = _run_decode(qz, codes, norms, n_rows, yt, ld)
+        # the output rows keep the input's padding where that is a legal pitch for their element size
+        # (a multiple of 16 bytes); fp16 rows otherwise take the next multiple of 8 elements
+        ld_y = None if ld is None else (ld if yt == tq.TQ_F32 or ld % 8 == 0 else (ld + 7) // 8 * 8)
+        y = _run_decode(qz, codes, norms, n_rows, yt, ld_y)
         if yt == tq.TQ_F32:
             stats["decode_err"] = check_decoded_f32(y, ref, norms, dt)
         else:
@@ -84,12 +88,28 @@ def test_matrix_f16(dt, bits):
     print(stats)
 
 
+@pytest.mark.parametrize("pad", [4, 8])
 @pytest.mark.parametrize("dt", [32, 128])
 @pytest.mark.parametrize("bits", [2, 3, 8])
-def test_matrix_f32_strided(dt, bits):
+def test_matrix_f32_strided(dt, bits, pad):
+    """fp32 rows with a padded stride: pad 4 makes the row pitch 16 mod 32 bytes (1040 B), pad 8 a
+    multiple of 32; encode reads and decode writes the rows in place."""
     hd, n_rows = 256, 129
     x = synth.normal_f32(7, 0, n_rows * hd).reshape(n_rows, hd) * 3.0
-    stats, *_ = _roundtrip(x, dt, bits, seed=5, x_dtype=tq.TQ_F32, norm_dtype=tq.TQ_F32, ld=hd + 8)
+    stats, *_ = _roundtrip(x, dt, bits, seed=5, x_dtype=tq.TQ_F32, norm_dtype=tq.TQ_F32, ld=hd + pad)
+    print(stats)
+
+
+@pytest.mark.parametrize("pad", [8, 16])
+@pytest.mark.parametrize("dt", [32, 64, 128])
+@pytest.mark.parametrize("bits", [3, 4, 8])
+def test_matrix_f16_strided(dt, bits, pad):
+    """fp16 rows with a padded stride (row pitch hd + 8 or hd + 16 elements): the strided forms of the
+    block-32 MFMA encode and decode (dt = 32, 3 and 4 bits; 8-bit decode takes the generic kernel) and
+    of the generic kernels (dt = 64, 128), fp16 and fp32 output rows of the same stride."""
+    hd, n_rows = 128, 333
+    x = synth.kv_tensor(dt + bits + pad, 1, 1, 1, n_rows, hd).reshape(n_rows, hd)
+    stats, *_ = _roundtrip(x, dt, bits, seed=dt + pad, x_dtype=tq.TQ_F16, norm_dtype=tq.TQ_F16, ld=hd + pad)
     print(stats)
 
 
@@ -113,10 +133,9 @@ def test_eight_bit_keys(dt, nc):
     w = qwen3_8b_kv(layers=1, heads=2, tokens=700)
     x = w["k"].reshape(-1, 128)
     stats, codes, norms, orc = _roundtrip(x, dt, 8, seed=8, x_dtype=tq.TQ_F16, norm_dtype=tq.TQ_F16, nc=nc)
+    # 255 cell edges put about 1e-4 of the coordinates inside the 1e-6 band (the 8-bit bar of
+    # assert_band_rate, applied in _roundtrip); the codes that actually differ there stay rare
     print(stats)
-    # 255 cell edges put about 1e-4 of the coordinates inside the 1e-6 band; the codes that actually
-    # differ there must stay rare
-    assert stats["in_band_mismatch"] <= 1e-5 * stats["coords"]
 
 
 def test_vectors_fp32_config_and_mse():
@@ -129,7 +148,7 @@ def test_vectors_fp32_config_and_mse():
     cb = Codebook.build(3, 128)
     codes, norms = _run_encode(qz, x)
     orc = quantize(x.astype(np.float64), w["signs"], cb, norm_dtype=np.float32)
-    check_codes(codes, orc, cb, 3, 128)
+    assert_band_rate(check_codes(codes, orc, cb, 3, 128), cb)
     check_norms(norms, orc["norms"])
     y = _run_decode(qz, codes, norms, len(x), tq.TQ_F32)
     ref = dequantize(codes.reshape(-1, 48), norms, w["signs"], cb)
@@ -230,12 +249,14 @@ def qwen_full():
 def test_block32_full_size_sampled(qwen_full, kbits, vbits):
     """The Qwen3-8B-shaped cache at full size (36 x 8 x 16384 x 128, K and V fp16) in block-32
     planes, each half encoded and decoded by one call as the step timing launches it (turbo3,
-    turbo4, and 8-bit keys with 4-bit values): codes, norms and decoded rows of sampled rows
-    (the first and last row among them) against the oracle."""
+    turbo4, and 8-bit keys with 4-bit values): codes, norms and decoded rows of 100000 sampled rows
+    (the first and last row among them) against the oracle.  The sample holds 12.8 M coordinates
+    per half, so the in-band count is held to the literal bound (1e-5 of the coordinates at 3 and 4
+    bits, where about 3.5e-6 and 6.7e-6 are expected)."""
     w = qwen_full
     rows = w["k"].shape[0] * w["k"].shape[1] * w["k"].shape[2]
     rng = np.random.default_rng(11 + kbits)
-    sample = np.unique(np.concatenate([rng.integers(0, rows, 3000), [0, rows - 1]]))
+    sample = np.unique(np.concatenate([rng.choice(rows, 100000, replace=False), [0, rows - 1]]))
     sidx = torch.from_numpy(sample).to(DEV)
     for half, s, bits in (("k", "signs_k", kbits), ("v", "signs_v", vbits)):
         x_np = w[half].reshape(rows, 128)
@@ -260,19 +281,20 @@ def test_block32_full_size_sampled(qwen_full, kbits, vbits):
         ref = dequantize(c.reshape(-1, 4 * bits), n, w[s], cb)
         stats["f16_ulp_off"] = check_decoded_f16(ys, ref, n, 32)
         print(half, bits, stats)
-        assert stats["in_band_mismatch"] <= 1e-5 * stats["coords"]
+        assert_band_rate(stats, cb, literal=True)
 
 
 def test_llama_full_size_sampled():
     """The Llama-3.2-1B-shaped cache at full size (16 x 8 x 2048 vectors of 64 per half, fp16),
     4 bits with a per-vector norm and norm correction, one call per half: codes, norms and
-    decoded rows of sampled rows against the oracle."""
+    decoded rows of 200000 of the 262144 rows of each half against the oracle (12.8 M coordinates,
+    in-band count held to the literal 1e-5 bound)."""
     from synth.workloads import llama_1b_kv
 
     w = llama_1b_kv()
     rows = w["k"].shape[0] * w["k"].shape[1] * w["k"].shape[2]
     rng = np.random.default_rng(5)
-    sample = np.unique(np.concatenate([rng.integers(0, rows, 4000), [0, rows - 1]]))
+    sample = np.unique(np.concatenate([rng.choice(rows, 200000, replace=False), [0, rows - 1]]))
     sidx = torch.from_numpy(sample).to(DEV)
     cb = Codebook.build(4, 64)
     for half, s in (("k", "signs_k"), ("v", "signs_v")):
@@ -294,4 +316,4 @@ def test_llama_full_size_sampled():
         ref = dequantize(c, n, w[s], cb, nc=True)
         stats["decode_err"] = check_decoded_f32(ys, ref, n, 64)
         print(half, stats)
-        assert stats["in_band_mismatch"] <= 1e-5 * stats["coords"]
+        assert_band_rate(stats, cb, literal=True)

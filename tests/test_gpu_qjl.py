@@ -5,7 +5,8 @@ import pytest
 
 import synth
 from oracle import Codebook, code_to_index, dequantize, quantize, unpack_codes
-from tests.parity import BAND, check_codes, check_decoded_f32, check_norms, check_sign_bits, edge_distance
+from tests.parity import (BAND, assert_band_rate, assert_sign_band_rate, check_codes, check_decoded_f32,
+                          check_norms, check_sign_bits, edge_distance)
 
 torch = pytest.importorskip("torch")
 import kv_cache_vector_amd as tq  # noqa: E402
@@ -35,7 +36,10 @@ def _encode(keys, dt, bits, m, seed, nc=False, codebook="gaussian"):
 @pytest.mark.parametrize("dt,m,bits,codebook", [(128, 128, 2, "gaussian"), (128, 64, 1, "gaussian"),
                                                  (64, 128, 3, "gaussian"), (64, 64, 2, "gaussian"),
                                                  (128, 96, 2, "gaussian"), (128, 128, 3, "beta"),
-                                                 (64, 64, 2, "beta")])
+                                                 (64, 64, 2, "beta"),
+                                                 (32, 256, 2, "gaussian"),   # one lane per unit, 32 KiB of S~
+                                                 (256, 64, 3, "gaussian"),   # eight lanes per unit, 64 KiB of S~
+                                                 (256, 32, 4, "gaussian")])
 def test_qjl_encode_decode(dt, m, bits, codebook):
     n = 1000  # several workgroups plus a ragged tail
     keys = synth.kv_tensor(dt + m + bits, 1, 1, 0, n, dt, n_outliers=0).reshape(n, dt)
@@ -44,12 +48,14 @@ def test_qjl_encode_decode(dt, m, bits, codebook):
     orc = quantize(keys.astype(np.float64), signs, cb, S=S)
     codes_np, norms_np = codes.cpu().numpy(), norms.cpu().numpy()
     stats = check_codes(codes_np, orc, cb, bits, dt)
+    assert_band_rate(stats, cb)
     check_norms(norms_np, orc["norms"])
     # sign bits and residual norms: compare units whose indices matched exactly
     same = np.all(unpack_codes(codes_np.reshape(n, -1), bits, dt) == unpack_codes(orc["codes"], bits, dt), axis=1)
     sb = sbits.cpu().numpy().reshape(n, m // 8)
     sub = {k: v[same] for k, v in orc.items()}
     st = check_sign_bits(sb[same], sub, m)
+    assert_sign_band_rate(st)
     check_norms(rnorm.cpu().numpy()[same], orc["rho"][same])
     print(stats, st)
     # dequantize with the QJL correction (fp32 output), oracle on the GPU's own codes
@@ -64,8 +70,8 @@ def test_qjl_encode_decode(dt, m, bits, codebook):
 
 
 def test_qjl_keys_full_size_sampled():
-    """65536 keys x 128 fp16, 2-bit MSE + 1-bit QJL, m = 128, S from seed 1: the whole set on the GPU,
-    the oracle on a strided sample of 2048 keys."""
+    """65536 keys x 128 fp16, 2-bit MSE + 1-bit QJL, m = 128, S from seed 1: the whole set on the GPU and
+    in the oracle (8.4 M coordinates and 8.4 M sign bits; in-band counts held to the literal 1e-5 bound)."""
     from synth.workloads import qjl_keys
 
     w = qjl_keys()
@@ -81,14 +87,17 @@ def test_qjl_keys_full_size_sampled():
     rnorm = torch.empty(n, dtype=torch.float16, device=DEV)
     tq.tq_quantize(qz, x, n, dt, codes, norms, sbits, rnorm)
     torch.cuda.synchronize()
-    idx = np.arange(0, n, 32)
     cb = Codebook.build(bits, dt)
-    orc = quantize(keys[idx].astype(np.float64), w["signs"], cb, S=w["S"])
-    c = codes.cpu().numpy().reshape(n, 32)[idx]
+    orc = quantize(keys.astype(np.float64), w["signs"], cb, S=w["S"])
+    c = codes.cpu().numpy().reshape(n, 32)
     st = check_codes(c, orc, cb, bits, dt)
-    check_norms(norms.cpu().numpy()[idx], orc["norms"])
-    sb = check_sign_bits(sbits.cpu().numpy().reshape(n, 16)[idx], orc, m)
-    assert st["in_band"] <= 1e-5 * st["coords"] + 1
+    assert_band_rate(st, cb, literal=True)
+    check_norms(norms.cpu().numpy(), orc["norms"])
+    # sign bits of the keys whose codes match the oracle's (an in-band code flip changes the residual)
+    same = np.all(unpack_codes(c, bits, dt) == unpack_codes(orc["codes"], bits, dt), axis=1)
+    sb = check_sign_bits(sbits.cpu().numpy().reshape(n, 16)[same], {k: v[same] for k, v in orc.items()}, m)
+    assert_sign_band_rate(sb, literal=True)
+    check_norms(rnorm.cpu().numpy()[same], orc["rho"][same])
     print(st, sb)
 
 
