@@ -259,6 +259,27 @@ tq_status tq_decode_attn(const tq_config* kcfg, const tq_config* vcfg, const voi
                          size_t ws_bytes, void* stream);
 
 /*
+ * tq_decode_attn for callers that cannot allocate: code inside HIP graph
+ * capture, tight serving loops, and harnesses that forbid hipMalloc.  Same
+ * arguments, kernels and results as tq_decode_attn, but no workspace: the
+ * per-workgroup softmax partials go to a static scratch array of 16 MiB that
+ * the library keeps on each device (resolved with hipGetSymbolAddress on the
+ * first call on a device, held until the process ends).  The call allocates
+ * and frees nothing.  A call whose partials need more than 16 MiB
+ * (tq_workspace_size(TQ_OP_DECODE_ATTN, ...) > 16 MiB; at head_dim 256 and 16
+ * query heads per KV head that is n_kv_heads * n_tokens above about 8.3 M,
+ * e.g. 4 KV heads of more than 2 M tokens) returns TQ_ERR_UNSUPPORTED before
+ * anything is launched.  All calls on one
+ * device share that device's scratch: calls that overlap in time on one
+ * device (different streams, or different threads without ordering) race and
+ * give undefined results; calls ordered on one stream are safe.
+ */
+tq_status tq_decode_attn_noalloc(const tq_config* kcfg, const tq_config* vcfg, const void* q, tq_dtype q_dtype,
+                                 int n_q_heads, int n_kv_heads, int64_t n_tokens, const uint8_t* k_codes,
+                                 const void* k_norms, const uint8_t* v_codes, const void* v_norms, float scale,
+                                 float* out, void* stream);
+
+/*
  * Attention of several query tokens over the same quantized cache (the
  * [Fork] "Fused tile path" with more than one query column: a prefill chunk
  * or a batch of draft tokens).  Query token i (0 <= i < n_q) with head h:

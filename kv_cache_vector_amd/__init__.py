@@ -23,7 +23,8 @@ TQ_NORM_CORRECT, TQ_QJL, TQ_BLOCKS = 1, 2, 4
 TQ_OP_QJL_SCORES, TQ_OP_DECODE_ATTN, TQ_OP_MULTI_ATTN = 1, 2, 3
 
 EXPORTED = ("tq_codebook_init", "tq_codebook_init_beta", "tq_qjl_params_size", "tq_qjl_prepare", "tq_quantize", "tq_dequantize",
-            "tq_qjl_scores", "tq_decode_attn", "tq_multi_attn", "tq_workspace_size", "tq_status_str",
+            "tq_qjl_scores", "tq_decode_attn", "tq_decode_attn_noalloc", "tq_multi_attn", "tq_workspace_size",
+            "tq_status_str",
             "tq_last_error")
 
 
@@ -70,6 +71,8 @@ def lib():
     L.tq_qjl_scores.argtypes = [cfgp, vp, c_int, i64, i64, vp, vp, vp, vp, i64, vp, i64, vp, sz, vp]
     L.tq_decode_attn.argtypes = [cfgp, cfgp, vp, c_int, c_int, c_int, i64, vp, vp, vp, vp, ctypes.c_float, vp, vp, sz,
                                  vp]
+    L.tq_decode_attn_noalloc.argtypes = [cfgp, cfgp, vp, c_int, c_int, c_int, i64, vp, vp, vp, vp, ctypes.c_float,
+                                         vp, vp]
     L.tq_multi_attn.argtypes = [cfgp, cfgp, vp, c_int, i64, c_int, c_int, i64, vp, vp, vp, vp, c_int, ctypes.c_float,
                                 vp, vp, sz, vp]
     L.tq_workspace_size.argtypes = [c_int, cfgp, i64, i64, i64]
@@ -78,7 +81,7 @@ def lib():
     L.tq_status_str.restype = ctypes.c_char_p
     L.tq_last_error.restype = ctypes.c_char_p
     for name in ("tq_codebook_init", "tq_codebook_init_beta", "tq_qjl_prepare", "tq_quantize", "tq_dequantize", "tq_qjl_scores",
-                 "tq_decode_attn", "tq_multi_attn"):
+                 "tq_decode_attn", "tq_decode_attn_noalloc", "tq_multi_attn"):
         getattr(L, name).restype = c_int
     _lib = L
     return L
@@ -189,6 +192,13 @@ def tq_decode_attn(kq: Quantizer, vq: Quantizer, q, q_dtype: int, n_q_heads: int
     _check(lib().tq_decode_attn(ctypes.byref(kq.cfg), ctypes.byref(vq.cfg), _ptr(q), q_dtype, n_q_heads, n_kv_heads,
                                 n_tokens, _ptr(k_codes), _ptr(k_norms), _ptr(v_codes), _ptr(v_norms), scale,
                                 _ptr(out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def tq_decode_attn_noalloc(kq: Quantizer, vq: Quantizer, q, q_dtype: int, n_q_heads: int, n_kv_heads: int,
+                           n_tokens: int, k_codes, k_norms, v_codes, v_norms, scale: float, out, stream=None):
+    _check(lib().tq_decode_attn_noalloc(ctypes.byref(kq.cfg), ctypes.byref(vq.cfg), _ptr(q), q_dtype, n_q_heads,
+                                        n_kv_heads, n_tokens, _ptr(k_codes), _ptr(k_norms), _ptr(v_codes),
+                                        _ptr(v_norms), scale, _ptr(out), _stream(stream)))
 
 
 def tq_multi_attn(kq: Quantizer, vq: Quantizer, q, q_dtype: int, n_q: int, n_q_heads: int, n_kv_heads: int,

@@ -592,6 +592,29 @@ int64_t attn_tokens_per_wg(int64_t columns, int64_t n_tokens, bool prefill) {
   return per;
 }
 
+// Scratch of tq_decode_attn_noalloc: the softmax partials of a decode call live in this array instead
+// of a caller workspace.  Every device the library runs on holds its own copy, at its own address, for
+// the life of the process; in host code `scratch` names a host-side stand-in, so kernels only ever get
+// the device address resolved here.  No kernel needs it cleared: each workgroup writes its whole
+// partial before the merge reads it.
+static __device__ __align__(256) uint8_t scratch[kAttnScratchBytes];
+
+hipError_t attn_scratch(void** ptr) {
+  static std::atomic<void*> addr[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {  // first call on this device (concurrent first calls resolve the same address)
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
+}
+
 hipError_t launch_decode_attn(int kbits, int vbits, const AttnArgs& a, hipStream_t s) {
   if (kbits == 3 && vbits == 3) return launch_bits<3, 3>(a, s);
   if (kbits == 4 && vbits == 4) return launch_bits<4, 4>(a, s);

@@ -815,6 +815,29 @@ tq_status tq_decode_attn(const tq_config* kcfg, const tq_config* vcfg, const voi
                   v_codes, v_norms, 0, scale, out, ws, ws_bytes, stream);
 }
 
+tq_status tq_decode_attn_noalloc(const tq_config* kcfg, const tq_config* vcfg, const void* q, tq_dtype q_dtype,
+                                 int n_q_heads, int n_kv_heads, int64_t n_tokens, const uint8_t* k_codes,
+                                 const void* k_norms, const uint8_t* v_codes, const void* v_norms, float scale,
+                                 float* out, void* stream) {
+  const char* who = "tq_decode_attn_noalloc";
+  tq_status st = check_attn_config(kcfg, vcfg, n_q_heads, n_kv_heads, n_tokens, who);
+  if (st) return st;
+  if (n_tokens == 0)  // a no-op; run_attn checks the remaining arguments
+    return run_attn(who, kcfg, vcfg, q, q_dtype, 1, n_q_heads, n_kv_heads, n_tokens, k_codes, k_norms, v_codes,
+                    v_norms, 0, scale, out, nullptr, 0, stream);
+  const size_t need = attn_workspace(*kcfg, n_q_heads, n_kv_heads, 1, n_tokens);
+  if (need > tq::kAttnScratchBytes)
+    return fail(TQ_ERR_UNSUPPORTED,
+                "%s: this call needs %zu bytes of scratch; the library's static scratch holds %zu (use "
+                "tq_decode_attn with a workspace)",
+                who, need, tq::kAttnScratchBytes);
+  void* ws = nullptr;
+  const hipError_t e = tq::attn_scratch(&ws);
+  if (e != hipSuccess) return hip_fail(e, who);
+  return run_attn(who, kcfg, vcfg, q, q_dtype, 1, n_q_heads, n_kv_heads, n_tokens, k_codes, k_norms, v_codes,
+                  v_norms, 0, scale, out, ws, tq::kAttnScratchBytes, stream);
+}
+
 tq_status tq_multi_attn(const tq_config* kcfg, const tq_config* vcfg, const void* q, tq_dtype q_dtype, int64_t n_q,
                         int n_q_heads, int n_kv_heads, int64_t n_tokens, const uint8_t* k_codes, const void* k_norms,
                         const uint8_t* v_codes, const void* v_norms, int causal, float scale, float* out, void* ws,

@@ -156,6 +156,11 @@ hipError_t launch_qjl_scores(const tq_config& cfg, const ScoreArgs& a, hipStream
 int64_t scores_key_tile(int bits);
 int64_t scores_query_block();
 hipError_t launch_decode_attn(int kbits, int vbits, const AttnArgs& a, hipStream_t s);
+// Device address of the library's static decode-attention scratch on the current device (resolved on
+// the first call per device), kAttnScratchBytes long.
+constexpr size_t kAttnScratchBytes = (size_t)16 << 20;
+constexpr int kMaxDevices = 64;
+hipError_t attn_scratch(void** ptr);
 int64_t attn_tokens_per_wg(int64_t columns, int64_t n_tokens, bool prefill);
 int attn_prefill_rows();  // rows per workgroup of the many-row (prefill) attention kernel
 hipError_t launch_prefill(int kbits, int vbits, const AttnArgs& a, hipStream_t s);  // its main kernel (no merge)

@@ -224,6 +224,27 @@ def test_attention_validation():
                             FAKE, 0.0, FAKE, None, 0, None) == W
 
 
+def test_decode_attn_noalloc_validation():
+    """tq_decode_attn_noalloc rejects bad arguments, and calls whose partials exceed its 16 MiB static
+    scratch, before it resolves the scratch or launches anything."""
+    E, U, OK = tq.TQ_ERR_INVALID_ARG, tq.TQ_ERR_UNSUPPORTED, tq.TQ_OK
+    L = tq.lib()
+    k3 = _q(head_dim=256, signs=np.ones(32))
+    v3 = _q(head_dim=256, signs=np.ones(32))
+
+    def call(hq=16, hkv=1, T=1000, kq=k3, vq=v3, qt=tq.TQ_F16):
+        return L.tq_decode_attn_noalloc(ctypes.byref(kq.cfg), ctypes.byref(vq.cfg), FAKE, qt, hq, hkv, T, FAKE, FAKE,
+                                        FAKE, FAKE, 0.0, FAKE, None)
+
+    assert _attn_ws(k3, 16, 1, 8_400_000, tq.TQ_OP_DECODE_ATTN) > 16 << 20
+    assert call(T=8_400_000) == U and "scratch" in L.tq_last_error().decode()
+    assert call(hq=64, hkv=4, T=2_100_000) == U
+    assert call(hq=16, hkv=3) == E  # query heads not a multiple of KV heads
+    assert call(vq=_q(head_dim=256, bits=8, signs=np.ones(32))) == U  # 8-bit values
+    assert call(T=-1) == E
+    assert call(T=0) == OK and call(T=0, qt=5) == E  # nothing to do, but the arguments are still checked
+
+
 def test_attention_workspace_sizes():
     """Partials: one (head_dim + 2)-float record per row and token range; up to 16 rows per KV head
     form one group (decode kernel), more go in 128-row groups (prefill kernel)."""
