@@ -1,18 +1,5 @@
 // Encode and decode kernels (no QJL stage) for gfx950.
 //
-// Work split: one lane owns one 32-coordinate group (64 contiguous bytes of
-// fp16, or 128 of fp32).  A unit of dt coordinates spans LPU = dt/32
-// consecutive lanes, so coordinate c of a unit lives in lane c/32, register
-// c%32.  The Walsh-Hadamard butterflies of coordinate bits 0..4 run inside a
-// lane's registers; bits 5.. (dt >= 64) pair lanes of the same quad with DPP
-// (or a swizzle for the third lane bit).  Norms are lane reductions.
-//
-// Memory: each wave moves its 64 groups through a private LDS tile, so every
-// global load and store instruction covers one contiguous 1 KiB span across
-// the wavefront (lane l <-> bytes [16 l, 16 l + 16)); the tile re-deals the
-// 16-byte chunks so that each lane ends up with its own group.  Codes and
-// norms are already contiguous per lane and go straight to memory.
-//
 // Encode ([Scratch] §2 steps 1-3; [Fork] "How it works"):
 //   n = ||x||, yhat = H_unnorm (D x); since sqrt(dt) * y = yhat / n the cell
 //   of a coordinate is found by comparing |yhat| with t_k * n (t_k the N(0,1)
@@ -21,10 +8,22 @@
 //   bucketize and bit-pack are one chain: per bit one compare and one
 //   add-with-carry (w = 2 w + [|yhat| > t]); the sign bit is shifted in from
 //   the float's sign.
-// Decode: c = level(code) looked up two coordinates at a time in an LDS
-//   table that already holds the first butterfly (c_a + c_b, c_a - c_b),
-//   optional norm correction, x~ = n * D H_unnorm c / dt (or with norm
-//   correction n * D H_unnorm c / (sqrt(dt) ||c||)).
+// Decode: c = level(code), optional norm correction, x~ = n D H_unnorm c / dt
+//   (with norm correction n D H_unnorm c / ||H_unnorm c||).
+//
+// Both directions work on 32-coordinate groups: a unit of dt coordinates is
+// LPU = dt / 32 consecutive groups, and H_dt = H_LPU (x) H_32.  fp16 rows are
+// encoded, and every decode runs, with the 32-point transforms of 32 groups at
+// a time on v_mfma_f32_32x32x16_f16 against the +-1 matrix (exact products,
+// fp32 sums) and the LPU-point part as butterflies between neighbouring lanes
+// (encode_mfma_kernel, decode_mfma_kernel).  fp32 rows are encoded by
+// encode_kernel, one group per lane with in-register fp32 butterflies (the
+// fp32 inputs do not fit an exact fp16 MFMA operand).
+//
+// Memory: each wave moves its 64 groups through a private LDS tile, so every
+// global load and store instruction of the rows covers one contiguous 1 KiB
+// span across the wavefront (lane l <-> bytes [16 l, 16 l + 16)); the tile
+// re-deals the 16-byte chunks so that each lane ends up with its own group.
 #include <hip/hip_fp16.h>
 
 #include "tq_device.h"
@@ -39,7 +38,8 @@ namespace {
 constexpr int kWaves = kBlock / 64;
 
 // Streaming hints and launch widths (nontemporal loads and stores, 32 workgroups per compute unit
-// for encode and 96 for the store-heavy decode measured fastest on MI355X).
+// for encode, 96 for the store-heavy block-32 decode and 32 for decodes of longer units measured
+// fastest on MI355X).
 #ifndef TQ_LOAD_NT
 #define TQ_LOAD_NT 1
 #endif
@@ -54,6 +54,9 @@ constexpr int kWaves = kBlock / 64;
 #endif
 #ifndef TQ_DEC_LGC
 #define TQ_DEC_LGC 1
+#endif
+#ifndef TQ_DEC_GRID_PER_CU_UNITS
+#define TQ_DEC_GRID_PER_CU_UNITS 32
 #endif
 
 __device__ __forceinline__ u32x4 load_stream(const u32x4* p) {
@@ -415,25 +418,6 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
   }
 }
 
-// Copy the code record and norm of group g (lane's own) into the wave's LDS slots: records at
-// rec_lds + 16 l (BITS = 3, 4) or word planes rec_lds + 256 k + 4 l (BITS = 1, 2), norms at
-// n_lds + 4 l.  Returns the number of copy instructions.
-template <int BITS, bool NORM_F32>
-__device__ __forceinline__ void copy_rec(const uint8_t* codes, const void* norms, int64_t g, uint8_t* rec_lds,
-                                         uint8_t* n_lds) {
-  const uint8_t* cp = codes + g * (4 * BITS);
-  if constexpr (BITS == 3 || BITS == 4) {
-    lds_copy<4 * BITS>(cp, rec_lds);
-  } else {
-#pragma unroll
-    for (int k = 0; k < BITS; ++k) lds_copy<4>(cp + 4 * k, rec_lds + 256 * k);
-  }
-  if constexpr (NORM_F32)
-    lds_copy<4>(static_cast<const float*>(norms) + g, n_lds);
-  else
-    lds_copy<2>(static_cast<const uint16_t*>(norms) + g, n_lds);
-}
-
 typedef _Float16 v8h_t __attribute__((ext_vector_type(8)));
 typedef float v16f_t __attribute__((ext_vector_type(16)));
 
@@ -453,19 +437,44 @@ __device__ __forceinline__ uint32_t join_halves(const uint32_t* lo, const uint32
   }
 }
 
-// Block-32 encode of fp16 rows with the Walsh-Hadamard transform on MFMA.
-// For a set of 32 groups, Yhat^T = M X^T with M = H_unnorm diag(D) (entries
-// +-1, exact in fp16) and X the fp16 inputs: products are exact and the sums
-// are accumulated in fp32, two v_mfma_f32_32x32x16_f16 per set and two sets
-// per wave (the wave's 64 groups, staged through LDS as in encode_kernel).
-// The rows of M are permuted so that output lane half h holds coordinates
-// 16h .. 16h+15 of its group in accumulator registers 0..15; each lane
-// bucketizes and packs those 16 with the same most-significant-first chain
-// as encode_kernel, and one permlane32 swap per segment word hands every lane
-// both halves of the record it stores.  The norm comes from the fp16 inputs
-// (dot2 of the lane's 16 values plus the partner lane's).
-template <int BITS, bool NORM_F32, bool CONTIG>
-__global__ __launch_bounds__(kBlock) void encode32_mfma_kernel(EncodeArgs a) {
+// Butterflies of coordinate bits 5.. across the LPU consecutive group columns of a unit (lanes
+// l ^ m, m < LPU, of the same lane half): the lane with bit m clear keeps a + b, its partner a - b.
+template <int LPU, int N>
+__device__ __forceinline__ void unit_butterflies(float* v, int q) {
+#pragma unroll
+  for (int m = 1; m < LPU; m <<= 1) {
+    const bool upper = (q & m) != 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const float p = lane_xor(v[i], m);
+      v[i] = upper ? p - v[i] : v[i] + p;
+    }
+  }
+}
+
+// Encode of fp16 rows with the 32-point Walsh-Hadamard transforms on MFMA.
+// For a set of 32 groups, Yhat^T = M X^T with M = H_unnorm (entries +-1,
+// exact in fp16) and X the fp16 inputs: products are exact and the sums are
+// accumulated in fp32, two v_mfma_f32_32x32x16_f16 per set and two sets per
+// wave (the wave's 64 groups, staged through LDS as in encode_kernel).  The
+// rows of M are permuted so that output lane half h holds coordinates
+// 16h .. 16h+15 of its group in accumulator registers 0..15.
+// A unit of dt = 32 LPU coordinates is LPU consecutive groups, i.e. LPU
+// neighbouring group columns: H_dt = H_LPU (x) H_32 in Sylvester order, so the
+// remaining log2(LPU) butterfly stages pair lanes l ^ 1, l ^ 2, l ^ 4.  The
+// sign flip D folds into M when a unit is one group (LPU = 1); otherwise each
+// group column has its own part of D, applied to the fp16 inputs' sign bits.
+// Each lane bucketizes and packs its 16 coordinates with the
+// most-significant-first chain of encode_kernel, and one permlane32 swap per
+// segment word hands every lane both halves of the group it stores.  The norm
+// comes from the fp16 inputs (dot2 of the lane's 16 values, the partner
+// lane's, and the unit's other groups).  Outputs: code and norm planes, or
+// (AOS) the fork's records, assembled in the wave's LDS tile and stored as
+// whole 16-byte chunks; 8-bit codes also go through the tile so that every
+// store instruction covers 1 KiB.
+template <int BITS, int LPU, bool NORM_F32, bool CONTIG, bool AOS>
+__global__ __launch_bounds__(kBlock) void encode_mfma_kernel(EncodeArgs a) {
+  static_assert(!(AOS && NORM_F32), "records carry fp16 norms");
   constexpr int CH = 4, PITCH = 16 * CH + 16;
   constexpr int SEGW = (16 * BITS + 31) / 32;  // words of one lane's 16-code segment
   constexpr bool B8 = BITS == 8;
@@ -478,11 +487,11 @@ __global__ __launch_bounds__(kBlock) void encode32_mfma_kernel(EncodeArgs a) {
   constexpr bool PIPE = BITS == 4 || BITS == 8;
   const int lane = threadIdx.x & 63;
   const int wave = PIPE ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : threadIdx.x >> 6;
-  const int n32 = lane & 31, h = lane >> 5;
+  const int n32 = lane & 31, h = lane >> 5, q = n32 % LPU;
   uint8_t* tile = stage[wave];
-  const uint32_t dword = a.dbits[0];
+  const uint32_t dword = a.dbits[LPU == 1 ? 0 : q];
   // A operand of K chunk kc: lane holds A[m][k] for row m = n32, k = 16 kc + 8 h + j, with
-  // A[m][k] = H[pi(m)][k] D[k] and pi(m) the coordinate that accumulator row m should carry
+  // A[m][k] = H[pi(m)][k] (D[k] too when LPU = 1) and pi(m) the coordinate accumulator row m carries
   const int pm = 16 * ((n32 >> 2) & 1) + 4 * (n32 >> 3) + (n32 & 3);
   v8h_t am[2];
 #pragma unroll
@@ -490,8 +499,17 @@ __global__ __launch_bounds__(kBlock) void encode32_mfma_kernel(EncodeArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int k = 16 * kc + 8 * h + j;
-      const uint32_t neg = ((uint32_t)__builtin_popcount(pm & k) ^ (dword >> k)) & 1u;
+      const uint32_t neg = ((uint32_t)__builtin_popcount(pm & k) ^ (LPU == 1 ? dword >> k : 0u)) & 1u;
       am[kc][j] = neg ? (_Float16)-1.0f : (_Float16)1.0f;
+    }
+  }
+  // LPU > 1: sign masks of D for the lane's B-operand words (coordinates 8h + 2i, +1 and 16 + 8h + 2i, +1)
+  uint32_t dmask[LPU == 1 ? 1 : 8];
+  if constexpr (LPU > 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      dmask[i] = pair_sign_mask(dword >> (8 * h), i);
+      dmask[4 + i] = pair_sign_mask(dword >> (16 + 8 * h), i);
     }
   }
   float thr[7];
@@ -520,8 +538,8 @@ __global__ __launch_bounds__(kBlock) void encode32_mfma_kernel(EncodeArgs a) {
     for (int s = 0; s < 2; ++s) {
       // B operand: coordinates 8h .. 8h+7 (chunk 0) and 16+8h .. 16+8h+7 (chunk 1) of group 32s + n32
       const uint8_t* gp = tile + (32 * s + n32) * PITCH + 16 * h;
-      const v8h_t b0 = *reinterpret_cast<const v8h_t*>(gp);
-      const v8h_t b1 = *reinterpret_cast<const v8h_t*>(gp + 32);
+      v8h_t b0 = *reinterpret_cast<const v8h_t*>(gp);
+      v8h_t b1 = *reinterpret_cast<const v8h_t*>(gp + 32);
       float ss = 0.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -529,13 +547,32 @@ __global__ __launch_bounds__(kBlock) void encode32_mfma_kernel(EncodeArgs a) {
         ss = __builtin_amdgcn_fdot2(p0, p0, ss, false);
         ss = __builtin_amdgcn_fdot2(p1, p1, ss, false);
       }
+      if constexpr (LPU > 1) {
+        u32x4 w0v = __builtin_bit_cast(u32x4, b0), w1v = __builtin_bit_cast(u32x4, b1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          w0v[i] ^= dmask[i];
+          w1v[i] ^= dmask[4 + i];
+        }
+        b0 = __builtin_bit_cast(v8h_t, w0v);
+        b1 = __builtin_bit_cast(v8h_t, w1v);
+      }
       const v16f_t z = {};
       v16f_t y = __builtin_amdgcn_mfma_f32_32x32x16_f16(am[0], b0, z, 0, 0, 0);
       y = __builtin_amdgcn_mfma_f32_32x32x16_f16(am[1], b1, y, 0, 0, 0);
       const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, ss), __builtin_bit_cast(uint32_t, ss),
                                                       false, false);
-      const float n = __builtin_sqrtf(__builtin_bit_cast(float, (uint32_t)r[0]) +
-                                      __builtin_bit_cast(float, (uint32_t)r[1]));
+      float us = __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+      float yv[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) yv[j] = y[j];
+      if constexpr (LPU > 1) {
+        us = unit_sum<LPU>(us);
+        unit_butterflies<LPU, 16>(yv, q);
+      }
+      // v_sqrt_f32 (1 ulp): the stored fp16 norm tolerates it, and the thresholds t n move by
+      // ~1e-7 of a cell edge, inside the 1e-6 band the codes are held to
+      const float n = __builtin_amdgcn_sqrtf(us);
       nrm[s] = n;
 #pragma unroll
       for (int k = 0; k < SEGW; ++k) seg[s][k] = 0u;
@@ -543,13 +580,13 @@ __global__ __launch_bounds__(kBlock) void encode32_mfma_kernel(EncodeArgs a) {
         const float kb = n > 0.0f ? a.bin_scale / n : 0.0f;
         const float top = (float)(a.n_bins - 1);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) seg[s][j >> 2] |= code8(y[j], n, kb, top, edge8, bin8) << (8 * (j & 3));
+        for (int j = 0; j < 16; ++j) seg[s][j >> 2] |= code8(yv[j], n, kb, top, edge8, bin8) << (8 * (j & 3));
       } else {
         float T[7];
 #pragma unroll
         for (int k = 0; k < 7; ++k) T[k] = thr[k] * n;
 #pragma unroll
-        for (int j = 15; j >= 0; --j) code_chain<BITS>(seg[s], j, y[j], T);
+        for (int j = 15; j >= 0; --j) code_chain<BITS>(seg[s], j, yv[j], T);
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -563,203 +600,118 @@ __global__ __launch_bounds__(kBlock) void encode32_mfma_kernel(EncodeArgs a) {
       hi[k] = r[1];
     }
     const float n = h ? nrm[1] : nrm[0];
+    uint32_t word[BITS];
+#pragma unroll
+    for (int k = 0; k < BITS; ++k) word[k] = n == 0.0f ? zero_unit_word<BITS>(k) : join_halves<BITS>(lo, hi, k);
     const int64_t g = w0 + lane;
-    if (PIPE ? (w0 + 64 <= a.n_groups || g < a.n_groups) : g < a.n_groups) {
-      uint32_t* cp = reinterpret_cast<uint32_t*>(a.codes + g * (4 * BITS));
-      if constexpr (B8) {  // 32 bytes per group: two 16-byte stores
+    const bool full = w0 + 64 <= a.n_groups;
+    if constexpr (AOS) {
+      constexpr int R = Record<BITS>::kBytes;
+      const uint16_t nb = __half_as_ushort(__float2half_rn(n));
+      if (full) {
+        put_record<BITS>(reinterpret_cast<uint16_t*>(tile + R * lane), nb, word);
+        __builtin_amdgcn_wave_barrier();
+        u32x4* out = reinterpret_cast<u32x4*>(a.codes + w0 * R);
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          u32x4 w;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) w[k] = n == 0.0f ? zero_unit_word<BITS>(4 * c + k) : join_halves<BITS>(lo, hi, 4 * c + k);
-          __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(cp) + c);
-        }
-      } else {
-#pragma unroll
-        for (int k = 0; k < BITS; ++k)
-          __builtin_nontemporal_store(n == 0.0f ? zero_unit_word<BITS>(k) : join_halves<BITS>(lo, hi, k), cp + k);
+        for (int c = lane; c < Record<BITS>::kChunks; c += 64)
+          store_stream(*reinterpret_cast<const u32x4*>(tile + 16 * c), out + c);
+        __builtin_amdgcn_wave_barrier();
+      } else if (g < a.n_groups) {
+        put_record<BITS>(reinterpret_cast<uint16_t*>(a.codes + g * R), nb, word);
       }
-      if constexpr (NORM_F32)
-        static_cast<float*>(a.norms)[g] = n;
-      else
-        static_cast<__half*>(a.norms)[g] = __float2half_rn(n);
+    } else {
+      if constexpr (B8) {  // 32 bytes per group, re-dealt through the tile into two 1 KiB spans
+        if (full) {
+          u32x4* t16 = reinterpret_cast<u32x4*>(tile);
+          t16[2 * lane] = u32x4{word[0], word[1], word[2], word[3]};
+          t16[2 * lane + 1] = u32x4{word[4], word[5], word[6], word[7]};
+          __builtin_amdgcn_wave_barrier();
+          u32x4* out = reinterpret_cast<u32x4*>(a.codes + w0 * 32);
+          store_stream(t16[lane], out + lane);
+          store_stream(t16[64 + lane], out + 64 + lane);
+          __builtin_amdgcn_wave_barrier();
+        } else if (g < a.n_groups) {
+          u32x4* cp = reinterpret_cast<u32x4*>(a.codes + g * 32);
+          store_stream(u32x4{word[0], word[1], word[2], word[3]}, cp);
+          store_stream(u32x4{word[4], word[5], word[6], word[7]}, cp + 1);
+        }
+      } else if (PIPE ? (full || g < a.n_groups) : g < a.n_groups) {
+        uint32_t* cp = reinterpret_cast<uint32_t*>(a.codes + g * (4 * BITS));
+#pragma unroll
+        for (int k = 0; k < BITS; ++k) __builtin_nontemporal_store(word[k], cp + k);
+      }
+      if ((LPU == 1 || q == 0) && g < a.n_groups) {
+        const int64_t u = g / LPU;
+        if constexpr (NORM_F32)
+          static_cast<float*>(a.norms)[u] = n;
+        else
+          static_cast<__half*>(a.norms)[u] = __float2half_rn(n);
+      }
     }
   }
 }
 
-// Pair table: entry (code_a | code_b << BITS) = (c_a + c_b, c_a - c_b), N(0,1) scale.
-template <int BITS>
-__device__ __forceinline__ void fill_pair_table(float2* tab, const float* level) {
-  constexpr int L = 1 << BITS;
-  for (int e = threadIdx.x; e < L * L; e += kBlock) {
-    const float ca = level[e & (L - 1)], cb = level[e >> BITS];
-    tab[e] = make_float2(ca + cb, ca - cb);
-  }
+// Bytes of one wave's prefetched code records in LDS: 4- or 16-byte slots per lane for the planes
+// (BITS = 1, 2: one 256-byte plane per word; 3, 4: 16-byte slots; 8: two 1 KiB halves); for the
+// fork's record format the 64 records of a full wave, 4 R 16-byte chunks (copy instruction i puts
+// chunk 64 i + l at 16 (64 i + l); lanes past the last chunk copy nothing).
+template <int BITS, bool AOS>
+constexpr int rec_lds_bytes() {
+  return AOS ? 16 * Record<BITS>::kChunks : BITS == 8 ? 2048 : 1024;
 }
 
-// Byte offset (8 * key) of the pair (2i, 2i+1) in the pair table.
-template <int BITS>
-__device__ __forceinline__ uint32_t pair_key8(const uint32_t* word, int i) {
-  constexpr int PB = 2 * BITS;
-  const int pos = PB * i;
-  const int wi = pos >> 5, sh = pos & 31;
-  uint32_t key;
-  if (sh + PB <= 32)
-    key = __builtin_amdgcn_ubfe(word[wi], sh, PB);
-  else
-    key = __builtin_amdgcn_ubfe(__builtin_amdgcn_alignbit(word[wi + 1], word[wi], sh), 0, PB);
-  return key << 3;
-}
-
+// Decode with the 32-point inverse transforms on MFMA: for a set of 32 groups,
+// Xhat^T = Minv C^T with Minv = H_unnorm (times diag(D) when a unit is one
+// group) and C the centroids in the N(0,1) scale, each split into fp16 hi + lo
+// parts.  Narrow codes (1..4 bits) use a pair table that yields, per lookup of
+// two codes, (hi pair, lo pair); 8-bit codes use a one-code (hi, lo) table
+// and byte permutes.  Two pairs form one B operand [hi hi lo lo hi hi lo lo]
+// of four coordinates, and the A operand repeats each Minv entry on the hi and
+// lo slot, so Minv (c_hi + c_lo) is summed in fp32 by four
+// v_mfma_f32_32x32x16_f16 per set.  Output rows are permuted as in
+// encode_mfma_kernel (lane half h: coordinates 16h..16h+15).  Units of LPU > 1
+// groups take their remaining butterfly stages across lanes l ^ 1, 2, 4 and D
+// at the output.  Scaled by n / dt (or n / ||Xhat|| with norm correction,
+// ||Xhat||^2 = dt ||c||^2), staged in LDS and stored coalesced.  Codes and
+// norms of the next iteration are copied into LDS with global_load_lds one
+// iteration ahead (the fork's records: whole 16-byte chunks of a full wave;
+// the last, partial wave reads its records directly).
 template <int BITS, int LPU, bool OUT_F32, bool NORM_F32, bool NC, bool CONTIG, bool AOS>
-__global__ __launch_bounds__(kBlock) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kBlock) void decode_mfma_kernel(DecodeArgs a) {
   static_assert(!(AOS && NORM_F32), "records carry fp16 norms");
-  static_assert(BITS <= 4 || BITS == 8, "1..4 or 8 bits");
   constexpr bool B8 = BITS == 8;
   constexpr int L = 1 << BITS;
-  constexpr int CH = OUT_F32 ? 8 : 4;
-  constexpr int PITCH = 16 * CH + 16;
-  __shared__ __attribute__((aligned(16))) uint8_t stage[kWaves][64 * PITCH];
-  // pair table (two codes -> first butterfly) for narrow codes; 8 bits: one level per code
-  __shared__ float2 ptab[B8 ? 1 : L * L];
-  __shared__ float lvl8[B8 ? 256 : 1];
-  if constexpr (B8) {
-    for (int e = threadIdx.x; e < 256; e += kBlock) lvl8[e] = a.level[e];
-  } else {
-    fill_pair_table<BITS>(ptab, a.level);
-  }
-  __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint8_t* tile = stage[wave];
-  const char* tabp = reinterpret_cast<const char*>(ptab);
-  const int q = lane % LPU;
-  const uint32_t dword = a.dbits[q];
-  char* ybase = static_cast<char*>(a.y);
-  constexpr int ES = OUT_F32 ? 4 : 2;
-
-  const int64_t stride = (int64_t)gridDim.x * kBlock;
-  for (int64_t w0 = (int64_t)blockIdx.x * kBlock + wave * 64; w0 < a.n_groups; w0 += stride) {
-    const int64_t g = w0 + lane;
-    const bool valid = g < a.n_groups;
-    uint32_t word[BITS];
-    float n = 0.0f;
-    if constexpr (AOS) {
-      // each group is scaled by the norm its own record carries
-      constexpr int R = Record<BITS>::kBytes;
-      if (w0 + 64 <= a.n_groups) {
-        const u32x4* src = reinterpret_cast<const u32x4*>(a.codes + w0 * R);
-        u32x4 t[(Record<BITS>::kChunks + 63) / 64];
-#pragma unroll
-        for (int i = 0; i * 64 < Record<BITS>::kChunks; ++i)
-          if (lane + 64 * i < Record<BITS>::kChunks) t[i] = load_stream(src + lane + 64 * i);
-#pragma unroll
-        for (int i = 0; i * 64 < Record<BITS>::kChunks; ++i)
-          if (lane + 64 * i < Record<BITS>::kChunks) *reinterpret_cast<u32x4*>(tile + 16 * (lane + 64 * i)) = t[i];
-        __builtin_amdgcn_wave_barrier();
-        n = get_record<BITS>(reinterpret_cast<const uint16_t*>(tile + R * lane), word);
-        __builtin_amdgcn_wave_barrier();
-      } else if (valid) {
-        n = get_record<BITS>(reinterpret_cast<const uint16_t*>(a.codes + g * R), word);
-      } else {
-#pragma unroll
-        for (int k = 0; k < BITS; ++k) word[k] = 0u;
-      }
-    } else if (valid) {
-      const uint32_t* cp = reinterpret_cast<const uint32_t*>(a.codes + g * (4 * BITS));
-#pragma unroll
-      for (int k = 0; k < BITS; ++k) word[k] = __builtin_nontemporal_load(cp + k);
-      const int64_t u = g / LPU;
-      if constexpr (NORM_F32)
-        n = static_cast<const float*>(a.norms)[u];
-      else
-        n = __half2float(static_cast<const __half*>(a.norms)[u]);
-    } else {
-#pragma unroll
-      for (int k = 0; k < BITS; ++k) word[k] = 0u;
-    }
-    float v[32];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if constexpr (B8) {
-        const uint32_t w = word[i >> 1] >> (16 * (i & 1));
-        const float ca = lvl8[w & 255u], cb = lvl8[(w >> 8) & 255u];
-        v[2 * i] = ca + cb;
-        v[2 * i + 1] = ca - cb;
-      } else {
-        const float2 e = *reinterpret_cast<const float2*>(tabp + pair_key8<BITS>(word, i));
-        v[2 * i] = e.x;
-        v[2 * i + 1] = e.y;
-      }
-    }
-    float scale;
-    if constexpr (NC) {
-      float ss = 0.0f;
-#pragma unroll
-      for (int j = 0; j < 32; ++j) ss = __builtin_fmaf(v[j], v[j], ss);
-      ss = unit_sum<LPU>(ss);  // = 2 * ||c||^2: each pair contributes (a+b)^2 + (a-b)^2
-      scale = n * a.inv_sqrt_dt * __builtin_sqrtf(2.0f / ss);
-    } else {
-      scale = n * a.inv_dt;
-    }
-    fwht32_from<1>(v);
-    fwht_crosslane<LPU>(v, q);
-
-    // ---- stage the group's output in LDS, then store it coalesced ----
-    uint32_t o[4 * CH];
-    if constexpr (!OUT_F32) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const __half lo = __float2half_rn(v[2 * i] * scale);
-        const __half hi = __float2half_rn(v[2 * i + 1] * scale);
-        o[i] = ((uint32_t)__half_as_ushort(lo) | ((uint32_t)__half_as_ushort(hi) << 16)) ^ pair_sign_mask(dword, i);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) o[i] = __builtin_bit_cast(uint32_t, v[i] * scale) ^ (((dword >> i) & 1u) << 31);
-    }
-#pragma unroll
-    for (int c = 0; c < CH; ++c)
-      *reinterpret_cast<u32x4*>(tile + lane * PITCH + 16 * c) = u32x4{o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]};
-    __builtin_amdgcn_wave_barrier();
-    stage_out<CH, PITCH, ES, CONTIG>(tile, ybase, w0, a.n_groups, a.groups_per_row, a.ld_y, lane);
-    __builtin_amdgcn_wave_barrier();
-  }
-}
-
-// Block-32 decode with the inverse transform on MFMA: for a set of 32 groups,
-// Xhat^T = Minv C^T with Minv = diag(D) H_unnorm (entries +-1) and C the
-// centroids in the N(0,1) scale, each split into fp16 hi + lo parts.  The pair
-// table yields, per lookup of two codes, (hi pair, lo pair); two lookups form
-// one B operand [hi hi lo lo hi hi lo lo] of four coordinates, and the A
-// operand repeats each Minv entry on the hi and lo slot, so Minv (c_hi + c_lo)
-// is summed in fp32 by four v_mfma_f32_32x32x16_f16 per set.  Output rows are
-// permuted as in encode32_mfma_kernel (lane half h: coordinates 16h..16h+15),
-// scaled by n / 32 (or n / ||Xhat|| with norm correction, ||Xhat||^2 =
-// 32 ||c||^2), staged in LDS and stored coalesced.
-template <int BITS, bool OUT_F32, bool NORM_F32, bool NC, bool CONTIG>
-__global__ __launch_bounds__(kBlock) void decode32_mfma_kernel(DecodeArgs a) {
-  constexpr int L = 1 << BITS;
   constexpr int CH = OUT_F32 ? 8 : 4, PITCH = 16 * CH + 16, ES = OUT_F32 ? 4 : 2;
-  constexpr int LGC = TQ_DEC_LGC, NCOPY = 1 << LGC;  // pair-table copies (lane l reads copy l % NCOPY)
+  constexpr int LGC = TQ_DEC_LGC, NCOPY = 1 << LGC;  // table copies (lane l reads copy l % NCOPY)
+  constexpr int R = Record<BITS>::kBytes, RLDS = rec_lds_bytes<BITS, AOS>();
   __shared__ __attribute__((aligned(16))) uint8_t stage[kWaves][64 * PITCH];
-  __shared__ __attribute__((aligned(16))) uint2 ptab[L * L * NCOPY];
-  __shared__ __attribute__((aligned(16))) uint8_t pre_rec[kWaves][1024];
-  __shared__ __attribute__((aligned(16))) uint8_t pre_norm[kWaves][256];
-  for (int x = threadIdx.x; x < L * L * NCOPY; x += kBlock) {
-    const int e = x >> LGC;
-    const float ca = a.level[e & (L - 1)], cb = a.level[e >> BITS];
-    const _Float16 ha = (_Float16)ca, hb = (_Float16)cb;
-    const _Float16 la = (_Float16)(ca - (float)ha), lb = (_Float16)(cb - (float)hb);
-    ptab[x] = make_uint2((uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16),
-                         (uint32_t)__builtin_bit_cast(uint16_t, la) | ((uint32_t)__builtin_bit_cast(uint16_t, lb) << 16));
+  __shared__ __attribute__((aligned(16))) uint2 ptab[B8 ? 1 : L * L * NCOPY];
+  __shared__ __attribute__((aligned(16))) uint32_t tab8[B8 ? 256 * NCOPY : 1];
+  __shared__ __attribute__((aligned(16))) uint8_t pre_rec[kWaves][RLDS];
+  __shared__ __attribute__((aligned(16))) uint8_t pre_norm[kWaves][AOS ? 16 : 256];
+  if constexpr (B8) {
+    for (int x = threadIdx.x; x < 256 * NCOPY; x += kBlock) {
+      const float c = a.level[x >> LGC];
+      const _Float16 hc = (_Float16)c, lc = (_Float16)(c - (float)hc);
+      tab8[x] = (uint32_t)__builtin_bit_cast(uint16_t, hc) | ((uint32_t)__builtin_bit_cast(uint16_t, lc) << 16);
+    }
+  } else {
+    for (int x = threadIdx.x; x < L * L * NCOPY; x += kBlock) {
+      const int e = x >> LGC;
+      const float ca = a.level[e & (L - 1)], cb = a.level[e >> BITS];
+      const _Float16 ha = (_Float16)ca, hb = (_Float16)cb;
+      const _Float16 la = (_Float16)(ca - (float)ha), lb = (_Float16)(cb - (float)hb);
+      ptab[x] = make_uint2((uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16),
+                           (uint32_t)__builtin_bit_cast(uint16_t, la) | ((uint32_t)__builtin_bit_cast(uint16_t, lb) << 16));
+    }
   }
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n32 = lane & 31, h = lane >> 5;
+  const int n32 = lane & 31, h = lane >> 5, q = n32 % LPU;
   uint8_t* tile = stage[wave];
-  const char* tabp = reinterpret_cast<const char*>(ptab);
-  const uint32_t toff = (uint32_t)(lane & (NCOPY - 1)) * 8u;
-  const uint32_t dword = a.dbits[0];
+  const char* tabp = B8 ? reinterpret_cast<const char*>(tab8) : reinterpret_cast<const char*>(ptab);
+  const uint32_t toff = (uint32_t)(lane & (NCOPY - 1)) * (B8 ? 4u : 8u);
+  const uint32_t dword = a.dbits[LPU == 1 ? 0 : q];
   // A operand of MFMA f: row m = n32 carries output coordinate pm; slot 8h + j is code
   // coordinate 8f + 4h + {0,1,0,1,2,3,2,3}[j] (hi parts on slots 0,1,4,5, lo parts on 2,3,6,7)
   const int pm = 16 * ((n32 >> 2) & 1) + 4 * (n32 >> 3) + (n32 & 3);
@@ -769,51 +721,91 @@ __global__ __launch_bounds__(kBlock) void decode32_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int c = 8 * f + 4 * h + ((j >> 2) << 1) + (j & 1);
-      const uint32_t neg = ((uint32_t)__builtin_popcount(pm & c) ^ (dword >> pm)) & 1u;
+      const uint32_t neg = ((uint32_t)__builtin_popcount(pm & c) ^ (LPU == 1 ? dword >> pm : 0u)) & 1u;
       am[f][j] = neg ? (_Float16)-1.0f : (_Float16)1.0f;
     }
   }
+  // LPU > 1: D of the lane's 16 output coordinates 16h .. 16h+15, as fp16 pair and fp32 sign masks
+  const uint32_t dout = LPU == 1 ? 0u : dword >> (16 * h);
   char* ybase = static_cast<char*>(a.y);
-
-  // The record and norm of the next iteration are copied into LDS before this iteration's stores
-  // are issued, so the wait for them at the top of an iteration leaves the previous iteration's
-  // stores (4 for a full wave) in flight.
   const int64_t stride = (int64_t)gridDim.x * kBlock;
   uint8_t* rec_lds = pre_rec[wave];
   uint8_t* n_lds = pre_norm[wave];
+
+  // copy the records (and norms) of the wave starting at group w into LDS; a full wave of records
+  // moves as whole 16-byte chunks, a partial one is read directly in its iteration
+  auto prefetch = [&](int64_t w) {
+    if constexpr (AOS) {
+      if (w + 64 <= a.n_groups) {
+        const uint8_t* src = a.codes + w * R;
+#pragma unroll
+        for (int i = 0; 64 * i < Record<BITS>::kChunks; ++i) {
+          const int c = 64 * i + lane;
+          if (c < Record<BITS>::kChunks) lds_copy<16>(src + 16 * c, rec_lds + 1024 * i);
+        }
+      }
+    } else {
+      const int64_t g = w + lane < a.n_groups ? w + lane : a.n_groups - 1;
+      const uint8_t* cp = a.codes + g * (4 * BITS);
+      if constexpr (BITS == 3 || BITS == 4) {
+        lds_copy<4 * BITS>(cp, rec_lds);
+      } else if constexpr (B8) {
+        lds_copy<16>(cp, rec_lds);
+        lds_copy<16>(cp + 16, rec_lds + 1024);
+      } else {
+#pragma unroll
+        for (int k = 0; k < BITS; ++k) lds_copy<4>(cp + 4 * k, rec_lds + 256 * k);
+      }
+      const int64_t u = g / LPU;
+      if constexpr (NORM_F32)
+        lds_copy<4>(static_cast<const float*>(a.norms) + u, n_lds);
+      else
+        lds_copy<2>(static_cast<const uint16_t*>(a.norms) + u, n_lds);
+    }
+  };
+
+  // The records and norms of the next iteration are copied into LDS before this iteration's stores
+  // are issued, so the wait for them at the top of an iteration leaves the previous iteration's
+  // stores (CH for a full wave) in flight.
   const int64_t first = (int64_t)blockIdx.x * kBlock + wave * 64;
-  copy_rec<BITS, NORM_F32>(a.codes, a.norms, first + lane < a.n_groups ? first + lane : a.n_groups - 1, rec_lds, n_lds);
+  prefetch(first);
   bool prev_full = false;
   for (int64_t w0 = first; w0 < a.n_groups; w0 += stride) {
     if (prev_full)
-      wait_vm<4>();
+      wait_vm<CH>();
     else
       wait_vm<0>();
     const int64_t g = w0 + lane;
+    const bool live = g < a.n_groups, full = w0 + 64 <= a.n_groups;
     uint32_t rec[BITS];
     float n = 0.0f;
-    {
-      uint32_t pr[BITS], pn;
+    if constexpr (AOS) {
+      const uint16_t* rp = reinterpret_cast<const uint16_t*>(full ? rec_lds + R * lane : a.codes + (live ? g : 0) * R);
+      const float nf = get_record<BITS>(rp, rec);
+      n = live ? nf : 0.0f;
+#pragma unroll
+      for (int k = 0; k < BITS; ++k) rec[k] = live ? rec[k] : 0u;
+    } else {
+      uint32_t pr[BITS];
       if constexpr (BITS == 3 || BITS == 4) {
 #pragma unroll
         for (int k = 0; k < BITS; ++k) pr[k] = reinterpret_cast<const uint32_t*>(rec_lds)[4 * lane + k];
+      } else if constexpr (B8) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) pr[k] = reinterpret_cast<const uint32_t*>(rec_lds + 1024 * (k >> 2))[4 * lane + (k & 3)];
       } else {
 #pragma unroll
         for (int k = 0; k < BITS; ++k) pr[k] = reinterpret_cast<const uint32_t*>(rec_lds + 256 * k)[lane];
       }
-      pn = reinterpret_cast<const uint32_t*>(n_lds)[lane];
-      const bool live = g < a.n_groups;
+      const uint32_t pn = reinterpret_cast<const uint32_t*>(n_lds)[lane];
 #pragma unroll
       for (int k = 0; k < BITS; ++k) rec[k] = live ? pr[k] : 0u;
       const float nf = NORM_F32 ? __builtin_bit_cast(float, pn) : __half2float(__ushort_as_half((uint16_t)pn));
       n = live ? nf : 0.0f;
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slots read before the next copy lands
-    {
-      const int64_t gn = w0 + stride + lane;
-      copy_rec<BITS, NORM_F32>(a.codes, a.norms, gn < a.n_groups ? gn : a.n_groups - 1, rec_lds, n_lds);
-    }
-    prev_full = w0 + 64 <= a.n_groups;
+    if (w0 + stride < a.n_groups) prefetch(w0 + stride);
+    prev_full = full;
     // every lane gets the records and norms of both sets (lanes 0..31: set 0, 32..63: set 1)
     uint32_t rs[2][BITS];
 #pragma unroll
@@ -827,34 +819,55 @@ __global__ __launch_bounds__(kBlock) void decode32_mfma_kernel(DecodeArgs a) {
     const float ns[2] = {__builtin_bit_cast(float, (uint32_t)rn[0]), __builtin_bit_cast(float, (uint32_t)rn[1])};
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      // this lane's codes start at coordinate 4h of each 8-coordinate chunk: shift the record by 4h codes
-      uint32_t w[BITS];
-#pragma unroll
-      for (int k = 0; k < BITS; ++k)
-        w[k] = __builtin_amdgcn_alignbit(k + 1 < BITS ? rs[s][k + 1] : 0u, rs[s][k], 4 * BITS * h);
       v16f_t y = {};
+      if constexpr (B8) {
+        // this lane's 4 codes of chunk f are bytes 8f + 4h .. 8f + 4h + 3, i.e. record word 2f + h
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        uint2 e[2];
+        for (int f = 0; f < 4; ++f) {
+          const uint32_t w = h ? rs[s][2 * f + 1] : rs[s][2 * f];
+          uint32_t e[4];
 #pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-          const int pos = 8 * BITS * f + 2 * BITS * pp, wi = pos >> 5, sh = pos & 31;
-          const uint32_t key = sh + 2 * BITS <= 32
-                                   ? __builtin_amdgcn_ubfe(w[wi], sh, 2 * BITS)
-                                   : __builtin_amdgcn_ubfe(__builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh), 0, 2 * BITS);
-          e[pp] = *reinterpret_cast<const uint2*>(tabp + ((key << (LGC + 3)) | toff));
+          for (int k = 0; k < 4; ++k)
+            e[k] = *reinterpret_cast<const uint32_t*>(tabp + ((__builtin_amdgcn_ubfe(w, 8 * k, 8) << (LGC + 2)) | toff));
+          const u32x4 bw = {__builtin_amdgcn_perm(e[1], e[0], 0x05040100u), __builtin_amdgcn_perm(e[1], e[0], 0x07060302u),
+                            __builtin_amdgcn_perm(e[3], e[2], 0x05040100u), __builtin_amdgcn_perm(e[3], e[2], 0x07060302u)};
+          y = __builtin_amdgcn_mfma_f32_32x32x16_f16(am[f], __builtin_bit_cast(v8h_t, bw), y, 0, 0, 0);
         }
-        const v8h_t b = __builtin_bit_cast(v8h_t, u32x4{e[0].x, e[0].y, e[1].x, e[1].y});
-        y = __builtin_amdgcn_mfma_f32_32x32x16_f16(am[f], b, y, 0, 0, 0);
+      } else {
+        // this lane's codes start at coordinate 4h of each 8-coordinate chunk: shift the record by 4h codes
+        uint32_t w[BITS];
+#pragma unroll
+        for (int k = 0; k < BITS; ++k)
+          w[k] = __builtin_amdgcn_alignbit(k + 1 < BITS ? rs[s][k + 1] : 0u, rs[s][k], 4 * BITS * h);
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          uint2 e[2];
+#pragma unroll
+          for (int pp = 0; pp < 2; ++pp) {
+            const int pos = 8 * BITS * f + 2 * BITS * pp, wi = pos >> 5, sh = pos & 31;
+            const uint32_t key = sh + 2 * BITS <= 32
+                                     ? __builtin_amdgcn_ubfe(w[wi], sh, 2 * BITS)
+                                     : __builtin_amdgcn_ubfe(__builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh), 0, 2 * BITS);
+            e[pp] = *reinterpret_cast<const uint2*>(tabp + ((key << (LGC + 3)) | toff));
+          }
+          const v8h_t b = __builtin_bit_cast(v8h_t, u32x4{e[0].x, e[0].y, e[1].x, e[1].y});
+          y = __builtin_amdgcn_mfma_f32_32x32x16_f16(am[f], b, y, 0, 0, 0);
+        }
       }
+      float yv[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) yv[j] = y[j];
+      if constexpr (LPU > 1) unit_butterflies<LPU, 16>(yv, q);
       float scale;
       if constexpr (NC) {
         float ss = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) ss = __builtin_fmaf(y[i], y[i], ss);
+        for (int i = 0; i < 16; ++i) ss = __builtin_fmaf(yv[i], yv[i], ss);
         const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, ss), __builtin_bit_cast(uint32_t, ss),
                                                         false, false);
-        scale = ns[s] / __builtin_sqrtf(__builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]));
+        float us = __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+        if constexpr (LPU > 1) us = unit_sum<LPU>(us);
+        scale = ns[s] / __builtin_sqrtf(us);
       } else {
         scale = ns[s] * a.inv_dt;
       }
@@ -863,17 +876,17 @@ __global__ __launch_bounds__(kBlock) void decode32_mfma_kernel(DecodeArgs a) {
         uint32_t o[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const __half lo = __float2half_rn(y[2 * i] * scale), hi = __float2half_rn(y[2 * i + 1] * scale);
-          o[i] = (uint32_t)__half_as_ushort(lo) | ((uint32_t)__half_as_ushort(hi) << 16);
+          const __half lo = __float2half_rn(yv[2 * i] * scale), hi = __float2half_rn(yv[2 * i + 1] * scale);
+          o[i] = ((uint32_t)__half_as_ushort(lo) | ((uint32_t)__half_as_ushort(hi) << 16)) ^ pair_sign_mask(dout, i);
         }
         reinterpret_cast<u32x4*>(dst)[0] = u32x4{o[0], o[1], o[2], o[3]};
         reinterpret_cast<u32x4*>(dst)[1] = u32x4{o[4], o[5], o[6], o[7]};
       } else {
+        uint32_t o[16];
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          reinterpret_cast<u32x4*>(dst)[c] =
-              u32x4{__builtin_bit_cast(uint32_t, y[4 * c] * scale), __builtin_bit_cast(uint32_t, y[4 * c + 1] * scale),
-                    __builtin_bit_cast(uint32_t, y[4 * c + 2] * scale), __builtin_bit_cast(uint32_t, y[4 * c + 3] * scale)};
+        for (int j = 0; j < 16; ++j) o[j] = __builtin_bit_cast(uint32_t, yv[j] * scale) ^ (((dout >> j) & 1u) << 31);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) reinterpret_cast<u32x4*>(dst)[c] = u32x4{o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]};
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -892,6 +905,8 @@ int64_t grid_for(int64_t n_groups, int per_cu) {
   return need < cap ? need : cap;
 }
 
+// fp16 rows: the MFMA kernel for every unit length and output form; fp32 rows: the one-group-per-lane
+// kernel (its transform is exact fp32 arithmetic on the fp32 inputs).
 template <int BITS, int LPU, bool CONTIG>
 hipError_t encode_dispatch_dtype(const tq_config& cfg, const EncodeArgs& a, hipStream_t s) {
   dim3 grid((unsigned)grid_for(a.n_groups, TQ_GRID_PER_CU)), block(kBlock);
@@ -900,20 +915,11 @@ hipError_t encode_dispatch_dtype(const tq_config& cfg, const EncodeArgs& a, hipS
     if (in32)
       hipLaunchKernelGGL((encode_kernel<BITS, LPU, true, false, CONTIG, true>), grid, block, 0, s, a);
     else
-      hipLaunchKernelGGL((encode_kernel<BITS, LPU, false, false, CONTIG, true>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((encode_mfma_kernel<BITS, LPU, false, CONTIG, true>), grid, block, 0, s, a);
     return hipGetLastError();
   }
-  if constexpr (LPU == 1) {
-    if (!in32) {
-      if (n32)
-        hipLaunchKernelGGL((encode32_mfma_kernel<BITS, true, CONTIG>), grid, block, 0, s, a);
-      else
-        hipLaunchKernelGGL((encode32_mfma_kernel<BITS, false, CONTIG>), grid, block, 0, s, a);
-      return hipGetLastError();
-    }
-  }
-  if (!in32 && !n32) hipLaunchKernelGGL((encode_kernel<BITS, LPU, false, false, CONTIG, false>), grid, block, 0, s, a);
-  if (!in32 && n32) hipLaunchKernelGGL((encode_kernel<BITS, LPU, false, true, CONTIG, false>), grid, block, 0, s, a);
+  if (!in32 && !n32) hipLaunchKernelGGL((encode_mfma_kernel<BITS, LPU, false, CONTIG, false>), grid, block, 0, s, a);
+  if (!in32 && n32) hipLaunchKernelGGL((encode_mfma_kernel<BITS, LPU, true, CONTIG, false>), grid, block, 0, s, a);
   if (in32 && !n32) hipLaunchKernelGGL((encode_kernel<BITS, LPU, true, false, CONTIG, false>), grid, block, 0, s, a);
   if (in32 && n32) hipLaunchKernelGGL((encode_kernel<BITS, LPU, true, true, CONTIG, false>), grid, block, 0, s, a);
   return hipGetLastError();
@@ -936,26 +942,19 @@ hipError_t encode_dispatch_lpu(const tq_config& cfg, const EncodeArgs& a, hipStr
 
 template <int BITS, int LPU, bool NC, bool CONTIG>
 hipError_t decode_dispatch_dtype(const tq_config& cfg, const DecodeArgs& a, tq_dtype yt, hipStream_t s) {
-  dim3 grid((unsigned)grid_for(a.n_groups, LPU == 1 ? TQ_DEC_GRID_PER_CU : TQ_GRID_PER_CU)), block(kBlock);
+  dim3 grid((unsigned)grid_for(a.n_groups, LPU == 1 ? TQ_DEC_GRID_PER_CU : TQ_DEC_GRID_PER_CU_UNITS)), block(kBlock);
   const bool o32 = yt == TQ_F32, n32 = cfg.norm_dtype == TQ_F32;
   if (cfg.flags & TQ_BLOCKS) {  // fp16 norms (checked on the host)
     if (o32)
-      hipLaunchKernelGGL((decode_kernel<BITS, LPU, true, false, NC, CONTIG, true>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((decode_mfma_kernel<BITS, LPU, true, false, NC, CONTIG, true>), grid, block, 0, s, a);
     else
-      hipLaunchKernelGGL((decode_kernel<BITS, LPU, false, false, NC, CONTIG, true>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((decode_mfma_kernel<BITS, LPU, false, false, NC, CONTIG, true>), grid, block, 0, s, a);
     return hipGetLastError();
   }
-  if constexpr (LPU == 1 && BITS <= 4) {
-    if (!o32 && !n32) hipLaunchKernelGGL((decode32_mfma_kernel<BITS, false, false, NC, CONTIG>), grid, block, 0, s, a);
-    if (!o32 && n32) hipLaunchKernelGGL((decode32_mfma_kernel<BITS, false, true, NC, CONTIG>), grid, block, 0, s, a);
-    if (o32 && !n32) hipLaunchKernelGGL((decode32_mfma_kernel<BITS, true, false, NC, CONTIG>), grid, block, 0, s, a);
-    if (o32 && n32) hipLaunchKernelGGL((decode32_mfma_kernel<BITS, true, true, NC, CONTIG>), grid, block, 0, s, a);
-    return hipGetLastError();
-  }
-  if (!o32 && !n32) hipLaunchKernelGGL((decode_kernel<BITS, LPU, false, false, NC, CONTIG, false>), grid, block, 0, s, a);
-  if (!o32 && n32) hipLaunchKernelGGL((decode_kernel<BITS, LPU, false, true, NC, CONTIG, false>), grid, block, 0, s, a);
-  if (o32 && !n32) hipLaunchKernelGGL((decode_kernel<BITS, LPU, true, false, NC, CONTIG, false>), grid, block, 0, s, a);
-  if (o32 && n32) hipLaunchKernelGGL((decode_kernel<BITS, LPU, true, true, NC, CONTIG, false>), grid, block, 0, s, a);
+  if (!o32 && !n32) hipLaunchKernelGGL((decode_mfma_kernel<BITS, LPU, false, false, NC, CONTIG, false>), grid, block, 0, s, a);
+  if (!o32 && n32) hipLaunchKernelGGL((decode_mfma_kernel<BITS, LPU, false, true, NC, CONTIG, false>), grid, block, 0, s, a);
+  if (o32 && !n32) hipLaunchKernelGGL((decode_mfma_kernel<BITS, LPU, true, false, NC, CONTIG, false>), grid, block, 0, s, a);
+  if (o32 && n32) hipLaunchKernelGGL((decode_mfma_kernel<BITS, LPU, true, true, NC, CONTIG, false>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
