@@ -21,19 +21,24 @@
 //            (8-bit keys: a one-code table, two lookups per pair) into fp16
 //            hi/lo operands, and three v_mfma_f32_16x16x32_f16
 //            (q_hi c_hi + q_lo c_hi + q_hi c_lo) give the block dot products
-//            to ~2^-22.  The query operand of subtile st is non-zero only in
-//            rows st*GP .. st*GP+GP-1 (GP = query heads padded to 4, 8 or 16),
-//            so 16/GP subtiles accumulate into one 16x16 result with every
-//            lane holding live scores; block norms scale it in fp32;
+//            to ~2^-22.  Row r of the query operand is head r % GP (GP = query
+//            heads padded to 4, 8 or 16), so each subtile's 16x16 product
+//            repeats its scores 16/GP times; lane group g keeps the product of
+//            subtile slot 4g/GP, and every lane holds live scores of a distinct
+//            (head, token); block norms scale them in fp32;
 //   exchange the waves' partial scores (over their own blocks) are summed
 //            through LDS, after which every wave holds the full scores;
 //   softmax  online per query head against a running reference that only
 //            moves when a score passes it by more than kSlack;
-//   V side   each lane expands one token's records (pair table, scaled by
-//            the block norm with one packed fp16 multiply per pair) into a
-//            wave-private LDS tile; ds_read_b64_tr_b16 returns four tokens of
-//            one coordinate per lane, the B layout of the value MFMA (K = 32
-//            tokens); the softmax weights are the fp16 A operand.
+//   V side   one 32-token half of the tile at a time: each lane expands one
+//            (token, block) record (pair table, scaled by the block norm with
+//            one packed fp16 multiply per pair; at head_dim 128 two lanes split
+//            a block) into a wave-private LDS tile of 32 rows;
+//            ds_read_b64_tr_b16 returns four tokens of one coordinate per lane,
+//            the B layout of the value MFMA (K = 32 tokens); the softmax
+//            weights are the fp16 A operand.  Halving the tile keeps a
+//            workgroup of up to 4 rows within a third of the LDS, so three
+//            workgroups share a compute unit.
 // Each workgroup writes one partial (acc, max, sum) per query head; a merge
 // kernel rescales and adds the partials, then applies D_V H once per block.
 #include <hip/hip_fp16.h>
@@ -56,18 +61,20 @@ template <int NBW, int KB, int VB, int NC>
 struct TileRegs {
   uint32_t kw[NBW][4][2];  // K: 2 words covering this lane's 8 coordinates, per owned block and subtile
   uint32_t kn[NC];         // K norms (fp16) of the token this lane scales, per accumulator; NBW halves
-  uint32_t vw[NBW * VB];   // V: whole records of token `lane`, owned blocks in order
-  uint32_t vn;             // V norms (fp16) of token `lane`, NBW halves
+  uint32_t vw[2][VB];      // V: per 32-token half, the whole record of this lane's (token, block)
+  uint32_t vn[2];          // V norms (fp16) of those two (token, block) units
 };
 
 template <int NB, int KB, int VB, int GP>
-__global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, GP == 4 ? 3 : 2) void attn_kernel(AttnArgs a) {
   constexpr int HD = NB * 32;
   constexpr int NBW = NB / kWaves;  // blocks per wave
-  constexpr int S = 16 / GP;        // subtiles stacked per 16x16 accumulator
+  constexpr int S = 16 / GP;        // subtiles whose products one lane group picks from (slot 4g / GP)
   constexpr int NC = 4 / S;         // accumulators per block for the 4 subtiles
   constexpr int KL = 1 << KB, VL = 1 << VB;
   constexpr int VROW = NBW * 32;    // fp16 per V tile row (one token, the wave's blocks)
+  constexpr int VT = kTile / 2;     // tokens per V tile: the value side runs in two 32-token halves
+  constexpr int NXS = GP == 16 ? 1 : 2;  // score exchange buffers (one at 16 rows, saving LDS)
   constexpr int NCH = 2 * NBW;      // 16-coordinate chunks per V tile row
   // fp16 offset of 16-byte half k of chunk c in V tile row t.  Chunks are permuted by token bits
   // above the rows that share 256 bytes of banks, and the halves by bit 3, so the 16 rows written
@@ -92,9 +99,9 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   struct Smem {
     uint32_t ktab[K8 ? KL * CK : 2 * KL * KL * CK + 1];
     uint32_t vtab[VL * VL * CV];
-    __attribute__((aligned(16))) _Float16 vt[kWaves][kTile * VROW];
+    __attribute__((aligned(16))) _Float16 vt[kWaves][VT * VROW];
     __attribute__((aligned(16))) _Float16 pt[kWaves][GP * kTile];
-    __attribute__((aligned(16))) float xs[2][64][XSTR];
+    __attribute__((aligned(16))) float xs[NXS][64][XSTR];
   };
   __shared__ Smem sm;
   uint32_t* ktab = sm.ktab;
@@ -165,29 +172,25 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
       const uint32_t t = min((uint32_t)ktok(cc), last);
       r.kn[cc] = NBW == 2 ? *reinterpret_cast<const uint32_t*>(knt + t * NB + b0) : (uint32_t)knt[t * NB + b0];
     }
-    const uint32_t t = min((uint32_t)lane, last);
-    const uint32_t* rp = reinterpret_cast<const uint32_t*>(vt8 + t * VREC + (uint32_t)(b0 * 4 * VB));
-    if constexpr (NBW * VB % 4 == 0) {  // 16-byte aligned whole quads
+    // V: in half hh, lane l holds token 32 hh + l % 32 and block b0 + l / 32 (head_dim 128: block b0,
+    // whose coordinates lanes l and l + 32 split)
+    const uint32_t vblk = (uint32_t)(b0 + (NBW == 2 ? (lane >> 5) : 0));
 #pragma unroll
-      for (int q = 0; q < NBW * VB / 4; ++q) {
-        const uint4 w = reinterpret_cast<const uint4*>(rp)[q];
-        r.vw[4 * q] = w.x;
-        r.vw[4 * q + 1] = w.y;
-        r.vw[4 * q + 2] = w.z;
-        r.vw[4 * q + 3] = w.w;
+    for (int hh = 0; hh < 2; ++hh) {
+      const uint32_t t = min((uint32_t)(32 * hh + (lane & 31)), last);
+      const uint8_t* rp = vt8 + t * VREC + vblk * (4 * VB);
+      if constexpr (VB == 4) {  // 16-byte records
+        const uint4 w = *reinterpret_cast<const uint4*>(rp);
+        r.vw[hh][0] = w.x;
+        r.vw[hh][1] = w.y;
+        r.vw[hh][2] = w.z;
+        r.vw[hh][3] = w.w;
+      } else {
+#pragma unroll
+        for (int q = 0; q < VB; ++q) r.vw[hh][q] = reinterpret_cast<const uint32_t*>(rp)[q];
       }
-    } else if constexpr (NBW * VB % 2 == 0) {  // 8-byte aligned pairs (24 B per token at 3 bits)
-#pragma unroll
-      for (int q = 0; q < NBW * VB / 2; ++q) {
-        const uint2 w = reinterpret_cast<const uint2*>(rp)[q];
-        r.vw[2 * q] = w.x;
-        r.vw[2 * q + 1] = w.y;
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < NBW * VB; ++q) r.vw[q] = rp[q];
+      r.vn[hh] = (uint32_t)vnt[t * NB + vblk];
     }
-    r.vn = NBW == 2 ? *reinterpret_cast<const uint32_t*>(vnt + t * NB + b0) : (uint32_t)vnt[t * NB + b0];
   };
 
   // the first tile's loads go out before the tables and the query are set up, hiding their latency
@@ -242,9 +245,9 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
     __syncthreads();
   }
 
-  // query operands of this lane, one masked copy per stacked subtile slot: row `row` of slot sv
-  // is head row % GP when row / GP == sv and zero otherwise
-  v8h qh8[NBW][S], ql8[NBW][S];
+  // query operands of this lane: row `row` of the A operand is head row % GP (every row live, so
+  // each subtile's product holds its scores in all 16 rows; a lane keeps the one of its own slot)
+  v8h qh8[NBW], ql8[NBW];
 #pragma unroll
   for (int bl = 0; bl < NBW; ++bl) {
     const int b = NBW * wave + bl;
@@ -252,13 +255,11 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
     for (int j = 0; j < 8; ++j) {
       const float v = qf[(row % GP) * HD + 32 * b + 8 * g + j] * 0.17677669529663688f;  // 1/sqrt(32)
       const _Float16 h = (_Float16)v, l = (_Float16)(v - (float)h);
-#pragma unroll
-      for (int sv = 0; sv < S; ++sv) {
-        qh8[bl][sv][j] = row / GP == sv ? h : (_Float16)0.0f;
-        ql8[bl][sv][j] = row / GP == sv ? l : (_Float16)0.0f;
-      }
+      qh8[bl][j] = h;
+      ql8[bl][j] = l;
     }
   }
+  const int slot = (4 * g) / GP;  // the subtile of a stack whose scores this lane's registers hold
   __syncthreads();  // query staging is overwritten by the V tiles below
 
   // last token each register's row may see: all tokens, or with a causal mask the row's query
@@ -283,32 +284,48 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   _Float16* vtile = vt[wave];
   _Float16* ptile = pt[wave];
   int parity = 0;
-  auto tile = [&](const Regs& cur, int64_t tb) {
-
-    // ---- value records of token `lane` -> V tile row `lane` (norm folded in, chunks swizzled)
+  // ---- value records of half hh -> V tile rows 0..31 (norm folded in, chunks swizzled): lane l
+  // expands its (token, block) record: a whole block (head_dim 256; chunks 2 (l / 32), +1) or half a
+  // block (head_dim 128; lanes l and l + 32 take coordinates 0..15 and 16..31, chunk l / 32)
+  auto write_v = [&](const Regs& cur, int hh) {
+    constexpr int NP = NBW == 2 ? 16 : 8;  // code pairs this lane expands
+    const int tl = lane & 31, up = lane >> 5;
+    uint32_t win[VB];  // this lane's codes from bit 0
+    if constexpr (NBW == 2) {
 #pragma unroll
-    for (int bl = 0; bl < NBW; ++bl) {
-      const _Float16 nv = __builtin_bit_cast(_Float16, (uint16_t)(cur.vn >> (16 * bl)));
-      const v2h nv2 = {nv, nv};
-      uint32_t o[16];
+      for (int k = 0; k < VB; ++k) win[k] = cur.vw[hh][k];
+    } else {
+      constexpr int WO = (16 * VB) / 32, SH = (16 * VB) % 32;  // codes 16.. start at word WO, bit SH
 #pragma unroll
-      for (int pp = 0; pp < 16; ++pp) {
-        const int pos = 2 * VB * pp, wi = pos >> 5, sh = pos & 31;
-        const uint32_t w = sh + 2 * VB <= 32 ? cur.vw[bl * VB + wi]
-                                             : __builtin_amdgcn_alignbit(cur.vw[bl * VB + wi + 1], cur.vw[bl * VB + wi], sh);
-        const int s2 = sh + 2 * VB <= 32 ? sh : 0;
-        const v2h c = __builtin_bit_cast(v2h, lut_word(vtab, w, s2, 2 * VB, LGCV, voff));
-        o[pp] = __builtin_bit_cast(uint32_t, c * nv2);
-      }
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int c = 2 * bl + half;
-        *reinterpret_cast<uint4*>(vtile + vslot(lane, c, 0)) =
-            make_uint4(o[8 * half], o[8 * half + 1], o[8 * half + 2], o[8 * half + 3]);
-        *reinterpret_cast<uint4*>(vtile + vslot(lane, c, 1)) =
-            make_uint4(o[8 * half + 4], o[8 * half + 5], o[8 * half + 6], o[8 * half + 7]);
+      for (int k = 0; k < VB; ++k) {
+        const uint32_t lo = k + WO < VB ? cur.vw[hh][k + WO] : 0u;
+        const uint32_t hi = k + WO + 1 < VB ? cur.vw[hh][k + WO + 1] : 0u;
+        const uint32_t sw = SH ? __builtin_amdgcn_alignbit(hi, lo, SH) : lo;
+        win[k] = up ? sw : cur.vw[hh][k];
       }
     }
+    const _Float16 nv = __builtin_bit_cast(_Float16, (uint16_t)cur.vn[hh]);
+    const v2h nv2 = {nv, nv};
+    uint32_t o[NP];
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp) {
+      const int pos = 2 * VB * pp, wi = pos >> 5, sh = pos & 31;
+      const uint32_t w = sh + 2 * VB <= 32 ? win[wi] : __builtin_amdgcn_alignbit(win[wi + 1], win[wi], sh);
+      const int s2 = sh + 2 * VB <= 32 ? sh : 0;
+      const v2h c = __builtin_bit_cast(v2h, lut_word(vtab, w, s2, 2 * VB, LGCV, voff));
+      o[pp] = __builtin_bit_cast(uint32_t, c * nv2);
+    }
+#pragma unroll
+    for (int ch = 0; ch < NP / 8; ++ch) {
+      const int c = NBW == 2 ? 2 * up + ch : up;
+      *reinterpret_cast<uint4*>(vtile + vslot(tl, c, 0)) = make_uint4(o[8 * ch], o[8 * ch + 1], o[8 * ch + 2], o[8 * ch + 3]);
+      *reinterpret_cast<uint4*>(vtile + vslot(tl, c, 1)) =
+          make_uint4(o[8 * ch + 4], o[8 * ch + 5], o[8 * ch + 6], o[8 * ch + 7]);
+    }
+  };
+
+  auto tile = [&](const Regs& cur, int64_t tb) {
+    write_v(cur, 0);
 
     // ---- key side: partial scores over the owned blocks
     float s[NC][4];
@@ -321,10 +338,11 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
     for (int bl = 0; bl < NBW; ++bl) {
 #pragma unroll
       for (int cc = 0; cc < NC; ++cc) {
-        v4f c = {0.0f, 0.0f, 0.0f, 0.0f};
+        v4f cs[S];
 #pragma unroll
         for (int sv = 0; sv < S; ++sv) {
           const int st = cc * S + sv;
+          cs[sv] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
           uint32_t bh[4], bo[4];
           if constexpr (K8) {
             // two one-code lookups per pair; byte permutes gather the two hi and the two lo halves
@@ -348,10 +366,16 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
           }
           const v8h bhi = __builtin_bit_cast(v8h, make_uint4(bh[0], bh[1], bh[2], bh[3]));
           const v8h blo = __builtin_bit_cast(v8h, make_uint4(bo[0], bo[1], bo[2], bo[3]));
-          const v8h ah = qh8[bl][sv], al = ql8[bl][sv];
-          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bhi, c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bhi, c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, blo, c, 0, 0, 0);
+          const v8h ah = qh8[bl], al = ql8[bl];
+          cs[sv] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bhi, cs[sv], 0, 0, 0);
+          cs[sv] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bhi, cs[sv], 0, 0, 0);
+          cs[sv] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, blo, cs[sv], 0, 0, 0);
+        }
+        v4f c = cs[0];
+#pragma unroll
+        for (int sv = 1; sv < S; ++sv) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) c[i] = slot == sv ? cs[sv][i] : c[i];
         }
         const float nk = __half2float(__ushort_as_half((uint16_t)(cur.kn[cc] >> (16 * bl))));
 #pragma unroll
@@ -362,15 +386,16 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
     // ---- sum the waves' partial scores
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc)
-      *reinterpret_cast<float4*>(&xs[parity][lane][(wave * NC + cc) * 4]) = make_float4(s[cc][0], s[cc][1], s[cc][2], s[cc][3]);
+      *reinterpret_cast<float4*>(&xs[parity % NXS][lane][(wave * NC + cc) * 4]) =
+          make_float4(s[cc][0], s[cc][1], s[cc][2], s[cc][3]);
     lds_barrier();
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) {
       const int64_t tok = tb + ktok(cc);
-      float4 v = *reinterpret_cast<const float4*>(&xs[parity][lane][cc * 4]);
+      float4 v = *reinterpret_cast<const float4*>(&xs[parity % NXS][lane][cc * 4]);
 #pragma unroll
       for (int w = 1; w < kWaves; ++w) {
-        const float4 u = *reinterpret_cast<const float4*>(&xs[parity][lane][(w * NC + cc) * 4]);
+        const float4 u = *reinterpret_cast<const float4*>(&xs[parity % NXS][lane][(w * NC + cc) * 4]);
         v.x += u.x;
         v.y += u.y;
         v.z += u.z;
@@ -388,6 +413,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
         s[cc][3] = tok <= lim[3] ? v.w * a.kscale : -INFINITY;
       }
     }
+    if constexpr (NXS == 1) lds_barrier();  // one exchange buffer: every wave has read it before the next tile's writes
 
     // ---- online softmax; register i of this lane belongs to head (4g + i) % GP.  The reference
     // m_run of a head only moves when some score of the tile exceeds it by more than kSlack (always
@@ -430,12 +456,18 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
     }
     wave_sync();
 
-    // ---- value side: acc[head][coordinate] += p[head][token] * (nV c)[token][coordinate]
+    // ---- value side: acc[head][coordinate] += p[head][token] * (nV c)[token][coordinate], one 32-token
+    // half of the tile at a time (the V tile holds one half; the second is expanded once the first is read)
 #pragma unroll
-    for (int half = 0; half < kTile / 32; ++half) {
+    for (int half = 0; half < kTile / VT; ++half) {
+      if (half > 0) {
+        wave_sync();  // the previous half's transposing reads are issued before its rows are overwritten
+        write_v(cur, half);
+        wave_sync();
+      }
       const v8h z = {0, 0, 0, 0, 0, 0, 0, 0};
-      const v8h av = row < grows ? *reinterpret_cast<const v8h*>(ptile + (row % GP) * kTile + 32 * half + 8 * g) : z;
-      const int t1 = 32 * half + 8 * g + (row >> 2), t2 = t1 + 4;
+      const v8h av = row < grows ? *reinterpret_cast<const v8h*>(ptile + (row % GP) * kTile + VT * half + 8 * g) : z;
+      const int t1 = 8 * g + (row >> 2), t2 = t1 + 4;
 #pragma unroll
       for (int bl = 0; bl < NBW; ++bl) {
 #pragma unroll
@@ -579,15 +611,20 @@ hipError_t launch_bits(const AttnArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// Token range per workgroup: a multiple of the 64-token tile that spreads the
-// cache over about 512 workgroups (two per compute unit; 256 for the 8-wave
-// prefill workgroups, one per compute unit), 64 .. 8192 tokens; `columns` = KV
-// heads x row groups, the workgroup columns that each walk it.
-int64_t attn_tokens_per_wg(int64_t columns, int64_t n_tokens, bool prefill) {
-  const int64_t target = prefill ? 256 : 512;
+// Token range per workgroup: a multiple of two 64-token tiles (the decode kernel walks its tiles in
+// pairs) that spreads the cache over about 512 workgroups (two per compute unit; 256 for the 8-wave
+// prefill workgroups, one per compute unit), 128 .. 8192 tokens; `columns` = KV heads x row groups,
+// the workgroup columns that each walk it, `grp` = rows per group.  (Groups of up to 4 rows fit three
+// workgroups per compute unit, but spreading them over 768 measured slower: 62 against 60 us for the
+// 131072-token decode.)
+#ifndef TQ_ATTN_WG_TARGET4
+#define TQ_ATTN_WG_TARGET4 512
+#endif
+int64_t attn_tokens_per_wg(int64_t columns, int64_t n_tokens, int64_t grp) {
+  const int64_t target = grp > 16 ? 256 : grp <= 4 ? TQ_ATTN_WG_TARGET4 : 512;
   int64_t per = (n_tokens * columns + target - 1) / target;
-  per = (per + kTile - 1) / kTile * kTile;
-  if (per < kTile) per = kTile;
+  per = (per + 2 * kTile - 1) / (2 * kTile) * (2 * kTile);
+  if (per < 2 * kTile) per = 2 * kTile;
   if (per > 8192) per = 8192;
   return per;
 }

@@ -664,7 +664,7 @@ AttnShape attn_shape(int n_q_heads, int n_kv_heads, int64_t n_q, int64_t n_token
   const bool prefill = sh.rows > 16;
   sh.grp = prefill ? tq::attn_prefill_rows() : sh.rows;
   sh.n_rg = (sh.rows + sh.grp - 1) / sh.grp;
-  sh.per_wg = tq::attn_tokens_per_wg((int64_t)n_kv_heads * sh.n_rg, n_tokens, prefill);
+  sh.per_wg = tq::attn_tokens_per_wg((int64_t)n_kv_heads * sh.n_rg, n_tokens, sh.grp);
   sh.wgs = (n_tokens + sh.per_wg - 1) / sh.per_wg;
   return sh;
 }

@@ -161,7 +161,7 @@ hipError_t launch_decode_attn(int kbits, int vbits, const AttnArgs& a, hipStream
 constexpr size_t kAttnScratchBytes = (size_t)16 << 20;
 constexpr int kMaxDevices = 64;
 hipError_t attn_scratch(void** ptr);
-int64_t attn_tokens_per_wg(int64_t columns, int64_t n_tokens, bool prefill);
+int64_t attn_tokens_per_wg(int64_t columns, int64_t n_tokens, int64_t grp);
 int attn_prefill_rows();  // rows per workgroup of the many-row (prefill) attention kernel
 hipError_t launch_prefill(int kbits, int vbits, const AttnArgs& a, hipStream_t s);  // its main kernel (no merge)
 
