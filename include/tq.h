@@ -215,8 +215,8 @@ tq_status tq_dequantize(const tq_config* cfg, const uint8_t* codes, const void* 
  * is rejected).  Supported: 1..3-bit MSE stage, head_dim <= 128, qjl_m <= 128
  * (TQ_ERR_UNSUPPORTED otherwise), at most 2^31 queries and keys per call.
  * ws: 256-byte aligned device workspace of
- * tq_workspace_size(TQ_OP_QJL_SCORES, cfg, n_q, n_k, 0) bytes (int8 operand
- * planes of the queries and keys; contents are scratch).
+ * tq_workspace_size(TQ_OP_QJL_SCORES, cfg, n_q, n_k, 0) bytes (the queries'
+ * int8 operand records and scales; contents are scratch).
  */
 tq_status tq_qjl_scores(const tq_config* cfg, const void* q, tq_dtype q_dtype, int64_t n_q, int64_t ld_q,
                         const uint8_t* codes, const void* norms, const uint8_t* qjl_bits, const void* qjl_rnorm,

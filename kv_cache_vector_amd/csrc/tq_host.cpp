@@ -594,8 +594,8 @@ tq_status tq_dequantize(const tq_config* cfg, const uint8_t* codes, const void* 
 namespace {
 
 struct ScoreLayout {
-  int64_t n_q_pad, n_k_pad, rq, rk, planes;
-  size_t off_qrec, off_qscale, off_krec, off_kscale, total;
+  int64_t n_q_pad, n_k_pad, rq, planes;
+  size_t off_qrec, off_qscale, total;
 };
 
 size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -609,12 +609,9 @@ ScoreLayout score_layout(const tq_config& cfg, int64_t n_q, int64_t n_k) {
   L.n_q_pad = (n_q + qb - 1) / qb * qb;
   L.n_k_pad = (n_k + tile - 1) / tile * tile;
   L.rq = 2 * (L.planes * kd + km);
-  L.rk = L.planes * kd + km;
   L.off_qrec = 0;
   L.off_qscale = round256(L.off_qrec + (size_t)(L.n_q_pad * L.rq));
-  L.off_krec = round256(L.off_qscale + (size_t)L.n_q_pad * 2 * sizeof(float));
-  L.off_kscale = round256(L.off_krec + (size_t)(L.n_k_pad * L.rk));
-  L.total = round256(L.off_kscale + (size_t)L.n_k_pad * 2 * sizeof(float));
+  L.total = round256(L.off_qscale + (size_t)L.n_q_pad * 2 * sizeof(float));
   return L;
 }
 
@@ -781,8 +778,6 @@ tq_status tq_qjl_scores(const tq_config* cfg, const void* q, tq_dtype q_dtype, i
   char* w = (char*)ws;
   a.qrec = (int8_t*)(w + L.off_qrec);
   a.qscale = (float*)(w + L.off_qscale);
-  a.krec = (int8_t*)(w + L.off_krec);
-  a.kscale = (float*)(w + L.off_kscale);
   a.s_rot32 = (const float*)((const char*)cfg->qjl_params + (size_t)cfg->qjl_m * cfg->dt * sizeof(double));
   fill_dbits(*cfg, a.dbits);
   // ternary plane weights: level(mag) = sum over the bit subsets t of mag of w_t (Moebius inversion)

@@ -93,8 +93,6 @@ struct ScoreArgs {
   int8_t* qrec;              // [n_q_pad / 32] blocks of 32 queries x 2*(planes*kd+km) int8 limbs (per plane
                              // w_t qhat hi, lo; then p hi, lo), each block laid out as 1 KiB MFMA fragments
   float* qscale;             // [n_q_pad][2]: fixed-point scale of qhat / sqrt(dt), of p * sqrt(pi/2)/m
-  int8_t* krec;              // [n_k_pad][planes*kd + km]: ternary planes, then the +-1 sign plane
-  float* kscale;             // [2][n_k_pad]: n_j, then n_j * rho_j
   const float* s_rot32;      // S~ [m][dt] float32
   uint32_t dbits[8];
   float plane_w[8];          // weight of each ternary plane (N(0,1) scale)

@@ -21,9 +21,9 @@
 //
 // Kernels: prep_queries (one workgroup per 16 queries: rotation in registers,
 // S~ projection on fp32 MFMA, fixed-point limbs written as MFMA operand
-// fragments), prep_keys (one lane per 16-byte piece of a key's operand
-// record), scores (each wave keeps the operand planes of 32*CB keys in
-// registers and streams 32-query blocks through an LDS ring).
+// fragments), scores (each wave builds the operand planes of 32*CB keys in
+// registers from their codes and sign bits, keeps them, and streams 32-query
+// blocks through an LDS ring shared by the workgroup's waves).
 #include <hip/hip_fp16.h>
 
 #include "tq_device.h"
@@ -38,9 +38,18 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kQB = 32;         // queries per block (the MFMA's N)
 #ifndef TQ_QCHUNK
-#define TQ_QCHUNK 512
+#define TQ_QCHUNK 1024
 #endif
 constexpr int kQChunk = TQ_QCHUNK;  // queries per scores workgroup
+#ifndef TQ_SCORES_WAVES
+#define TQ_SCORES_WAVES 8
+#endif
+#ifndef TQ_SCORES_CB2
+#define TQ_SCORES_CB2 1
+#endif
+constexpr int kSW = TQ_SCORES_WAVES;  // waves per scores workgroup, each with its own keys
+// 32-key tiles held by one scores wave: TQ_SCORES_CB2 for 1- and 2-plane keys, one for 4 planes
+constexpr int scores_cb(int np) { return np <= 2 ? TQ_SCORES_CB2 : 1; }
 constexpr float kFixed = 32000.0f;
 
 // Byte offset of element idx (of a Kd- or Km-long int8 vector) of query r inside its block's
@@ -184,67 +193,27 @@ __global__ __launch_bounds__(256) void prep_queries(ScoreArgs a) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// key preparation: one lane per 16-byte piece of a key's record (NP ternary
-// planes of Kd bytes, then Km bytes of the +-1 sign plane)
-// ---------------------------------------------------------------------------
-template <int BITS, bool NORM_F32, int KD, int KM>
-__global__ __launch_bounds__(256) void prep_keys(ScoreArgs a) {
-  constexpr int NP = 1 << (BITS - 1);
-  constexpr int Kd = 64 * KD, Km = 64 * KM;
-  constexpr int pieces = (NP * Kd + Km) / 16;
-  const int dt = a.dt, m = a.m;
-  // keys of this workgroup: 256 / pieces (rounded down) whole records per 256 lanes
-  constexpr int KPW = 256 / pieces;
-  const int c = threadIdx.x % pieces, kl = threadIdx.x / pieces;
-  if (kl >= KPW) return;
-  const int64_t j = (int64_t)blockIdx.x * KPW + kl;
-  if (j >= a.n_k_pad) return;
-  const bool live = j < a.n_k;
-  u32x4 out = {0u, 0u, 0u, 0u};
-  if (c < NP * Kd / 16) {
-    const int t = c / (Kd / 16), d0 = (c % (Kd / 16)) * 16;
-    if (live && d0 < dt) {
-      // the key's codes form one little-endian bitstream of dt * BITS bits; take bits BITS*d0 .. +16*BITS
-      const uint32_t* wp = reinterpret_cast<const uint32_t*>(a.codes + j * (dt * BITS / 8));
-      const int pos = BITS * d0, w0 = pos >> 5;
-      const int last = (pos + 16 * BITS - 1) >> 5;
-      uint64_t bits = wp[w0];
-      if (last > w0) bits |= (uint64_t)wp[w0 + 1] << 32;
-      bits >>= (pos & 31);
-      uint32_t b[4] = {0u, 0u, 0u, 0u};
+// Ternary plane t of 16 consecutive codes (the low 16 * BITS bits of `bits`): byte i is +1 or -1 (the
+// code's sign) where the code's magnitude contains the bits of t, else 0.
+template <int BITS>
+__device__ __forceinline__ v4i ternary_piece(uint64_t bits, int t) {
+  uint32_t b[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t code = (uint32_t)(bits >> (BITS * i)) & ((1u << BITS) - 1);
-        const uint32_t mag = code & ((1u << (BITS - 1)) - 1);
-        const uint32_t v = ((mag & (uint32_t)t) == (uint32_t)t) ? ((code >> (BITS - 1)) ? 0xFFu : 0x01u) : 0u;
-        b[i >> 2] |= v << (8 * (i & 3));
-      }
-      out = u32x4{b[0], b[1], b[2], b[3]};
-    }
-  } else {
-    const int p0 = (c - NP * Kd / 16) * 16;
-    if (live && p0 < m) {
-      const uint32_t sb = reinterpret_cast<const uint16_t*>(a.qjl_bits + j * (m / 8))[p0 >> 4];
-      uint32_t b[4] = {0u, 0u, 0u, 0u};
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t code = (uint32_t)(bits >> (BITS * i)) & ((1u << BITS) - 1);
+    const uint32_t mag = code & ((1u << (BITS - 1)) - 1);
+    const uint32_t v = ((mag & (uint32_t)t) == (uint32_t)t) ? ((code >> (BITS - 1)) ? 0xFFu : 0x01u) : 0u;
+    b[i >> 2] |= v << (8 * (i & 3));
+  }
+  return v4i{(int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+}
+
+// The +-1 sign plane of 16 projections (bit set: +1).
+__device__ __forceinline__ v4i sign_piece(uint32_t sb) {
+  uint32_t b[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) b[i >> 2] |= (((sb >> i) & 1u) ? 0x01u : 0xFFu) << (8 * (i & 3));  // bit set: +1
-      out = u32x4{b[0], b[1], b[2], b[3]};
-    }
-  }
-  reinterpret_cast<u32x4*>(a.krec + j * (NP * Kd + Km))[c] = out;
-  if (c == 0) {
-    float n = 0.0f, rho = 0.0f;
-    if (live) {
-      if constexpr (NORM_F32)
-        n = static_cast<const float*>(a.norms)[j];
-      else
-        n = __half2float(static_cast<const __half*>(a.norms)[j]);
-      rho = __half2float(__ushort_as_half(a.rnorm[j]));
-    }
-    a.kscale[j] = n;
-    a.kscale[a.n_k_pad + j] = n * rho;
-  }
+  for (int i = 0; i < 16; ++i) b[i >> 2] |= (((sb >> i) & 1u) ? 0x01u : 0xFFu) << (8 * (i & 3));
+  return v4i{(int)b[0], (int)b[1], (int)b[2], (int)b[3]};
 }
 
 // ---------------------------------------------------------------------------
@@ -265,18 +234,18 @@ template <int NP, int KD, int KM, int CB>
 struct ScoresLds {
   static constexpr int RQ = 2 * (NP * 32 * KD + 32 * KM);  // bytes per query record
   static constexpr int KIB = kQB * RQ / 1024;               // 1 KiB copies per block
-  static_assert(KIB % 4 == 0, "every wave copies the same number of 1 KiB pieces");
-  static constexpr int KEYS = 128 * CB;                     // keys per workgroup
+  static constexpr int KPW = (KIB + kSW - 1) / kSW;         // 1 KiB copies per wave and block
+  static constexpr int KEYS = 32 * CB * kSW;                // keys per workgroup
   static constexpr int QS = 3 * kQB * RQ;
   static constexpr int KSN = QS + 3 * kQB * 2 * 4;
   static constexpr int TOTAL = KSN + 2 * KEYS * 4;
   static_assert(TOTAL <= 160 * 1024, "fits the LDS of one compute unit");
 };
 
-template <int NP, int KD, int KM, int CB>
-__global__ __launch_bounds__(256) void scores_kernel(ScoreArgs a) {
+template <int NP, int KD, int KM, int CB, bool NORM_F32>
+__global__ __launch_bounds__(64 * kSW, kSW == 8 ? 2 : 1) void scores_kernel(ScoreArgs a) {
   using LY = ScoresLds<NP, KD, KM, CB>;
-  constexpr int Kd = 32 * KD, Km = 32 * KM, RQ = LY::RQ, RK = NP * Kd + Km;
+  constexpr int RQ = LY::RQ;
   constexpr int KIB = LY::KIB;
   constexpr int KEYS = LY::KEYS;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -289,32 +258,67 @@ __global__ __launch_bounds__(256) void scores_kernel(ScoreArgs a) {
   const int64_t wg_key0 = (int64_t)blockIdx.x * KEYS;
   const int64_t key0 = wg_key0 + wave * (32 * CB);
 
-  // this wave's key-side operands (row col of each 32-key tile), kept in registers
+  // this wave's key-side operands (row col of each 32-key tile), built in registers from the codes and
+  // sign bits and kept for the whole query loop: lane (col, half) holds coordinates (projections)
+  // 32 ks + 16 half .. + 15 of its key, as NP ternary planes and the sign plane
+  constexpr int BITS = NP == 1 ? 1 : NP == 2 ? 2 : 3;
+  const int dt = a.dt, m = a.m;
   v4i bT[CB][NP][KD], bS[CB][KM];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
-    const int8_t* rec = a.krec + (key0 + 32 * cb + col) * RK + 16 * half;
+    const int64_t j = key0 + 32 * cb + col;
+    const bool live = j < a.n_k;
 #pragma unroll
-    for (int t = 0; t < NP; ++t)
+    for (int ks = 0; ks < KD; ++ks) {
+      const int d0 = 32 * ks + 16 * half;
+      uint64_t bits = 0;
+      const bool on = live && d0 < dt;
+      if (on) {  // the key's codes are one little-endian bitstream of dt * BITS bits
+        const uint32_t* wp = reinterpret_cast<const uint32_t*>(a.codes + j * (dt * BITS / 8));
+        const int pos = BITS * d0, w0 = pos >> 5;
+        bits = wp[w0];
+        if (((pos + 16 * BITS - 1) >> 5) > w0) bits |= (uint64_t)wp[w0 + 1] << 32;
+        bits >>= (pos & 31);
+      }
 #pragma unroll
-      for (int ks = 0; ks < KD; ++ks) bT[cb][t][ks] = *reinterpret_cast<const v4i*>(rec + t * Kd + 32 * ks);
+      for (int t = 0; t < NP; ++t) bT[cb][t][ks] = on ? ternary_piece<BITS>(bits, t) : v4i{0, 0, 0, 0};
+    }
 #pragma unroll
-    for (int ks = 0; ks < KM; ++ks) bS[cb][ks] = *reinterpret_cast<const v4i*>(rec + NP * Kd + 32 * ks);
+    for (int ks = 0; ks < KM; ++ks) {
+      const int p0 = 32 * ks + 16 * half;
+      const bool on = live && p0 < m;
+      const uint32_t sb = on ? reinterpret_cast<const uint16_t*>(a.qjl_bits + j * (m / 8))[p0 >> 4] : 0u;
+      bS[cb][ks] = on ? sign_piece(sb) : v4i{0, 0, 0, 0};
+    }
   }
-  for (int e = tid; e < KEYS; e += 256) {
-    ks_n[e] = a.kscale[wg_key0 + e];
-    ks_nr[e] = a.kscale[a.n_k_pad + wg_key0 + e];
+  for (int e = tid; e < KEYS; e += 64 * kSW) {  // key scales n_j and n_j rho_j (0 past the last key)
+    const int64_t j = wg_key0 + e;
+    float n = 0.0f, rho = 0.0f;
+    if (j < a.n_k) {
+      if constexpr (NORM_F32)
+        n = static_cast<const float*>(a.norms)[j];
+      else
+        n = __half2float(static_cast<const __half*>(a.norms)[j]);
+      rho = __half2float(__ushort_as_half(a.rnorm[j]));
+    }
+    ks_n[e] = n;
+    ks_nr[e] = n * rho;
   }
   // 16-byte stores need 16-byte aligned rows
   const bool vec = ((a.ld_s & 3) == 0) && ((reinterpret_cast<uintptr_t>(a.scores) & 15) == 0);
 
   const int64_t q_begin = (int64_t)blockIdx.y * kQChunk;
   const int64_t q_end = q_begin + kQChunk < a.n_q_pad ? q_begin + kQChunk : a.n_q_pad;
-  // copy the records (KIB pieces of 1 KiB, KIB / 4 per wave) and scales (wave 0) of block r0 into buffer buf
+  // copy the records (KIB pieces of 1 KiB) and scales (wave 0) of block r0 into buffer buf; every wave
+  // issues KPW copies (past the last piece a wave copies the last one again: the same bytes to the same
+  // place), so the vmcnt bookkeeping below is the same for all waves
   auto fetch = [&](int64_t r0, int buf) {
     const char* src = reinterpret_cast<const char*>(a.qrec) + r0 * RQ;
 #pragma unroll
-    for (int k = wave; k < KIB; k += 4) lds_copy<16>(src + 1024 * k + 16 * lane, qblk[buf] + 1024 * k);
+    for (int i = 0; i < LY::KPW; ++i) {
+      const int k = wave + kSW * i < KIB ? wave + kSW * i : KIB - 1;
+      lds_copy<16>(src + 1024 * k + 16 * lane, qblk[buf] + 1024 * k);
+    }
     if (wave == 0) lds_copy<4>(a.qscale + r0 * 2 + lane, qs[buf]);
   };
   // blocks b and b + 1 are resident when block b starts; block b + 2 is copied during it
@@ -394,9 +398,9 @@ __global__ __launch_bounds__(256) void scores_kernel(ScoreArgs a) {
       if (!ahead)
         wait_vm<8 * CB>();
       else if (wave == 0)
-        wait_vm<8 * CB + KIB / 4 + 1>();
+        wait_vm<8 * CB + LY::KPW + 1>();
       else
-        wait_vm<8 * CB + KIB / 4>();
+        wait_vm<8 * CB + LY::KPW>();
     } else {
       wait_vm<0>();  // also completes the copy of block b + 1, whatever follows
     }
@@ -405,59 +409,45 @@ __global__ __launch_bounds__(256) void scores_kernel(ScoreArgs a) {
   wait_vm<0>();
 }
 
-#ifndef TQ_SCORES_CB2
-#define TQ_SCORES_CB2 2
-#endif
-template <int NP, int KD, int KM>
+template <int NP, int KD, int KM, bool NORM_F32>
 hipError_t launch_scores_t(const ScoreArgs& a, hipStream_t s) {
-  constexpr int CB = NP <= 2 ? TQ_SCORES_CB2 : 1;
+  constexpr int CB = scores_cb(NP);
   constexpr int lds = ScoresLds<NP, KD, KM, CB>::TOTAL;
   // more than the default 64 KiB of dynamic LDS for the larger records; setting it twice from
   // racing first calls is harmless
   static std::atomic<bool> ready{false};
   if (!ready.load(std::memory_order_acquire)) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scores_kernel<NP, KD, KM, CB>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scores_kernel<NP, KD, KM, CB, NORM_F32>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     ready.store(true, std::memory_order_release);
   }
-  dim3 grid((unsigned)(a.n_k_pad / (128 * CB)), (unsigned)((a.n_q_pad + kQChunk - 1) / kQChunk));
-  hipLaunchKernelGGL((scores_kernel<NP, KD, KM, CB>), grid, dim3(256), lds, s, a);
+  dim3 grid((unsigned)(a.n_k_pad / (32 * CB * kSW)), (unsigned)((a.n_q_pad + kQChunk - 1) / kQChunk));
+  hipLaunchKernelGGL((scores_kernel<NP, KD, KM, CB, NORM_F32>), grid, dim3(64 * kSW), lds, s, a);
   return hipGetLastError();
 }
 
-template <int NP>
+template <int NP, bool NORM_F32>
 hipError_t launch_scores_np(const ScoreArgs& a, hipStream_t s) {
   const int kd = a.kd / 64, km = a.km / 64;
-  if (kd == 1 && km == 1) return launch_scores_t<NP, 2, 2>(a, s);
-  if (kd == 1 && km == 2) return launch_scores_t<NP, 2, 4>(a, s);
-  if (kd == 2 && km == 1) return launch_scores_t<NP, 4, 2>(a, s);
-  return launch_scores_t<NP, 4, 4>(a, s);
+  if (kd == 1 && km == 1) return launch_scores_t<NP, 2, 2, NORM_F32>(a, s);
+  if (kd == 1 && km == 2) return launch_scores_t<NP, 2, 4, NORM_F32>(a, s);
+  if (kd == 2 && km == 1) return launch_scores_t<NP, 4, 2, NORM_F32>(a, s);
+  return launch_scores_t<NP, 4, 4, NORM_F32>(a, s);
 }
 
-template <int BITS, int KD, int KM>
-void launch_prep_keys_t(const tq_config& cfg, const ScoreArgs& a, hipStream_t s) {
-  constexpr int NP = 1 << (BITS - 1);
-  constexpr int KPW = 256 / ((NP * 64 * KD + 64 * KM) / 16);
-  dim3 grid((unsigned)((a.n_k_pad + KPW - 1) / KPW));
-  if (cfg.norm_dtype == TQ_F32)
-    hipLaunchKernelGGL((prep_keys<BITS, true, KD, KM>), grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((prep_keys<BITS, false, KD, KM>), grid, dim3(256), 0, s, a);
-}
-
-template <int BITS>
-void launch_prep_keys(const tq_config& cfg, const ScoreArgs& a, hipStream_t s) {
-  const int kd = a.kd / 64, km = a.km / 64;
-  if (kd == 1 && km == 1) launch_prep_keys_t<BITS, 1, 1>(cfg, a, s);
-  else if (kd == 1 && km == 2) launch_prep_keys_t<BITS, 1, 2>(cfg, a, s);
-  else if (kd == 2 && km == 1) launch_prep_keys_t<BITS, 2, 1>(cfg, a, s);
-  else launch_prep_keys_t<BITS, 2, 2>(cfg, a, s);
+template <bool NORM_F32>
+hipError_t launch_scores_norm(const tq_config& cfg, const ScoreArgs& a, hipStream_t s) {
+  switch (cfg.bits) {
+    case 1: return launch_scores_np<1, NORM_F32>(a, s);
+    case 2: return launch_scores_np<2, NORM_F32>(a, s);
+    default: return launch_scores_np<4, NORM_F32>(a, s);
+  }
 }
 
 }  // namespace
 
-int64_t scores_key_tile(int bits) { return bits <= 2 ? 256 : 128; }
+int64_t scores_key_tile(int bits) { return 32 * scores_cb(1 << (bits - 1)) * kSW; }
 int64_t scores_query_block() { return kQB; }
 
 hipError_t launch_qjl_scores(const tq_config& cfg, const ScoreArgs& a, hipStream_t s) {
@@ -474,18 +464,7 @@ hipError_t launch_qjl_scores(const tq_config& cfg, const ScoreArgs& a, hipStream
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  switch (cfg.bits) {
-    case 1: launch_prep_keys<1>(cfg, a, s); break;
-    case 2: launch_prep_keys<2>(cfg, a, s); break;
-    default: launch_prep_keys<3>(cfg, a, s); break;
-  }
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  switch (cfg.bits) {
-    case 1: return launch_scores_np<1>(a, s);
-    case 2: return launch_scores_np<2>(a, s);
-    default: return launch_scores_np<4>(a, s);
-  }
+  return cfg.norm_dtype == TQ_F32 ? launch_scores_norm<true>(cfg, a, s) : launch_scores_norm<false>(cfg, a, s);
 }
 
 }  // namespace tq
