@@ -82,12 +82,13 @@ struct QjlDecodeArgs {
 struct ScoreArgs {
   const void* q;
   int64_t ld_q;
-  int64_t n_q, n_q_pad;      // queries, padded to a multiple of 16
+  int64_t n_q, n_q_pad;      // queries, padded to a multiple of 32
   const uint8_t* codes;
   const void* norms;
   const uint8_t* qjl_bits;
   const uint16_t* rnorm;
   int64_t n_k, n_k_pad;      // keys, padded to the scores key tile
+  int64_t q_chunk;           // queries per scores workgroup (a multiple of 32; set by the launcher)
   float* scores;
   int64_t ld_s;
   int8_t* qrec;              // [n_q_pad / 32] blocks of 32 queries x 2*(planes*kd+km) int8 limbs (per plane

@@ -36,11 +36,12 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kQB = 32;         // queries per block (the MFMA's N)
-#ifndef TQ_QCHUNK
-#define TQ_QCHUNK 1024
+constexpr int kQB = 32;         // queries per block (the MFMA's M)
+#ifndef TQ_SCORES_WG_PER_CU
+#define TQ_SCORES_WG_PER_CU 2
 #endif
-constexpr int kQChunk = TQ_QCHUNK;  // queries per scores workgroup
+// the queries are cut into as few chunks (one workgroup row each) as give this many workgroups per compute unit
+constexpr int kScoresWgPerCu = TQ_SCORES_WG_PER_CU;
 #ifndef TQ_SCORES_WAVES
 #define TQ_SCORES_WAVES 8
 #endif
@@ -51,6 +52,7 @@ constexpr int kSW = TQ_SCORES_WAVES;  // waves per scores workgroup, each with i
 // 32-key tiles held by one scores wave: TQ_SCORES_CB2 for 1- and 2-plane keys, one for 4 planes
 constexpr int scores_cb(int np) { return np <= 2 ? TQ_SCORES_CB2 : 1; }
 constexpr float kFixed = 32000.0f;
+constexpr int kStoreNT = 2;  // cache-policy operand of the buffer stores: nontemporal (streaming)
 
 // Byte offset of element idx (of a Kd- or Km-long int8 vector) of query r inside its block's
 // fragment f0 + idx / 32: fragment = 1 KiB, lane 32 h + r holds bytes 16 h .. 16 h + 15 of the
@@ -217,11 +219,14 @@ __device__ __forceinline__ v4i sign_piece(uint32_t sb) {
 }
 
 // ---------------------------------------------------------------------------
-// scores: workgroup = 4 waves x (32*CB keys each), loops over 32-query blocks
+// scores: workgroup = kSW waves x (32*CB keys each), loops over 32-query blocks
 //
-// Keys are the MFMA's A operand (rows) and queries its B operand (columns):
-// lane l's accumulator holds, for query l % 32, the keys 8 g + 4 (l / 32) + i
-// (i = 0..3) of each group g, so one 16-byte store writes four scores.
+// Queries are the MFMA's A operand (rows) and keys its B operand (columns):
+// lane l's accumulator holds, for key l % 32 of each tile, the queries
+// 8 g + 4 (l / 32) + i (i = 0..3) of each group g.  So the key scales are two
+// registers per tile, and one 4-byte store per accumulator writes a whole
+// 128-byte row piece per 32 lanes: each store instruction fills two cache
+// lines, where the transposed layout would touch 32 lines with 32 bytes each.
 // Query records are copied straight into a ring of three LDS buffers
 // (global_load_lds) two blocks ahead.  vmcnt counts stores and copies
 // together, in issue order, so the wait that makes block b + 1 resident
@@ -229,7 +234,7 @@ __device__ __forceinline__ v4i sign_piece(uint32_t sb) {
 // younger than two blocks, and the write stream stays deep enough to keep
 // HBM busy.
 // ---------------------------------------------------------------------------
-// Dynamic LDS of one scores workgroup: a ring of three query blocks, their scales, the key scales.
+// Dynamic LDS of one scores workgroup: a ring of three query blocks and their scales.
 template <int NP, int KD, int KM, int CB>
 struct ScoresLds {
   static constexpr int RQ = 2 * (NP * 32 * KD + 32 * KM);  // bytes per query record
@@ -237,9 +242,10 @@ struct ScoresLds {
   static constexpr int KPW = (KIB + kSW - 1) / kSW;         // 1 KiB copies per wave and block
   static constexpr int KEYS = 32 * CB * kSW;                // keys per workgroup
   static constexpr int QS = 3 * kQB * RQ;
-  static constexpr int KSN = QS + 3 * kQB * 2 * 4;
-  static constexpr int TOTAL = KSN + 2 * KEYS * 4;
+  static constexpr int TOTAL = QS + 3 * kQB * 2 * 4;
   static_assert(TOTAL <= 160 * 1024, "fits the LDS of one compute unit");
+  // vmcnt (6 bits) must hold two blocks of stores plus one block of copies
+  static_assert(2 * 16 * CB + KPW + 1 <= 63, "outstanding memory operations fit vmcnt");
 };
 
 template <int NP, int KD, int KM, int CB, bool NORM_F32>
@@ -251,14 +257,12 @@ __global__ __launch_bounds__(64 * kSW, kSW == 8 ? 2 : 1) void scores_kernel(Scor
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   int8_t (*qblk)[kQB * RQ] = reinterpret_cast<int8_t (*)[kQB * RQ]>(smem);
   float (*qs)[kQB * 2] = reinterpret_cast<float (*)[kQB * 2]>(smem + LY::QS);
-  float* ks_n = reinterpret_cast<float*>(smem + LY::KSN);
-  float* ks_nr = ks_n + KEYS;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
   const int64_t wg_key0 = (int64_t)blockIdx.x * KEYS;
   const int64_t key0 = wg_key0 + wave * (32 * CB);
 
-  // this wave's key-side operands (row col of each 32-key tile), built in registers from the codes and
+  // this wave's key-side operands (column col of each 32-key tile), built in registers from the codes and
   // sign bits and kept for the whole query loop: lane (col, half) holds coordinates (projections)
   // 32 ks + 16 half .. + 15 of its key, as NP ternary planes and the sign plane
   constexpr int BITS = NP == 1 ? 1 : NP == 2 ? 2 : 3;
@@ -291,8 +295,11 @@ __global__ __launch_bounds__(64 * kSW, kSW == 8 ? 2 : 1) void scores_kernel(Scor
       bS[cb][ks] = on ? sign_piece(sb) : v4i{0, 0, 0, 0};
     }
   }
-  for (int e = tid; e < KEYS; e += 64 * kSW) {  // key scales n_j and n_j rho_j (0 past the last key)
-    const int64_t j = wg_key0 + e;
+  // key scales n_j and n_j rho_j of this lane's key in each tile (0 past the last key)
+  float kn[CB], knr[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const int64_t j = key0 + 32 * cb + col;
     float n = 0.0f, rho = 0.0f;
     if (j < a.n_k) {
       if constexpr (NORM_F32)
@@ -301,14 +308,18 @@ __global__ __launch_bounds__(64 * kSW, kSW == 8 ? 2 : 1) void scores_kernel(Scor
         n = __half2float(static_cast<const __half*>(a.norms)[j]);
       rho = __half2float(__ushort_as_half(a.rnorm[j]));
     }
-    ks_n[e] = n;
-    ks_nr[e] = n * rho;
+    kn[cb] = n;
+    knr[cb] = n * rho;
   }
-  // 16-byte stores need 16-byte aligned rows
-  const bool vec = ((a.ld_s & 3) == 0) && ((reinterpret_cast<uintptr_t>(a.scores) & 15) == 0);
 
-  const int64_t q_begin = (int64_t)blockIdx.y * kQChunk;
-  const int64_t q_end = q_begin + kQChunk < a.n_q_pad ? q_begin + kQChunk : a.n_q_pad;
+  // byte offsets from a 32-query block's first score: this lane's (4 rows further for half 1) and one row's;
+  // 32 bits hold every offset within a block when rows are shorter than 2^24 floats
+  const bool narrow = a.ld_s < (int64_t(1) << 24);
+  const int lane_boff = (int)(4 * half * a.ld_s + col) * 4;
+  const int row_bytes = (int)a.ld_s * 4;
+
+  const int64_t q_begin = (int64_t)blockIdx.y * a.q_chunk;
+  const int64_t q_end = q_begin + a.q_chunk < a.n_q_pad ? q_begin + a.q_chunk : a.n_q_pad;
   // copy the records (KIB pieces of 1 KiB) and scales (wave 0) of block r0 into buffer buf; every wave
   // issues KPW copies (past the last piece a wave copies the last one again: the same bytes to the same
   // place), so the vmcnt bookkeeping below is the same for all waves
@@ -325,7 +336,7 @@ __global__ __launch_bounds__(64 * kSW, kSW == 8 ? 2 : 1) void scores_kernel(Scor
   fetch(q_begin, 0);
   if (q_begin + kQB < q_end) fetch(q_begin + kQB, 1);
   wait_vm<0>();
-  __syncthreads();  // also publishes the key scales
+  __syncthreads();
 
   int cur = 0;
   for (int64_t r0 = q_begin; r0 < q_end; r0 += kQB, cur = cur == 2 ? 0 : cur + 1) {
@@ -352,55 +363,70 @@ __global__ __launch_bounds__(64 * kSW, kSW == 8 ? 2 : 1) void scores_kernel(Scor
           const v4i bq = *reinterpret_cast<const v4i*>(qfrag + 1024 * ((2 * t + limb) * KD + ks));
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb)
-            accT[cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bT[cb][t][ks], bq, accT[cb], 0, 0, 0);
+            accT[cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bq, bT[cb][t][ks], accT[cb], 0, 0, 0);
         }
       }
 #pragma unroll
       for (int ks = 0; ks < KM; ++ks) {
         const v4i bp = *reinterpret_cast<const v4i*>(qfrag + 1024 * (2 * NP * KD + limb * KM + ks));
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) accS[cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bS[cb][ks], bp, accS[cb], 0, 0, 0);
+        for (int cb = 0; cb < CB; ++cb) accS[cb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bp, bS[cb][ks], accS[cb], 0, 0, 0);
       }
     }
 
-    // epilogue: query r0 + col, keys key0 + 32 cb + 8 g + 4 half + i
-    const float alpha = qs[cur][2 * col], beta = qs[cur][2 * col + 1];
-    const int64_t row = r0 + col;
-    float* out = a.scores + row * a.ld_s + key0 + 4 * half;
-    const bool fast = vec && key0 + 32 * CB <= a.n_k && r0 + kQB <= a.n_q;  // wave-uniform
+    // epilogue: key key0 + 32 cb + col, queries r0 + 8 g + 4 half + i
+    float val[CB][16];
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      v4f val[4];
+    for (int g = 0; g < 4; ++g) {
+      const int q0 = 8 * g + 4 * half;
+      const v4f ab01 = *reinterpret_cast<const v4f*>(&qs[cur][2 * q0]);  // alpha, beta of queries q0, q0 + 1
+      const v4f ab23 = *reinterpret_cast<const v4f*>(&qs[cur][2 * q0 + 4]);
+      const float alpha[4] = {ab01[0], ab01[2], ab23[0], ab23[2]};
+      const float beta[4] = {ab01[1], ab01[3], ab23[1], ab23[3]};
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int kl = wave * (32 * CB) + 32 * cb + 8 * g + 4 * half;  // key index within the workgroup
-        const v4f kn = *reinterpret_cast<const v4f*>(ks_n + kl);
-        const v4f knr = *reinterpret_cast<const v4f*>(ks_nr + kl);
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          val[cb][4 * g + i] = (kn[cb] * alpha[i]) * (float)accT[cb][4 * g + i] +
+                               (knr[cb] * beta[i]) * (float)accS[cb][4 * g + i];
+    }
+    const bool fast = narrow && key0 + 32 * CB <= a.n_k && r0 + kQB <= a.n_q;  // wave-uniform
+    if (fast) {
+      // buffer stores: the block's base and each row's offset in scalar registers, the lane's offset in
+      // one vector register, so a store is a single instruction; nontemporal, since no kernel of this
+      // call reads the scores back
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(a.scores + r0 * a.ld_s + key0, (short)0, -1, 0x00020000);
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          val[g][i] = (kn[i] * alpha) * (float)accT[cb][4 * g + i] + (knr[i] * beta) * (float)accS[cb][4 * g + i];
-      }
-      if (fast) {
-        // plain (cached) stores: L2 merges the 16-byte row pieces into whole lines
 #pragma unroll
-        for (int g = 0; g < 4; ++g) *reinterpret_cast<v4f*>(out + 32 * cb + 8 * g) = val[g];
-      } else if (row < a.n_q) {
+          for (int cb = 0; cb < CB; ++cb)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val[cb][4 * g + i]), rs, lane_boff + 128 * cb,
+                                                  (8 * g + i) * row_bytes, kStoreNT);
+    } else {
+      int64_t ld = a.ld_s;
+      asm volatile("" : "+s"(ld));  // keeps the addresses of this rare path out of the loop's registers
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
+      for (int g = 0; g < 4; ++g)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (key0 + 32 * cb + 8 * g + 4 * half + i < a.n_k) out[32 * cb + 8 * g + i] = val[g][i];
-      }
+        for (int i = 0; i < 4; ++i) {
+          const int64_t row = r0 + 8 * g + 4 * half + i;
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb)
+            if (row < a.n_q && key0 + 32 * cb + col < a.n_k) a.scores[row * ld + key0 + 32 * cb + col] = val[cb][4 * g + i];
+        }
     }
     if (fast) {
       // the copy of block b + 1 (issued one block ago) must land; younger than it are the previous block's
-      // 4 CB stores, this block's copies and this block's 4 CB stores, none of which are waited for
+      // 16 CB stores, this block's copies and this block's 16 CB stores, none of which are waited for
       if (!ahead)
-        wait_vm<8 * CB>();
+        wait_vm<32 * CB>();
       else if (wave == 0)
-        wait_vm<8 * CB + LY::KPW + 1>();
+        wait_vm<32 * CB + LY::KPW + 1>();
       else
-        wait_vm<8 * CB + LY::KPW>();
+        wait_vm<32 * CB + LY::KPW>();
     } else {
       wait_vm<0>();  // also completes the copy of block b + 1, whatever follows
     }
@@ -422,8 +448,16 @@ hipError_t launch_scores_t(const ScoreArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     ready.store(true, std::memory_order_release);
   }
-  dim3 grid((unsigned)(a.n_k_pad / (32 * CB * kSW)), (unsigned)((a.n_q_pad + kQChunk - 1) / kQChunk));
-  hipLaunchKernelGGL((scores_kernel<NP, KD, KM, CB, NORM_F32>), grid, dim3(64 * kSW), lds, s, a);
+  // query chunks: enough workgroups for kScoresWgPerCu per compute unit, each chunk as long as possible (every
+  // workgroup rebuilds its key operands once)
+  const int64_t key_wgs = a.n_k_pad / (32 * CB * kSW), blocks = a.n_q_pad / kQB;
+  int64_t chunks = ((int64_t)kScoresWgPerCu * device_cu_count() + key_wgs - 1) / key_wgs;
+  chunks = chunks < 1 ? 1 : (chunks > blocks ? blocks : chunks);
+  const int64_t chunk_blocks = (blocks + chunks - 1) / chunks;
+  ScoreArgs b = a;
+  b.q_chunk = chunk_blocks * kQB;
+  dim3 grid((unsigned)key_wgs, (unsigned)((blocks + chunk_blocks - 1) / chunk_blocks));
+  hipLaunchKernelGGL((scores_kernel<NP, KD, KM, CB, NORM_F32>), grid, dim3(64 * kSW), lds, s, b);
   return hipGetLastError();
 }
 

@@ -122,10 +122,11 @@ def test_scores_beta_codebook(bits, dt):
     print(f"beta bits={bits} dt={dt}: worst error {worst:.2e} of n*||q||")
 
 
-@pytest.mark.parametrize("n_k,n_q", [(1000, 70), (4100, 200)])
+@pytest.mark.parametrize("n_k,n_q", [(1000, 70), (4100, 200), (4100, 3000)])
 def test_scores_dense_rows_ragged(n_k, n_q):
-    """ld_s == n_k (16-byte row pieces where a whole tile fits, element stores on the ragged key tile
-    and query block): every score of the matrix against the oracle."""
+    """ld_s == n_k (buffer stores where a whole key tile and query block fit, element stores on the
+    ragged key tile and query block): every score of the matrix against the oracle.  At 4100 x 3000
+    each workgroup streams several query blocks through its ring, the last chunk a shorter one."""
     bits, dt, m = 2, 128, 128
     keys = synth.kv_tensor(77, 1, 1, 0, n_k, dt, n_outliers=0).reshape(n_k, dt)
     signs = synth.signs(78, 2, dt)
@@ -136,6 +137,27 @@ def test_scores_dense_rows_ragged(n_k, n_q):
     orc = K.oracle(q)
     worst = _check(gpu, orc, q, K.host()[1])
     print(f"n_k={n_k} n_q={n_q}: worst error {worst:.2e} of n*||q||")
+
+
+def test_scores_wide_rows():
+    """Rows of 2^24 + 3 floats: the byte offsets within a query block no longer fit 32 bits, so every
+    tile takes the element-store path.  Every score against the oracle; the padding is untouched."""
+    n_k, n_q, bits, dt, m = 300, 40, 2, 128, 128
+    ld_s = (1 << 24) + 3
+    keys = synth.kv_tensor(81, 1, 1, 0, n_k, dt, n_outliers=0).reshape(n_k, dt)
+    K = Keys(keys, dt, bits, m, synth.signs(82, 2, dt), synth.gaussian_matrix(83, 0, m, dt))
+    q = synth.normal_f16(84, 6, n_q * dt).reshape(n_q, dt)
+    out = torch.full((n_q, ld_s), -99.0, dtype=torch.float32, device=DEV)
+    wsb = tq.tq_workspace_size(tq.TQ_OP_QJL_SCORES, K.qz, n_q, n_k)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    tq.tq_qjl_scores(K.qz, torch.from_numpy(q).to(DEV), tq.TQ_F16, n_q, dt, K.codes, K.norms, K.sbits, K.rnorm,
+                     n_k, out, ld_s, ws, wsb)
+    torch.cuda.synchronize()
+    assert bool((out[:, n_k:n_k + 4096] == -99.0).all()) and bool((out[:, -4096:] == -99.0).all())
+    gpu = out[:, :n_k].cpu().numpy()
+    del out
+    worst = _check(gpu, K.oracle(q), q, K.host()[1])
+    print(f"ld_s=2^24+3: worst error {worst:.2e} of n*||q||")
 
 
 def test_scores_full_size_sampled():
