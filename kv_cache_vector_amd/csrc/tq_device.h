@@ -34,6 +34,40 @@ __device__ __forceinline__ double lane_xor(double v, int mask) {
                                         ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32));
 }
 
+// One v_permlane16_swap / v_permlane32_swap exchange with the lane DIST (16 or 32) lanes away: in a lane
+// whose DIST bit is clear, r0 is its own value and r1 its partner's; in the other lane of the pair the reverse.
+template <int DIST>
+__device__ __forceinline__ void lane_swap_pair(float v, float& r0, float& r1) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  if constexpr (DIST == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    r0 = __builtin_bit_cast(float, (uint32_t)r[0]);
+    r1 = __builtin_bit_cast(float, (uint32_t)r[1]);
+  } else {
+    static_assert(DIST == 32, "lanes 16 or 32 apart");
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    r0 = __builtin_bit_cast(float, (uint32_t)r[0]);
+    r1 = __builtin_bit_cast(float, (uint32_t)r[1]);
+  }
+}
+
+// Butterfly across lanes DIST apart: a + b in the lane whose DIST bit is clear (own a, partner b), a - b in its
+// partner; s is +1 in the first lane and -1 in the second, so both are one fma of the swapped pair.
+template <int DIST>
+__device__ __forceinline__ float xlane_butterfly(float v, float s) {
+  float r0, r1;
+  lane_swap_pair<DIST>(v, r0, r1);
+  return __builtin_fmaf(s, r1, r0);
+}
+
+// v plus the value of the lane DIST apart (the same sum in both lanes).
+template <int DIST>
+__device__ __forceinline__ float xlane_sum(float v) {
+  float r0, r1;
+  lane_swap_pair<DIST>(v, r0, r1);
+  return r0 + r1;
+}
+
 // Sum of v over the LPU consecutive lanes of a unit (LPU in {1,2,4,8}).
 template <int LPU, typename T>
 __device__ __forceinline__ T unit_sum(T v) {

@@ -4,10 +4,12 @@
 //
 // The residual's sign bits sign((S r)_p) are only meaningful to the
 // estimator if they agree with the exact projection.  head_dim 128 encodes in
-// fp32 with the projection on fp32 MFMA, whose error (about 2e-7 of the
-// residual norm) stays inside the 1e-6-of-rho band around z = 0; the other
-// head sizes encode in float64, exact except within ~1e-15 of an edge.
-// S~ = S D H (host-prepared) is staged in LDS; because H and D are symmetric
+// fp32 with the projection on fp16 MFMA in split precision (hi/lo pieces of
+// both operands, fp32 accumulation), whose error (about 1e-7 of the residual
+// norm in the median, as for fp32 products) leaves a sign bit wrong only
+// where |z| is within a few 1e-6 of rho; the other head sizes encode in
+// float64, exact except within ~1e-15 of an edge.  S~ = S D H
+// (host-prepared) is staged in LDS; because H and D are symmetric
 // involutions, S (u - D H c) = S~ (y - c), so the residual never leaves the
 // rotated domain.
 #include <hip/hip_fp16.h>
@@ -133,37 +135,60 @@ __global__ __launch_bounds__(kBlock) void qjl_encode_kernel(QjlEncodeArgs a, con
   }
 }
 
-// Encode for head_dim = 128 in fp32, with the projection z = S~ e on fp32 MFMA
-// (v_mfma_f32_16x16x4_f32).  Eight waves share one LDS copy of S~; a wave encodes 16 keys: lane l holds the 32
-// coordinates 32 (l / 16) .. + 31 of key l % 16, so the A operand of k-step s
-// is the lane's coordinate s and each lane packs one whole 32-group.  S~ sits
-// in LDS as B-operand fragments, four k-steps per 16-byte read.  The sign bit
-// [z_p >= 0] of (key 4 (l / 16) + r, p = 16 pt + l % 16) comes out of the
-// accumulator as a wave ballot; the ballots are regrouped into each key's
-// m-bit row through a small LDS table.  fp32 moves z by ~2e-7 of rho (the
-// residual norm), so a sign bit can only differ from the exact one inside
-// the |z| < 1e-6 rho band that the parity contract allows.
+// Encode for head_dim = 128 in fp32, with the projection z = S~ e on fp16 MFMA
+// (v_mfma_f32_16x16x32_f16) in split precision: e and S~ are each split into fp16 pieces x = hi + lo
+// (hi = fp16(x), lo = fp16(x - hi), about 22 significant bits), and z accumulates hi.hi + hi.lo + lo.hi in
+// fp32.  The products of fp16 pieces are exact in fp32, the dropped lo.lo term is 2^-22 of a product, so z
+// carries the error of an fp32 dot product (about 1e-7 of rho, the residual norm, in the median): a sign
+// bit can only differ from the exact one where |z| is within a few 1e-6 of rho, about as often as with
+// fp32 products, and three fp16 passes cost a fifth of one fp32 pass.  e is scaled by 2^10 before the
+// split (the sign of z is all that is kept), so its low pieces stay in fp16's normal range.
+//
+// Eight waves share one LDS copy of the S~ pieces; a wave encodes 16 keys: lane l holds the 32 coordinates
+// 32 (l / 16) .. + 31 of key l % 16, and each lane packs one whole 32-group.  The contraction over the
+// 128 coordinates is taken in the order in which the lanes hold them: K-step s of the MFMA takes
+// coordinates 32 g + 8 s .. + 7 from lane group g, for both operands, so the A operand of step s is 8
+// consecutive coordinates of the lane's own 32, and S~ sits in LDS as B-operand fragments in the same
+// order.  The sign bit [z_p >= 0] of (key 4 (l / 16) + r, p = 16 pt + l % 16) comes out of the
+// accumulator as a wave ballot; the ballots are regrouped into each key's m-bit row through a small LDS
+// table.
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 constexpr int kEncBlock = 512;  // 8 waves share one copy of S~ in LDS
+constexpr float kResidualScale = 1024.0f;  // 2^10: e's fp16 pieces stay normal; z's sign does not change
 
 template <int BITS, bool IN_F32, bool NORM_F32>
 __global__ __launch_bounds__(kEncBlock) void qjl_encode128_kernel(QjlEncodeArgs a, const float* __restrict__ s_rot32) {
   constexpr int W = kEncBlock / 64;
-  extern __shared__ v4f sfrag[];                  // [m/16][8][64]: S~[16 pt + ln%16][32 (ln/16) + 4 s4 + i]
+  // [m/16][4 s][hi, lo][64 lanes] x 8 halves: S~[16 pt + l%16][32 (l/16) + 8 s + i] split into fp16 pieces
+  extern __shared__ u32x4 sfrag[];
   __shared__ uint64_t ballots[W][32];             // per wave: [pt * 4 + r]
   __shared__ float lvl_s[16];
   const int m = a.m, npt = m / 16, words = m / 32;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = tid; e < npt * 512; e += kEncBlock) {
-    const int pt = e >> 9, s4 = (e >> 6) & 7, ln = e & 63;
-    sfrag[e] = *reinterpret_cast<const v4f*>(s_rot32 + (16 * pt + (ln & 15)) * 128 + 32 * (ln >> 4) + 4 * s4);
+  for (int e = tid; e < npt * 256; e += kEncBlock) {
+    const int pt = e >> 8, st = (e >> 6) & 3, ln = e & 63;
+    const v4f* src = reinterpret_cast<const v4f*>(s_rot32 + (16 * pt + (ln & 15)) * 128 + 32 * (ln >> 4) + 8 * st);
+    const v4f x0 = src[0], x1 = src[1];
+    const float xs[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const _Float16 h0 = (_Float16)xs[2 * i], h1 = (_Float16)xs[2 * i + 1];
+      const _Float16 l0 = (_Float16)(xs[2 * i] - (float)h0), l1 = (_Float16)(xs[2 * i + 1] - (float)h1);
+      hi[i] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+      lo[i] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+    }
+    sfrag[(pt * 8 + 2 * st) * 64 + ln] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+    sfrag[(pt * 8 + 2 * st + 1) * 64 + ln] = u32x4{lo[0], lo[1], lo[2], lo[3]};
   }
   if (tid < 16) lvl_s[tid] = (float)a.level[tid];
   __syncthreads();
 
   const int q = lane >> 4, kl = lane & 15;
   const uint32_t dword = q == 0 ? a.dbits[0] : q == 1 ? a.dbits[1] : q == 2 ? a.dbits[2] : a.dbits[3];
+  const float s16 = (q & 1) ? -1.0f : 1.0f, s32 = (q & 2) ? -1.0f : 1.0f;  // cross-lane butterfly signs
   float thr[7];
 #pragma unroll
   for (int k = 0; k < 7; ++k) thr[k] = (float)a.thr[k];
@@ -203,20 +228,14 @@ __global__ __launch_bounds__(kEncBlock) void qjl_encode128_kernel(QjlEncodeArgs 
       ss = __builtin_fmaf(v[j], v[j], ss);
       if ((dword >> j) & 1u) v[j] = -v[j];
     }
-    ss += __shfl_xor(ss, 16);
-    ss += __shfl_xor(ss, 32);
+    ss = xlane_sum<32>(xlane_sum<16>(ss));
     const float n = __builtin_sqrtf(ss);
     // unnormalised FWHT over the 128 coordinates: bits 0..4 in the lane, bits 5 and 6 across lanes 16 and 32 apart
     fwht32_inlane(v);
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const bool upper = (q >> b) & 1;
+    for (int j = 0; j < 32; ++j) v[j] = xlane_butterfly<16>(v[j], s16);
 #pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        const float o = __shfl_xor(v[j], 16 << b);
-        v[j] = upper ? o - v[j] : v[j] + o;
-      }
-    }
+    for (int j = 0; j < 32; ++j) v[j] = xlane_butterfly<32>(v[j], s32);
     // codes (|y| against the N(0,1) edges scaled by n) and the residual e' = y / n - c in N(0,1) units
     float T[7];
 #pragma unroll
@@ -246,23 +265,43 @@ __global__ __launch_bounds__(kEncBlock) void qjl_encode128_kernel(QjlEncodeArgs 
       v[j] = __builtin_fmaf(y, inv_n, -lvl_s[code]);
       rr = __builtin_fmaf(v[j], v[j], rr);
     }
-    rr += __shfl_xor(rr, 16);
-    rr += __shfl_xor(rr, 32);
+    rr = xlane_sum<32>(xlane_sum<16>(rr));
+    // fp16 pieces of 2^10 e, two coordinates per register: eh[4 s + i / 2] holds coordinates 8 s + i
+    uint32_t eh[16], el[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float x0 = v[2 * j] * kResidualScale, x1 = v[2 * j + 1] * kResidualScale;
+      const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+      const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
+      eh[j] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+      el[j] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+    }
 
-    // z = S~ e' for the 16 keys, 16 projections per pass; ballots of z >= 0
-    for (int pt = 0; pt < npt; ++pt) {
-      v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      const v4f* bf = sfrag + pt * 512 + lane;
+    // z = S~ e for the 16 keys, 16 projections per pass, passes 2k and 2k + 1 on two accumulators
+    // (independent MFMA chains; m is a multiple of 32); ballots of z >= 0
+    for (int pt = 0; pt < npt; pt += 2) {
+      v4f acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
+      const u32x4* bf = sfrag + pt * 512 + lane;
 #pragma unroll
-      for (int s4 = 0; s4 < 8; ++s4) {
-        const v4f b = bf[64 * s4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(v[4 * s4 + i], b[i], acc, 0, 0, 0);
+      for (int st = 0; st < 4; ++st) {
+        const v8h ah = __builtin_bit_cast(v8h, u32x4{eh[4 * st], eh[4 * st + 1], eh[4 * st + 2], eh[4 * st + 3]});
+        const v8h al = __builtin_bit_cast(v8h, u32x4{el[4 * st], el[4 * st + 1], el[4 * st + 2], el[4 * st + 3]});
+        const v8h bh0 = __builtin_bit_cast(v8h, bf[128 * st]), bl0 = __builtin_bit_cast(v8h, bf[128 * st + 64]);
+        const v8h bh1 = __builtin_bit_cast(v8h, bf[512 + 128 * st]), bl1 = __builtin_bit_cast(v8h, bf[512 + 128 * st + 64]);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh0, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh1, acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl0, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl1, acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh0, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh1, acc1, 0, 0, 0);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const uint64_t bal = __ballot(acc[r] >= 0.0f);
-        if (lane == 0) ballots[wave][pt * 4 + r] = bal;
+        const uint64_t bal0 = __ballot(acc0[r] >= 0.0f), bal1 = __ballot(acc1[r] >= 0.0f);
+        if (lane == 0) {
+          ballots[wave][pt * 4 + r] = bal0;
+          ballots[wave][(pt + 1) * 4 + r] = bal1;
+        }
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -411,7 +450,7 @@ hipError_t qjl_encode128(const tq_config& cfg, const QjlEncodeArgs& a, hipStream
 
 template <int BITS>
 hipError_t qjl_encode_lpu(const tq_config& cfg, const QjlEncodeArgs& a, hipStream_t s) {
-  if (cfg.dt == 128 && a.m % 16 == 0) return qjl_encode128<BITS>(cfg, a, s);
+  if (cfg.dt == 128 && a.m % 32 == 0) return qjl_encode128<BITS>(cfg, a, s);
   switch (cfg.dt) {
     case 32: return qjl_encode_dispatch<BITS, 1>(cfg, a, s);
     case 64: return qjl_encode_dispatch<BITS, 2>(cfg, a, s);
