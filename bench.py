@@ -505,11 +505,17 @@ def batch_ms(torch, fn, reps):
     return e0.elapsed_time(e1) / reps
 
 
-def graph_ms(torch, fn, outputs, reps):
-    """Average device duration (ms) of fn() from `reps` replays of a HIP graph holding one call,
-    between two HIP events (the host cost of the Python call is not timed).  The replay is checked
-    against an eager call first; falls back to back-to-back eager calls if it differs."""
-    graph = capture_step(torch, fn, outputs)
+def graph_ms(torch, fn, outputs, reps, calls=1):
+    """Average device duration (ms) of one fn() call from `reps` replays of a HIP graph holding
+    `calls` calls back to back, between two HIP events (the host cost of the Python call is not
+    timed; several calls per graph spread a replay's launch latency, which is comparable to a kernel
+    of ~20 us, over them).  The replay is checked against an eager call first; falls back to
+    back-to-back eager calls if it differs."""
+    def many():
+        for _ in range(calls):
+            fn()
+
+    graph = capture_step(torch, many, outputs)
     if graph is None:
         return batch_ms(torch, fn, reps)
     torch.cuda.synchronize()
@@ -520,7 +526,7 @@ def graph_ms(torch, fn, outputs, reps):
         graph.replay()
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps
+    return e0.elapsed_time(e1) / (reps * calls)
 
 
 def bench_vectors_fp32(tq, torch, dev, reps):
@@ -545,8 +551,8 @@ def bench_vectors_fp32(tq, torch, dev, reps):
 
     enc()
     dec()
-    enc_ms = graph_ms(torch, enc, [codes, norms], reps)
-    dec_ms = graph_ms(torch, dec, [y], reps)
+    enc_ms = graph_ms(torch, enc, [codes, norms], reps, calls=10)
+    dec_ms = graph_ms(torch, dec, [y], reps, calls=10)
     nbytes = n * (4 * d + d * bits // 8 + 4)  # fp32 vectors + codes + fp32 norms, per direction
     out = {"workload": "4096 vectors x 128 fp32 N(0,1), 3 bits, whole-vector units, fp32 norm per vector",
            "encode_us": round(enc_ms * 1e3, 2), "decode_us": round(dec_ms * 1e3, 2),
@@ -660,9 +666,10 @@ def bench_qjl(tq, torch, dev, reps):
     for _ in range(2):
         enc()
         score()
-    # device time: one call per graph replay (the kernels are far shorter than the host cost of a call)
-    enc_ms = graph_ms(torch, enc, [codes, norms, sbits, rnorm], reps)
-    sc_ms = graph_ms(torch, score, [scores], reps)
+    # device time per call from graph replays of several calls (the kernels are far shorter than the host
+    # cost of a call)
+    enc_ms = graph_ms(torch, enc, [codes, norms, sbits, rnorm], reps, calls=10)
+    sc_ms = graph_ms(torch, score, [scores], reps, calls=4)
     key_bytes = n * (d * 2 + d * bits // 8 + 2 + m // 8 + 2)  # fp16 key in; codes, norm, signs, rho out
     n_scores = nq * n
     # int8 MFMA work of the scoring kernel: per score, hi and lo limbs of the rotated query against

@@ -35,7 +35,8 @@ def _encode(keys, dt, bits, m, seed, nc=False, codebook="gaussian"):
 
 @pytest.mark.parametrize("dt,m,bits,codebook", [(128, 128, 2, "gaussian"), (128, 64, 1, "gaussian"),
                                                  (64, 128, 3, "gaussian"), (64, 64, 2, "gaussian"),
-                                                 (128, 96, 2, "gaussian"), (128, 128, 3, "beta"),
+                                                 (128, 96, 2, "gaussian"), (128, 32, 2, "gaussian"),
+                                                 (128, 128, 3, "beta"),
                                                  (64, 64, 2, "beta"),
                                                  (32, 256, 2, "gaussian"),   # one lane per unit, 32 KiB of S~
                                                  (256, 64, 3, "gaussian"),   # eight lanes per unit, 64 KiB of S~
