@@ -485,6 +485,13 @@ __global__ __launch_bounds__(kBlock) void encode_mfma_kernel(EncodeArgs a) {
   // 4 and 8 bits: the next tile's loads go out before this tile's compute and stores (measured
   // faster at 4 and 8 bits, slower at 3)
   constexpr bool PIPE = BITS == 4 || BITS == 8;
+  // Units of 2 or 4 groups at up to 3 bits: the whole H_dt = H_LPU (x) H_32 runs on the MFMA.  A lane's B
+  // operand takes the LPU groups of its unit in turn (K = 32 LPU), each negated where H_LPU[q][j] = -1,
+  // against the same H_32 A operand; D is applied to the inputs as they are staged.  Measured on the
+  // fork's 128-value records: 14 % faster at 3 bits, 5 % slower at 4 bits (whose pipelined loads and
+  // longer bucketing leave less room for the LPU-fold B reads), so 4 and 8 bits keep the cross-lane
+  // stages, as do units of 8 groups (8 times the B reads and 7 sign flips per read).
+  constexpr bool MH = (LPU == 2 || LPU == 4) && BITS <= 3;
   const int lane = threadIdx.x & 63;
   const int wave = PIPE ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : threadIdx.x >> 6;
   const int n32 = lane & 31, h = lane >> 5, q = n32 % LPU;
@@ -503,9 +510,21 @@ __global__ __launch_bounds__(kBlock) void encode_mfma_kernel(EncodeArgs a) {
       am[kc][j] = neg ? (_Float16)-1.0f : (_Float16)1.0f;
     }
   }
-  // LPU > 1: sign masks of D for the lane's B-operand words (coordinates 8h + 2i, +1 and 16 + 8h + 2i, +1)
-  uint32_t dmask[LPU == 1 ? 1 : 8];
-  if constexpr (LPU > 1) {
+  // MH: sign masks of D for the staged words of this lane's 16-byte input pieces (piece lane % 4 of a
+  // group at position (lane / 4) % LPU in its unit), and of H_LPU[q][j] for the B operand read from
+  // group j of the unit
+  uint32_t smask[MH ? 4 : 1], hmask[MH ? LPU : 1];
+  if constexpr (MH) {
+    const uint32_t sd = a.dbits[(lane >> 2) % LPU] >> (8 * (lane & 3));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) smask[i] = pair_sign_mask(sd, i);
+#pragma unroll
+    for (int j = 0; j < LPU; ++j) hmask[j] = (__builtin_popcount(q & j) & 1) ? 0x80008000u : 0u;
+  }
+  // LPU > 1 (no MH): sign masks of D for the lane's B-operand words (coordinates 8h + 2i, +1 and
+  // 16 + 8h + 2i, +1)
+  uint32_t dmask[LPU == 1 || MH ? 1 : 8];
+  if constexpr (LPU > 1 && !MH) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       dmask[i] = pair_sign_mask(dword >> (8 * h), i);
@@ -518,16 +537,28 @@ __global__ __launch_bounds__(kBlock) void encode_mfma_kernel(EncodeArgs a) {
   const char* xbase = static_cast<const char*>(a.x);
 
   const int64_t stride = (int64_t)gridDim.x * kBlock;
-  u32x4 pre[PIPE ? CH : 1];
+  u32x4 pre[PIPE || MH ? CH : 1];
+  auto put_tile = [&]() {  // pre -> the wave's tile (MH: with D's sign flips)
+    if constexpr (MH) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pre[c][i] ^= smask[i];
+    }
+    stage_put<CH, PITCH>(tile, pre, lane);
+  };
   if constexpr (PIPE) {
     const int64_t f0 = (int64_t)blockIdx.x * kBlock + wave * 64;
     if (f0 < a.n_groups) stage_load<CH, 2, CONTIG>(pre, xbase, f0, a.n_groups, a.groups_per_row, a.ld_x, lane);
   }
   for (int64_t w0 = (int64_t)blockIdx.x * kBlock + wave * 64; w0 < a.n_groups; w0 += stride) {
     if constexpr (PIPE) {
-      stage_put<CH, PITCH>(tile, pre, lane);
+      put_tile();
       if (w0 + stride < a.n_groups)
         stage_load<CH, 2, CONTIG>(pre, xbase, w0 + stride, a.n_groups, a.groups_per_row, a.ld_x, lane);
+    } else if constexpr (MH) {
+      stage_load<CH, 2, CONTIG>(pre, xbase, w0, a.n_groups, a.groups_per_row, a.ld_x, lane);
+      put_tile();
     } else {
       stage_in<CH, PITCH, 2, CONTIG>(tile, xbase, w0, a.n_groups, a.groups_per_row, a.ld_x, lane);
     }
@@ -547,7 +578,7 @@ __global__ __launch_bounds__(kBlock) void encode_mfma_kernel(EncodeArgs a) {
         ss = __builtin_amdgcn_fdot2(p0, p0, ss, false);
         ss = __builtin_amdgcn_fdot2(p1, p1, ss, false);
       }
-      if constexpr (LPU > 1) {
+      if constexpr (LPU > 1 && !MH) {
         u32x4 w0v = __builtin_bit_cast(u32x4, b0), w1v = __builtin_bit_cast(u32x4, b1);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -558,8 +589,29 @@ __global__ __launch_bounds__(kBlock) void encode_mfma_kernel(EncodeArgs a) {
         b1 = __builtin_bit_cast(v8h_t, w1v);
       }
       const v16f_t z = {};
-      v16f_t y = __builtin_amdgcn_mfma_f32_32x32x16_f16(am[0], b0, z, 0, 0, 0);
-      y = __builtin_amdgcn_mfma_f32_32x32x16_f16(am[1], b1, y, 0, 0, 0);
+      v16f_t y;
+      if constexpr (MH) {
+        // y = sum_j H_LPU[q][j] H_32 x_j over the unit's groups j (D already in the tile)
+        const uint8_t* up = tile + (32 * s + n32 - q) * PITCH + 16 * h;
+        y = z;
+#pragma unroll
+        for (int j = 0; j < LPU; ++j) {
+          u32x4 w0v = *reinterpret_cast<const u32x4*>(up + j * PITCH);
+          u32x4 w1v = *reinterpret_cast<const u32x4*>(up + j * PITCH + 32);
+          if (j > 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              w0v[i] ^= hmask[j];
+              w1v[i] ^= hmask[j];
+            }
+          }
+          y = __builtin_amdgcn_mfma_f32_32x32x16_f16(am[0], __builtin_bit_cast(v8h_t, w0v), y, 0, 0, 0);
+          y = __builtin_amdgcn_mfma_f32_32x32x16_f16(am[1], __builtin_bit_cast(v8h_t, w1v), y, 0, 0, 0);
+        }
+      } else {
+        y = __builtin_amdgcn_mfma_f32_32x32x16_f16(am[0], b0, z, 0, 0, 0);
+        y = __builtin_amdgcn_mfma_f32_32x32x16_f16(am[1], b1, y, 0, 0, 0);
+      }
       const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, ss), __builtin_bit_cast(uint32_t, ss),
                                                       false, false);
       float us = __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
@@ -568,7 +620,7 @@ __global__ __launch_bounds__(kBlock) void encode_mfma_kernel(EncodeArgs a) {
       for (int j = 0; j < 16; ++j) yv[j] = y[j];
       if constexpr (LPU > 1) {
         us = unit_sum<LPU>(us);
-        unit_butterflies<LPU, 16>(yv, q);
+        if constexpr (!MH) unit_butterflies<LPU, 16>(yv, q);
       }
       // v_sqrt_f32 (1 ulp): the stored fp16 norm tolerates it, and the thresholds t n move by
       // ~1e-7 of a cell edge, inside the 1e-6 band the codes are held to
