@@ -197,17 +197,75 @@ __global__ __launch_bounds__(256, GP == 4 ? 3 : 2) void attn_kernel(AttnArgs a) 
   Regs rs[2];
   if (t_begin < T) load(rs[0], t_begin);
 
+  // Set-up reads from global memory in one round trip: the levels (staged in the score-exchange
+  // area, which the first tile's exchange is the first to use) and this thread's EPT consecutive
+  // query elements, all of one row and one 32-block.
+  constexpr int EPT = GP * HD / 256;  // query elements per thread (2 .. 16)
+  constexpr int TPB = 32 / EPT;       // threads per 32-block, consecutive lanes of one wave
+  static_assert(GP * HD % 256 == 0 && EPT >= 2 && EPT <= 32, "query staging splits evenly");
+  float* lv = &xs[0][0][0];
+  static_assert(sizeof(xs) >= sizeof(float) * (KL + VL), "levels fit the exchange area");
+  for (int x = tid; x < KL; x += 256) lv[x] = a.klevel[x];
+  if (tid < VL) lv[KL + tid] = a.vlevel[tid];
+  const int qe0 = tid * EPT, qr = qe0 / HD, qd0 = qe0 % HD;
+  float qv[EPT];
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) qv[k] = 0.0f;
+  if (qr < grows) {
+    const int64_t rr = row0 + qr, i = rr / G;  // query token and head of the row
+    const int64_t off = (i * a.n_q_heads + (int64_t)kvh * G + rr % G) * HD + qd0;
+#pragma unroll
+    for (int k = 0; k < EPT; ++k)
+      qv[k] = a.q_f32 ? static_cast<const float*>(a.q)[off + k] : __half2float(static_cast<const __half*>(a.q)[off + k]);
+  }
+
+  // rotated query blocks qhat_b = H D_K q_b / sqrt(32) of the group's rows (rows past the live
+  // ones zero): the sign flips, then the butterflies over coordinate bits from the lowest up, the
+  // first log2 EPT inside the thread and the rest between the TPB threads of the block (the same
+  // additions in the same order as a textbook FWHT); staged in fp32 over the V tile area
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) qv[k] = ((a.kdbits >> ((qd0 + k) & 31)) & 1u) ? -qv[k] : qv[k];
+#pragma unroll
+  for (int hb = 1; hb < EPT; hb <<= 1) {
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+      if (!(k & hb)) {
+        const float x = qv[k], y = qv[k | hb];
+        qv[k] = x + y;
+        qv[k | hb] = x - y;
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < TPB; m <<= 1) {
+    const bool upper = (lane & m) != 0;  // this thread holds the coordinates with the bit set
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+      const float o = __shfl_xor(qv[k], m);
+      qv[k] = upper ? o - qv[k] : qv[k] + o;
+    }
+  }
+  float* qf = reinterpret_cast<float*>(&vt[0][0]);
+  static_assert(sizeof(vt) >= sizeof(float) * GP * HD, "query staging fits the V tiles");
+  if constexpr (EPT == 2) {
+    *reinterpret_cast<float2*>(qf + qe0) = make_float2(qv[0], qv[1]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < EPT; k += 4)
+      *reinterpret_cast<float4*>(qf + qe0 + k) = make_float4(qv[k], qv[k + 1], qv[k + 2], qv[k + 3]);
+  }
+  __syncthreads();  // levels and the rotated query are in LDS
 
   if constexpr (K8) {
     for (int x = tid; x < KL * CK; x += 256) {  // code -> (fp16 hi part, fp16 lo part)
-      const float c = a.klevel[x / CK];
+      const float c = lv[x / CK];
       const _Float16 h = (_Float16)c;
       kth[x] = pack_h2(h, (_Float16)(c - (float)h));
     }
   } else {
     for (int x = tid; x < KL * KL * CK; x += 256) {
       const int e = x / CK;
-      const float ca = a.klevel[e & (KL - 1)], cb = a.klevel[e >> KB];
+      const float ca = lv[e & (KL - 1)], cb = lv[e >> KB];
       const _Float16 ha = (_Float16)ca, hb = (_Float16)cb;
       kth[x] = pack_h2(ha, hb);
       ktl[x] = pack_h2((_Float16)(ca - (float)ha), (_Float16)(cb - (float)hb));
@@ -215,34 +273,7 @@ __global__ __launch_bounds__(256, GP == 4 ? 3 : 2) void attn_kernel(AttnArgs a) 
   }
   for (int x = tid; x < VL * VL * CV; x += 256) {
     const int e = x / CV;
-    vtab[x] = pack_h2((_Float16)a.vlevel[e & (VL - 1)], (_Float16)a.vlevel[e >> VB]);
-  }
-
-  // rotated query blocks qhat_b = H D_K q_b / sqrt(32) of the group's rows (rows past the live
-  // ones zero), FWHT staged in fp32 over the V tile area
-  float* qf = reinterpret_cast<float*>(&vt[0][0]);
-  static_assert(sizeof(vt) >= sizeof(float) * GP * HD, "query staging fits the V tiles");
-  for (int e = tid; e < GP * HD; e += 256) {
-    const int r = e / HD, d = e % HD;
-    float v = 0.0f;
-    if (r < grows) {
-      const int64_t rr = row0 + r, i = rr / G;  // query token and head of the row
-      const int64_t off = (i * a.n_q_heads + (int64_t)kvh * G + rr % G) * HD + d;
-      v = a.q_f32 ? static_cast<const float*>(a.q)[off] : __half2float(static_cast<const __half*>(a.q)[off]);
-    }
-    qf[e] = ((a.kdbits >> (d & 31)) & 1u) ? -v : v;
-  }
-  __syncthreads();
-  for (int hb = 1; hb < 32; hb <<= 1) {
-    for (int e = tid; e < GP * HD / 2; e += 256) {
-      const int r = e / (HD / 2), rem = e % (HD / 2), b = rem / 16, p = rem % 16;
-      const int i = (p / hb) * 2 * hb + (p % hb);
-      float* blk = qf + r * HD + 32 * b;
-      const float x = blk[i], y = blk[i + hb];
-      blk[i] = x + y;
-      blk[i + hb] = x - y;
-    }
-    __syncthreads();
+    vtab[x] = pack_h2((_Float16)lv[KL + (e & (VL - 1))], (_Float16)lv[KL + (e >> VB)]);
   }
 
   // query operands of this lane: row `row` of the A operand is head row % GP (every row live, so
