@@ -36,9 +36,9 @@
 //            a block) into a wave-private LDS tile of 32 rows;
 //            ds_read_b64_tr_b16 returns four tokens of one coordinate per lane,
 //            the B layout of the value MFMA (K = 32 tokens); the softmax
-//            weights are the fp16 A operand.  Halving the tile keeps a
-//            workgroup of up to 4 rows within a third of the LDS, so three
-//            workgroups share a compute unit.
+//            weights are the fp16 A operand.  Halving the tile keeps every
+//            workgroup within half of the LDS: two share a compute unit, and
+//            each wave may use up to 256 VGPRs.
 // Each workgroup writes one partial (acc, max, sum) per query head; a merge
 // kernel rescales and adds the partials, then applies D_V H once per block.
 #include <hip/hip_fp16.h>
@@ -66,7 +66,7 @@ struct TileRegs {
 };
 
 template <int NB, int KB, int VB, int GP>
-__global__ __launch_bounds__(256, GP == 4 ? 3 : 2) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
   constexpr int HD = NB * 32;
   constexpr int NBW = NB / kWaves;  // blocks per wave
   constexpr int S = 16 / GP;        // subtiles whose products one lane group picks from (slot 4g / GP)
@@ -645,9 +645,9 @@ hipError_t launch_bits(const AttnArgs& a, hipStream_t s) {
 // Token range per workgroup: a multiple of two 64-token tiles (the decode kernel walks its tiles in
 // pairs) that spreads the cache over about 512 workgroups (two per compute unit; 256 for the 8-wave
 // prefill workgroups, one per compute unit), 128 .. 8192 tokens; `columns` = KV heads x row groups,
-// the workgroup columns that each walk it, `grp` = rows per group.  (Groups of up to 4 rows fit three
-// workgroups per compute unit, but spreading them over 768 measured slower: 62 against 60 us for the
-// 131072-token decode.)
+// the workgroup columns that each walk it, `grp` = rows per group.  (Groups of up to 4 rows would fit
+// three workgroups per compute unit, but spreading them over 768 measured slower: 62 against 60 us
+// for the 131072-token decode; the kernel is built for two, with the registers that leaves.)
 #ifndef TQ_ATTN_WG_TARGET4
 #define TQ_ATTN_WG_TARGET4 512
 #endif

@@ -101,45 +101,44 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(AttnArgs a) {
   Raw raw;  // raw words of the next tile to decode
   if (decoder && t_begin < T) load(raw, t_begin);
 
-  if constexpr (K8) {
-    for (int x = tid; x < KL * CK; x += NT) {
-      const float c = a.klevel[x / CK];
-      const _Float16 h = (_Float16)c;
-      kth[x] = pack_h2(h, (_Float16)(c - (float)h));
-    }
-  } else {
-    for (int x = tid; x < KL * KL * CK; x += NT) {
-      const int e = x / CK;
-      const float ca = a.klevel[e & (KL - 1)], cb = a.klevel[e >> KB];
-      const _Float16 ha = (_Float16)ca, hb = (_Float16)cb;
-      kth[x] = pack_h2(ha, hb);
-      ktl[x] = pack_h2((_Float16)(ca - (float)ha), (_Float16)(cb - (float)hb));
-    }
-  }
-  for (int x = tid; x < VL * VL * CV; x += NT) {
-    const int e = x / CV;
-    sm.vtab[x] = pack_h2((_Float16)a.vlevel[e & (VL - 1)], (_Float16)a.vlevel[e >> VB]);
-  }
+  // Set-up reads from global memory in one round trip: the levels, staged in the K norm tile (which
+  // the first tile is the first to write), and the query elements, all issued before any is used.
+  float* lv = &sm.kn[0][0];
+  static_assert(sizeof(sm.kn) >= sizeof(float) * (KL + VL), "levels fit the K norm tile");
+  for (int x = tid; x < KL; x += NT) lv[x] = a.klevel[x];
+  if (tid < VL) lv[KL + tid] = a.vlevel[tid];
 
   // query operands: row `row` of each row tile, coordinates 8g .. 8g + 7 of each block, rotated
   // by H D_K (butterflies in registers, then across the lanes 16 and 32 apart) and split into fp16
-  // hi + lo parts of qhat / sqrt(32)
+  // hi + lo parts of qhat / sqrt(32).  Rows past the live ones read row 0's query and are zeroed.
   v8h qh8[kPRT][NB], ql8[kPRT][NB];
 #pragma unroll
   for (int rt = 0; rt < kPRT; ++rt) {
     const int64_t rr = row0 + 16 * rt + row;
     const bool live = rr < a.rows;
     const int64_t i = live ? rr / G : 0;
-    const _Float16* q16 = static_cast<const _Float16*>(a.q);
-    const float* q32 = static_cast<const float*>(a.q);
     const int64_t qoff = (i * a.n_q_heads + (int64_t)kvh * G + (live ? rr % G : 0)) * HD;
+    float qx[NB][8];
+    if (a.q_f32) {
+      const float* q32 = static_cast<const float*>(a.q) + qoff;
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) qx[b][j] = q32[32 * b + 8 * g + j];
+    } else {
+      const _Float16* q16 = static_cast<const _Float16*>(a.q) + qoff;
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) qx[b][j] = (float)q16[32 * b + 8 * g + j];
+    }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       float v[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int d = 32 * b + 8 * g + j;
-        const float x = live ? (a.q_f32 ? q32[qoff + d] : (float)q16[qoff + d]) : 0.0f;
+        const float x = live ? qx[b][j] : 0.0f;
         v[j] = ((a.kdbits >> (d & 31)) & 1u) ? -x : x;
       }
 #pragma unroll
@@ -165,6 +164,27 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void prefill_kernel(AttnArgs a) {
         ql8[rt][b][j] = (_Float16)(x - (float)qh8[rt][b][j]);
       }
     }
+  }
+  __syncthreads();  // levels
+
+  if constexpr (K8) {
+    for (int x = tid; x < KL * CK; x += NT) {
+      const float c = lv[x / CK];
+      const _Float16 h = (_Float16)c;
+      kth[x] = pack_h2(h, (_Float16)(c - (float)h));
+    }
+  } else {
+    for (int x = tid; x < KL * KL * CK; x += NT) {
+      const int e = x / CK;
+      const float ca = lv[e & (KL - 1)], cb = lv[e >> KB];
+      const _Float16 ha = (_Float16)ca, hb = (_Float16)cb;
+      kth[x] = pack_h2(ha, hb);
+      ktl[x] = pack_h2((_Float16)(ca - (float)ha), (_Float16)(cb - (float)hb));
+    }
+  }
+  for (int x = tid; x < VL * VL * CV; x += NT) {
+    const int e = x / CV;
+    sm.vtab[x] = pack_h2((_Float16)lv[KL + (e & (VL - 1))], (_Float16)lv[KL + (e >> VB)]);
   }
 
   const int64_t all_live = T - (a.causal ? a.n_q : 1);  // last token every row sees
