@@ -86,58 +86,32 @@ __device__ __forceinline__ int64_t group_offset(int64_t g, int32_t gpr, int64_t 
   }
 }
 
-// Copy the wave's 64 groups (CH 16-byte chunks each) from global memory into
-// the wave's LDS tile, group grp at tile + grp * PITCH.  Instruction k moves
-// chunks 64k .. 64k+63 of the wave's span, so each instruction covers one
-// contiguous 1 KiB when rows are contiguous.  Full waves issue every load
-// before the first LDS write; the last, partial wave checks each chunk.
-template <int CH, int PITCH, int ES, bool CONTIG>
-__device__ __forceinline__ void stage_in(uint8_t* tile, const char* base, int64_t w0, int64_t n_groups, int32_t gpr,
-                                         int64_t ld, int lane) {
-  u32x4 t[CH];
-  if (w0 + 64 <= n_groups) {
-#pragma unroll
-    for (int k = 0; k < CH; ++k) {
-      const int ci = 64 * k + lane;
-      const int grp = ci / CH, c = ci % CH;
-      t[k] = load_stream(reinterpret_cast<const u32x4*>(base + ES * group_offset<CONTIG>(w0 + grp, gpr, ld) + 16 * c));
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < CH; ++k) {
-      const int ci = 64 * k + lane;
-      const int grp = ci / CH, c = ci % CH;
-      t[k] = u32x4{0u, 0u, 0u, 0u};
-      if (w0 + grp < n_groups)
-        t[k] = load_stream(reinterpret_cast<const u32x4*>(base + ES * group_offset<CONTIG>(w0 + grp, gpr, ld) + 16 * c));
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < CH; ++k) {
-    const int ci = 64 * k + lane;
-    *reinterpret_cast<u32x4*>(tile + (ci / CH) * PITCH + 16 * (ci % CH)) = t[k];
-  }
-}
-
-// stage_in in two halves, for a loop that loads one tile ahead: the loads into registers ...
+// Load the wave's 64 groups (CH 16-byte chunks each) from global memory into
+// registers: instruction k moves chunks 64k .. 64k+63 of the wave's span, so
+// each instruction covers one contiguous 1 KiB when rows are contiguous.  In
+// the last, partial wave the groups past the end re-read the last group (the
+// caller has w0 < n_groups): every load stays in bounds, full waves take no
+// branch, and those groups' results are never stored.
 template <int CH, int ES, bool CONTIG>
 __device__ __forceinline__ void stage_load(u32x4* t, const char* base, int64_t w0, int64_t n_groups, int32_t gpr,
                                            int64_t ld, int lane) {
+  const int64_t room = n_groups - 1 - w0;
+  const uint32_t last = room < 63 ? (uint32_t)room : 63u;
 #pragma unroll
   for (int k = 0; k < CH; ++k) {
     const int ci = 64 * k + lane;
-    const int grp = ci / CH, c = ci % CH;
-    if (w0 + 64 <= n_groups) {
-      t[k] = load_stream(reinterpret_cast<const u32x4*>(base + ES * group_offset<CONTIG>(w0 + grp, gpr, ld) + 16 * c));
+    const int c = ci % CH;
+    const uint32_t grp = min((uint32_t)(ci / CH), last);
+    if constexpr (CONTIG) {  // uniform base + unsigned 32-bit lane offset
+      const char* wb = base + (int64_t)ES * 32 * w0;
+      t[k] = load_stream(reinterpret_cast<const u32x4*>(wb + (grp * (ES * 32u) + 16u * (uint32_t)c)));
     } else {
-      t[k] = u32x4{0u, 0u, 0u, 0u};
-      if (w0 + grp < n_groups)
-        t[k] = load_stream(reinterpret_cast<const u32x4*>(base + ES * group_offset<CONTIG>(w0 + grp, gpr, ld) + 16 * c));
+      t[k] = load_stream(reinterpret_cast<const u32x4*>(base + ES * group_offset<CONTIG>(w0 + grp, gpr, ld) + 16 * c));
     }
   }
 }
 
-// ... and their copy into the wave's LDS tile
+// ... and their copy into the wave's LDS tile, group grp at tile + grp * PITCH
 template <int CH, int PITCH>
 __device__ __forceinline__ void stage_put(uint8_t* tile, const u32x4* t, int lane) {
 #pragma unroll
@@ -145,6 +119,15 @@ __device__ __forceinline__ void stage_put(uint8_t* tile, const u32x4* t, int lan
     const int ci = 64 * k + lane;
     *reinterpret_cast<u32x4*>(tile + (ci / CH) * PITCH + 16 * (ci % CH)) = t[k];
   }
+}
+
+// Both: every load of a full wave goes out before the first LDS write.
+template <int CH, int PITCH, int ES, bool CONTIG>
+__device__ __forceinline__ void stage_in(uint8_t* tile, const char* base, int64_t w0, int64_t n_groups, int32_t gpr,
+                                         int64_t ld, int lane) {
+  u32x4 t[CH];
+  stage_load<CH, ES, CONTIG>(t, base, w0, n_groups, gpr, ld, lane);
+  stage_put<CH, PITCH>(tile, t, lane);
 }
 
 // Write the wave's 64 staged groups from the LDS tile to global memory, one
@@ -168,10 +151,13 @@ __device__ __forceinline__ void stage_out(const uint8_t* tile, char* base, int64
   }
 }
 
-// w = 2 w + [|y| > t]; returns the lane mask of the comparison.
+// w = 2 w + [|y| > t]; returns the lane mask of the comparison.  On gfx950 a VALU read of an SGPR
+// (as carry-in or lane mask) needs two wait states after the VALU write of it: the s_nop supplies
+// them inside the block, and every later reader of the mask is further away still.
 __device__ __forceinline__ uint64_t shift_in_gt(uint32_t& w, float y, float t) {
   uint64_t m, carry;
   asm("v_cmp_gt_f32_e64 %1, |%3|, %4\n\t"
+      "s_nop 1\n\t"
       "v_addc_co_u32_e64 %0, %2, %0, %0, %1"
       : "+v"(w), "=&s"(m), "=&s"(carry)
       : "v"(y), "v"(t));
@@ -193,6 +179,12 @@ __device__ __forceinline__ void shift_in_sign(uint32_t& w, float y) {
 // packed words.  Bit p of the 32-coordinate group (p = BITS*j + k) lives in
 // word p/32; since the caller walks j downwards and the bits of one code
 // from the top, every word receives its bits from bit 31 down to bit 0.
+//
+// y may come straight from an MFMA, and inline asm is exempt from the compiler's
+// checks of MFMA-result hazards, so every compare must depend on a compiler-made
+// read of y: the sign shift (same word, or the select of its threshold), or,
+// where a 3-bit code's first magnitude bit starts the next lower word, a copy
+// of |y| made here (one instruction per 32 bits).
 template <int BITS>
 __device__ __forceinline__ void code_chain(uint32_t* word, int j, float y, const float* T) {
   const int p_top = BITS * j + BITS - 1;
@@ -200,8 +192,9 @@ __device__ __forceinline__ void code_chain(uint32_t* word, int j, float y, const
   if constexpr (BITS == 2) {
     shift_in_gt(word[(p_top - 1) >> 5], y, T[0]);
   } else if constexpr (BITS == 3) {
-    const uint64_t c1 = shift_in_gt(word[(p_top - 1) >> 5], y, T[1]);
-    shift_in_gt(word[(p_top - 2) >> 5], y, select_mask(c1, T[0], T[2]));
+    const float ym = (p_top & 31) == 0 ? __builtin_fabsf(y) : y;
+    const uint64_t c1 = shift_in_gt(word[(p_top - 1) >> 5], ym, T[1]);
+    shift_in_gt(word[(p_top - 2) >> 5], ym, select_mask(c1, T[0], T[2]));
   } else if constexpr (BITS == 4) {
     const uint64_t c1 = shift_in_gt(word[(p_top - 1) >> 5], y, T[3]);
     const float lo = select_mask(c1, T[0], T[4]);

@@ -135,17 +135,18 @@ __device__ __forceinline__ uint32_t get_code(const uint32_t* w, int j) {
 // assembly: the compiler neither waits for them nor orders later LDS reads behind them, so a copy
 // for the next iteration can stay in flight across this iteration's stores; the caller waits by
 // hand (vmcnt counts these copies, loads and stores together, in issue order).
+// (An LDS-direct load needs one wait state after the SALU write of M0: the s_nop.)
 template <int BYTES>
 __device__ __forceinline__ void lds_copy(const void* g, const void* lds) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
   if constexpr (BYTES == 16)
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory");
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory");
   else if constexpr (BYTES == 12)
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx3 %0, off" ::"v"(g), "s"(m0) : "memory");
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx3 %0, off" ::"v"(g), "s"(m0) : "memory");
   else if constexpr (BYTES == 4)
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0) : "memory");
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m0) : "memory");
   else
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_ushort %0, off" ::"v"(g), "s"(m0) : "memory");
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_ushort %0, off" ::"v"(g), "s"(m0) : "memory");
 }
 template <int N>
 __device__ __forceinline__ void wait_vm() {

@@ -238,6 +238,49 @@ def test_deterministic_repeat():
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
 
 
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("dt,records", [(32, False), (128, False), (128, True)])
+@pytest.mark.parametrize("pad", [0, 8])
+def test_lone_waves_repeat(bits, dt, records, pad):
+    """Regression test for missing wait states in hand-written instruction sequences (a VALU-written
+    SGPR read too soon, an M0 write before an LDS-direct load, an MFMA result read before it is
+    ready): such a read picks up a stale value only when nothing else runs between the two
+    instructions, i.e. when a wave has its SIMD to itself.  64 rows = 256 groups = one workgroup of
+    four waves on an otherwise idle GPU; the encode is repeated 64 times and every repeat must give
+    the same bytes, and the first must match the oracle outside the edge band."""
+    if records and bits == 8:
+        pytest.skip("the fork's records hold 1-4 bit codes")
+    hd, n_rows = 128, 64
+    x_np = synth.kv_tensor(7 * bits + dt + pad, 1, 1, 1, n_rows, hd).reshape(n_rows, hd)
+    signs = synth.signs(bits + dt, 2, dt)
+    flags = tq.TQ_BLOCKS if records else 0
+    qz = tq.Quantizer(hd, dt, bits, signs, flags=flags, x_dtype=tq.TQ_F16, norm_dtype=tq.TQ_F16,
+                      codebook="beta" if records else "gaussian")
+    ld = hd + pad
+    host = np.zeros((n_rows, ld), dtype=np.float16)
+    host[:, :hd] = x_np
+    x = torch.from_numpy(host).to(DEV)
+    units = n_rows * qz.units_per_row
+    nbytes = n_rows * (hd // 32) * qz.record_bytes() if records else units * qz.code_bytes()
+    outs = []
+    for _ in range(64):
+        codes = torch.full((nbytes,), 0xA5, dtype=torch.uint8, device=DEV)
+        norms = None if records else torch.full((units,), -7.0, dtype=torch.float16, device=DEV)
+        tq.tq_quantize(qz, x, n_rows, ld, codes, norms)
+        outs.append((codes, norms))
+    torch.cuda.synchronize()
+    for codes, norms in outs[1:]:
+        assert torch.equal(codes, outs[0][0])
+        if norms is not None:
+            assert torch.equal(norms, outs[0][1])
+    if not records:
+        cb = Codebook.build(bits, dt)
+        orc = quantize(x_np.astype(np.float64), signs, cb, norm_dtype=np.float16)
+        stats = check_codes(outs[0][0].cpu().numpy(), orc, cb, bits, dt)
+        assert_band_rate(stats, cb)
+        stats.update(check_norms(outs[0][1].cpu().numpy(), orc["norms"]))
+
 @pytest.fixture(scope="module")
 def qwen_full():
     from synth.workloads import qwen3_8b_kv
