@@ -152,16 +152,50 @@ __device__ __forceinline__ void stage_out(const uint8_t* tile, char* base, int64
 }
 
 // w = 2 w + [|y| > t]; returns the lane mask of the comparison.  On gfx950 a VALU read of an SGPR
-// (as carry-in or lane mask) needs two wait states after the VALU write of it: the s_nop supplies
-// them inside the block, and every later reader of the mask is further away still.
+// (as carry-in or lane mask) needs two wait states after a VALU write of that SGPR, but none after
+// an SALU write, and an SALU read of a VALU-written SGPR needs none either: the mask goes through
+// a scalar copy into another register pair, which the add and every later select read.
 __device__ __forceinline__ uint64_t shift_in_gt(uint32_t& w, float y, float t) {
-  uint64_t m, carry;
-  asm("v_cmp_gt_f32_e64 %1, |%3|, %4\n\t"
-      "s_nop 1\n\t"
-      "v_addc_co_u32_e64 %0, %2, %0, %0, %1"
-      : "+v"(w), "=&s"(m), "=&s"(carry)
+  uint64_t c, m, carry;
+  asm("v_cmp_gt_f32_e64 %1, |%4|, %5\n\t"
+      "s_mov_b64 %2, %1\n\t"
+      "v_addc_co_u32_e64 %0, %3, %0, %0, %2"
+      : "+v"(w), "=&s"(c), "=&s"(m), "=&s"(carry)
       : "v"(y), "v"(t));
   return m;
+}
+
+// The two magnitude bits of a 3-bit code: with c_k = [|y| > t_k] and t_0 < t_1 < t_2 (so
+// c_0 >= c_1 >= c_2), the magnitude index is c_0 + c_1 + c_2, whose high bit is c_1 and whose low
+// bit is c_0 ^ c_1 ^ c_2.  Three independent compares, the parity on the scalar unit, and each
+// mask read by the adds is written by a scalar instruction (no wait states; see shift_in_gt).
+__device__ __forceinline__ void shift_in_mag3(uint32_t& w1, uint32_t& w0, bool same, float y, const float* T) {
+  uint64_t c0, c1, c2, m1, m0, carry;
+  if (same) {
+    asm("v_cmp_gt_f32_e64 %2, |%7|, %9\n\t"
+        "v_cmp_gt_f32_e64 %1, |%7|, %8\n\t"
+        "v_cmp_gt_f32_e64 %3, |%7|, %10\n\t"
+        "s_mov_b64 %4, %2\n\t"
+        "s_xor_b64 %5, %1, %2\n\t"
+        "s_xor_b64 %5, %5, %3\n\t"
+        "v_addc_co_u32_e64 %0, %6, %0, %0, %4\n\t"
+        "v_addc_co_u32_e64 %0, %6, %0, %0, %5"
+        : "+v"(w1), "=&s"(c0), "=&s"(c1), "=&s"(c2), "=&s"(m1), "=&s"(m0), "=&s"(carry)
+        : "v"(y), "v"(T[0]), "v"(T[1]), "v"(T[2])
+        : "scc");
+  } else {
+    asm("v_cmp_gt_f32_e64 %3, |%8|, %10\n\t"
+        "v_cmp_gt_f32_e64 %2, |%8|, %9\n\t"
+        "v_cmp_gt_f32_e64 %4, |%8|, %11\n\t"
+        "s_mov_b64 %5, %3\n\t"
+        "s_xor_b64 %6, %2, %3\n\t"
+        "s_xor_b64 %6, %6, %4\n\t"
+        "v_addc_co_u32_e64 %0, %7, %0, %0, %5\n\t"
+        "v_addc_co_u32_e64 %1, %7, %1, %1, %6"
+        : "+v"(w1), "+v"(w0), "=&s"(c0), "=&s"(c1), "=&s"(c2), "=&s"(m1), "=&s"(m0), "=&s"(carry)
+        : "v"(y), "v"(T[0]), "v"(T[1]), "v"(T[2])
+        : "scc");
+  }
 }
 
 __device__ __forceinline__ float select_mask(uint64_t m, float if_false, float if_true) {
@@ -193,8 +227,7 @@ __device__ __forceinline__ void code_chain(uint32_t* word, int j, float y, const
     shift_in_gt(word[(p_top - 1) >> 5], y, T[0]);
   } else if constexpr (BITS == 3) {
     const float ym = (p_top & 31) == 0 ? __builtin_fabsf(y) : y;
-    const uint64_t c1 = shift_in_gt(word[(p_top - 1) >> 5], ym, T[1]);
-    shift_in_gt(word[(p_top - 2) >> 5], ym, select_mask(c1, T[0], T[2]));
+    shift_in_mag3(word[(p_top - 1) >> 5], word[(p_top - 2) >> 5], (p_top - 1) >> 5 == (p_top - 2) >> 5, ym, T);
   } else if constexpr (BITS == 4) {
     const uint64_t c1 = shift_in_gt(word[(p_top - 1) >> 5], y, T[3]);
     const float lo = select_mask(c1, T[0], T[4]);
@@ -950,6 +983,15 @@ int64_t grid_for(int64_t n_groups, int per_cu) {
   return need < cap ? need : cap;
 }
 
+// The 3-bit block-32 encode (fp16 rows, code and norm planes) runs fastest with five workgroups per
+// compute unit: on a Qwen3-8B-shaped half-cache 255 us, against 268 us with the eight that its
+// 59 VGPRs and 20 KiB of LDS would otherwise allow, 264 with six and 258 with four; more waves in
+// flight slow its mixed read/write stream.  Dynamic LDS that the kernel never touches holds it at
+// five (32 KiB less a margin per workgroup).  The 4- and 8-bit encodes, VALU-bound, run slower
+// with fewer waves and get none.
+constexpr unsigned kEnc3StageLds = kWaves * 64 * 80;  // the stage tile of encode_mfma_kernel
+constexpr unsigned kEnc3LdsPad = 160u * 1024u / 5u - kEnc3StageLds - 512u;
+
 // fp16 rows: the MFMA kernel for every unit length and output form; fp32 rows: the one-group-per-lane
 // kernel (its transform is exact fp32 arithmetic on the fp32 inputs).
 template <int BITS, int LPU, bool CONTIG>
@@ -963,8 +1005,9 @@ hipError_t encode_dispatch_dtype(const tq_config& cfg, const EncodeArgs& a, hipS
       hipLaunchKernelGGL((encode_mfma_kernel<BITS, LPU, false, CONTIG, true>), grid, block, 0, s, a);
     return hipGetLastError();
   }
-  if (!in32 && !n32) hipLaunchKernelGGL((encode_mfma_kernel<BITS, LPU, false, CONTIG, false>), grid, block, 0, s, a);
-  if (!in32 && n32) hipLaunchKernelGGL((encode_mfma_kernel<BITS, LPU, true, CONTIG, false>), grid, block, 0, s, a);
+  const unsigned pad = (BITS == 3 && LPU == 1) ? kEnc3LdsPad : 0u;
+  if (!in32 && !n32) hipLaunchKernelGGL((encode_mfma_kernel<BITS, LPU, false, CONTIG, false>), grid, block, pad, s, a);
+  if (!in32 && n32) hipLaunchKernelGGL((encode_mfma_kernel<BITS, LPU, true, CONTIG, false>), grid, block, pad, s, a);
   if (in32 && !n32) hipLaunchKernelGGL((encode_kernel<BITS, LPU, true, false, CONTIG, false>), grid, block, 0, s, a);
   if (in32 && n32) hipLaunchKernelGGL((encode_kernel<BITS, LPU, true, true, CONTIG, false>), grid, block, 0, s, a);
   return hipGetLastError();
