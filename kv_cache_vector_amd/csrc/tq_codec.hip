@@ -983,14 +983,27 @@ int64_t grid_for(int64_t n_groups, int per_cu) {
   return need < cap ? need : cap;
 }
 
-// The 3-bit block-32 encode (fp16 rows, code and norm planes) runs fastest with five workgroups per
-// compute unit: on a Qwen3-8B-shaped half-cache 255 us, against 268 us with the eight that its
-// 59 VGPRs and 20 KiB of LDS would otherwise allow, 264 with six and 258 with four; more waves in
-// flight slow its mixed read/write stream.  Dynamic LDS that the kernel never touches holds it at
-// five (32 KiB less a margin per workgroup).  The 4- and 8-bit encodes, VALU-bound, run slower
+// The 3-bit block-32 kernels (fp16 rows, code and norm planes) run fastest with five workgroups per
+// compute unit: on a Qwen3-8B-shaped half-cache the encode takes 255 us against 268 us with the
+// eight that its 59 VGPRs and 20 KiB of LDS would otherwise allow (264 with six, 258 with four), and
+// the decode 248 us against 257 with six; more waves in flight slow their mixed read/write streams.
+// Dynamic LDS that the kernel never touches holds it at five.  The 4- and 8-bit kernels run slower
 // with fewer waves and get none.
-constexpr unsigned kEnc3StageLds = kWaves * 64 * 80;  // the stage tile of encode_mfma_kernel
-constexpr unsigned kEnc3LdsPad = 160u * 1024u / 5u - kEnc3StageLds - 512u;
+constexpr unsigned kLdsPerCu = 160u * 1024u;
+constexpr unsigned kResident3 = 5;
+
+// Dynamic LDS bytes that leave room for `wgs` workgroups of `kernel` per compute unit (once per
+// instantiation: the kernel's static LDS is read from its attributes).
+template <typename K>
+unsigned lds_pad(K kernel, unsigned wgs) {
+  hipFuncAttributes attr;
+  if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(kernel)) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0u;
+  }
+  const size_t per = kLdsPerCu / wgs - 512u;  // a margin under the per-workgroup share
+  return attr.sharedSizeBytes < per ? (unsigned)(per - attr.sharedSizeBytes) : 0u;
+}
 
 // fp16 rows: the MFMA kernel for every unit length and output form; fp32 rows: the one-group-per-lane
 // kernel (its transform is exact fp32 arithmetic on the fp32 inputs).
@@ -1005,9 +1018,16 @@ hipError_t encode_dispatch_dtype(const tq_config& cfg, const EncodeArgs& a, hipS
       hipLaunchKernelGGL((encode_mfma_kernel<BITS, LPU, false, CONTIG, true>), grid, block, 0, s, a);
     return hipGetLastError();
   }
-  const unsigned pad = (BITS == 3 && LPU == 1) ? kEnc3LdsPad : 0u;
-  if (!in32 && !n32) hipLaunchKernelGGL((encode_mfma_kernel<BITS, LPU, false, CONTIG, false>), grid, block, pad, s, a);
-  if (!in32 && n32) hipLaunchKernelGGL((encode_mfma_kernel<BITS, LPU, true, CONTIG, false>), grid, block, pad, s, a);
+  if (!in32 && !n32) {
+    static const unsigned pad =
+        BITS == 3 && LPU == 1 ? lds_pad(encode_mfma_kernel<BITS, LPU, false, CONTIG, false>, kResident3) : 0u;
+    hipLaunchKernelGGL((encode_mfma_kernel<BITS, LPU, false, CONTIG, false>), grid, block, pad, s, a);
+  }
+  if (!in32 && n32) {
+    static const unsigned pad =
+        BITS == 3 && LPU == 1 ? lds_pad(encode_mfma_kernel<BITS, LPU, true, CONTIG, false>, kResident3) : 0u;
+    hipLaunchKernelGGL((encode_mfma_kernel<BITS, LPU, true, CONTIG, false>), grid, block, pad, s, a);
+  }
   if (in32 && !n32) hipLaunchKernelGGL((encode_kernel<BITS, LPU, true, false, CONTIG, false>), grid, block, 0, s, a);
   if (in32 && n32) hipLaunchKernelGGL((encode_kernel<BITS, LPU, true, true, CONTIG, false>), grid, block, 0, s, a);
   return hipGetLastError();
@@ -1039,7 +1059,12 @@ hipError_t decode_dispatch_dtype(const tq_config& cfg, const DecodeArgs& a, tq_d
       hipLaunchKernelGGL((decode_mfma_kernel<BITS, LPU, false, false, NC, CONTIG, true>), grid, block, 0, s, a);
     return hipGetLastError();
   }
-  if (!o32 && !n32) hipLaunchKernelGGL((decode_mfma_kernel<BITS, LPU, false, false, NC, CONTIG, false>), grid, block, 0, s, a);
+  if (!o32 && !n32) {
+    static const unsigned pad = BITS == 3 && LPU == 1
+                                    ? lds_pad(decode_mfma_kernel<BITS, LPU, false, false, NC, CONTIG, false>, kResident3)
+                                    : 0u;
+    hipLaunchKernelGGL((decode_mfma_kernel<BITS, LPU, false, false, NC, CONTIG, false>), grid, block, pad, s, a);
+  }
   if (!o32 && n32) hipLaunchKernelGGL((decode_mfma_kernel<BITS, LPU, false, true, NC, CONTIG, false>), grid, block, 0, s, a);
   if (o32 && !n32) hipLaunchKernelGGL((decode_mfma_kernel<BITS, LPU, true, false, NC, CONTIG, false>), grid, block, 0, s, a);
   if (o32 && n32) hipLaunchKernelGGL((decode_mfma_kernel<BITS, LPU, true, true, NC, CONTIG, false>), grid, block, 0, s, a);
