@@ -987,10 +987,12 @@ int64_t grid_for(int64_t n_groups, int per_cu) {
 // compute unit: on a Qwen3-8B-shaped half-cache the encode takes 255 us against 268 us with the
 // eight that its 59 VGPRs and 20 KiB of LDS would otherwise allow (264 with six, 258 with four), and
 // the decode 248 us against 257 with six; more waves in flight slow their mixed read/write streams.
-// Dynamic LDS that the kernel never touches holds it at five.  The 4- and 8-bit kernels run slower
-// with fewer waves and get none.
+// Dynamic LDS that the kernel never touches holds it at five.  The 8-bit block-32 decode likewise
+// runs best with four (302 against 312 us with the five its LDS allows).  The 4-bit kernels, the
+// 8-bit encode and the fork's records run slower with fewer waves (records by 8-40 %) and get none.
 constexpr unsigned kLdsPerCu = 160u * 1024u;
 constexpr unsigned kResident3 = 5;
+constexpr unsigned kResident8 = 4;
 
 // Dynamic LDS bytes that leave room for `wgs` workgroups of `kernel` per compute unit (once per
 // instantiation: the kernel's static LDS is read from its attributes).
@@ -1060,9 +1062,10 @@ hipError_t decode_dispatch_dtype(const tq_config& cfg, const DecodeArgs& a, tq_d
     return hipGetLastError();
   }
   if (!o32 && !n32) {
-    static const unsigned pad = BITS == 3 && LPU == 1
-                                    ? lds_pad(decode_mfma_kernel<BITS, LPU, false, false, NC, CONTIG, false>, kResident3)
-                                    : 0u;
+    static const unsigned pad =
+        LPU == 1 && (BITS == 3 || BITS == 8)
+            ? lds_pad(decode_mfma_kernel<BITS, LPU, false, false, NC, CONTIG, false>, BITS == 3 ? kResident3 : kResident8)
+            : 0u;
     hipLaunchKernelGGL((decode_mfma_kernel<BITS, LPU, false, false, NC, CONTIG, false>), grid, block, pad, s, a);
   }
   if (!o32 && n32) hipLaunchKernelGGL((decode_mfma_kernel<BITS, LPU, false, true, NC, CONTIG, false>), grid, block, 0, s, a);
