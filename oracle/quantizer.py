@@ -16,7 +16,7 @@ Dequantize reverses it: c[idx] -> D H c (H is its own inverse) -> optional
 QJL correction -> optional norm correction -> times the stored n
 ([Scratch] §2 and §6).
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
   * u is formed with the unrounded n; decode multiplies by the stored n.
   * a zero unit stores n = 0 and u = 0 (so idx = bucketize(0) = L/2 - 1).
   * stored code: sign-magnitude form of idx.  With h = L/2, idx >= h stores
