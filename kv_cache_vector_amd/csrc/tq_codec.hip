@@ -26,6 +26,8 @@
 // re-deals the 16-byte chunks so that each lane ends up with its own group.
 #include <hip/hip_fp16.h>
 
+#include <atomic>
+
 #include "tq_device.h"
 #include "tq_internal.h"
 
@@ -994,17 +996,27 @@ constexpr unsigned kLdsPerCu = 160u * 1024u;
 constexpr unsigned kResident3 = 5;
 constexpr unsigned kResident8 = 4;
 
-// Dynamic LDS bytes that leave room for `wgs` workgroups of `kernel` per compute unit (once per
-// instantiation: the kernel's static LDS is read from its attributes).
+// Dynamic LDS bytes that leave room for `wgs` workgroups of `kernel` per compute unit.  The kernel's
+// static LDS is read from its attributes once and cached; while the launch stream is being captured
+// into a graph before that, the launch goes without the padding (same results, slower).
 template <typename K>
-unsigned lds_pad(K kernel, unsigned wgs) {
+unsigned lds_pad(std::atomic<int>& cache, K kernel, unsigned wgs, hipStream_t s) {
+  const int known = cache.load(std::memory_order_relaxed);
+  if (known >= 0) return (unsigned)known;
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &st) != hipSuccess || st != hipStreamCaptureStatusNone) {
+    (void)hipGetLastError();
+    return 0u;
+  }
   hipFuncAttributes attr;
   if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(kernel)) != hipSuccess) {
     (void)hipGetLastError();
     return 0u;
   }
   const size_t per = kLdsPerCu / wgs - 512u;  // a margin under the per-workgroup share
-  return attr.sharedSizeBytes < per ? (unsigned)(per - attr.sharedSizeBytes) : 0u;
+  const int pad = attr.sharedSizeBytes < per ? (int)(per - attr.sharedSizeBytes) : 0;
+  cache.store(pad, std::memory_order_relaxed);
+  return (unsigned)pad;
 }
 
 // fp16 rows: the MFMA kernel for every unit length and output form; fp32 rows: the one-group-per-lane
@@ -1021,13 +1033,15 @@ hipError_t encode_dispatch_dtype(const tq_config& cfg, const EncodeArgs& a, hipS
     return hipGetLastError();
   }
   if (!in32 && !n32) {
-    static const unsigned pad =
-        BITS == 3 && LPU == 1 ? lds_pad(encode_mfma_kernel<BITS, LPU, false, CONTIG, false>, kResident3) : 0u;
+    static std::atomic<int> known{-1};
+    const unsigned pad =
+        BITS == 3 && LPU == 1 ? lds_pad(known, encode_mfma_kernel<BITS, LPU, false, CONTIG, false>, kResident3, s) : 0u;
     hipLaunchKernelGGL((encode_mfma_kernel<BITS, LPU, false, CONTIG, false>), grid, block, pad, s, a);
   }
   if (!in32 && n32) {
-    static const unsigned pad =
-        BITS == 3 && LPU == 1 ? lds_pad(encode_mfma_kernel<BITS, LPU, true, CONTIG, false>, kResident3) : 0u;
+    static std::atomic<int> known{-1};
+    const unsigned pad =
+        BITS == 3 && LPU == 1 ? lds_pad(known, encode_mfma_kernel<BITS, LPU, true, CONTIG, false>, kResident3, s) : 0u;
     hipLaunchKernelGGL((encode_mfma_kernel<BITS, LPU, true, CONTIG, false>), grid, block, pad, s, a);
   }
   if (in32 && !n32) hipLaunchKernelGGL((encode_kernel<BITS, LPU, true, false, CONTIG, false>), grid, block, 0, s, a);
@@ -1062,10 +1076,11 @@ hipError_t decode_dispatch_dtype(const tq_config& cfg, const DecodeArgs& a, tq_d
     return hipGetLastError();
   }
   if (!o32 && !n32) {
-    static const unsigned pad =
-        LPU == 1 && (BITS == 3 || BITS == 8)
-            ? lds_pad(decode_mfma_kernel<BITS, LPU, false, false, NC, CONTIG, false>, BITS == 3 ? kResident3 : kResident8)
-            : 0u;
+    static std::atomic<int> known{-1};
+    const unsigned pad = LPU == 1 && (BITS == 3 || BITS == 8)
+                             ? lds_pad(known, decode_mfma_kernel<BITS, LPU, false, false, NC, CONTIG, false>,
+                                       BITS == 3 ? kResident3 : kResident8, s)
+                             : 0u;
     hipLaunchKernelGGL((decode_mfma_kernel<BITS, LPU, false, false, NC, CONTIG, false>), grid, block, pad, s, a);
   }
   if (!o32 && n32) hipLaunchKernelGGL((decode_mfma_kernel<BITS, LPU, false, true, NC, CONTIG, false>), grid, block, 0, s, a);

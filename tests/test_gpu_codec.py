@@ -281,6 +281,45 @@ def test_lone_waves_repeat(bits, dt, records, pad):
         assert_band_rate(stats, cb)
         stats.update(check_norms(outs[0][1].cpu().numpy(), orc["norms"]))
 
+
+def test_graph_capture_codec():
+    """Encode and decode captured in a HIP graph: several replays, with eager work in between, give the
+    bytes of an eager call.  The 3-bit block-32 encode with fp32 norms and strided rows is launched
+    here for the first time inside the capture, where it runs without the residency padding."""
+    hd, n_rows, ld = 128, 1000, 136
+    x_np = synth.kv_tensor(91, 1, 1, 1, n_rows, hd).reshape(n_rows, hd)
+    host = np.zeros((n_rows, ld), dtype=np.float16)
+    host[:, :hd] = x_np
+    x = torch.from_numpy(host).to(DEV)
+    qz = tq.Quantizer(hd, 32, 3, synth.signs(91, 2, 32), norm_dtype=tq.TQ_F32)
+    units = n_rows * qz.units_per_row
+    codes = torch.zeros(units * qz.code_bytes(), dtype=torch.uint8, device=DEV)
+    norms = torch.zeros(units, dtype=torch.float32, device=DEV)
+    y = torch.zeros((n_rows, hd), dtype=torch.float16, device=DEV)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        tq.tq_quantize(qz, x, n_rows, ld, codes, norms, stream=stream)
+        tq.tq_dequantize(qz, codes, norms, None, None, n_rows, y, tq.TQ_F16, hd, stream=stream)
+    torch.cuda.synchronize()
+    ref_codes = torch.empty_like(codes)
+    ref_norms = torch.empty_like(norms)
+    ref_y = torch.empty_like(y)
+    tq.tq_quantize(qz, x, n_rows, ld, ref_codes, ref_norms)
+    tq.tq_dequantize(qz, ref_codes, ref_norms, None, None, n_rows, ref_y, tq.TQ_F16, hd)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        codes.zero_()
+        norms.zero_()
+        y.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(codes, ref_codes) and torch.equal(norms, ref_norms) and torch.equal(y, ref_y)
+        tq.tq_quantize(qz, x, n_rows, ld, ref_codes, ref_norms)  # eager work between the replays
+        torch.cuda.synchronize()
+
 @pytest.fixture(scope="module")
 def qwen_full():
     from synth.workloads import qwen3_8b_kv
