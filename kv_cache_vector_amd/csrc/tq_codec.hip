@@ -200,27 +200,22 @@ __device__ __forceinline__ void shift_in_mag3(uint32_t& w1, uint32_t& w0, bool s
   }
 }
 
-__device__ __forceinline__ float select_mask(uint64_t m, float if_false, float if_true) {
-  float r;
-  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(if_false), "v"(if_true), "s"(m));
-  return r;
-}
-
 // w = (w << 1) | signbit(y)
 __device__ __forceinline__ void shift_in_sign(uint32_t& w, float y) {
   w = __builtin_amdgcn_alignbit(w, __builtin_bit_cast(uint32_t, y), 31);
 }
 
-// Shift the code of one coordinate, most significant bit first, into the
-// packed words.  Bit p of the 32-coordinate group (p = BITS*j + k) lives in
-// word p/32; since the caller walks j downwards and the bits of one code
-// from the top, every word receives its bits from bit 31 down to bit 0.
+// Shift the code of one coordinate (1 to 3 bits; 4 and 8 bits use the bucket
+// table) most significant bit first into the packed words.  Bit p of the
+// 32-coordinate group (p = BITS*j + k) lives in word p/32; since the caller
+// walks j downwards and the bits of one code from the top, every word
+// receives its bits from bit 31 down to bit 0.
 //
 // y may come straight from an MFMA, and inline asm is exempt from the compiler's
 // checks of MFMA-result hazards, so every compare must depend on a compiler-made
-// read of y: the sign shift (same word, or the select of its threshold), or,
-// where a 3-bit code's first magnitude bit starts the next lower word, a copy
-// of |y| made here (one instruction per 32 bits).
+// read of y: the sign shift into the same word, or, where a 3-bit code's first
+// magnitude bit starts the next lower word, a copy of |y| made here (one
+// instruction per 32 bits).
 template <int BITS>
 __device__ __forceinline__ void code_chain(uint32_t* word, int j, float y, const float* T) {
   const int p_top = BITS * j + BITS - 1;
@@ -230,12 +225,6 @@ __device__ __forceinline__ void code_chain(uint32_t* word, int j, float y, const
   } else if constexpr (BITS == 3) {
     const float ym = (p_top & 31) == 0 ? __builtin_fabsf(y) : y;
     shift_in_mag3(word[(p_top - 1) >> 5], word[(p_top - 2) >> 5], (p_top - 1) >> 5 == (p_top - 2) >> 5, ym, T);
-  } else if constexpr (BITS == 4) {
-    const uint64_t c1 = shift_in_gt(word[(p_top - 1) >> 5], y, T[3]);
-    const float lo = select_mask(c1, T[0], T[4]);
-    const float hi = select_mask(c1, T[2], T[6]);
-    const uint64_t c2 = shift_in_gt(word[(p_top - 2) >> 5], y, select_mask(c1, T[1], T[5]));
-    shift_in_gt(word[(p_top - 3) >> 5], y, select_mask(c2, lo, hi));
   }
 }
 
@@ -302,47 +291,108 @@ __device__ __forceinline__ float get_record(const uint16_t* r, uint32_t* word) {
   return __half2float(__ushort_as_half(r[0]));
 }
 
-// 8-bit bucketize tables in LDS: edges t_0 = -1 (sentinel below |u|), t_1..t_127, t_128 = +inf,
-// and for each bin of |u| (bins a third of the narrowest cell, so two neighbouring bins hold at
-// most one edge) the number of edges below the bin's lower end, found by binary search.
-__device__ __forceinline__ void setup_bins8(const EncodeArgs& a, float* edge8, uint8_t* bin8) {
-  for (int i = threadIdx.x; i < 129; i += kBlock) edge8[i] = i == 0 ? -1.0f : a.thr[i - 1];
+// Bucket tables of the 4- and 8-bit encoders.  |u| = |y| / n is binned uniformly with kb = bin_scale / n
+// bins per unit of |y| (bin_scale is 1.6 bins per narrowest cell, so consecutive edges lie at least 1.6
+// bins apart).  The bin index of a coordinate is |y| kb rounded or truncated to an integer, so when it
+// comes out as i, |y| kb lies in [i - 0.51, i + 1.01]: a window of 1.52 bins that holds at most one
+// edge.  Entry i holds the number m0 of edges at or below the window's start and the first edge e above
+// it (+inf past the last one); the magnitude is m0 + [|y| > e n], the comparison the narrow codes make
+// against t n, so the codes do not depend on the binning.  Entries: 256 at 4 bits (every index a
+// saturating byte conversion can give), n_bins at 8 bits (indices clamped to the last, whose window
+// starts above every edge).
+template <int BITS>
+__device__ __forceinline__ void setup_lut(const EncodeArgs& a, float* edge, uint2* lut) {
+  constexpr int H = 1 << (BITS - 1);  // edges t_1 .. t_{H-1}, then thr[H-1] = +inf
+  if constexpr (BITS == 4) {  // seven edges: counted straight from the arguments
+    for (int b = threadIdx.x; b < kLutEntries4; b += kBlock) {
+      const float x = ((float)b - 0.51f) / a.bin_scale;
+      uint32_t m0 = 0;
+      float e = __builtin_inff();
+#pragma unroll
+      for (int k = 0; k < H - 1; ++k) {
+        const float t = a.thr[k];
+        if (t <= x)
+          ++m0;
+        else
+          e = __builtin_fminf(e, t);
+      }
+      lut[b] = make_uint2(__builtin_bit_cast(uint32_t, e), m0);
+    }
+    __syncthreads();
+    return;
+  }
+  for (int i = threadIdx.x; i < H; i += kBlock) edge[i] = a.thr[i];
   __syncthreads();
   for (int b = threadIdx.x; b < a.n_bins; b += kBlock) {
-    const float x = (float)b / a.bin_scale;
-    int lo = 0, hi = 127;  // count of t_1..t_127 below x
+    const float x = ((float)b - 0.51f) / a.bin_scale;
+    int lo = 0, hi = H - 1;  // first k with t_k > x
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
-      if (edge8[mid + 1] < x)
+      if (edge[mid] <= x)
         lo = mid + 1;
       else
         hi = mid;
     }
-    bin8[b] = (uint8_t)lo;
+    lut[b] = make_uint2(__builtin_bit_cast(uint32_t, edge[lo]), (uint32_t)lo);
   }
   __syncthreads();
 }
 
-// 8-bit code of rotated coordinate y of a unit with norm n (kb = bins per unit of |y|):
-// the bin of |u| = |y| / n (possibly one off), then the two edges around the bin's count
-// give magnitude = #{t_i < |u|} exactly, compared as |y| against t n like the narrow codes.
-__device__ __forceinline__ uint32_t code8(float y, float n, float kb, float top, const float* edge8,
-                                          const uint8_t* bin8) {
-  const float ay = __builtin_fabsf(y);
-  const int m0 = bin8[(int)__builtin_fminf(ay * kb, top)];
-  const float lo = edge8[m0], hi = edge8[m0 + 1];
-  const uint32_t mag = (uint32_t)(m0 + (ay > hi * n ? 1 : 0) - (ay <= lo * n ? 1 : 0));
-  return ((__builtin_bit_cast(uint32_t, y) >> 31) << 7) | (mag & 127u);
+// w = (w << SHIFT) + m0 + [|y| > t], the comparison's lane mask going through a scalar copy (see
+// shift_in_gt).
+template <int SHIFT>
+__device__ __forceinline__ void shift_in_mag_lut(uint32_t& w, uint32_t m0, float y, float t) {
+  uint64_t c, m, carry;
+  asm("v_cmp_gt_f32_e64 %1, |%4|, %5\n\t"
+      "s_mov_b64 %2, %1\n\t"
+      "v_lshl_add_u32 %0, %0, %7, %6\n\t"
+      "v_addc_co_u32_e64 %0, %3, %0, 0, %2"
+      : "+v"(w), "=&s"(c), "=&s"(m), "=&s"(carry)
+      : "v"(y), "v"(t), "v"(m0), "i"(SHIFT));
+}
+
+// The bucket-table entry of coordinate y (kb = bins per unit of |y|; top: the last entry at 8 bits).
+template <int BITS>
+__device__ __forceinline__ uint2 lut_entry(float y, float kb, float top, const uint2* lut) {
+  const float u = __builtin_fabsf(y) * kb;
+  if constexpr (BITS == 4)
+    return lut[__builtin_amdgcn_cvt_pk_u8_f32(u, 0, 0u)];
+  else
+    return lut[(uint32_t)__builtin_fminf(u, top)];
+}
+
+// Codes of coordinates J-1 .. 0 of v (sign, then magnitude), shifted into their words most significant
+// bit first like code_chain (BITS divides 32, so a code never straddles two words).  The table reads go
+// out four at a time ahead of the compares that use them (the 4-bit block-32 encode measured 2-4 %
+// faster than with one; 8 and 16 no better).  Each compare reads y after the compiler-made product
+// |y| kb that its threshold depends on.
+template <int BITS, int J>
+__device__ __forceinline__ void code_lut(uint32_t* word, const float* v, float n, float kb, float top,
+                                         const uint2* lut) {
+  constexpr int LB = 4;
+#pragma unroll
+  for (int j0 = J - 1; j0 >= 0; j0 -= LB) {
+    uint2 e[LB];
+#pragma unroll
+    for (int k = 0; k < LB; ++k) e[k] = lut_entry<BITS>(v[j0 - k], kb, top, lut);
+#pragma unroll
+    for (int k = 0; k < LB; ++k) {
+      const int j = j0 - k;
+      uint32_t& w = word[(BITS * j) >> 5];
+      shift_in_sign(w, v[j]);
+      shift_in_mag_lut<BITS - 1>(w, e[k].y, v[j], __builtin_bit_cast(float, e[k].x) * n);
+    }
+  }
 }
 
 template <int BITS, int LPU, bool IN_F32, bool NORM_F32, bool CONTIG, bool AOS>
 __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
   static_assert(!(AOS && NORM_F32), "records carry fp16 norms");
   static_assert(BITS <= 4 || BITS == 8, "1..4 or 8 bits");
-  constexpr bool B8 = BITS == 8;
-  __shared__ float edge8[B8 ? 132 : 1];
-  __shared__ uint8_t bin8[B8 ? kMaxBins8 : 1];
-  if constexpr (B8) setup_bins8(a, edge8, bin8);
+  constexpr bool LUT = BITS == 4 || BITS == 8;
+  __shared__ float edge[BITS == 8 ? 128 : 1];
+  __shared__ uint2 lut[BITS == 4 ? kLutEntries4 : BITS == 8 ? kMaxBins8 : 1];
+  if constexpr (LUT) setup_lut<BITS>(a, edge, lut);
   constexpr int CH = IN_F32 ? 8 : 4;  // 16-byte chunks per group
   constexpr int PITCH = 16 * CH + 16;  // LDS bytes per staged group (padded against bank conflicts)
   __shared__ __attribute__((aligned(16))) uint8_t stage[kWaves][64 * PITCH];
@@ -403,11 +453,10 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
     uint32_t word[BITS];
 #pragma unroll
     for (int k = 0; k < BITS; ++k) word[k] = 0u;
-    if constexpr (B8) {
+    if constexpr (LUT) {
       const float kb = n > 0.0f ? a.bin_scale / n : 0.0f;
       const float top = (float)(a.n_bins - 1);
-#pragma unroll
-      for (int j = 0; j < 32; ++j) word[j >> 2] |= code8(v[j], n, kb, top, edge8, bin8) << (8 * (j & 3));
+      code_lut<BITS, 32>(word, v, n, kb, top, lut);
     } else {
 #pragma unroll
       for (int j = 31; j >= 0; --j) code_chain<BITS>(word, j, v[j], T);
@@ -507,9 +556,10 @@ __global__ __launch_bounds__(kBlock) void encode_mfma_kernel(EncodeArgs a) {
   constexpr int SEGW = (16 * BITS + 31) / 32;  // words of one lane's 16-code segment
   constexpr bool B8 = BITS == 8;
   __shared__ __attribute__((aligned(16))) uint8_t stage[kWaves][64 * PITCH];
-  __shared__ float edge8[B8 ? 132 : 1];
-  __shared__ uint8_t bin8[B8 ? kMaxBins8 : 1];
-  if constexpr (B8) setup_bins8(a, edge8, bin8);
+  constexpr bool LUT = BITS == 4 || BITS == 8;
+  __shared__ float edge[BITS == 8 ? 128 : 1];
+  __shared__ uint2 lut[BITS == 4 ? kLutEntries4 : BITS == 8 ? kMaxBins8 : 1];
+  if constexpr (LUT) setup_lut<BITS>(a, edge, lut);
   // 4 and 8 bits: the next tile's loads go out before this tile's compute and stores (measured
   // faster at 4 and 8 bits, slower at 3)
   constexpr bool PIPE = BITS == 4 || BITS == 8;
@@ -656,11 +706,10 @@ __global__ __launch_bounds__(kBlock) void encode_mfma_kernel(EncodeArgs a) {
       nrm[s] = n;
 #pragma unroll
       for (int k = 0; k < SEGW; ++k) seg[s][k] = 0u;
-      if constexpr (B8) {
+      if constexpr (LUT) {
         const float kb = n > 0.0f ? a.bin_scale / n : 0.0f;
         const float top = (float)(a.n_bins - 1);
-#pragma unroll
-        for (int j = 0; j < 16; ++j) seg[s][j >> 2] |= code8(yv[j], n, kb, top, edge8, bin8) << (8 * (j & 3));
+        code_lut<BITS, 16>(seg[s], yv, n, kb, top, lut);
       } else {
         float T[7];
 #pragma unroll
@@ -989,11 +1038,14 @@ int64_t grid_for(int64_t n_groups, int per_cu) {
 // compute unit: on a Qwen3-8B-shaped half-cache the encode takes 255 us against 268 us with the
 // eight that its 59 VGPRs and 20 KiB of LDS would otherwise allow (264 with six, 258 with four), and
 // the decode 248 us against 257 with six; more waves in flight slow their mixed read/write streams.
-// Dynamic LDS that the kernel never touches holds it at five.  The 8-bit block-32 decode likewise
-// runs best with four (302 against 312 us with the five its LDS allows).  The 4-bit kernels, the
-// 8-bit encode and the fork's records run slower with fewer waves (records by 8-40 %) and get none.
+// Dynamic LDS that the kernel never touches holds it at five.  The 4-bit block-32 encode (bucket
+// table) also runs best with five: 270-276 us in a captured step against 288 with the seven its 71
+// VGPRs and 22 KiB of LDS allow.  The 8-bit block-32 decode likewise runs best with four (302
+// against 312 us with the five its LDS allows).  The 4-bit decode, the 8-bit encode and the fork's
+// records run slower or no faster with fewer waves (records by 8-40 %) and get none.
 constexpr unsigned kLdsPerCu = 160u * 1024u;
 constexpr unsigned kResident3 = 5;
+constexpr unsigned kResident4 = 5;
 constexpr unsigned kResident8 = 4;
 
 // Dynamic LDS bytes that leave room for `wgs` workgroups of `kernel` per compute unit.  The kernel's
@@ -1032,16 +1084,17 @@ hipError_t encode_dispatch_dtype(const tq_config& cfg, const EncodeArgs& a, hipS
       hipLaunchKernelGGL((encode_mfma_kernel<BITS, LPU, false, CONTIG, true>), grid, block, 0, s, a);
     return hipGetLastError();
   }
+  constexpr unsigned kRes = BITS == 3 ? kResident3 : BITS == 4 ? kResident4 : 0;
   if (!in32 && !n32) {
     static std::atomic<int> known{-1};
     const unsigned pad =
-        BITS == 3 && LPU == 1 ? lds_pad(known, encode_mfma_kernel<BITS, LPU, false, CONTIG, false>, kResident3, s) : 0u;
+        kRes && LPU == 1 ? lds_pad(known, encode_mfma_kernel<BITS, LPU, false, CONTIG, false>, kRes, s) : 0u;
     hipLaunchKernelGGL((encode_mfma_kernel<BITS, LPU, false, CONTIG, false>), grid, block, pad, s, a);
   }
   if (!in32 && n32) {
     static std::atomic<int> known{-1};
     const unsigned pad =
-        BITS == 3 && LPU == 1 ? lds_pad(known, encode_mfma_kernel<BITS, LPU, true, CONTIG, false>, kResident3, s) : 0u;
+        kRes && LPU == 1 ? lds_pad(known, encode_mfma_kernel<BITS, LPU, true, CONTIG, false>, kRes, s) : 0u;
     hipLaunchKernelGGL((encode_mfma_kernel<BITS, LPU, true, CONTIG, false>), grid, block, pad, s, a);
   }
   if (in32 && !n32) hipLaunchKernelGGL((encode_kernel<BITS, LPU, true, false, CONTIG, false>), grid, block, 0, s, a);

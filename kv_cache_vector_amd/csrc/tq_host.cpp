@@ -360,21 +360,20 @@ void fill_thr(const tq_codebook& cb, T (&thr)[N]) {
   for (int k = 0; k + 1 < h && k < N; ++k) thr[k] = (T)cb.unit_bounds[h + k];  // edges above 0, ascending
 }
 
-// Bucket index of the 8-bit encoder: |u| (unit scale) is binned uniformly with
-// bins a third of the narrowest cell, so that any two neighbouring bins hold at
-// most one cell edge; a table gives the number of edges below each bin, and two
-// comparisons against the edges next to that count fix the exact cell even if
-// the bin was computed one off.
+// Bins of the 4- and 8-bit encoders' bucket tables: consecutive edges (the
+// first one and 0 too) lie at least 1.6 bins apart, so any window of 1.52 bins
+// holds at most one edge; the last entry is the first bin whose window (from
+// 0.51 below it) starts at or above the top edge.
 void fill_bins(const tq_codebook& cb, tq::EncodeArgs& a) {
   a.bin_scale = 0.0f;
   a.n_bins = 0;
-  if (cb.bits != 8) return;
-  const int h = 128;
+  if (cb.bits != 4 && cb.bits != 8) return;
+  const int h = 1 << (cb.bits - 1);
   double w = cb.unit_bounds[h];  // the cell [0, t_1]
   for (int k = 1; k + 1 < h; ++k) w = std::min(w, cb.unit_bounds[h + k] - cb.unit_bounds[h + k - 1]);
-  const double scale = 3.0 / w;
+  const double scale = 1.6 / w;
   a.bin_scale = (float)scale;
-  a.n_bins = (int32_t)std::ceil((cb.unit_bounds[2 * h - 2] + w) * scale) + 1;
+  a.n_bins = (int32_t)std::ceil(cb.unit_bounds[2 * h - 2] * scale + 0.51) + 1;
 }
 
 void fwht_inplace(double* v, int d) {
@@ -528,9 +527,10 @@ tq_status tq_quantize(const tq_config* cfg, const void* x, int64_t n_rows, int64
   fill_dbits(*cfg, a.dbits);
   fill_thr(*cfg->cb, a.thr);
   fill_bins(*cfg->cb, a);
-  if (a.n_bins > tq::kMaxBins8)
-    return fail(TQ_ERR_INVALID_ARG, "%s: the 8-bit codebook's narrowest cell needs %d bins (max %d)", who, a.n_bins,
-                tq::kMaxBins8);
+  const int max_bins = cfg->cb->bits == 4 ? tq::kLutEntries4 : tq::kMaxBins8;
+  if (a.n_bins > max_bins)
+    return fail(TQ_ERR_INVALID_ARG, "%s: the %d-bit codebook's narrowest cell needs %d bins (max %d)", who,
+                cfg->cb->bits, a.n_bins, max_bins);
   hipError_t e = tq::launch_encode(*cfg, a, s);
   if (e != hipSuccess) return hip_fail(e, who);
   return ok();

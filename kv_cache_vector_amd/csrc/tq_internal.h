@@ -24,10 +24,11 @@ struct EncodeArgs {
   int32_t contiguous;      // ld_x == head_dim
   uint32_t dbits[8];       // D: bit c%32 of word c/32 set when D_c = -1
   float thr[128];          // positive N(0,1) cell edges t_1 < t_2 < ... (the edge at 0 is implicit), then +inf
-  float bin_scale;         // 8 bits: bins per unit of |u| (N(0,1) scale)
-  int32_t n_bins;          // 8 bits: number of bins (<= kMaxBins8)
+  float bin_scale;         // 4 and 8 bits: bucket-table bins per unit of |u| (N(0,1) scale)
+  int32_t n_bins;          // 4 and 8 bits: bucket-table entries in use (<= kLutEntries4, kMaxBins8)
 };
 
+constexpr int kLutEntries4 = 256;  // 4-bit bucket table: every index of a saturating byte conversion
 constexpr int kMaxBins8 = 1024;
 
 // Arguments of the decode kernel.

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import synth
-from oracle import Codebook, dequantize, quantize
+from oracle import Codebook, dequantize, hadamard_matrix, quantize
 from tests.parity import assert_band_rate, check_codes, check_decoded_f16, check_decoded_f32, check_norms
 
 torch = pytest.importorskip("torch")
@@ -319,6 +319,62 @@ def test_graph_capture_codec():
         assert torch.equal(codes, ref_codes) and torch.equal(norms, ref_norms) and torch.equal(y, ref_y)
         tq.tq_quantize(qz, x, n_rows, ld, ref_codes, ref_norms)  # eager work between the replays
         torch.cuda.synchronize()
+
+def _bucket_targets(cb, rng):
+    """Rotated coordinates (sqrt(dt) y) on the 4- and 8-bit encoders' bucket-table grid: the bin of |y|/n is
+    the rounded or truncated product |y| kb with 1.6 bins per narrowest cell, so every bin centre, bin edge
+    and the points a quarter bin either side are taken, out past the top cell edge, with random signs."""
+    h = 1 << (cb.bits - 1)
+    pos = np.asarray(cb.unit_bounds, dtype=np.float64)[h:]
+    w = min(pos[0], float(np.diff(pos).min()))
+    bs = float(np.float32(1.6 / w))
+    top = int(math.ceil(pos[-1] * bs)) + 3
+    grid = np.arange(0.0, top, 0.25) / bs
+    return grid * rng.choice([-1.0, 1.0], size=grid.size)
+
+
+def _units_with(targets, dt, rng):
+    """Units z (rows of dt values with sum z^2 = dt) that carry the targets, at most dt/2 per unit and a
+    sum of squares up to 3/4 dt, the other coordinates equal in magnitude and filling the rest."""
+    units, cur = [], []
+    for t in rng.permutation(targets):
+        if len(cur) == dt // 2 or sum(v * v for v in cur) + t * t > 0.75 * dt:
+            units.append(cur)
+            cur = []
+        cur.append(t)
+    units.append(cur)
+    out = np.empty((len(units), dt))
+    for i, u in enumerate(units):
+        rest = dt - len(u)
+        f = math.sqrt((dt - sum(v * v for v in u)) / rest)
+        row = np.concatenate([u, f * rng.choice([-1.0, 1.0], size=rest)])
+        out[i] = rng.permutation(row)
+    return out
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("dt,x_dtype", [(32, tq.TQ_F16), (128, tq.TQ_F16), (32, tq.TQ_F32)])
+def test_bucket_table_bins(bits, dt, x_dtype):
+    """The 4- and 8-bit encoders find a code's magnitude from a table entry chosen by the bin of |y|/n; inputs
+    whose rotated coordinates sit on that bin grid (centres, edges, quarter points) would show an entry off by
+    one as a code mismatch away from every cell edge.  Each unit is x = D H z / sqrt(dt) (H orthonormal), so
+    that the oracle's sqrt(dt) y is z itself (checked here on the CPU first)."""
+    rng = np.random.default_rng(100 + bits + dt)
+    cb = Codebook.build(bits, dt)
+    signs = synth.signs(7, 2, dt)
+    z = np.concatenate([_units_with(_bucket_targets(cb, rng), dt, rng) for _ in range(3)])
+    x = (z @ hadamard_matrix(dt).T) / math.sqrt(dt) * signs.astype(np.float64)
+    hd = 128
+    pad_units = (-len(z)) % (hd // dt)
+    x = np.concatenate([x, x[:pad_units]]).reshape(-1, hd)
+    x_np = x.astype(np.float16 if x_dtype == tq.TQ_F16 else np.float32)
+    orc = quantize(x_np.astype(np.float64), signs, cb, norm_dtype=np.float16)
+    if x_dtype == tq.TQ_F32:
+        assert np.allclose(orc["y_unit"][:len(z)], z, atol=1e-5), "construction: sqrt(dt) y is not z"
+    qz = tq.Quantizer(hd, dt, bits, signs, x_dtype=x_dtype)
+    codes, _ = _run_encode(qz, x_np)
+    check_codes(codes, orc, cb, bits, dt)  # targets at 0, or within 1e-6 of an edge after fp16 rounding, are in band
+
 
 @pytest.fixture(scope="module")
 def qwen_full():
