@@ -194,7 +194,7 @@ def test_edge_cases():
     x[5, ::2] = -2.5
     x[6] = synth.normal_f16(1, 0, hd)
     x[7:] = synth.normal_f16(2, 0, 63 * hd).reshape(63, hd)
-    for bits in (1, 2, 3, 4):
+    for bits in (1, 2, 3, 4, 8):
         signs = synth.signs(9, 2, dt)
         qz = tq.Quantizer(hd, dt, bits, signs)
         cb = Codebook.build(bits, dt)
