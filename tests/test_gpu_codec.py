@@ -239,8 +239,9 @@ def test_deterministic_repeat():
 
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4, 8])
-@pytest.mark.parametrize("dt,records", [(32, False), (128, False), (128, True)])
+@pytest.mark.parametrize("bits,dt,records", [(b, dt, rec) for b in (2, 3, 4, 8)
+                                              for dt, rec in ((32, False), (128, False), (128, True))
+                                              if not (rec and b == 8)])  # records hold 1-4 bit codes
 @pytest.mark.parametrize("pad", [0, 8])
 def test_lone_waves_repeat(bits, dt, records, pad):
     """Regression test for missing wait states in hand-written instruction sequences (a VALU-written
@@ -249,8 +250,6 @@ def test_lone_waves_repeat(bits, dt, records, pad):
     instructions, i.e. when a wave has its SIMD to itself.  64 rows = 256 groups = one workgroup of
     four waves on an otherwise idle GPU; the encode is repeated 64 times and every repeat must give
     the same bytes, and the first must match the oracle outside the edge band."""
-    if records and bits == 8:
-        pytest.skip("the fork's records hold 1-4 bit codes")
     hd, n_rows = 128, 64
     x_np = synth.kv_tensor(7 * bits + dt + pad, 1, 1, 1, n_rows, hd).reshape(n_rows, hd)
     signs = synth.signs(bits + dt, 2, dt)
