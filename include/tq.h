@@ -190,6 +190,10 @@ tq_status tq_qjl_prepare(const tq_config* cfg, const float* S_host, void* params
  *   norms    device, aligned to norm_dtype (TQ_BLOCKS: NULL)
  *   qjl_bits, qjl_rnorm  device (TQ_QJL), otherwise ignored
  * A zero unit stores norm 0 and the codes of idx = 2^(b-1) - 1.
+ * At 4 and 8 bits the encoder finds a code's cell through a uniform bin table
+ * of |y| with 1.6 bins per narrowest cell; a codebook whose edges would need
+ * more than 256 bins at 4 bits or 1024 at 8 (the built-in codebooks need
+ * about 17 and 420) is rejected with TQ_ERR_INVALID_ARG.
  */
 tq_status tq_quantize(const tq_config* cfg, const void* x, int64_t n_rows, int64_t ld_x, uint8_t* codes,
                       void* norms, uint8_t* qjl_bits, void* qjl_rnorm, void* stream);
