@@ -142,6 +142,19 @@ def test_quantize_validation():
         assert _quantize(bad) == U
 
 
+@pytest.mark.parametrize("bits", [4, 8])
+def test_bucket_table_codebook_limit(bits):
+    """A codebook with a cell too narrow for the 4- or 8-bit encoder's bin table (1.6 bins per narrowest
+    cell, at most 256 / 1024 entries) is rejected before any launch: here two neighbouring edges 1e-5
+    apart, which would need about 4e5 bins."""
+    qz = _q(bits=bits)
+    h = 1 << (bits - 1)
+    cb = qz.codebook
+    cb.unit_bounds[h + 1] = cb.unit_bounds[h] + 1e-5
+    assert _quantize(qz) == tq.TQ_ERR_INVALID_ARG
+    assert "narrowest cell" in tq.lib().tq_last_error().decode()
+
+
 def test_blocks_validation():
     """TQ_BLOCKS: fp16 norms only, no QJL, 16-byte aligned records, norms must be NULL."""
     E, U = tq.TQ_ERR_INVALID_ARG, tq.TQ_ERR_UNSUPPORTED
