@@ -784,8 +784,8 @@ def main():
     global CODEBOOK
     CODEBOOK = args.codebook
     if args.gpus != 1:
-        print("bench.py measures one GPU: this quantizer's hot path has no cross-GPU step, and runs on more "
-              "than one GPU are not part of this build (use --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: this quantizer's hot path has no cross-GPU step, so a run over "
+              "several GPUs would only repeat the one-GPU figure per GPU (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import torch

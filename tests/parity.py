@@ -1,6 +1,6 @@
 """Comparison helpers for GPU-vs-oracle parity (test infrastructure).
 
-Tolerances (the spec criteria for this quantizer, read as follows):
+Tolerances (the accuracy criteria this quantizer is held to, read as follows):
   * codes: bit-exact except coordinates whose oracle value sqrt(dt)*y lies
     within BAND = 1e-6 of a cell edge (0 included); there the GPU code must be
     one of the two cells next to that edge.  The in-band fraction is reported.
