@@ -421,6 +421,42 @@ def test_block32_full_size_sampled(qwen_full, kbits, vbits):
         assert_band_rate(stats, cb, literal=True)
 
 
+@pytest.mark.parametrize("bits,dt", [(3, 32), (4, 32), (4, 64)])
+def test_grid_threshold_ragged(bits, dt):
+    """A launch just over four workgroups per compute unit, where the codec grids switch to two groups
+    per lane: 4 x CUs x 256 + 148 groups, so the grid of 4 x CUs workgroups leaves a ragged second
+    iteration of 148 groups.  Codes, norms and decoded rows of the last 600 rows and 20000 others
+    against the oracle."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    hd = 128
+    rows = cus * 256 + 37  # 4 groups per row
+    x_np = synth.normal_f16(11 + bits, dt, rows * hd).reshape(rows, hd)
+    signs = synth.signs(13, 2, dt)
+    qz = tq.Quantizer(hd, dt, bits, signs)
+    cb = Codebook.build(bits, dt)
+    x = torch.from_numpy(x_np).to(DEV)
+    units = rows * (hd // dt)
+    codes = torch.empty(units * qz.code_bytes(), dtype=torch.uint8, device=DEV)
+    norms = torch.empty(units, dtype=torch.float16, device=DEV)
+    tq.tq_quantize(qz, x, rows, hd, codes, norms)
+    y = torch.empty((rows, hd), dtype=torch.float32, device=DEV)
+    tq.tq_dequantize(qz, codes, norms, None, None, rows, y, tq.TQ_F32, hd)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(bits + dt)
+    sample = np.unique(np.concatenate([rng.choice(rows - 600, 20000, replace=False), np.arange(rows - 600, rows)]))
+    upr = hd // dt
+    usample = (sample[:, None] * upr + np.arange(upr)[None, :]).reshape(-1)
+    c = codes.view(units, -1).cpu().numpy()[usample]
+    n = norms.cpu().numpy()[usample]
+    ys = y.cpu().numpy()[sample]
+    orc = quantize(x_np[sample].astype(np.float64), signs, cb)
+    stats = check_codes(c, orc, cb, bits, dt)
+    stats.update(check_norms(n, orc["norms"]))
+    ref = dequantize(c, n, signs, cb)
+    check_decoded_f32(ys, ref.reshape(len(sample), hd), n, dt)
+    assert_band_rate(stats, cb)
+
+
 def test_llama_full_size_sampled():
     """The Llama-3.2-1B-shaped cache at full size (16 x 8 x 2048 vectors of 64 per half, fp16),
     4 bits with a per-vector norm and norm correction, one call per half: codes, norms and
