@@ -454,7 +454,7 @@ __global__ __launch_bounds__(kBlock) void encode_kernel(EncodeArgs a) {
 #pragma unroll
     for (int k = 0; k < BITS; ++k) word[k] = 0u;
     if constexpr (LUT) {
-      const float kb = n > 0.0f ? a.bin_scale / n : 0.0f;
+      const float kb = n > 0.0f ? a.bin_scale * __builtin_amdgcn_rcpf(n) : 0.0f;  // 1 ulp: only picks the bin
       const float top = (float)(a.n_bins - 1);
       code_lut<BITS, 32>(word, v, n, kb, top, lut);
     } else {
@@ -707,7 +707,7 @@ __global__ __launch_bounds__(kBlock) void encode_mfma_kernel(EncodeArgs a) {
 #pragma unroll
       for (int k = 0; k < SEGW; ++k) seg[s][k] = 0u;
       if constexpr (LUT) {
-        const float kb = n > 0.0f ? a.bin_scale / n : 0.0f;
+        const float kb = n > 0.0f ? a.bin_scale * __builtin_amdgcn_rcpf(n) : 0.0f;  // 1 ulp: only picks the bin
         const float top = (float)(a.n_bins - 1);
         code_lut<BITS, 16>(seg[s], yv, n, kb, top, lut);
       } else {
