@@ -563,13 +563,14 @@ __global__ __launch_bounds__(kBlock) void encode_mfma_kernel(EncodeArgs a) {
   // 4 and 8 bits: the next tile's loads go out before this tile's compute and stores (measured
   // faster at 4 and 8 bits, slower at 3)
   constexpr bool PIPE = BITS == 4 || BITS == 8;
-  // Units of 2 or 4 groups at up to 3 bits: the whole H_dt = H_LPU (x) H_32 runs on the MFMA.  A lane's B
-  // operand takes the LPU groups of its unit in turn (K = 32 LPU), each negated where H_LPU[q][j] = -1,
-  // against the same H_32 A operand; D is applied to the inputs as they are staged.  Measured on the
-  // fork's 128-value records: 14 % faster at 3 bits, 5 % slower at 4 bits (whose pipelined loads and
-  // longer bucketing leave less room for the LPU-fold B reads), so 4 and 8 bits keep the cross-lane
-  // stages, as do units of 8 groups (8 times the B reads and 7 sign flips per read).
-  constexpr bool MH = (LPU == 2 || LPU == 4) && BITS <= 3;
+  // Units of 2 groups at up to 3 bits and of 4 groups at up to 2: the whole H_dt = H_LPU (x) H_32 runs on
+  // the MFMA.  A lane's B operand takes the LPU groups of its unit in turn (K = 32 LPU), each negated
+  // where H_LPU[q][j] = -1, against the same H_32 A operand; D is applied to the inputs as they are
+  // staged.  Against the cross-lane stages: 1-2 % faster for 3-bit units of 64 and 1-2 bit units of 128;
+  // for the fork's 3-bit records (units of 128) once 14 % faster, now 8 % slower (0.297-0.307 against
+  // 0.275-0.280 ms in a captured step) since the code chain lost its wait-state nops; 17 % slower at 4
+  // bits.  Units of 8 groups keep the stages too (8 times the B reads and 7 sign flips per read).
+  constexpr bool MH = (LPU == 2 && BITS <= 3) || (LPU == 4 && BITS <= 2);
   const int lane = threadIdx.x & 63;
   const int wave = PIPE ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : threadIdx.x >> 6;
   const int n32 = lane & 31, h = lane >> 5, q = n32 % LPU;
